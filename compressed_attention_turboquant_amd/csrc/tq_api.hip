@@ -1,0 +1,326 @@
+// C ABI: argument checking on the host, then kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "tq_kernels.h"
+
+namespace tq {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Plan {  // split-K plan of one decode call
+  int nsplit;
+  int64_t keys_per_split;
+  int64_t rows_total;
+  size_t off_qrot, off_qproj, off_part, total;
+};
+
+Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
+  Plan p{};
+  const int64_t seqs = (int64_t)B * Hkv;
+  int64_t want = (2048 + seqs - 1) / seqs;
+  const int64_t max_split = (N + 63) / 64;
+  if (want > max_split) want = max_split;
+  if (want < 1) want = 1;
+  p.keys_per_split = (N + want - 1) / want;
+  p.nsplit = (int)((N + p.keys_per_split - 1) / p.keys_per_split);
+  p.rows_total = (int64_t)B * Hq * Tq;
+  size_t o = 0;
+  p.off_qrot = o;  o = align_up(o + (size_t)p.rows_total * d * sizeof(float), 256);
+  p.off_qproj = o; o = align_up(o + (size_t)p.rows_total * d * sizeof(float), 256);
+  p.off_part = o;  o = align_up(o + (size_t)p.nsplit * p.rows_total * (d + 2) * sizeof(float), 256);
+  p.total = o;
+  return p;
+}
+
+tq_status check_layer(const tq_layer* L) {
+  if (!L) return fail(TQ_ERR_INVALID_ARG, "layer is NULL");
+  if (!supported_d(L->d)) return fail(TQ_ERR_UNSUPPORTED, "d must be 64, 128 or 256");
+  if (L->rot != TQ_ROT_HAAR && L->rot != TQ_ROT_HADAMARD)
+    return fail(TQ_ERR_INVALID_ARG, "rot must be TQ_ROT_HAAR or TQ_ROT_HADAMARD");
+  if (L->k_bits < 1 || L->k_bits > 4 || L->v_bits < 1 || L->v_bits > 4)
+    return fail(TQ_ERR_INVALID_ARG, "bit widths must be 1..4");
+  if (L->k_qjl != 0 && L->k_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "k_qjl must be 0 or 1");
+  if (!L->blob) return fail(TQ_ERR_INVALID_ARG, "layer blob is NULL");
+  if (L->blob_bytes < blob_layout(L->d).total) return fail(TQ_ERR_INVALID_ARG, "layer blob too small");
+  return TQ_OK;
+}
+
+tq_status check_cache(const tq_layer* L, int which, const tq_cache* c, const char* name) {
+  const std::string n(name);
+  if (!c) return fail(TQ_ERR_INVALID_ARG, n + " cache is NULL");
+  if (c->seqs < 0) return fail(TQ_ERR_INVALID_ARG, n + ": seqs must be >= 0");
+  if (c->cap <= 0 || c->cap % 8) return fail(TQ_ERR_INVALID_ARG, n + ": cap must be a positive multiple of 8");
+  const bool qjl = which == TQ_KEYS && L->k_qjl;
+  if (!c->idx || !c->norm) return fail(TQ_ERR_INVALID_ARG, n + ": idx and norm are required");
+  if (qjl && (!c->sign || !c->rnorm))
+    return fail(TQ_ERR_INVALID_ARG, n + ": keys with QJL need sign and rnorm");
+  if (!aligned16(c->idx) || !aligned16(c->norm) || (qjl && (!aligned16(c->sign) || !aligned16(c->rnorm))))
+    return fail(TQ_ERR_ALIGNMENT, n + ": cache pointers must be 16-byte aligned");
+  return TQ_OK;
+}
+
+const float* blob_f(const tq_layer* L, size_t off) {
+  return reinterpret_cast<const float*>(static_cast<const unsigned char*>(L->blob) + off);
+}
+const void* blob_p(const tq_layer* L, size_t off) {
+  return static_cast<const unsigned char*>(L->blob) + off;
+}
+
+tq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TQ_OK;
+  return fail(TQ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+}  // namespace
+
+tq_status fail(tq_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+int32_t tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+const char* tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported";
+    case TQ_ERR_ALIGNMENT: return "misaligned pointer";
+    case TQ_ERR_WORKSPACE: return "workspace too small";
+    case TQ_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+size_t tq_layer_blob_bytes(int32_t d) { return supported_d(d) ? blob_layout(d).total : 0; }
+
+tq_status tq_cache_bytes(const tq_layer* layer, int32_t which, int64_t seqs, int64_t cap,
+                         size_t out[4]) {
+  if (!layer || !out) return fail(TQ_ERR_INVALID_ARG, "layer and out are required");
+  if (!supported_d(layer->d)) return fail(TQ_ERR_UNSUPPORTED, "d must be 64, 128 or 256");
+  if (which != TQ_KEYS && which != TQ_VALUES) return fail(TQ_ERR_INVALID_ARG, "which must be TQ_KEYS or TQ_VALUES");
+  if (seqs < 0 || cap <= 0 || cap % 8) return fail(TQ_ERR_INVALID_ARG, "need seqs >= 0 and cap a positive multiple of 8");
+  const int bits = which == TQ_KEYS ? layer->k_bits : layer->v_bits;
+  if (bits < 1 || bits > 4) return fail(TQ_ERR_INVALID_ARG, "bit widths must be 1..4");
+  const bool qjl = which == TQ_KEYS && layer->k_qjl;
+  const size_t tokens = (size_t)seqs * (size_t)cap;
+  out[0] = tokens * layer->d * bits / 8;
+  out[1] = qjl ? tokens * layer->d / 8 : 0;
+  out[2] = tokens * sizeof(float);
+  out[3] = qjl ? tokens * sizeof(float) : 0;
+  return TQ_OK;
+}
+
+tq_status tq_host_tables(int32_t d, int32_t rot, uint64_t seed, double* rotation,
+                         double* projection) {
+  if (!supported_d(d)) return fail(TQ_ERR_UNSUPPORTED, "d must be 64, 128 or 256");
+  if (rot != TQ_ROT_HAAR && rot != TQ_ROT_HADAMARD) return fail(TQ_ERR_INVALID_ARG, "bad rot");
+  if (rotation) make_rotation_f64(d, rot, seed, rotation);
+  if (projection) make_projection_f64(d, seed, projection);
+  return TQ_OK;
+}
+
+tq_status tq_get_codebook(int32_t d, int32_t bits, float* centroids, float* boundaries) {
+  if (!supported_d(d)) return fail(TQ_ERR_UNSUPPORTED, "d must be 64, 128 or 256");
+  if (bits < 1 || bits > 4) return fail(TQ_ERR_INVALID_ARG, "bits must be 1..4");
+  if (!centroids || !boundaries) return fail(TQ_ERR_INVALID_ARG, "outputs are required");
+  lloyd_max_codebook(bits, d, centroids, boundaries);
+  return TQ_OK;
+}
+
+tq_status tq_make_rotation(tq_layer* layer, int32_t d, int32_t rot, uint64_t seed, int32_t k_bits,
+                           int32_t k_qjl, int32_t v_bits, void* dev_blob, size_t blob_bytes,
+                           void* stream) {
+  if (!layer) return fail(TQ_ERR_INVALID_ARG, "layer is NULL");
+  if (!supported_d(d)) return fail(TQ_ERR_UNSUPPORTED, "d must be 64, 128 or 256");
+  if (rot != TQ_ROT_HAAR && rot != TQ_ROT_HADAMARD) return fail(TQ_ERR_INVALID_ARG, "bad rot");
+  if (k_bits < 1 || k_bits > 4 || v_bits < 1 || v_bits > 4)
+    return fail(TQ_ERR_INVALID_ARG, "bit widths must be 1..4");
+  if (k_qjl != 0 && k_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "k_qjl must be 0 or 1");
+  if (!dev_blob) return fail(TQ_ERR_INVALID_ARG, "dev_blob is NULL");
+  if (!aligned16(dev_blob)) return fail(TQ_ERR_ALIGNMENT, "dev_blob must be 16-byte aligned");
+  const BlobLayout BL = blob_layout(d);
+  if (blob_bytes < BL.total) return fail(TQ_ERR_INVALID_ARG, "blob_bytes < tq_layer_blob_bytes(d)");
+  std::vector<unsigned char> image(BL.total);
+  build_blob_image(d, rot, seed, k_bits, v_bits, image.data());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  tq_status s = hip_status(hipMemcpyAsync(dev_blob, image.data(), BL.total, hipMemcpyHostToDevice, st),
+                           "copy layer tables");
+  if (s != TQ_OK) return s;
+  s = hip_status(hipStreamSynchronize(st), "wait for layer tables");
+  if (s != TQ_OK) return s;
+  layer->d = d;
+  layer->rot = rot;
+  layer->k_bits = k_bits;
+  layer->k_qjl = k_qjl;
+  layer->v_bits = v_bits;
+  layer->reserved = 0;
+  layer->seed = seed;
+  layer->blob = dev_blob;
+  layer->blob_bytes = blob_bytes;
+  return TQ_OK;
+}
+
+tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, int32_t dtype,
+                         int64_t seqs, int64_t n, int64_t t0, const tq_cache* cache,
+                         void* stream) {
+  tq_status s = check_layer(layer);
+  if (s != TQ_OK) return s;
+  if (which != TQ_KEYS && which != TQ_VALUES) return fail(TQ_ERR_INVALID_ARG, "which must be TQ_KEYS or TQ_VALUES");
+  if (dtype != TQ_F32 && dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARG, "dtype must be TQ_F32 or TQ_F16");
+  if ((s = check_cache(layer, which, cache, which == TQ_KEYS ? "K" : "V")) != TQ_OK) return s;
+  if (seqs < 0 || n < 0 || t0 < 0) return fail(TQ_ERR_INVALID_ARG, "seqs, n and t0 must be >= 0");
+  if (seqs > cache->seqs) return fail(TQ_ERR_INVALID_ARG, "seqs exceeds the cache's sequence count");
+  if (t0 + n > cache->cap) return fail(TQ_ERR_INVALID_ARG, "t0 + n exceeds the cache capacity");
+  if (seqs > 65535) return fail(TQ_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (n > 0 && seqs > 0) {
+    if (!x) return fail(TQ_ERR_INVALID_ARG, "x is NULL");
+    if (!aligned16(x)) return fail(TQ_ERR_ALIGNMENT, "x must be 16-byte aligned");
+  }
+  const BlobLayout BL = blob_layout(layer->d);
+  QuantizeArgs a{};
+  a.x = x;
+  a.dtype = dtype;
+  a.seqs = seqs;
+  a.n = n;
+  a.t0 = t0;
+  a.cap = cache->cap;
+  a.d = layer->d;
+  a.bits = which == TQ_KEYS ? layer->k_bits : layer->v_bits;
+  a.qjl = which == TQ_KEYS ? layer->k_qjl : 0;
+  a.value_layout = which == TQ_VALUES;
+  a.R = blob_f(layer, BL.rot);
+  a.SR = blob_f(layer, BL.projr);
+  a.cent = blob_f(layer, BL.codebook) + (which == TQ_KEYS ? 0 : 2 * kMaxLevels);
+  a.bnd = a.cent + kMaxLevels;
+  a.rot_hi = blob_p(layer, BL.rot_hi);
+  a.rot_lo = blob_p(layer, BL.rot_lo);
+  a.projr_hi = blob_p(layer, BL.projr_hi);
+  a.projr_lo = blob_p(layer, BL.projr_lo);
+  a.idx = cache->idx;
+  a.sign = cache->sign;
+  a.norm = cache->norm;
+  a.rnorm = cache->rnorm;
+  return hip_status(launch_quantize_ref(a, static_cast<hipStream_t>(stream)), "quantize launch");
+}
+
+size_t tq_decode_workspace_bytes(const tq_layer* layer, int32_t B, int32_t Hq, int32_t Hkv,
+                                 int32_t Tq, int64_t N) {
+  if (!layer || !supported_d(layer->d) || B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || N < 1) return 0;
+  return decode_plan(layer->d, B, Hq, Hkv, Tq, N).total;
+}
+
+tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t Tq, int64_t N, int32_t causal,
+                         const tq_cache* K, const tq_cache* V, float* out, float* scores,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  tq_status s = check_layer(layer);
+  if (s != TQ_OK) return s;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARG, "q_dtype must be TQ_F32 or TQ_F16");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1) return fail(TQ_ERR_INVALID_ARG, "B, Hq, Hkv and Tq must be >= 1");
+  if (Hq % Hkv) return fail(TQ_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  if (N < 1) return fail(TQ_ERR_INVALID_ARG, "N must be >= 1");
+  if (causal != 0 && causal != 1) return fail(TQ_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (causal && Tq > N) return fail(TQ_ERR_INVALID_ARG, "causal decode needs Tq <= N");
+  if ((s = check_cache(layer, TQ_KEYS, K, "K")) != TQ_OK) return s;
+  if ((s = check_cache(layer, TQ_VALUES, V, "V")) != TQ_OK) return s;
+  if (K->seqs != (int64_t)B * Hkv || V->seqs != (int64_t)B * Hkv)
+    return fail(TQ_ERR_INVALID_ARG, "K and V must hold B*Hkv sequences");
+  if (K->cap != V->cap) return fail(TQ_ERR_INVALID_ARG, "K and V must have the same capacity");
+  if (N > K->cap) return fail(TQ_ERR_INVALID_ARG, "N exceeds the cache capacity");
+  if (!q || !out) return fail(TQ_ERR_INVALID_ARG, "q and out are required");
+  if (!aligned16(q) || !aligned16(out) || (scores && !aligned16(scores)))
+    return fail(TQ_ERR_ALIGNMENT, "q, out and scores must be 16-byte aligned");
+  const int rows = Hq / Hkv * Tq;
+  if (!ref_decode_supports(layer->d, rows))
+    return fail(TQ_ERR_UNSUPPORTED, "(Hq/Hkv)*Tq too large for this head dimension");
+  if ((int64_t)B * Hkv > 0x7FFFFFFF) return fail(TQ_ERR_UNSUPPORTED, "too many sequences");
+  const Plan P = decode_plan(layer->d, B, Hq, Hkv, Tq, N);
+  if (P.nsplit > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many key splits");
+  if (!workspace) return fail(TQ_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(TQ_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < P.total) return fail(TQ_ERR_WORKSPACE, "workspace smaller than tq_decode_workspace_bytes");
+
+  const BlobLayout BL = blob_layout(layer->d);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Tq = Tq;
+  a.N = N;
+  a.cap = K->cap;
+  a.causal = causal;
+  a.d = layer->d;
+  a.kb = layer->k_bits;
+  a.vb = layer->v_bits;
+  a.qjl = layer->k_qjl;
+  a.R = blob_f(layer, BL.rot);
+  a.S = blob_f(layer, BL.proj);
+  a.cb = blob_f(layer, BL.codebook);
+  a.kidx = K->idx;
+  a.ksign = K->sign;
+  a.knorm = K->norm;
+  a.krnorm = K->rnorm;
+  a.vidx = V->idx;
+  a.vnorm = V->norm;
+  a.out = out;
+  a.scores = scores;
+  a.q_rot = reinterpret_cast<float*>(ws + P.off_qrot);
+  a.q_proj = reinterpret_cast<float*>(ws + P.off_qproj);
+  a.part = reinterpret_cast<float*>(ws + P.off_part);
+  a.nsplit = P.nsplit;
+  a.keys_per_split = P.keys_per_split;
+  return hip_status(launch_decode_ref(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,
+                        void* out, int32_t out_dtype, void* stream) {
+  tq_status s = check_layer(layer);
+  if (s != TQ_OK) return s;
+  if (which != TQ_KEYS && which != TQ_VALUES) return fail(TQ_ERR_INVALID_ARG, "which must be TQ_KEYS or TQ_VALUES");
+  if (out_dtype != TQ_F32 && out_dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARG, "out_dtype must be TQ_F32 or TQ_F16");
+  if (!cache || !cache->idx || !cache->norm) return fail(TQ_ERR_INVALID_ARG, "cache idx and norm are required");
+  if (cache->seqs < 0 || cache->cap <= 0 || cache->cap % 8)
+    return fail(TQ_ERR_INVALID_ARG, "cache needs seqs >= 0 and cap a positive multiple of 8");
+  if (!aligned16(cache->idx) || !aligned16(cache->norm)) return fail(TQ_ERR_ALIGNMENT, "cache pointers must be 16-byte aligned");
+  if (n < 0 || n > cache->cap) return fail(TQ_ERR_INVALID_ARG, "n must be in [0, cap]");
+  if (cache->seqs > 65535) return fail(TQ_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (n > 0 && cache->seqs > 0) {
+    if (!out) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
+    if (!aligned16(out)) return fail(TQ_ERR_ALIGNMENT, "out must be 16-byte aligned");
+  }
+  const BlobLayout BL = blob_layout(layer->d);
+  DequantArgs a{};
+  a.idx = cache->idx;
+  a.norm = cache->norm;
+  a.seqs = cache->seqs;
+  a.n = n;
+  a.cap = cache->cap;
+  a.d = layer->d;
+  a.bits = which == TQ_KEYS ? layer->k_bits : layer->v_bits;
+  a.value_layout = which == TQ_VALUES;
+  a.R = blob_f(layer, BL.rot);
+  a.cent = blob_f(layer, BL.codebook) + (which == TQ_KEYS ? 0 : 2 * kMaxLevels);
+  a.out = out;
+  a.out_dtype = out_dtype;
+  return hip_status(launch_dequant_ref(a, static_cast<hipStream_t>(stream)), "dequantize launch");
+}
+
+}  // extern "C"

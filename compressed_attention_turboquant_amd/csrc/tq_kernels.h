@@ -1,0 +1,52 @@
+// Kernel launch interfaces (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+struct QuantizeArgs {
+  const void* x;
+  int dtype;
+  int64_t seqs, n, t0, cap;
+  int d, bits, qjl, value_layout;
+  const float *R, *SR, *cent, *bnd;  // rotation, S R^T, codebook
+  const void *rot_hi, *rot_lo, *projr_hi, *projr_lo;  // half splits for MFMA
+  uint8_t *idx, *sign;
+  float *norm, *rnorm;
+};
+
+struct DecodeArgs {
+  const void* q;
+  int q_dtype;
+  int B, Hq, Hkv, Tq;
+  int64_t N, cap;
+  int causal, d, kb, vb, qjl;
+  const float *R, *S, *cb;
+  const uint8_t *kidx, *ksign, *vidx;
+  const float *knorm, *krnorm, *vnorm;
+  float *out, *scores;
+  // workspace pieces
+  float *q_rot, *q_proj, *part;
+  int nsplit;
+  int64_t keys_per_split;
+};
+
+struct DequantArgs {
+  const uint8_t* idx;
+  const float* norm;
+  int64_t seqs, n, cap;
+  int d, bits, value_layout;
+  const float *R, *cent;
+  void* out;
+  int out_dtype;
+};
+
+hipError_t launch_quantize_ref(const QuantizeArgs& a, hipStream_t st);
+hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_dequant_ref(const DequantArgs& a, hipStream_t st);
+bool ref_decode_supports(int d, int rows);
+
+}  // namespace tq

@@ -1,0 +1,186 @@
+/*
+ * tq.h -- C ABI of the TurboQuant KV-cache library for AMD Instinct MI355X (gfx950).
+ *
+ * The library compresses attention keys and values with TurboQuant and runs
+ * decode attention directly on the compressed cache.  Sources of the method
+ * (titles of the pages it is defined on):
+ *   [Mobilint] "TurboQuant explained: near-optimal KV cache compression and why
+ *              the theory breaks down in practice" (Mobilint blog);
+ *   [cuTile]   function listing of DevTechJr/turboquant_cutile (codehub.bot);
+ *   [tq-kv]    docs.rs page of the tq-kv crate;
+ *   [ginkgoq]  "Limits And Assumptions" (ginkgoq TurboQuant docs).
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  Ownership   The library never allocates device memory.  Every device buffer
+ *              (rotation blob, packed cache, queries, outputs, workspace) is
+ *              owned by the caller and must stay alive until the stream work
+ *              that uses it has finished.  Only tq_make_rotation copies host
+ *              data to the device (the layer tables, once, at set-up).
+ *  Streams     `stream` is a hipStream_t passed as void* (NULL = the default
+ *              stream).  Compute calls only enqueue work: results are valid in
+ *              stream order, and no call synchronises except tq_make_rotation.
+ *  Errors      Every argument is validated on the host before any HIP call; on
+ *              an invalid argument nothing is written and nothing is enqueued.
+ *              tq_last_error() returns a message for the calling thread's most
+ *              recent failure.  A failed kernel launch returns TQ_ERR_HIP.
+ *              No C++ exception or abort crosses this boundary.
+ *  Alignment   Device pointers must be 16-byte aligned (TQ_ERR_ALIGNMENT).
+ *  Threads     Calls hold no global mutable state and may be made from several
+ *              threads; calls that write the same buffers must be ordered by
+ *              the caller.
+ *
+ * Data layout in device memory
+ * ----------------------------
+ *  A "sequence" is one (batch, KV head) pair; a layer with B batches and Hkv
+ *  KV heads has seqs = B*Hkv sequences, sequence s = b*Hkv + h.  Each holds up
+ *  to `cap` tokens (cap a multiple of 8).  Per token t of sequence s the cache
+ *  holds (the pages fix what is stored, not its layout; the layout below is
+ *  this library's contract):
+ *    idx   the b-bit codes.  A "stream" is little-endian: a b-bit code at
+ *          stream position p occupies bits [p*b, p*b+b), LSB first, and bit k
+ *          of a stream is bit (k mod 8) of byte k/8.
+ *            keys:   one stream per token, positions = coordinates 0..d-1,
+ *                    starting at byte (s*cap + t) * d*b/8;
+ *            values: tokens grouped in tiles of 8; one stream per tile with
+ *                    position 8*j + (t mod 8) for coordinate j (coordinate-
+ *                    major tile), tile k starting at byte (s*cap/8 + k) * d*b.
+ *    sign  keys with QJL: one stream of d sign bits per token (bit 1 means
+ *          sign +1), starting at byte (s*cap + t) * d/8.
+ *    norm  float32 ||x||_2 at index s*cap + t.
+ *    rnorm keys with QJL: float32 residual norm ||r||_2 at index s*cap + t.
+ *  Queries and outputs are [B][Hq][Tq][d]; query head h reads KV head
+ *  h / (Hq/Hkv).  Inputs to quantize are [seqs][n][d] in the given dtype.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = 1, /* a size, count, enum or pointer is out of range */
+  TQ_ERR_UNSUPPORTED = 2, /* valid in principle, not implemented (e.g. d=96) */
+  TQ_ERR_ALIGNMENT = 3,   /* a device pointer is not 16-byte aligned */
+  TQ_ERR_WORKSPACE = 4,   /* workspace smaller than tq_decode_workspace_bytes */
+  TQ_ERR_HIP = 5          /* the HIP runtime reported an error */
+} tq_status;
+
+enum { TQ_ROT_HAAR = 0, TQ_ROT_HADAMARD = 1 };
+enum { TQ_F32 = 0, TQ_F16 = 1 };
+enum { TQ_KEYS = 0, TQ_VALUES = 1 };
+
+/* One layer's codec: filled by tq_make_rotation, plain data, owned by the caller. */
+typedef struct tq_layer {
+  int32_t d;       /* head dimension: 64, 128 or 256 */
+  int32_t rot;     /* TQ_ROT_HAAR or TQ_ROT_HADAMARD */
+  int32_t k_bits;  /* MSE bits per key coordinate, 1..4 */
+  int32_t k_qjl;   /* 1: keys also store QJL sign bits and the residual norm */
+  int32_t v_bits;  /* MSE bits per value coordinate, 1..4 */
+  int32_t reserved;
+  uint64_t seed;   /* seed of the rotation, projection and sign streams */
+  void* blob;      /* device: rotation, projection, signs and codebooks */
+  size_t blob_bytes;
+} tq_layer;
+
+/* A compressed key or value cache for `seqs` sequences of capacity `cap`.
+ * All pointers are device pointers owned by the caller. */
+typedef struct tq_cache {
+  uint8_t* idx;   /* codes, seqs*cap*d*bits/8 bytes */
+  uint8_t* sign;  /* keys with QJL: seqs*cap*d/8 bytes; otherwise NULL */
+  float* norm;    /* seqs*cap floats */
+  float* rnorm;   /* keys with QJL: seqs*cap floats; otherwise NULL */
+  int64_t seqs;
+  int64_t cap;    /* tokens per sequence, a positive multiple of 8 */
+} tq_cache;
+
+int32_t tq_abi_version(void);
+const char* tq_status_string(tq_status s);
+/* Message describing the calling thread's most recent failure ("" if none). */
+const char* tq_last_error(void);
+
+/* Bytes of device memory the layer blob needs for head dimension d (0 if d is unsupported). */
+size_t tq_layer_blob_bytes(int32_t d);
+
+/* Bytes of each cache array for `which` (TQ_KEYS/TQ_VALUES): out[0]=idx,
+ * out[1]=sign, out[2]=norm, out[3]=rnorm (0 where the array is not used). */
+tq_status tq_cache_bytes(const tq_layer* layer, int32_t which, int64_t seqs, int64_t cap,
+                         size_t out[4]);
+
+/* Set up a layer: draws the Haar rotation Pi (QR of a seeded Gaussian with a
+ * positive R diagonal; [cuTile] "Haar-distributed random orthogonal matrix via
+ * QR of Gaussian") or the randomized Hadamard H*D ([Mobilint] "How JL Matrices
+ * Evolved"), the QJL projection S with i.i.d. N(0,1) entries ([Mobilint]
+ * "Two-Stage Approach", stage 2), and the Lloyd-Max codebooks for the N(0,1/d)
+ * coordinate law ([Mobilint] "Designing the Optimal Codebook Without Data";
+ * [cuTile] "Returns (centroids, boundaries) as sorted float32").  The random
+ * matrices come from the SplitMix64 stream with Box-Muller normals, tags
+ * 0 (Pi), 1 (S), 2 (D).  Builds the tables on the host in float64, copies them
+ * into `dev_blob` (tq_layer_blob_bytes(d) bytes, caller-owned) on `stream` and
+ * waits for the copy.  Fills *layer. */
+tq_status tq_make_rotation(tq_layer* layer, int32_t d, int32_t rot, uint64_t seed,
+                           int32_t k_bits, int32_t k_qjl, int32_t v_bits,
+                           void* dev_blob, size_t blob_bytes, void* stream);
+
+/* Host-only: the float64 rotation matrix R (Pi or H*D, row-major, y = R u) and
+ * projection S (row-major) the layer with this (d, rot, seed) uses.  Either
+ * output may be NULL.  No GPU needed. */
+tq_status tq_host_tables(int32_t d, int32_t rot, uint64_t seed, double* rotation,
+                         double* projection);
+
+/* Host-only: the float32 codebook for `bits` at head dimension d: 2^bits sorted
+ * centroids and 2^bits-1 sorted boundaries ([cuTile] codebook function). */
+tq_status tq_get_codebook(int32_t d, int32_t bits, float* centroids, float* boundaries);
+
+/* Compress tokens t0..t0+n-1 of every sequence into `cache` ([cuTile] "K:
+ * (seq_k, head_dim) -> compressed dict" and "V: ... MSE only, no QJL";
+ * [Mobilint] "Two-Stage Approach").  Per token: store n = ||x||; rotate
+ * u = x/n (u = 0 when n = 0); code each coordinate as #{i : beta_i < y_j};
+ * bit-pack.  Keys with QJL also store gamma = ||r|| and sign(S r) for the
+ * residual r = u - R^T c[idx] (sign(0) = +1).  x is [seqs][n][d] of `dtype`
+ * (TQ_F32 or TQ_F16), device memory.  Tokens outside [t0, t0+n) are left as
+ * they were, including the other tokens that share a value tile. */
+tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, int32_t dtype,
+                         int64_t seqs, int64_t n, int64_t t0, const tq_cache* cache,
+                         void* stream);
+
+/* Workspace bytes tq_attn_decode needs for this shape. */
+size_t tq_decode_workspace_bytes(const tq_layer* layer, int32_t B, int32_t Hq, int32_t Hkv,
+                                 int32_t Tq, int64_t N);
+
+/* Decode attention on the compressed cache ([cuTile] "Asymmetric estimator:
+ * term1 (MSE dot) + term2 (QJL correction)", "Full pipeline: scores -> softmax
+ * -> weighted V sum", "Fused attention + online softmax, decompresses ... V
+ * on-chip"; [Mobilint] "Two-Stage Approach": <q, x~> = <Pi q, y~>).  For each
+ * query row the query is rotated once (R q, S q); key t scores
+ *   s_t = n_t * (<R q, c_k[idx_t]> + gamma_t*sqrt(pi/2)/d * <S q, sigma_t>) / sqrt(d);
+ * softmax over keys 0..N-1 (with `causal`, query i of Tq sees keys
+ * t <= N - Tq + i); the values n_v * c_v[idx_v] are summed in the rotated
+ * domain and the sum is un-rotated once per query row.
+ * q: [B][Hq][Tq][d] of q_dtype; out: [B][Hq][Tq][d] float32; scores: NULL or
+ * [B][Hq][Tq][N] float32 (masked keys get -inf).  K and V hold B*Hkv
+ * sequences with at least N tokens.  `workspace`: device scratch of at least
+ * tq_decode_workspace_bytes(...) bytes, 256-byte aligned. */
+tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t Tq, int64_t N, int32_t causal,
+                         const tq_cache* K, const tq_cache* V, float* out, float* scores,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Reconstruct tokens 0..n-1 of every sequence: x_hat = n * R^T c[idx]
+ * ([cuTile] "indices -> centroids -> un-rotate -> rescale").  out is
+ * [seqs][n][d] of out_dtype (TQ_F32 or TQ_F16). */
+tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,
+                        void* out, int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

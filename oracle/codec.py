@@ -103,38 +103,30 @@ def unpack_stream(data, bits: int, count: int) -> np.ndarray:
 
 def pack_key_codes(idx, bits: int) -> np.ndarray:
     """[rows, d] codes -> [rows, d*b/8] bytes, one stream per token."""
-    idx = np.asarray(idx)
-    return np.stack([pack_stream(row, bits) for row in idx]) if len(idx) else \
-        np.zeros((0, idx.shape[1] * bits // 8), np.uint8)
+    idx = np.asarray(idx, dtype=np.int64)
+    rows, d = idx.shape
+    return pack_stream(idx.reshape(-1), bits).reshape(rows, d * bits // 8)
 
 
 def unpack_key_codes(data, bits: int, d: int) -> np.ndarray:
     data = np.asarray(data, dtype=np.uint8).reshape(-1, d * bits // 8)
-    return np.stack([unpack_stream(row, bits, d) for row in data]) if len(data) else \
-        np.zeros((0, d), np.int64)
+    return unpack_stream(data, bits, data.shape[0] * d).reshape(-1, d)
 
 
 def pack_value_codes(idx, bits: int) -> np.ndarray:
     """[S, cap, d] codes -> [S, cap/8, d*b] bytes, 8-token tiles stored coordinate-major."""
-    idx = np.asarray(idx)
+    idx = np.asarray(idx, dtype=np.int64)
     S, cap, d = idx.shape
     if cap % 8:
         raise ValueError("capacity must be a multiple of 8")
-    out = np.empty((S, cap // 8, d * bits), dtype=np.uint8)
-    for s in range(S):
-        for k in range(cap // 8):
-            tile = idx[s, 8 * k: 8 * k + 8, :]          # [8 tokens, d]
-            out[s, k] = pack_stream(tile.T, bits)        # position 8*j + t
-    return out
+    tiles = idx.reshape(S, cap // 8, 8, d).transpose(0, 1, 3, 2)   # [S, tile, j, t]: position 8*j + t
+    return pack_stream(tiles.reshape(-1), bits).reshape(S, cap // 8, d * bits)
 
 
 def unpack_value_codes(data, bits: int, S: int, cap: int, d: int) -> np.ndarray:
-    data = np.asarray(data, dtype=np.uint8).reshape(S, cap // 8, d * bits)
-    out = np.empty((S, cap, d), dtype=np.int64)
-    for s in range(S):
-        for k in range(cap // 8):
-            out[s, 8 * k: 8 * k + 8, :] = unpack_stream(data[s, k], bits, 8 * d).reshape(d, 8).T
-    return out
+    data = np.asarray(data, dtype=np.uint8).reshape(-1)
+    tiles = unpack_stream(data, bits, S * cap * d).reshape(S, cap // 8, d, 8)
+    return tiles.transpose(0, 1, 3, 2).reshape(S, cap, d)
 
 
 # --------------------------------------------------------- whole tensors --

@@ -1,0 +1,239 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Sizes here are the five layer configurations cut down (fewer batches and
+tokens, ragged token counts that end inside a tile) so the oracle finishes in
+seconds; tests/test_gpu_fullsize.py covers the full sizes on sampled outputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from compressed_attention_turboquant_amd import binding as B
+from oracle import attention, codec
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = {
+    "C1": workloads.CONFIGS["C1"],
+    "C2": workloads.CONFIGS["C2"].with_(N=1003),
+    "C3": workloads.CONFIGS["C3"].with_(B=1, N=777),
+    "C4": workloads.CONFIGS["C4"].with_(B=2, N=600),
+    "C5": workloads.CONFIGS["C5"].with_(B=1, N=515),
+}
+
+
+def _kv(cfg, which, seed=0):
+    x = workloads.kv_numpy(cfg, seed, which)
+    return x.reshape(cfg.B * cfg.Hkv, cfg.N, cfg.d)
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_quantize_keys_parity(name):
+    cfg = REDUCED[name]
+    H.log(f"[quantize K] {name} {cfg}")
+    x = _kv(cfg, "K")
+    S, n, d = x.shape
+    layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, B.TQ_KEYS)
+    rows = np.array([s * cap + t for s in range(S) for t in range(n)])
+    gidx = H.gpu_codes_key(cache, S, cap, d, cfg.k_bits, rows)
+    flipped = H.compare_codes(gidx, enc, ol.bk, f"{name} K codes")
+    assert flipped.mean() < 0.01
+    np.testing.assert_allclose(cache["norm"].cpu().numpy()[rows], enc["norm"], rtol=2e-6)
+    # packed bytes are identical for every row without a band difference
+    rb = d * cfg.k_bits // 8
+    gbytes = cache["idx"].cpu().numpy().reshape(S * cap, rb)[rows]
+    obytes = codec.pack_key_codes(enc["idx"], cfg.k_bits)
+    assert np.array_equal(gbytes[~flipped], obytes[~flipped])
+    if cfg.k_qjl:
+        gs = H.gpu_signs(cache, S, cap, d, rows)
+        H.compare_key_extras(gs, cache["rnorm"].cpu().numpy()[rows], enc, flipped, f"{name} K")
+    H.log(f"  rows={len(rows)} band-flipped rows={int(flipped.sum())}")
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_quantize_values_parity(name):
+    cfg = REDUCED[name]
+    H.log(f"[quantize V] {name}")
+    x = _kv(cfg, "V")
+    S, n, d = x.shape
+    layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, B.TQ_VALUES)
+    rows = np.array([s * cap + t for s in range(S) for t in range(n)])
+    gidx = H.gpu_codes_value(cache, S, cap, d, cfg.v_bits)[rows]
+    flipped = H.compare_codes(gidx, enc, ol.bv, f"{name} V codes")
+    assert flipped.mean() < 0.01
+    np.testing.assert_allclose(cache["norm"].cpu().numpy()[rows], enc["norm"], rtol=2e-6)
+
+
+def _decode_both(cfg, packed, q_np, N, want_scores=True):
+    S = cfg.B * cfg.Hkv
+    cap = (N + 7) // 8 * 8
+    layer = H.gpu_layer(cfg)
+    ol = H.OracleLayer(cfg)
+    K, V = H.upload_packed(layer, cfg, packed, S, cap)
+    q = torch.from_numpy(q_np).cuda()
+    out, scores = B.attn_decode(layer, q, K, V, N, cfg.Hkv, cfg.causal, want_scores=want_scores)
+    torch.cuda.synchronize()
+    cache = attention.unpack_cache(packed, cfg.B, cfg.Hkv, cap, cfg.d, cfg.k_bits, cfg.v_bits, cfg.k_qjl)
+    ref_out, ref_scores = attention.decode(q_np, ol.R, ol.S, ol.ck, ol.cv, cache, N, cfg.causal)
+    return out.cpu().numpy(), (scores.cpu().numpy() if scores is not None else None), \
+        ref_out, ref_scores, cache, ol
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_decode_on_random_cache(name):
+    """Decode alone: any byte pattern is a valid packed cache, so both sides read
+    the same seeded random cache and must agree on every score and output."""
+    cfg = REDUCED[name]
+    N = cfg.N
+    cap = (N + 7) // 8 * 8
+    H.log(f"[decode random cache] {name} N={N}")
+    packed = workloads.random_packed_numpy(cfg, cfg.B * cfg.Hkv, cap, seed=1)
+    q = workloads.q_numpy(cfg, seed=1)
+    out, scores, ref_out, ref_scores, cache, ol = _decode_both(cfg, packed, q, N)
+    scale = H.score_scale(q, ol.R, ol.S, ol.ck, cache, N, cfg.G, cfg.k_qjl)
+    rel = H.compare_scores(scores, ref_scores, scale, name)
+    err = H.compare_out(out, ref_out, name)
+    H.log(f"  score rel err {rel:.2e}  out abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_end_to_end_from_raw_inputs(name):
+    """Quantize K and V and decode on the GPU; the oracle encodes the same raw
+    inputs itself.  Keys whose code differs inside the boundary band are left
+    out of the score comparison; the output must still be within 2e-3."""
+    cfg = REDUCED[name]
+    H.log(f"[end to end] {name}")
+    xk, xv = _kv(cfg, "K", seed=2), _kv(cfg, "V", seed=2)
+    S, N, d = xk.shape
+    layer = H.gpu_layer(cfg)
+    ol = H.OracleLayer(cfg)
+    _, _, K, ek, cap = H.run_quantize_both(cfg, xk, B.TQ_KEYS, layer, ol)
+    _, _, V, ev, _ = H.run_quantize_both(cfg, xv, B.TQ_VALUES, layer, ol)
+    rows = np.array([s * cap + t for s in range(S) for t in range(N)])
+    kflip = H.compare_codes(H.gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), ek, ol.bk, "K")
+    q_np = workloads.q_numpy(cfg, seed=2)
+    q = torch.from_numpy(q_np).cuda()
+    out, scores = B.attn_decode(layer, q, K, V, N, cfg.Hkv, cfg.causal, want_scores=True)
+    torch.cuda.synchronize()
+    pk = {"k_idx": codec.pack_key_codes(ek["idx"], cfg.k_bits),
+          "k_norm": ek["norm"].astype(np.float32),
+          "v_idx": codec.pack_value_codes(ev["idx"].reshape(S, N, d), cfg.v_bits) if N % 8 == 0 else None}
+    cache = {"k_idx": ek["idx"].reshape(cfg.B, cfg.Hkv, N, d), "k_norm": ek["norm"].reshape(cfg.B, cfg.Hkv, N),
+             "v_idx": ev["idx"].reshape(cfg.B, cfg.Hkv, N, d), "v_norm": ev["norm"].reshape(cfg.B, cfg.Hkv, N)}
+    if cfg.k_qjl:
+        cache["k_sign"] = ek["sign"].reshape(cfg.B, cfg.Hkv, N, d)
+        cache["k_rnorm"] = ek["rnorm"].reshape(cfg.B, cfg.Hkv, N)
+    ref_out, ref_scores = attention.decode(q_np, ol.R, ol.S, ol.ck, ol.cv, cache, N, cfg.causal)
+    scale = H.score_scale(q_np, ol.R, ol.S, ol.ck, cache, N, cfg.G, cfg.k_qjl)
+    keep = (~kflip).reshape(cfg.B, cfg.Hkv, N)
+    key_mask = np.repeat(keep, cfg.G, axis=1)[:, :, None, :]
+    rel = H.compare_scores(scores.cpu().numpy(), ref_scores, scale, name, key_mask)
+    err = H.compare_out(out.cpu().numpy(), ref_out, name)
+    H.log(f"  flipped keys {int(kflip.sum())}  score rel {rel:.2e}  out abs {err:.2e}")
+
+
+@pytest.mark.parametrize("name", ["C1", "C3", "C5"])
+@pytest.mark.parametrize("which", [B.TQ_KEYS, B.TQ_VALUES])
+def test_dequantize_parity(name, which):
+    cfg = REDUCED[name]
+    H.log(f"[dequantize] {name} which={which}")
+    x = _kv(cfg, "K" if which == B.TQ_KEYS else "V", seed=3)
+    S, n, d = x.shape
+    layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, which)
+    got = B.dequantize(layer, which, cache, n).cpu().numpy().reshape(-1, d)
+    c, bnd = (ol.ck, ol.bk) if which == B.TQ_KEYS else (ol.cv, ol.bv)
+    ref = codec.reconstruct_mse(enc["idx"], enc["norm"], ol.R, c)
+    rows = np.array([s * cap + t for s in range(S) for t in range(n)])
+    gidx = (H.gpu_codes_key(cache, S, cap, d, cfg.k_bits, rows) if which == B.TQ_KEYS
+            else H.gpu_codes_value(cache, S, cap, d, cfg.v_bits)[rows])
+    flipped = H.compare_codes(gidx, enc, bnd, "codes")
+    scale = enc["norm"][:, None]
+    err = np.abs(got - ref) / np.maximum(scale, 1e-30)
+    assert err[~flipped].max() < 2e-6
+    half = B.dequantize(layer, which, cache, n, out_dtype=torch.float16).cpu().numpy().reshape(-1, d)
+    np.testing.assert_allclose(half[~flipped], got[~flipped], rtol=2e-3, atol=1e-3)
+
+
+def test_append_in_pieces_matches_one_call():
+    """Quantizing tokens in several calls (starting inside a value tile) gives
+    the same bytes as one call, and leaves other tokens untouched."""
+    cfg = workloads.CONFIGS["C2"].with_(N=40)
+    layer = H.gpu_layer(cfg)
+    x = torch.from_numpy(_kv(cfg, "V", seed=4)).cuda()
+    S = x.shape[0]
+    for which in (B.TQ_KEYS, B.TQ_VALUES):
+        one = B.Cache(layer, which, S, 48)
+        B.quantize_kv(layer, which, x, one)
+        parts = B.Cache(layer, which, S, 48)
+        for a, b in ((0, 13), (13, 14), (14, 27), (27, 40)):
+            B.quantize_kv(layer, which, x[:, a:b].contiguous(), parts, t0=a)
+        torch.cuda.synchronize()
+        for k in ("idx", "norm", "sign", "rnorm"):
+            if one[k] is not None:
+                assert torch.equal(one[k], parts[k]), (which, k)
+        # a single-token append into the middle of a tile changes only that token
+        before = parts["idx"].clone()
+        B.quantize_kv(layer, which, torch.zeros_like(x[:, 21:22]), parts, t0=21)
+        torch.cuda.synchronize()
+        d = cfg.d
+        if which == B.TQ_VALUES:
+            g0 = codec.unpack_value_codes(before.cpu().numpy(), cfg.v_bits, S, 48, d)
+            g1 = codec.unpack_value_codes(parts["idx"].cpu().numpy(), cfg.v_bits, S, 48, d)
+            changed = (g0 != g1).any(axis=2)
+            assert not changed[:, :21].any() and not changed[:, 22:40].any()
+            assert (g1[:, 21] == (1 << (cfg.v_bits - 1)) - 1).all()  # zero row: lower-middle code
+        assert torch.equal(parts["norm"].view(S, 48)[:, 21], torch.zeros(S, device="cuda"))
+
+
+def test_edge_shapes_single_key_zero_rows_and_head_dims():
+    """N=1, zero input rows, d=64 and d=256 with 1- and 4-bit codes, Hadamard
+    with QJL, fp32 inputs, and a causal chunk as long as the cache."""
+    cases = [
+        workloads.CONFIGS["C1"].with_(N=1),
+        workloads.CONFIGS["C2"].with_(d=64, N=37, k_bits=1, v_bits=4, Hq=8, Hkv=2),
+        workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=1, N=21, k_qjl=1, k_bits=3, v_bits=1),
+        workloads.CONFIGS["C4"].with_(B=1, N=16, Tq=16),
+        workloads.CONFIGS["C1"].with_(N=9, Tq=3, causal=1, Hq=2, Hkv=1, rot="hadamard"),
+    ]
+    for cfg in cases:
+        H.log(f"[edge] {cfg}")
+        xk, xv = _kv(cfg, "K", seed=5), _kv(cfg, "V", seed=5)
+        xk[:, 0] = 0  # a zero key row
+        layer = H.gpu_layer(cfg)
+        ol = H.OracleLayer(cfg)
+        _, _, K, ek, cap = H.run_quantize_both(cfg, xk, B.TQ_KEYS, layer, ol)
+        _, _, V, ev, _ = H.run_quantize_both(cfg, xv, B.TQ_VALUES, layer, ol)
+        S, N, d = xk.shape
+        rows = np.array([s * cap + t for s in range(S) for t in range(N)])
+        kflip = H.compare_codes(H.gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), ek, ol.bk, "K")
+        assert K["norm"].view(S, cap)[:, 0].abs().max().item() == 0.0
+        q_np = workloads.q_numpy(cfg, seed=5)
+        out, scores = B.attn_decode(layer, torch.from_numpy(q_np).cuda(), K, V, N, cfg.Hkv,
+                                    cfg.causal, want_scores=True)
+        cache = {"k_idx": ek["idx"].reshape(cfg.B, cfg.Hkv, N, d), "k_norm": ek["norm"].reshape(cfg.B, cfg.Hkv, N),
+                 "v_idx": ev["idx"].reshape(cfg.B, cfg.Hkv, N, d), "v_norm": ev["norm"].reshape(cfg.B, cfg.Hkv, N)}
+        if cfg.k_qjl:
+            cache["k_sign"] = ek["sign"].reshape(cfg.B, cfg.Hkv, N, d)
+            cache["k_rnorm"] = ek["rnorm"].reshape(cfg.B, cfg.Hkv, N)
+        ref_out, ref_scores = attention.decode(q_np, ol.R, ol.S, ol.ck, ol.cv, cache, N, cfg.causal)
+        scale = H.score_scale(q_np, ol.R, ol.S, ol.ck, cache, N, cfg.G, cfg.k_qjl)
+        keep = np.repeat((~kflip).reshape(cfg.B, cfg.Hkv, N), cfg.G, axis=1)[:, :, None, :]
+        H.compare_scores(scores.cpu().numpy(), ref_scores, np.maximum(scale, 1e-30), str(cfg), keep)
+        H.compare_out(out.cpu().numpy(), ref_out, str(cfg))
+
+
+def test_decode_is_deterministic():
+    cfg = REDUCED["C2"]
+    cap = (cfg.N + 7) // 8 * 8
+    packed = workloads.random_packed_numpy(cfg, cfg.B * cfg.Hkv, cap, seed=6)
+    layer = H.gpu_layer(cfg)
+    K, V = H.upload_packed(layer, cfg, packed, cfg.B * cfg.Hkv, cap)
+    q = torch.from_numpy(workloads.q_numpy(cfg, seed=6)).cuda()
+    a, _ = B.attn_decode(layer, q, K, V, cfg.N, cfg.Hkv)
+    b, _ = B.attn_decode(layer, q, K, V, cfg.N, cfg.Hkv)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
