@@ -15,25 +15,41 @@ thread_local std::string g_last_error;
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Plan {  // split-K plan of one decode call
+  bool mfma;     // matrix-core kernel (else the reference kernels)
   int nsplit;
   int64_t keys_per_split;
   int64_t rows_total;
-  size_t off_qrot, off_qproj, off_part, total;
+  size_t off_qrot, off_qproj, off_rowc, off_part, total;
 };
 
 Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
   Plan p{};
   const int64_t seqs = (int64_t)B * Hkv;
-  int64_t want = (2048 + seqs - 1) / seqs;
-  const int64_t max_split = (N + 63) / 64;
-  if (want > max_split) want = max_split;
-  if (want < 1) want = 1;
-  p.keys_per_split = (N + want - 1) / want;
-  p.nsplit = (int)((N + p.keys_per_split - 1) / p.keys_per_split);
+  p.mfma = mfma_decode_supports(d, Hq / Hkv * Tq);
+  if (p.mfma) {
+    // Work in blocks of 32 keys; aim for ~2048 workgroups (8 per CU) while
+    // giving each of a workgroup's 4 waves at least 4 blocks.
+    const int64_t blocks = (N + 31) / 32;
+    int64_t want = (2048 + seqs - 1) / seqs;
+    const int64_t max_split = (blocks + 15) / 16;
+    if (want > max_split) want = max_split;
+    if (want < 1) want = 1;
+    const int64_t bps = (blocks + want - 1) / want;
+    p.keys_per_split = bps * 32;
+    p.nsplit = (int)((blocks + bps - 1) / bps);
+  } else {
+    int64_t want = (2048 + seqs - 1) / seqs;
+    const int64_t max_split = (N + 63) / 64;
+    if (want > max_split) want = max_split;
+    if (want < 1) want = 1;
+    p.keys_per_split = (N + want - 1) / want;
+    p.nsplit = (int)((N + p.keys_per_split - 1) / p.keys_per_split);
+  }
   p.rows_total = (int64_t)B * Hq * Tq;
   size_t o = 0;
   p.off_qrot = o;  o = align_up(o + (size_t)p.rows_total * d * sizeof(float), 256);
   p.off_qproj = o; o = align_up(o + (size_t)p.rows_total * d * sizeof(float), 256);
+  p.off_rowc = o;  o = align_up(o + (size_t)p.rows_total * 4 * sizeof(float), 256);
   p.off_part = o;  o = align_up(o + (size_t)p.nsplit * p.rows_total * (d + 2) * sizeof(float), 256);
   p.total = o;
   return p;
@@ -246,7 +262,7 @@ tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, 
   if (!aligned16(q) || !aligned16(out) || (scores && !aligned16(scores)))
     return fail(TQ_ERR_ALIGNMENT, "q, out and scores must be 16-byte aligned");
   const int rows = Hq / Hkv * Tq;
-  if (!ref_decode_supports(layer->d, rows))
+  if (!mfma_decode_supports(layer->d, rows) && !ref_decode_supports(layer->d, rows))
     return fail(TQ_ERR_UNSUPPORTED, "(Hq/Hkv)*Tq too large for this head dimension");
   if ((int64_t)B * Hkv > 0x7FFFFFFF) return fail(TQ_ERR_UNSUPPORTED, "too many sequences");
   const Plan P = decode_plan(layer->d, B, Hq, Hkv, Tq, N);
@@ -287,7 +303,12 @@ tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, 
   a.part = reinterpret_cast<float*>(ws + P.off_part);
   a.nsplit = P.nsplit;
   a.keys_per_split = P.keys_per_split;
-  return hip_status(launch_decode_ref(a, static_cast<hipStream_t>(stream)), "decode launch");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (P.mfma)
+    return hip_status(launch_decode_mfma(a, blob_f(layer, BL.scales),
+                                         reinterpret_cast<float*>(ws + P.off_rowc), st),
+                      "decode launch");
+  return hip_status(launch_decode_ref(a, st), "decode launch");
 }
 
 tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,

@@ -213,6 +213,41 @@ void split_half(const double* M, size_t count, double scale, uint16_t* hi, uint1
 }
 }  // namespace
 
+float centroid_half_scale(const float* centroids, int levels, float* max_rel_err) {
+  // The decode kernels multiply fp16 copies of the centroids on the matrix
+  // cores.  Scaling the whole codebook by one factor s (undone on the query
+  // side) does not change the result, so s is chosen to make every s*c_i land
+  // as close as possible to an fp16 value.  Search s over [1, 2) * 2^k with
+  // s * max|c| in [1, 2), 2^18 candidates (finer grids gain < 1%).
+  double cmax = 0.0;
+  for (int i = 0; i < levels; ++i) cmax = std::fmax(cmax, std::fabs((double)centroids[i]));
+  const double base = std::ldexp(1.0, -(int)std::floor(std::log2(cmax)));
+  const int steps = 1 << 18;
+  double best_s = base, best_err = INFINITY;
+  for (int k = 0; k < steps; ++k) {
+    const double s = base * (1.0 + (double)k / steps);
+    double err = 0.0;
+    for (int i = levels / 2; i < levels && err < best_err; ++i) {  // codebooks are symmetric
+      const double v = s * (double)centroids[i];
+      const double h = (double)from_half(to_half((float)v));
+      err = std::fmax(err, std::fabs(h / v - 1.0));
+    }
+    if (err < best_err) {
+      best_err = err;
+      best_s = s;
+    }
+  }
+  // Report the error of the float32 scale actually stored.
+  const float sf = (float)best_s;
+  double err = 0.0;
+  for (int i = 0; i < levels; ++i) {
+    const double v = (double)sf * (double)centroids[i];
+    if (v != 0.0) err = std::fmax(err, std::fabs((double)from_half(to_half((float)v)) / v - 1.0));
+  }
+  *max_rel_err = (float)err;
+  return sf;
+}
+
 void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, unsigned char* image) {
   const BlobLayout L = blob_layout(d);
   std::memset(image, 0, L.total);
@@ -240,6 +275,9 @@ void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, uns
   float* cb = reinterpret_cast<float*>(image + L.codebook);
   lloyd_max_codebook(k_bits, d, cb, cb + kMaxLevels);
   lloyd_max_codebook(v_bits, d, cb + 2 * kMaxLevels, cb + 3 * kMaxLevels);
+  float* sc = reinterpret_cast<float*>(image + L.scales);
+  sc[0] = centroid_half_scale(cb, 1 << k_bits, &sc[2]);
+  sc[1] = centroid_half_scale(cb + 2 * kMaxLevels, 1 << v_bits, &sc[3]);
   split_half(R.data(), dd, std::sqrt((double)d), reinterpret_cast<uint16_t*>(image + L.rot_hi),
              reinterpret_cast<uint16_t*>(image + L.rot_lo));
   split_half(SR.data(), dd, 1.0, reinterpret_cast<uint16_t*>(image + L.projr_hi),

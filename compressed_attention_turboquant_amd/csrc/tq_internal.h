@@ -18,6 +18,8 @@ struct BlobLayout {
   size_t projr;     // [d][d] S R^T, so that S r = (S R^T)(R r) for a residual kept rotated
   size_t signs;     // [d] D (all +1 for the Haar kind)
   size_t codebook;  // [4][16]: key centroids, key boundaries, value centroids, value boundaries
+  size_t scales;    // [4]: fp16 table scale for key and value centroids, and their worst relative
+                    // fp16 rounding error (see centroid_half_scale)
   size_t rot_hi;    // half [d][d]: sqrt(d)*R split as hi + lo (MFMA operands)
   size_t rot_lo;
   size_t projr_hi;  // half [d][d]: S R^T split as hi + lo
@@ -39,6 +41,7 @@ inline BlobLayout blob_layout(int d) {
   L.projr = o;     o = align_up(o + mat, 256);
   L.signs = o;     o = align_up(o + d * sizeof(float), 256);
   L.codebook = o;  o = align_up(o + 4 * kMaxLevels * sizeof(float), 256);
+  L.scales = o;    o = align_up(o + 4 * sizeof(float), 256);
   L.rot_hi = o;    o = align_up(o + hmat, 256);
   L.rot_lo = o;    o = align_up(o + hmat, 256);
   L.projr_hi = o;  o = align_up(o + hmat, 256);
@@ -53,6 +56,9 @@ void stream_signs(uint64_t seed, uint64_t tag, size_t count, double* out);
 void make_rotation_f64(int d, int rot, uint64_t seed, double* R);
 void make_projection_f64(int d, uint64_t seed, double* S);
 void lloyd_max_codebook(int bits, int d, float* centroids, float* boundaries);
+// Common factor s for a codebook such that every s*c_i rounds to fp16 with the
+// smallest worst-case relative error; returns s and writes that error.
+float centroid_half_scale(const float* centroids, int levels, float* max_rel_err);
 // Fills a host image of the whole blob (layout.total bytes).
 void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, unsigned char* image);
 

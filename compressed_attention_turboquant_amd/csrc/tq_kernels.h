@@ -44,7 +44,22 @@ struct DequantArgs {
   int out_dtype;
 };
 
+// Arguments of the matrix-core decode split kernel (tq_decode_mfma.hip).
+struct DecodeMfmaParams {
+  const float *qa, *qb, *rowc;      // normalised R q and S q rows, per-row constants
+  const uint8_t *kidx, *ksign, *vidx;
+  const float *knorm, *krnorm, *vnorm, *cb;
+  const float* scales;              // blob: fp16 table factors for key and value centroids
+  int Hq, Hkv, Tq, causal;
+  int64_t N, cap, keys_per_split;
+  float *part, *scores;
+};
+
 hipError_t launch_quantize_ref(const QuantizeArgs& a, hipStream_t st);
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
+bool mfma_decode_supports(int d, int rows);
+// rowc: workspace for 4 floats per query row.
+hipError_t launch_decode_mfma(const DecodeArgs& a, const float* scales, float* rowc, hipStream_t st);
 hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_dequant_ref(const DequantArgs& a, hipStream_t st);
 bool ref_decode_supports(int d, int rows);

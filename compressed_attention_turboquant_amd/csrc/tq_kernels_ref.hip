@@ -431,6 +431,11 @@ hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st) {
                      a.Hkv, a.Tq, a.N, a.cap, a.causal, a.d, a.kb, a.vb, a.qjl, KC,
                      a.keys_per_split, a.kidx, a.ksign, a.knorm, a.krnorm, a.vidx, a.vnorm,
                      a.cb, a.part, a.scores);
+  return launch_decode_combine(a, st);
+}
+
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
+  const int64_t qrows = (int64_t)a.B * a.Hq * a.Tq;
   hipLaunchKernelGGL(decode_combine_ref, dim3((unsigned)qrows), dim3(kThreads), 0, st, a.part,
                      a.nsplit, qrows, a.d, a.R, a.out);
   return hipGetLastError();
