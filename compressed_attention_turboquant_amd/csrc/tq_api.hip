@@ -231,7 +231,9 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
   a.sign = cache->sign;
   a.norm = cache->norm;
   a.rnorm = cache->rnorm;
-  return hip_status(launch_quantize_ref(a, static_cast<hipStream_t>(stream)), "quantize launch");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mfma_quantize_supports(a.d, a.dtype)) return hip_status(launch_quantize_mfma(a, st), "quantize launch");
+  return hip_status(launch_quantize_ref(a, st), "quantize launch");
 }
 
 size_t tq_decode_workspace_bytes(const tq_layer* layer, int32_t B, int32_t Hq, int32_t Hkv,

@@ -55,7 +55,19 @@ struct DecodeMfmaParams {
   float *part, *scores;
 };
 
+// Arguments of the matrix-core quantize kernel (tq_quantize_mfma.hip, d = 128, fp16 input).
+struct QuantMfmaParams {
+  const _Float16* x;
+  int64_t seqs, n, t0, cap, tile_first, tile_last;
+  const _Float16 *rot_hi, *rot_lo, *projr_hi, *projr_lo;
+  const float *cent, *bnd;
+  uint8_t *idx, *sign;
+  float *norm, *rnorm;
+};
+
 hipError_t launch_quantize_ref(const QuantizeArgs& a, hipStream_t st);
+bool mfma_quantize_supports(int d, int dtype);
+hipError_t launch_quantize_mfma(const QuantizeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 bool mfma_decode_supports(int d, int rows);
 // rowc: workspace for 4 floats per query row.

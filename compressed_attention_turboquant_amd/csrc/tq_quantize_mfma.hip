@@ -1,0 +1,355 @@
+// Key/value compression on the matrix cores (gfx950), head dimension 128.
+//
+// Per token x ([cuTile] "K: (seq_k, head_dim) -> compressed dict", "V: ... MSE
+// only, no QJL"; [Mobilint] "Coordinates Become Predictable After Rotation",
+// "Designing the Optimal Codebook Without Data", "Two-Stage Approach"):
+//   n = ||x||;  y = R x / n;  idx_j = #{i : beta_i < y_j};  pack idx;
+//   keys with QJL: r = y - c[idx] (rotated residual), gamma = ||r||,
+//                  sign bits of (S R^T) r = S (u - R^T c[idx]).
+//
+// Mapping to CDNA4:
+//  * The rotation and the projection are [32 tokens x 128] x [128 x 128] GEMMs
+//    on v_mfma_f32_16x16x32_f16.  fp16 inputs are exact; the weights sqrt(d) R
+//    and S R^T are split into fp16 hi + lo (2 passes, ~2^-22 relative); the fp32
+//    residual is split too (3 passes: hi*hi, hi*lo, lo*hi).
+//  * Weights are stationary: wave w of a workgroup keeps the rows of 32 output
+//    coordinates in VGPRs for the whole kernel; tokens stream through LDS in
+//    tiles of 4 x 8 tokens (one 8-token value tile each), the workgroup looping
+//    over tiles (persistent grid).
+//  * Operand roles are chosen per tensor so that each lane ends with exactly
+//    what it stores: keys (row-major streams) use D = W * X^T, a lane holding 8
+//    consecutive coordinates of a token; values (8-token coordinate-major
+//    tiles) use D = X * W^T, a lane holding one coordinate of 8 tokens.
+//  * The scalar quantizer compares |y| with the positive half of the symmetric
+//    boundaries and picks the centroid magnitude in the same pass.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cmath>
+#include <type_traits>
+
+#include "tq_kernels.h"
+
+namespace tq {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSlots = 32;  // tokens per tile: 4 value tiles of 8
+
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Output coordinate held by weight row rho (0..15) of coordinate tile ct in
+// wave w: lanes of group g = rho/4 get 8 consecutive coordinates 32w + 8g + 4ct + rho%4.
+__device__ __forceinline__ int out_coord(int w, int ct, int rho) {
+  return 32 * w + 8 * (rho / 4) + 4 * ct + (rho % 4);
+}
+
+template <int BITS>
+struct Quantizer {
+  static constexpr int K = (1 << (BITS - 1)) - 1;  // positive boundaries
+  float beta[K > 0 ? K : 1];
+  float mag[K + 1];
+  __device__ void init(const float* cent, const float* bnd) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) beta[i] = bnd[K + 1 + i];
+#pragma unroll
+    for (int i = 0; i <= K; ++i) mag[i] = cent[K + 1 + i];
+  }
+  // code = #{i : boundary_i < y}; c = centroid of that code.
+  __device__ __forceinline__ uint32_t code(float y, float& c) const {
+    const float a = fabsf(y);
+    uint32_t cnt = 0;
+    float m = mag[0];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const bool gt = a > beta[i];
+      cnt += gt ? 1u : 0u;
+      m = gt ? mag[i + 1] : m;
+    }
+    const bool pos = y > 0.f;
+    c = pos ? m : -m;
+    return pos ? (uint32_t)(K + 1) + cnt : (uint32_t)K - cnt;
+  }
+};
+
+template <int BITS, int QJL, int VALUES>
+__global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams p) {
+  __shared__ __align__(16) _Float16 xs[kSlots][D + 8];       // token rows (padded)
+  __shared__ __align__(16) _Float16 rs[2][kSlots][D + 8];    // residual hi / lo
+  __shared__ float nrm[kSlots];
+  __shared__ float rsq[kSlots][16];
+
+  const int tid = threadIdx.x;
+  const int w = tid / 64, lane = tid % 64;
+  const int l16 = lane % 16, g4 = lane / 16;
+
+  // Stationary weights: rows out_coord(w, ct, l16), columns 32 kb + 8 g4 + e.
+  h8 wr[2][4][2], wp[QJL ? 2 : 1][4][2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int row = out_coord(w, ct, l16);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int col = 32 * kb + 8 * g4;
+      wr[ct][kb][0] = *reinterpret_cast<const h8*>(p.rot_hi + row * D + col);
+      wr[ct][kb][1] = *reinterpret_cast<const h8*>(p.rot_lo + row * D + col);
+      if constexpr (QJL) {
+        wp[ct][kb][0] = *reinterpret_cast<const h8*>(p.projr_hi + row * D + col);
+        wp[ct][kb][1] = *reinterpret_cast<const h8*>(p.projr_lo + row * D + col);
+      }
+    }
+  }
+  Quantizer<BITS> qz;
+  qz.init(p.cent, p.bnd);
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+
+  const int64_t tiles_per_seq = p.tile_last - p.tile_first + 1;
+  const int64_t groups = (p.seqs * tiles_per_seq + 3) / 4;
+  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    // ---- load 32 token rows (4 value tiles) into LDS, with their norms ----
+    {
+      const int slot = tid / 8, part = tid % 8;  // 8 threads per token, 16 halves each
+      const int64_t tix = grp * 4 + slot / 8;
+      const int64_t s = tix / tiles_per_seq;
+      const int64_t t = (p.tile_first + tix % tiles_per_seq) * 8 + slot % 8;
+      const bool ok = tix < p.seqs * tiles_per_seq && t >= p.t0 && t < p.t0 + p.n;
+      h8 v0 = h8{0, 0, 0, 0, 0, 0, 0, 0}, v1 = v0;
+      if (ok) {
+        const _Float16* src = p.x + (s * p.n + (t - p.t0)) * D + part * 16;
+        v0 = *reinterpret_cast<const h8*>(src);
+        v1 = *reinterpret_cast<const h8*>(src + 8);
+      }
+      *reinterpret_cast<h8*>(&xs[slot][part * 16]) = v0;
+      *reinterpret_cast<h8*>(&xs[slot][part * 16 + 8]) = v1;
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf((float)v0[e], (float)v0[e], fmaf((float)v1[e], (float)v1[e], ss));
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      ss += __shfl_xor(ss, 4);
+      if (part == 0) nrm[slot] = sqrtf(ss);
+    }
+    __syncthreads();
+
+    // ---- rotation: acc[ct][tt] ----
+    f4 acc[2][2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) acc[ct][tt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        // token operand: keys read slot 16 tt + l16; values read the slot that makes
+        // lane group g4 hold value tile g4 (slot 8 (l16/4) + 4 tt + l16 % 4).
+        const int slot = VALUES ? 8 * (l16 / 4) + 4 * tt + (l16 % 4) : 16 * tt + l16;
+        const h8 xv = *reinterpret_cast<const h8*>(&xs[slot][32 * kb + 8 * g4]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          if constexpr (VALUES) {
+            acc[ct][tt] = mfma(xv, wr[ct][kb][0], acc[ct][tt]);
+            acc[ct][tt] = mfma(xv, wr[ct][kb][1], acc[ct][tt]);
+          } else {
+            acc[ct][tt] = mfma(wr[ct][kb][0], xv, acc[ct][tt]);
+            acc[ct][tt] = mfma(wr[ct][kb][1], xv, acc[ct][tt]);
+          }
+        }
+      }
+    }
+
+    if constexpr (!VALUES) {
+      // Lane (g4, l16) holds coordinates 32w + 8g4 + 4ct + r of token slot 16tt + l16.
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int slot = 16 * tt + l16;
+        const float nn = nrm[slot];
+        const float inv = nn > 0.f ? inv_sqrt_d / nn : 0.f;
+        uint32_t packed = 0;
+        float r[8];
+        float rr = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float y = acc[ct][tt][q] * inv;
+            float c;
+            const uint32_t code = qz.code(y, c);
+            packed |= code << (BITS * (4 * ct + q));
+            r[4 * ct + q] = y - c;
+            rr = fmaf(r[4 * ct + q], r[4 * ct + q], rr);
+          }
+        const int64_t tix = grp * 4 + slot / 8;
+        const int64_t s = tix / tiles_per_seq;
+        const int64_t t = (p.tile_first + tix % tiles_per_seq) * 8 + slot % 8;
+        const bool ok = tix < p.seqs * tiles_per_seq && t >= p.t0 && t < p.t0 + p.n;
+        if (ok) {
+          uint8_t* dst = p.idx + (s * p.cap + t) * (D * BITS / 8) + (4 * w + g4) * BITS;
+#pragma unroll
+          for (int b = 0; b < BITS; ++b) dst[b] = (uint8_t)(packed >> (8 * b));
+        }
+        if constexpr (QJL) {
+          h8 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = r[e] * 64.f;  // keep the lo half away from fp16 subnormals
+            hi[e] = (_Float16)v;
+            lo[e] = (_Float16)(v - (float)hi[e]);
+          }
+          *reinterpret_cast<h8*>(&rs[0][slot][32 * w + 8 * g4]) = hi;
+          *reinterpret_cast<h8*>(&rs[1][slot][32 * w + 8 * g4]) = lo;
+          rsq[slot][4 * w + g4] = rr;
+        }
+        if (w == 0 && g4 == 0 && ok) p.norm[s * p.cap + t] = nn;
+      }
+      if constexpr (QJL) {
+        __syncthreads();
+        f4 pacc[2][2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) pacc[ct][tt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int slot = 16 * tt + l16;
+            const h8 rh = *reinterpret_cast<const h8*>(&rs[0][slot][32 * kb + 8 * g4]);
+            const h8 rl = *reinterpret_cast<const h8*>(&rs[1][slot][32 * kb + 8 * g4]);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+              pacc[ct][tt] = mfma(wp[ct][kb][0], rh, pacc[ct][tt]);
+              pacc[ct][tt] = mfma(wp[ct][kb][0], rl, pacc[ct][tt]);
+              pacc[ct][tt] = mfma(wp[ct][kb][1], rh, pacc[ct][tt]);
+            }
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int slot = 16 * tt + l16;
+          uint32_t bits = 0;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bits |= (pacc[ct][tt][q] >= 0.f ? 1u : 0u) << (4 * ct + q);
+          const int64_t tix = grp * 4 + slot / 8;
+          const int64_t s = tix / tiles_per_seq;
+          const int64_t t = (p.tile_first + tix % tiles_per_seq) * 8 + slot % 8;
+          const bool ok = tix < p.seqs * tiles_per_seq && t >= p.t0 && t < p.t0 + p.n;
+          if (ok) {
+            p.sign[(s * p.cap + t) * (D / 8) + 4 * w + g4] = (uint8_t)bits;
+            if (w == 0 && g4 == 0) {
+              float g = 0.f;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) g += rsq[slot][i];
+              p.rnorm[s * p.cap + t] = sqrtf(g);
+            }
+          }
+        }
+      }
+    } else {
+      // Lane (g4, l16) holds, for coordinate tile ct, coordinate out_coord(w, ct, l16)
+      // of the 8 tokens of value tile g4 (token 4 tt + r in D row 4 g4 + r of tile tt).
+      const int64_t tix = grp * 4 + g4;
+      const bool tile_ok = tix < p.seqs * tiles_per_seq;
+      const int64_t s = tile_ok ? tix / tiles_per_seq : 0;
+      const int64_t tile = p.tile_first + (tile_ok ? tix % tiles_per_seq : 0);
+      uint32_t keep = 0;  // code bits of tokens outside [t0, t0+n) are left unchanged
+      float inv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t t = tile * 8 + k;
+        const bool ok = t >= p.t0 && t < p.t0 + p.n;
+        if (!ok) keep |= ((1u << BITS) - 1u) << (BITS * k);
+        const float nn = nrm[8 * g4 + k];
+        inv[k] = nn > 0.f ? inv_sqrt_d / nn : 0.f;
+        if (ok && tile_ok && w == 0 && l16 == 0) p.norm[s * p.cap + t] = nn;
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int k = 4 * tt + q;
+            float c;
+            packed |= qz.code(acc[ct][tt][q] * inv[k], c) << (BITS * k);
+          }
+        if (tile_ok) {
+          uint8_t* dst = p.idx + (s * (p.cap / 8) + tile) * (D * BITS) + out_coord(w, ct, l16) * BITS;
+          if (keep) {
+            uint32_t old = 0;
+#pragma unroll
+            for (int b = 0; b < BITS; ++b) old |= (uint32_t)dst[b] << (8 * b);
+            packed = (packed & ~keep) | (old & keep);
+          }
+#pragma unroll
+          for (int b = 0; b < BITS; ++b) dst[b] = (uint8_t)(packed >> (8 * b));
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int BITS, int QJL, int VALUES>
+hipError_t launch(const QuantMfmaParams& p, int64_t groups, hipStream_t st) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const int64_t grid = groups < (int64_t)cus * 4 ? groups : (int64_t)cus * 4;
+  hipLaunchKernelGGL((quantize_mfma_kernel<BITS, QJL, VALUES>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int QJL, int VALUES>
+hipError_t dispatch_bits(const QuantMfmaParams& p, int bits, int64_t groups, hipStream_t st) {
+  switch (bits) {
+    case 1: return launch<1, QJL, VALUES>(p, groups, st);
+    case 2: return launch<2, QJL, VALUES>(p, groups, st);
+    case 3: return launch<3, QJL, VALUES>(p, groups, st);
+    default: return launch<4, QJL, VALUES>(p, groups, st);
+  }
+}
+
+}  // namespace
+
+bool mfma_quantize_supports(int d, int dtype) { return d == D && dtype == TQ_F16; }
+
+hipError_t launch_quantize_mfma(const QuantizeArgs& a, hipStream_t st) {
+  if (a.n == 0 || a.seqs == 0) return hipSuccess;
+  QuantMfmaParams p{};
+  p.x = static_cast<const _Float16*>(a.x);
+  p.seqs = a.seqs;
+  p.n = a.n;
+  p.t0 = a.t0;
+  p.cap = a.cap;
+  p.tile_first = a.t0 / 8;
+  p.tile_last = (a.t0 + a.n - 1) / 8;
+  p.rot_hi = static_cast<const _Float16*>(a.rot_hi);
+  p.rot_lo = static_cast<const _Float16*>(a.rot_lo);
+  p.projr_hi = static_cast<const _Float16*>(a.projr_hi);
+  p.projr_lo = static_cast<const _Float16*>(a.projr_lo);
+  p.cent = a.cent;
+  p.bnd = a.bnd;
+  p.idx = a.idx;
+  p.sign = a.sign;
+  p.norm = a.norm;
+  p.rnorm = a.rnorm;
+  const int64_t groups = (a.seqs * (p.tile_last - p.tile_first + 1) + 3) / 4;
+  if (a.value_layout) return dispatch_bits<0, 1>(p, a.bits, groups, st);
+  if (a.qjl) return dispatch_bits<1, 0>(p, a.bits, groups, st);
+  return dispatch_bits<0, 0>(p, a.bits, groups, st);
+}
+
+}  // namespace tq
