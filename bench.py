@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="C3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path is "
@@ -215,6 +217,13 @@ def main():
                               "traffic": traffic_from_profile("quantize", cfg.name, digest, 1)},
         "sources_digest": digest,
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB device-to-device copy kernel done")
+        del src, dst
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a sample)")
         res["cpu_baseline"] = cpu_baseline(cfg, Kx, Vx, q)

@@ -19,7 +19,7 @@ struct Plan {  // split-K plan of one decode call
   int nsplit;
   int64_t keys_per_split;
   int64_t rows_total;
-  size_t off_qrot, off_qproj, off_rowc, off_part, total;
+  size_t off_qrot, off_qproj, off_rowc, off_count, off_part, total;
 };
 
 Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
@@ -33,6 +33,7 @@ Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
     int64_t want = (2048 + seqs - 1) / seqs;
     const int64_t max_split = (blocks + 15) / 16;
     if (want > max_split) want = max_split;
+    if (want > 1024) want = 1024;  // the combine kernel keeps one weight per split in LDS
     if (want < 1) want = 1;
     const int64_t bps = (blocks + want - 1) / want;
     p.keys_per_split = bps * 32;
@@ -41,6 +42,7 @@ Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
     int64_t want = (2048 + seqs - 1) / seqs;
     const int64_t max_split = (N + 63) / 64;
     if (want > max_split) want = max_split;
+    if (want > 1024) want = 1024;
     if (want < 1) want = 1;
     p.keys_per_split = (N + want - 1) / want;
     p.nsplit = (int)((N + p.keys_per_split - 1) / p.keys_per_split);
@@ -50,6 +52,7 @@ Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
   p.off_qrot = o;  o = align_up(o + (size_t)p.rows_total * d * sizeof(float), 256);
   p.off_qproj = o; o = align_up(o + (size_t)p.rows_total * d * sizeof(float), 256);
   p.off_rowc = o;  o = align_up(o + (size_t)p.rows_total * 4 * sizeof(float), 256);
+  p.off_count = o; o = align_up(o + (size_t)seqs * sizeof(int), 256);
   p.off_part = o;  o = align_up(o + (size_t)p.nsplit * p.rows_total * (d + 2) * sizeof(float), 256);
   p.total = o;
   return p;
@@ -306,10 +309,15 @@ tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, 
   a.nsplit = P.nsplit;
   a.keys_per_split = P.keys_per_split;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (P.mfma)
-    return hip_status(launch_decode_mfma(a, blob_f(layer, BL.scales),
-                                         reinterpret_cast<float*>(ws + P.off_rowc), st),
-                      "decode launch");
+  if (P.mfma) {
+    DecodeMfmaExtra x{};
+    x.Rt = blob_f(layer, BL.rot_t);
+    x.St = blob_f(layer, BL.proj_t);
+    x.scales = blob_f(layer, BL.scales);
+    x.rowc = reinterpret_cast<float*>(ws + P.off_rowc);
+    x.counters = reinterpret_cast<int*>(ws + P.off_count);
+    return hip_status(launch_decode_mfma(a, x, st), "decode launch");
+  }
   return hip_status(launch_decode_ref(a, st), "decode launch");
 }
 

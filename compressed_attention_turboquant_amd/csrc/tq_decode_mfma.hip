@@ -33,8 +33,14 @@
 //    accumulators are rescaled only in the (rare) blocks where a score exceeds
 //    the current maximum of its row.
 //  * Split-K over keys: grid (sequence, split); 4 waves per workgroup take every
-//    4th block of 32 keys; their partial (max, sum, acc) merge in LDS and one
-//    partial per split goes to the workspace for the combine kernel.
+//    4th block of 32 keys, each keeping two blocks of loads in flight (three
+//    rotating register sets); the waves' partial (max, sum, acc) merge in LDS
+//    and one partial per split goes to the workspace; a small kernel merges the
+//    splits and un-rotates.  (Merging in the last workgroup instead needs an
+//    agent-scope fence per workgroup, which writes back the L2 of its XCD and
+//    cost more than the extra launch.)
+//  * Loads go through buffer descriptors with per-sequence SGPR bases: 32-bit
+//    offsets, and reads past the capacity (or past N for the norms) return 0.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -141,6 +147,7 @@ struct Shape {
   static constexpr int VTILE = D * VB;        // value-code bytes per 8-token tile
 };
 
+// Registers of one 32-key block, as this lane needs them.
 template <int D, int KB, int QJL, int VB>
 struct Block {
   using S = Shape<D, KB, QJL, VB>;
@@ -150,36 +157,191 @@ struct Block {
   uint32_t vw[S::NWV];
 };
 
+// Per-sequence buffer descriptors: 32-bit offsets from an SGPR base; reads past
+// the described range return 0 (keys at or beyond the capacity, norms of keys
+// at or beyond N).
+struct SeqBuffers {
+  __amdgpu_buffer_rsrc_t kidx, ksign, knorm, krnorm, vidx, vnorm;
+};
+
+constexpr int kBufCfg = 0x00020000;  // raw (untyped) buffer on gfx9
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufCfg);
+}
+
 template <int N>
-__device__ __forceinline__ void load_words(uint32_t (&dst)[N], const uint32_t* src, bool ok) {
+__device__ __forceinline__ void buf_load(uint32_t (&dst)[N], __amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (N == 1) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (N == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    dst[0] = v[0];
+    dst[1] = v[1];
+  } else if constexpr (N == 3) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    dst[0] = v[0];
+    dst[1] = v[1];
+    dst[2] = v[2];
+  } else {
+    static_assert(N % 4 == 0 || N == 6 || N == 12, "unsupported width");
+    if constexpr (N % 4 == 0) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) dst[i] = ok ? src[i] : 0u;
+      for (int i = 0; i < N; i += 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0);
+        dst[i] = v[0];
+        dst[i + 1] = v[1];
+        dst[i + 2] = v[2];
+        dst[i + 3] = v[3];
+      }
+    } else {  // 6 or 12 dwords: b128 + b64 pieces
+#pragma unroll
+      for (int i = 0; i < N; i += 6) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0);
+        const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * i + 16, 0, 0);
+        dst[i] = v[0];
+        dst[i + 1] = v[1];
+        dst[i + 2] = v[2];
+        dst[i + 3] = v[3];
+        dst[i + 4] = u[0];
+        dst[i + 5] = u[1];
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
 template <int D, int KB, int QJL, int VB>
-__device__ __forceinline__ void load_block(Block<D, KB, QJL, VB>& b, const DecodeMfmaParams& p,
-                                           int64_t seq, int64_t k0, int l16, int g4) {
+__device__ __forceinline__ void load_block(Block<D, KB, QJL, VB>& b, const SeqBuffers& sb, int k0,
+                                           int l16, int g4) {
   using S = Shape<D, KB, QJL, VB>;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int64_t key = k0 + 16 * t + l16;
-    const bool in = key < p.cap;
-    const int64_t row = seq * p.cap + key;
-    load_words(b.kw[t], reinterpret_cast<const uint32_t*>(p.kidx + row * S::KROW + g4 * (S::KROW / 4)), in);
-    if constexpr (QJL)
-      load_words(b.sw[t], reinterpret_cast<const uint32_t*>(p.ksign + row * (D / 8) + g4 * (D / 32)), in);
-    const bool valid = key < p.N;
-    b.kn[t] = valid ? p.knorm[row] : 0.f;
-    b.kg[t] = (QJL && valid) ? p.krnorm[row] : 0.f;
-    b.vn[t] = valid ? p.vnorm[row] : 0.f;
+    const int key = k0 + 16 * t + l16;
+    buf_load(b.kw[t], sb.kidx, key * S::KROW + g4 * (S::KROW / 4));
+    if constexpr (QJL) buf_load(b.sw[t], sb.ksign, key * (D / 8) + g4 * (D / 32));
+    b.kn[t] = buf_f32(sb.knorm, key * 4);
+    if constexpr (QJL) b.kg[t] = buf_f32(sb.krnorm, key * 4);
+    b.vn[t] = buf_f32(sb.vnorm, key * 4);
   }
-  const int64_t vt = k0 / 8 + g4;
-  const bool vin = vt < p.cap / 8;
-  load_words(b.vw, reinterpret_cast<const uint32_t*>(p.vidx + (seq * (p.cap / 8) + vt) * S::VTILE +
-                                                     l16 * (S::VTILE / 16)), vin);
+  buf_load(b.vw, sb.vidx, (k0 / 8 + g4) * S::VTILE + l16 * (S::VTILE / 16));
 }
 
+// Per-wave state of the running softmax and the query operands.
 template <int D, int KB, int QJL, int VB>
+struct WaveState {
+  using S = Shape<D, KB, QJL, VB>;
+  h8 Ak[S::KBLK], As[QJL ? S::KBLK : 1];
+  f4 acc[S::CB];
+  float m, msafe, lsum;
+  float ca, c2, c0;
+  int limit;
+  int64_t srow;
+  uint32_t kt0, kt1, vt0, vt1;
+};
+
+template <int D, int KB, int QJL, int VB, int SCORES>
+__device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, const Block<D, KB, QJL, VB>& cur,
+                                              int k0, const DecodeMfmaParams& p, _Float16 (*pb)[4][32],
+                                              int l16, int g4, int rows) {
+  using S = Shape<D, KB, QJL, VB>;
+  // Phase 1: all key-code lookups of both 16-key tiles go out before any MFMA
+  // needs one, so the bpermute latency overlaps instead of serialising.
+  u4 bk[2][S::KBLK];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    sfor<0, S::KBLK>([&](auto kb) {
+      sfor<0, 4>([&](auto w) {
+        bk[t][kb][decltype(w)::value] = decode_pair<KB, 0, 4 * kb + w>(cur.kw[t], ws.kt0, ws.kt1);
+      });
+    });
+  __builtin_amdgcn_sched_barrier(0);
+  // Phase 2: score MFMAs.  Separate accumulators for the centroid and sign parts
+  // halve the dependency chains; each fills only its own rows (parts 0,1 / 2,3).
+  f4 sk[2], ss[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    sk[t] = f4{0.f, 0.f, 0.f, 0.f};
+    ss[t] = sk[t];
+  }
+  sfor<0, S::KBLK>([&](auto kb) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      sk[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ws.Ak[kb], __builtin_bit_cast(h8, bk[t][kb]), sk[t], 0, 0, 0);
+    if constexpr (QJL) {
+      constexpr int r = kb % 4;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t word = cur.sw[t][kb / 4];
+        const uint32_t rot = r == 0 ? word : __builtin_amdgcn_alignbit(word, word, 32 - 4 * r);
+        u4 bw;
+        sfor<0, 4>([&](auto w) { bw[decltype(w)::value] = sign_dword<decltype(w)::value>(rot); });
+        ss[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ws.As[kb], __builtin_bit_cast(h8, bw), ss[t], 0, 0, 0);
+      }
+    }
+  });
+  // Phase 3: value-code lookups, in flight while the softmax arithmetic runs.
+  u4 bv[S::CB];
+  sfor<0, S::CB>([&](auto cb) {
+    sfor<0, 4>([&](auto w) {
+      bv[cb][decltype(w)::value] = decode_pair<VB, 8 * VB * cb, w>(cur.vw, ws.vt0, ws.vt1);
+    });
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  // Phase 4: scores of lane (query row g4, key l16), online softmax.
+  float st[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float s = (cur.kn[t] * ws.ca) * (sk[t][0] + sk[t][1]);
+    if constexpr (QJL) s = fmaf(cur.kn[t] * cur.kg[t], fmaf(ws.c2, ss[t][2] + ss[t][3], ws.c0), s);
+    const int key = k0 + 16 * t + l16;
+    s = key < ws.limit ? s : -INFINITY;
+    if constexpr (SCORES) {
+      if (g4 < rows && key < p.N) p.scores[ws.srow * p.N + key] = s * kLn2;
+    }
+    st[t] = s;
+  }
+  const float mx = fmaxf(st[0], st[1]);
+  if (__any(mx > ws.m)) {
+    float rmax = mx;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
+    const float mnew = fmaxf(ws.m, rmax);
+    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(ws.m - mnew);
+    ws.lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < S::CB; ++i) ws.acc[i] *= alpha;
+    ws.m = mnew;
+    ws.msafe = mnew == -INFINITY ? 0.f : mnew;
+  }
+  // v_exp_f32 directly: weights below 2^-126 of the running maximum become 0.
+  const float p0 = __builtin_amdgcn_exp2f(st[0] - ws.msafe), p1 = __builtin_amdgcn_exp2f(st[1] - ws.msafe);
+  ws.lsum += p0 + p1;
+  const float q0 = p0 * cur.vn[0], q1 = p1 * cur.vn[1];
+  const _Float16 h0 = (_Float16)q0, h1 = (_Float16)q1;
+  pb[0][g4][l16] = h0;
+  pb[0][g4][16 + l16] = h1;
+  pb[1][g4][l16] = (_Float16)(q0 - (float)h0);
+  pb[1][g4][16 + l16] = (_Float16)(q1 - (float)h1);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  h8 ap = h8{0, 0, 0, 0, 0, 0, 0, 0};
+  {
+    const int part = l16 % 4, qr = l16 / 4;
+    if (part < 2) ap = *reinterpret_cast<const h8*>(&pb[part][qr][8 * g4]);
+  }
+  // Phase 5: P.V.
+  sfor<0, S::CB>([&](auto cb) {
+    ws.acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(h8, bv[cb]), ws.acc[cb], 0, 0, 0);
+  });
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int D, int KB, int QJL, int VB, int SCORES>
 __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams p) {
   using S = Shape<D, KB, QJL, VB>;
   __shared__ __align__(16) _Float16 pbuf[kWaves][2][4][32];
@@ -197,159 +359,103 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   const int rows = G * p.Tq;
   auto qrow_of = [&](int r) -> int64_t { return (b_ * p.Hq + (int64_t)hkv * G + r / p.Tq) * p.Tq + r % p.Tq; };
 
-  const float* ck = p.cb;
-  const float* cv = p.cb + 2 * kMaxLevels;
-  uint32_t kt0, kt1, vt0, vt1;
+  SeqBuffers sb;
+  sb.kidx = make_rsrc(p.kidx + seq * p.cap * S::KROW, p.cap * S::KROW);
+  sb.ksign = make_rsrc(QJL ? p.ksign + seq * p.cap * (D / 8) : p.kidx, p.cap * (D / 8));
+  sb.knorm = make_rsrc(p.knorm + seq * p.cap, p.N * 4);
+  sb.krnorm = make_rsrc(QJL ? p.krnorm + seq * p.cap : p.knorm, p.N * 4);
+  sb.vidx = make_rsrc(p.vidx + seq * (p.cap / 8) * S::VTILE, (p.cap / 8) * S::VTILE);
+  sb.vnorm = make_rsrc(p.vnorm + seq * p.cap, p.N * 4);
+
+  WaveState<D, KB, QJL, VB> ws;
   const float scale_k = p.scales[0], scale_v = p.scales[1];
-  make_tables<KB>(ck, scale_k, lane, kt0, kt1);
-  make_tables<VB>(cv, scale_v, lane, vt0, vt1);
+  make_tables<KB>(p.cb, scale_k, lane, ws.kt0, ws.kt1);
+  make_tables<VB>(p.cb + 2 * kMaxLevels, scale_v, lane, ws.vt0, ws.vt1);
 
   // Query operands: lane (row rho = l16, k-group g4).
-  h8 Ak[S::KBLK], As[QJL ? S::KBLK : 1];
   {
     const int qr = l16 / 4, part = l16 % 4;
     const bool ok = qr < rows;
-    const int64_t qrow = ok ? qrow_of(qr) : 0;
+    const float* qa = p.qa + (ok ? qrow_of(qr) : 0) * D + (D / 4) * g4;
+    const float* qb = p.qb + (ok ? qrow_of(qr) : 0) * D + (D / 4) * g4;
     sfor<0, S::KBLK>([&](auto kb) {
       h8 a;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = 0.f;
-        if (ok && part < 2) x = p.qa[qrow * D + (D / 4) * g4 + 8 * kb + e];
+        const float x = (ok && part < 2) ? qa[8 * kb + e] : 0.f;
         const _Float16 hi = (_Float16)x;
         const _Float16 lo = (_Float16)(x - (float)hi);
         a[e] = part == 0 ? hi : (part == 1 ? lo : (_Float16)0.f);
       }
-      Ak[kb] = a;
+      ws.Ak[kb] = a;
       if constexpr (QJL) {
         h8 s;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int w = e / 2, h = e % 2;
-          float x = 0.f;
-          if (ok && part >= 2)
-            x = p.qb[qrow * D + (D / 4) * g4 + 32 * (kb / 4) + sign_coord(kb % 4, w, h)] * sign_comp(w);
+          const float x = (ok && part >= 2) ? qb[32 * (kb / 4) + sign_coord(kb % 4, w, h)] * sign_comp(w) : 0.f;
           const _Float16 hi = (_Float16)x;
           const _Float16 lo = (_Float16)(x - (float)hi);
           s[e] = part == 2 ? hi : (part == 3 ? lo : (_Float16)0.f);
         }
-        As[kb] = s;
+        ws.As[kb] = s;
       }
     });
   }
-
-  // Score-side constants of this lane's query row g4.
-  float ca = 0.f, cb2 = 0.f, c2 = 0.f, c0 = 0.f;
-  int64_t limit = -1;
-  int64_t srow = 0;
+  // Score-side constants of this lane's query row g4 (log2 domain).
+  ws.ca = ws.c2 = ws.c0 = 0.f;
+  ws.limit = -1;
+  ws.srow = 0;
   if (g4 < rows) {
-    srow = qrow_of(g4);
-    const float* rc = p.rowc + srow * 4;
+    ws.srow = qrow_of(g4);
+    const float* rc = p.rowc + ws.srow * 4;
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    ca = rc[0] * inv_sqrt_d * kLog2e;
-    cb2 = sqrtf(0.5f * (float)M_PI) / (float)D * inv_sqrt_d * kLog2e;
-    c2 = rc[1];
-    c0 = rc[2];
-    limit = p.causal ? p.N - p.Tq + (g4 % p.Tq) + 1 : p.N;
+    const float cq = sqrtf(0.5f * (float)M_PI) / (float)D * inv_sqrt_d * kLog2e;
+    ws.ca = rc[0] * inv_sqrt_d * kLog2e;
+    ws.c2 = rc[1] * cq;
+    ws.c0 = rc[2] * cq;
+    ws.limit = (int)(p.causal ? p.N - p.Tq + (g4 % p.Tq) + 1 : p.N);
   }
-
-  f4 acc[S::CB];
 #pragma unroll
-  for (int i = 0; i < S::CB; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, msafe = 0.f, lsum = 0.f;
+  for (int i = 0; i < S::CB; ++i) ws.acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+  ws.m = -INFINITY;
+  ws.msafe = 0.f;
+  ws.lsum = 0.f;
 
-  const int64_t nblk = (p.N + 31) / 32;
-  const int64_t blk0 = (int64_t)split * (p.keys_per_split / 32);
-  const int64_t blk1 = min(nblk, blk0 + p.keys_per_split / 32);
+  const int nblk = (int)((p.N + 31) / 32);
+  const int blk0 = (int)(split * (p.keys_per_split / 32));
+  const int blk1 = min(nblk, blk0 + (int)(p.keys_per_split / 32));
 
-  Block<D, KB, QJL, VB> cur;
-  int64_t blk = blk0 + wave;
-  if (blk < blk1) load_block(cur, p, seq, blk * 32, l16, g4);
-  for (; blk < blk1; blk += kWaves) {
-    Block<D, KB, QJL, VB> nxt;
-    const bool more = blk + kWaves < blk1;
-    if (more) load_block(nxt, p, seq, (blk + kWaves) * 32, l16, g4);
-    const int64_t k0 = blk * 32;
-
-    float st[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f4 sacc = f4{0.f, 0.f, 0.f, 0.f};
-      sfor<0, S::KBLK>([&](auto kb) {
-        u4 bw;
-        sfor<0, 4>([&](auto w) { bw[decltype(w)::value] = decode_pair<KB, 0, 4 * kb + w>(cur.kw[t], kt0, kt1); });
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ak[kb], __builtin_bit_cast(h8, bw), sacc, 0, 0, 0);
-      });
-      if constexpr (QJL) {
-        sfor<0, S::KBLK>([&](auto kb) {
-          const uint32_t word = cur.sw[t][kb / 4];
-          constexpr int r = kb % 4;
-          const uint32_t rot = r == 0 ? word : __builtin_amdgcn_alignbit(word, word, 32 - 4 * r);
-          u4 bw;
-          sfor<0, 4>([&](auto w) { bw[decltype(w)::value] = sign_dword<decltype(w)::value>(rot); });
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(As[kb], __builtin_bit_cast(h8, bw), sacc, 0, 0, 0);
-        });
-      }
-      // lane (query row g4, key l16)
-      float s = (cur.kn[t] * ca) * (sacc[0] + sacc[1]);
-      if constexpr (QJL) s = fmaf(cur.kn[t] * cur.kg[t] * cb2, fmaf(c2, sacc[2] + sacc[3], c0), s);
-      const int64_t key = k0 + 16 * t + l16;
-      s = key < limit ? s : -INFINITY;
-      if (p.scores && g4 < rows && key < p.N) p.scores[srow * p.N + key] = s * kLn2;
-      st[t] = s;
-    }
-
-    const float mx = fmaxf(st[0], st[1]);
-    if (__any(mx > m)) {
-      float rmax = mx;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
-      const float mnew = fmaxf(m, rmax);
-      const float alpha = mnew == -INFINITY ? 1.f : exp2f(m - mnew);
-      lsum *= alpha;
-#pragma unroll
-      for (int i = 0; i < S::CB; ++i) acc[i] *= alpha;
-      m = mnew;
-      msafe = m == -INFINITY ? 0.f : m;
-    }
-    const float p0 = exp2f(st[0] - msafe), p1 = exp2f(st[1] - msafe);
-    lsum += p0 + p1;
-    const float q0 = p0 * cur.vn[0], q1 = p1 * cur.vn[1];
-    const _Float16 h0 = (_Float16)q0, h1 = (_Float16)q1;
-    pbuf[wave][0][g4][l16] = h0;
-    pbuf[wave][0][g4][16 + l16] = h1;
-    pbuf[wave][1][g4][l16] = (_Float16)(q0 - (float)h0);
-    pbuf[wave][1][g4][16 + l16] = (_Float16)(q1 - (float)h1);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    h8 ap;
-    {
-      const int part = l16 % 4, qr = l16 / 4;
-      if (part < 2)
-        ap = *reinterpret_cast<const h8*>(&pbuf[wave][part][qr][8 * g4]);
-      else
-        ap = h8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-    sfor<0, S::CB>([&](auto cb) {
-      u4 bw;
-      sfor<0, 4>([&](auto w) { bw[decltype(w)::value] = decode_pair<VB, 8 * VB * cb, w>(cur.vw, vt0, vt1); });
-      acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(h8, bw), acc[cb], 0, 0, 0);
-    });
-    __builtin_amdgcn_wave_barrier();
-    if (more) cur = nxt;
+  // Three register sets rotate so two blocks are in flight while one is used.
+  // The prefetches are unconditional (reads past the split land in the same
+  // sequence, reads past its capacity return 0), which keeps the loop body
+  // straight-line and lets the compiler count outstanding loads exactly.
+  Block<D, KB, QJL, VB> b0, b1, b2;
+  int blk = blk0 + wave;
+  load_block(b0, sb, blk * 32, l16, g4);
+  load_block(b1, sb, (blk + kWaves) * 32, l16, g4);
+  for (; blk < blk1; blk += 3 * kWaves) {
+    load_block(b2, sb, (blk + 2 * kWaves) * 32, l16, g4);
+    process_block<D, KB, QJL, VB, SCORES>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
+    if (blk + kWaves >= blk1) break;
+    load_block(b0, sb, (blk + 3 * kWaves) * 32, l16, g4);
+    process_block<D, KB, QJL, VB, SCORES>(ws, b1, (blk + kWaves) * 32, p, pbuf[wave], l16, g4, rows);
+    if (blk + 2 * kWaves >= blk1) break;
+    load_block(b1, sb, (blk + 4 * kWaves) * 32, l16, g4);
+    process_block<D, KB, QJL, VB, SCORES>(ws, b2, (blk + 2 * kWaves) * 32, p, pbuf[wave], l16, g4, rows);
   }
 
   // Merge the waves of this workgroup.
+  float lsum = ws.lsum;
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) lsum += __shfl_xor(lsum, o);
   if (l16 == 0) {
-    mrg_m[wave][g4] = m;
+    mrg_m[wave][g4] = ws.m;
     mrg_l[wave][g4] = lsum;
   }
   const float inv_sv = 1.0f / scale_v;
 #pragma unroll
-  for (int cb = 0; cb < S::CB; ++cb) mrg_acc[wave][g4][l16 * S::CB + cb] = (acc[cb][0] + acc[cb][1]) * inv_sv;
+  for (int cb = 0; cb < S::CB; ++cb) mrg_acc[wave][g4][l16 * S::CB + cb] = (ws.acc[cb][0] + ws.acc[cb][1]) * inv_sv;
   __syncthreads();
   const int64_t rows_total = (int64_t)gridDim.x / p.Hkv * p.Hq * p.Tq;
   for (int idx = tid; idx < rows * D; idx += kThreads) {
@@ -369,70 +475,96 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
     float* dst = p.part + ((int64_t)split * rows_total + qrow_of(r)) * (D + 2);
     dst[j] = a;
     if (j == 0) {
-      dst[D] = M * kLn2;
+      dst[D] = M * kLn2;  // natural-log units, as the combine kernel expects
       dst[D + 1] = L;
     }
   }
 }
 
-// Rotates every query row once and normalises it for the fp16 operand split.
-// qa = (R q) / (s_k * c1), qb = (S q) / (c2 / 2), with c1, c2 powers of two
-// that bring the largest entry into [1, 2); rowc = {c1, c2, -sum(S q), 0}.
-__global__ void __launch_bounds__(256) prerotate_mfma_kernel(const void* __restrict__ q, int qdt, int d,
-                                                              const float* __restrict__ R,
-                                                              const float* __restrict__ Sm, int qjl,
-                                                              const float* __restrict__ scales,
-                                                              float* __restrict__ qa,
-                                                              float* __restrict__ qb,
-                                                              float* __restrict__ rowc) {
+// One block per query row: rotates it once (R q, S q, reading R^T and S^T so
+// that neighbouring threads read neighbouring addresses) and normalises it for
+// the fp16 operand split: qa = (R q) / (s_k c1), qb = (S q) 2 / c2 with c1, c2
+// powers of two bringing the largest entry into [1, 2); rowc = {c1, c2,
+// -sum(S q), 0}.  The first row of each KV head also clears its split counter.
+__global__ void __launch_bounds__(256) prerotate_mfma_kernel(PrerotateParams p) {
   __shared__ float qs[256];
-  __shared__ float red[3][256];
-  const int64_t row = blockIdx.x;
-  const int j = threadIdx.x;
-  if (j < d)
-    qs[j] = qdt == TQ_F16 ? __half2float(static_cast<const __half*>(q)[row * d + j])
-                          : static_cast<const float*>(q)[row * d + j];
+  __shared__ float part[2][2][256];
+  __shared__ float red[3][4];
+  const int64_t row = blockIdx.x;  // = (b * Hq + h) * Tq + t
+  const int tid = threadIdx.x;
+  const int d = p.d;
+  if (tid < d)
+    qs[tid] = p.qdt == TQ_F16 ? __half2float(static_cast<const __half*>(p.q)[row * d + tid])
+                              : static_cast<const float*>(p.q)[row * d + tid];
+  {
+    const int64_t h = (row / p.Tq) % p.Hq, t = row % p.Tq, b = row / ((int64_t)p.Tq * p.Hq);
+    const int G = p.Hq / p.Hkv;
+    if (tid == 0 && h % G == 0 && t == 0) p.counters[b * p.Hkv + h / G] = 0;
+  }
+  __syncthreads();
+  // thread -> output j, k-range half hk (d = 128: two halves of 64; d = 256: one)
+  const int j = tid % d, hk = tid / d, nk = 256 / d, kspan = d / nk;
+  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+  for (int k = hk * kspan; k < (hk + 1) * kspan; k += 2) {
+    a0 = fmaf(p.Rt[(size_t)k * d + j], qs[k], a0);
+    a1 = fmaf(p.Rt[(size_t)(k + 1) * d + j], qs[k + 1], a1);
+    if (p.qjl) {
+      b0 = fmaf(p.St[(size_t)k * d + j], qs[k], b0);
+      b1 = fmaf(p.St[(size_t)(k + 1) * d + j], qs[k + 1], b1);
+    }
+  }
+  part[0][hk][j] = a0 + a1;
+  part[1][hk][j] = b0 + b1;
   __syncthreads();
   float a = 0.f, b = 0.f;
-  if (j < d) {
-    for (int k = 0; k < d; ++k) {
-      a = fmaf(R[(size_t)j * d + k], qs[k], a);
-      if (qjl) b = fmaf(Sm[(size_t)j * d + k], qs[k], b);
+  if (tid < d) {
+    for (int h = 0; h < nk; ++h) {
+      a += part[0][h][tid];
+      b += part[1][h][tid];
     }
+    a /= p.scales[0];
   }
-  a /= scales[0];
-  red[0][j] = j < d ? fabsf(a) : 0.f;
-  red[1][j] = j < d ? fabsf(b) : 0.f;
-  red[2][j] = j < d ? b : 0.f;
+  float x = tid < d ? fabsf(a) : 0.f, y = tid < d ? fabsf(b) : 0.f, z = tid < d ? b : 0.f;
+  for (int o = 32; o > 0; o >>= 1) {
+    x = fmaxf(x, __shfl_xor(x, o));
+    y = fmaxf(y, __shfl_xor(y, o));
+    z += __shfl_xor(z, o);
+  }
+  if (tid % 64 == 0) {
+    red[0][tid / 64] = x;
+    red[1][tid / 64] = y;
+    red[2][tid / 64] = z;
+  }
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (j < o) {
-      red[0][j] = fmaxf(red[0][j], red[0][j + o]);
-      red[1][j] = fmaxf(red[1][j], red[1][j + o]);
-      red[2][j] += red[2][j + o];
-    }
-    __syncthreads();
+  float ma = 0.f, mb = 0.f, sbv = 0.f;
+  for (int w = 0; w < 4; ++w) {
+    ma = fmaxf(ma, red[0][w]);
+    mb = fmaxf(mb, red[1][w]);
+    sbv += red[2][w];
   }
   int e1 = 0, e2 = 0;
-  frexpf(red[0][0], &e1);
-  frexpf(red[1][0], &e2);
-  const float c1 = red[0][0] > 0.f ? ldexpf(1.f, e1 - 1) : 1.f;
-  const float c2 = red[1][0] > 0.f ? ldexpf(1.f, e2) : 2.f;
-  if (j < d) {
-    qa[row * d + j] = a / c1;
-    qb[row * d + j] = b * 2.f / c2;
+  frexpf(ma, &e1);
+  frexpf(mb, &e2);
+  const float c1 = ma > 0.f ? ldexpf(1.f, e1 - 1) : 1.f;
+  const float c2 = mb > 0.f ? ldexpf(1.f, e2) : 2.f;
+  if (tid < d) {
+    p.qa[row * d + tid] = a / c1;
+    p.qb[row * d + tid] = b * 2.f / c2;
   }
-  if (j == 0) {
-    rowc[row * 4 + 0] = c1;
-    rowc[row * 4 + 1] = c2;
-    rowc[row * 4 + 2] = -red[2][0];
-    rowc[row * 4 + 3] = 0.f;
+  if (tid == 0) {
+    p.rowc[row * 4 + 0] = c1;
+    p.rowc[row * 4 + 1] = c2;
+    p.rowc[row * 4 + 2] = -sbv;
+    p.rowc[row * 4 + 3] = 0.f;
   }
 }
 
 template <int D, int KB, int QJL, int VB>
 hipError_t launch_split(const DecodeMfmaParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB>), grid, dim3(kThreads), 0, st, p);
+  if (p.scores)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 1>), grid, dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 0>), grid, dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
@@ -468,15 +600,28 @@ hipError_t dispatch_d(const DecodeMfmaParams& p, int kb, int qjl, int vb, dim3 g
 
 bool mfma_decode_supports(int d, int rows) { return (d == 128 || d == 256) && rows >= 1 && rows <= 4; }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, const float* scales, float* rowc, hipStream_t st) {
-  const int64_t qrows = (int64_t)a.B * a.Hq * a.Tq;
-  hipLaunchKernelGGL(prerotate_mfma_kernel, dim3((unsigned)qrows), dim3(256), 0, st, a.q, a.q_dtype,
-                     a.d, a.R, a.S, a.qjl, scales, a.q_rot, a.q_proj, rowc);
+hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st) {
+  PrerotateParams pr{};
+  pr.q = a.q;
+  pr.qdt = a.q_dtype;
+  pr.d = a.d;
+  pr.Hq = a.Hq;
+  pr.Hkv = a.Hkv;
+  pr.Tq = a.Tq;
+  pr.qjl = a.qjl;
+  pr.Rt = x.Rt;
+  pr.St = x.St;
+  pr.scales = x.scales;
+  pr.qa = a.q_rot;
+  pr.qb = a.q_proj;
+  pr.rowc = x.rowc;
+  pr.counters = x.counters;
+  hipLaunchKernelGGL(prerotate_mfma_kernel, dim3((unsigned)((int64_t)a.B * a.Hq * a.Tq)), dim3(256), 0, st, pr);
   DecodeMfmaParams p{};
   p.qa = a.q_rot;
   p.qb = a.q_proj;
-  p.rowc = rowc;
-  p.scales = scales;
+  p.rowc = x.rowc;
+  p.scales = x.scales;
   p.kidx = a.kidx;
   p.ksign = a.ksign;
   p.knorm = a.knorm;
@@ -484,6 +629,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const float* scales, float* r
   p.vidx = a.vidx;
   p.vnorm = a.vnorm;
   p.cb = a.cb;
+  p.R = a.R;
+  p.out = a.out;
+  p.counters = x.counters;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.Tq = a.Tq;
@@ -494,8 +642,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const float* scales, float* r
   p.part = a.part;
   p.scores = a.scores;
   const dim3 grid((unsigned)(a.B * a.Hkv), (unsigned)a.nsplit);
-  hipError_t e = a.d == 128 ? dispatch_d<128>(p, a.kb, a.qjl, a.vb, grid, st)
-                            : dispatch_d<256>(p, a.kb, a.qjl, a.vb, grid, st);
+  const hipError_t e = a.d == 128 ? dispatch_d<128>(p, a.kb, a.qjl, a.vb, grid, st)
+                                  : dispatch_d<256>(p, a.kb, a.qjl, a.vb, grid, st);
   if (e != hipSuccess) return e;
   return launch_decode_combine(a, st);
 }

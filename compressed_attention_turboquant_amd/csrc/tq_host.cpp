@@ -272,6 +272,13 @@ void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, uns
     projr_f[i] = (float)SR[i];
   }
   for (int i = 0; i < d; ++i) signs_f[i] = (float)D[i];
+  float* rot_t = reinterpret_cast<float*>(image + L.rot_t);
+  float* proj_t = reinterpret_cast<float*>(image + L.proj_t);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      rot_t[(size_t)j * d + i] = (float)R[(size_t)i * d + j];
+      proj_t[(size_t)j * d + i] = (float)S[(size_t)i * d + j];
+    }
   float* cb = reinterpret_cast<float*>(image + L.codebook);
   lloyd_max_codebook(k_bits, d, cb, cb + kMaxLevels);
   lloyd_max_codebook(v_bits, d, cb + 2 * kMaxLevels, cb + 3 * kMaxLevels);

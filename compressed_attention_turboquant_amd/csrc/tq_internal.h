@@ -17,6 +17,8 @@ struct BlobLayout {
   size_t proj;      // [d][d] S row-major (QJL projection)
   size_t projr;     // [d][d] S R^T, so that S r = (S R^T)(R r) for a residual kept rotated
   size_t signs;     // [d] D (all +1 for the Haar kind)
+  size_t rot_t;     // [d][d] R^T row-major (coalesced reads of R by output index)
+  size_t proj_t;    // [d][d] S^T row-major
   size_t codebook;  // [4][16]: key centroids, key boundaries, value centroids, value boundaries
   size_t scales;    // [4]: fp16 table scale for key and value centroids, and their worst relative
                     // fp16 rounding error (see centroid_half_scale)
@@ -40,6 +42,8 @@ inline BlobLayout blob_layout(int d) {
   L.proj = o;      o = align_up(o + mat, 256);
   L.projr = o;     o = align_up(o + mat, 256);
   L.signs = o;     o = align_up(o + d * sizeof(float), 256);
+  L.rot_t = o;     o = align_up(o + mat, 256);
+  L.proj_t = o;    o = align_up(o + mat, 256);
   L.codebook = o;  o = align_up(o + 4 * kMaxLevels * sizeof(float), 256);
   L.scales = o;    o = align_up(o + 4 * sizeof(float), 256);
   L.rot_hi = o;    o = align_up(o + hmat, 256);

@@ -50,9 +50,27 @@ struct DecodeMfmaParams {
   const uint8_t *kidx, *ksign, *vidx;
   const float *knorm, *krnorm, *vnorm, *cb;
   const float* scales;              // blob: fp16 table factors for key and value centroids
+  const float* R;                   // rotation (row-major) for the final un-rotation
+  float* out;
+  int* counters;                    // per sequence: workgroups finished (reset to 0 after use)
   int Hq, Hkv, Tq, causal;
   int64_t N, cap, keys_per_split;
   float *part, *scores;
+};
+
+struct PrerotateParams {
+  const void* q;
+  int qdt, d, Hq, Hkv, Tq, qjl;
+  const float *Rt, *St, *scales;
+  float *qa, *qb, *rowc;
+  int* counters;
+};
+
+// Blob and workspace pieces the matrix-core decode needs besides DecodeArgs.
+struct DecodeMfmaExtra {
+  const float *Rt, *St, *scales;
+  float* rowc;
+  int* counters;
 };
 
 // Arguments of the matrix-core quantize kernel (tq_quantize_mfma.hip, d = 128, fp16 input).
@@ -70,8 +88,7 @@ bool mfma_quantize_supports(int d, int dtype);
 hipError_t launch_quantize_mfma(const QuantizeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 bool mfma_decode_supports(int d, int rows);
-// rowc: workspace for 4 floats per query row.
-hipError_t launch_decode_mfma(const DecodeArgs& a, const float* scales, float* rowc, hipStream_t st);
+hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st);
 hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_dequant_ref(const DequantArgs& a, hipStream_t st);
 bool ref_decode_supports(int d, int rows);

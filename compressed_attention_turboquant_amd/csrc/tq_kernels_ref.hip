@@ -322,28 +322,64 @@ __global__ void __launch_bounds__(kThreads) decode_split_ref(
 }
 
 // Merge the per-split partial softmax sums and un-rotate once per query row.
+// Partial rows are [acc (d) | max (natural log) | sum].
 __global__ void __launch_bounds__(kThreads) decode_combine_ref(const float* __restrict__ part,
                                                                int nsplit, int64_t rows_total,
                                                                int d, const float* __restrict__ R,
                                                                float* __restrict__ out) {
   __shared__ float o[256];
+  __shared__ float wts[2][1024];  // per-split weight, and its contribution to the sum
+  __shared__ float invL;
   const int64_t row = blockIdx.x;
   const int j = threadIdx.x;
+  // max over splits, then weights: one thread per split (looping if more splits than threads)
+  __shared__ float red[kThreads];
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[((int64_t)s * rows_total + row) * (d + 2) + d]);
-  float L = 0.f, a = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
+  for (int s = j; s < nsplit; s += kThreads) M = fmaxf(M, part[((int64_t)s * rows_total + row) * (d + 2) + d]);
+  red[j] = M;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (j < off) red[j] = fmaxf(red[j], red[j + off]);
+    __syncthreads();
+  }
+  M = red[0];
+  __syncthreads();
+  float lsum = 0.f;
+  for (int s = j; s < nsplit; s += kThreads) {
     const float* p = part + ((int64_t)s * rows_total + row) * (d + 2);
     const float w = p[d] == -INFINITY ? 0.f : expf(p[d] - M);
-    L = fmaf(w, p[d + 1], L);
-    if (j < d) a = fmaf(w, p[j], a);
+    if (s < 1024) wts[0][s] = w;
+    lsum = fmaf(w, p[d + 1], lsum);
   }
-  if (j < d) o[j] = a / L;
+  red[j] = lsum;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (j < off) red[j] += red[j + off];
+    __syncthreads();
+  }
+  if (j == 0) invL = 1.0f / red[0];
+  __syncthreads();
+  if (j < d) {
+    float a0 = 0.f, a1 = 0.f;
+    int s = 0;
+    for (; s + 1 < nsplit; s += 2) {
+      const float w0 = s < 1024 ? wts[0][s] : 0.f, w1 = s + 1 < 1024 ? wts[0][s + 1] : 0.f;
+      a0 = fmaf(w0, part[((int64_t)s * rows_total + row) * (d + 2) + j], a0);
+      a1 = fmaf(w1, part[((int64_t)(s + 1) * rows_total + row) * (d + 2) + j], a1);
+    }
+    for (; s < nsplit; ++s) a0 = fmaf(s < 1024 ? wts[0][s] : 0.f, part[((int64_t)s * rows_total + row) * (d + 2) + j], a0);
+    o[j] = (a0 + a1) * invL;
+  }
   __syncthreads();
   if (j >= d) return;
-  float v = 0.f;
-  for (int k = 0; k < d; ++k) v = fmaf(R[(size_t)k * d + j], o[k], v);  // (R^T o)_j
-  out[row * d + j] = v;
+  float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+  for (int k = 0; k < d; k += 4) {  // (R^T o)_j
+    v0 = fmaf(R[(size_t)k * d + j], o[k], v0);
+    v1 = fmaf(R[(size_t)(k + 1) * d + j], o[k + 1], v1);
+    v2 = fmaf(R[(size_t)(k + 2) * d + j], o[k + 2], v2);
+    v3 = fmaf(R[(size_t)(k + 3) * d + j], o[k + 3], v3);
+  }
+  out[row * d + j] = (v0 + v1) + (v2 + v3);
 }
 
 // ------------------------------------------------------------- dequantize --
