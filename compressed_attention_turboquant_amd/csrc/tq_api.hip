@@ -206,6 +206,8 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
   if (seqs > cache->seqs) return fail(TQ_ERR_INVALID_ARG, "seqs exceeds the cache's sequence count");
   if (t0 + n > cache->cap) return fail(TQ_ERR_INVALID_ARG, "t0 + n exceeds the cache capacity");
   if (seqs > 65535) return fail(TQ_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (cache->cap > ((int64_t)1 << 24) || n * layer->d > ((int64_t)1 << 31) / 4)
+    return fail(TQ_ERR_UNSUPPORTED, "at most 2^24 tokens per sequence");
   if (n > 0 && seqs > 0) {
     if (!x) return fail(TQ_ERR_INVALID_ARG, "x is NULL");
     if (!aligned16(x)) return fail(TQ_ERR_ALIGNMENT, "x must be 16-byte aligned");

@@ -60,6 +60,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kSlack = 4.f;            // log2 headroom of the lazily updated maximum
+constexpr float kInvSlack = 1.f / 16.f;  // 2^-kSlack
 
 template <int I, int N, class F>
 __device__ __forceinline__ void sfor(F&& f) {
@@ -304,8 +306,11 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, con
     }
     st[t] = s;
   }
+  // The reference maximum only moves when a score exceeds it by more than
+  // kSlack (log2 units): weights stay <= 2^kSlack, and the rare rescale keeps
+  // the sum exact (every term is relative to the same reference).
   const float mx = fmaxf(st[0], st[1]);
-  if (__any(mx > ws.m)) {
+  if (__any(mx > ws.m + kSlack)) {
     float rmax = mx;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
@@ -320,7 +325,8 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, con
   // v_exp_f32 directly: weights below 2^-126 of the running maximum become 0.
   const float p0 = __builtin_amdgcn_exp2f(st[0] - ws.msafe), p1 = __builtin_amdgcn_exp2f(st[1] - ws.msafe);
   ws.lsum += p0 + p1;
-  const float q0 = p0 * cur.vn[0], q1 = p1 * cur.vn[1];
+  // P carries 2^-kSlack so p * ||v|| keeps the fp16 range of ||v||.
+  const float q0 = p0 * cur.vn[0] * kInvSlack, q1 = p1 * cur.vn[1] * kInvSlack;
   const _Float16 h0 = (_Float16)q0, h1 = (_Float16)q1;
   pb[0][g4][l16] = h0;
   pb[0][g4][16 + l16] = h1;
@@ -453,7 +459,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
     mrg_m[wave][g4] = ws.m;
     mrg_l[wave][g4] = lsum;
   }
-  const float inv_sv = 1.0f / scale_v;
+  const float inv_sv = 16.f / scale_v;  // undoes 2^-kSlack and the fp16 table factor
 #pragma unroll
   for (int cb = 0; cb < S::CB; ++cb) mrg_acc[wave][g4][l16 * S::CB + cb] = (ws.acc[cb][0] + ws.acc[cb][1]) * inv_sv;
   __syncthreads();

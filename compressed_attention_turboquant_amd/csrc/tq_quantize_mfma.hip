@@ -110,31 +110,47 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
   qz.init(p.cent, p.bnd);
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
-  const int64_t tiles_per_seq = p.tile_last - p.tile_first + 1;
-  const int64_t groups = (p.seqs * tiles_per_seq + 3) / 4;
-  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
-    // ---- load 32 token rows (4 value tiles) into LDS, with their norms ----
+  // Work unit: 4 consecutive value tiles (32 token slots) of one sequence.
+  const int tiles = (int)(p.tile_last - p.tile_first + 1);  // tiles per sequence touched
+  const int gps = (tiles + 3) / 4;                             // groups per sequence
+  const int groups = (int)p.seqs * gps;  // < 2^31 (checked on the host)
+  const int t0 = (int)p.t0, tend = (int)(p.t0 + p.n);
+  const int rowb = D * BITS / 8;
+
+  // Loader role: 8 threads per token slot, 16 halves each.
+  const int lslot = tid / 8, lpart = tid % 8;
+  auto load_x = [&](int grp, h8& v0, h8& v1) {
+    v0 = h8{0, 0, 0, 0, 0, 0, 0, 0};
+    v1 = v0;
+    if (grp >= groups) return;
+    const int64_t s = grp / gps;  // uniform
+    const int tile = (int)p.tile_first + 4 * (grp % gps) + lslot / 8;
+    const int t = tile * 8 + lslot % 8;
+    if (4 * (grp % gps) + lslot / 8 < tiles && t >= t0 && t < tend) {
+      const _Float16* src = p.x + s * p.n * D + (t - t0) * D + lpart * 16;
+      v0 = *reinterpret_cast<const h8*>(src);
+      v1 = *reinterpret_cast<const h8*>(src + 8);
+    }
+  };
+  h8 nx0, nx1;
+  load_x((int)blockIdx.x, nx0, nx1);
+
+  for (int grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    const int64_t s = grp / gps;  // wave-uniform: scalar
+    const int gt = 4 * (grp % gps);  // first tile of the group, relative to tile_first
+    // ---- token rows into LDS, with their norms; prefetch the next group ----
     {
-      const int slot = tid / 8, part = tid % 8;  // 8 threads per token, 16 halves each
-      const int64_t tix = grp * 4 + slot / 8;
-      const int64_t s = tix / tiles_per_seq;
-      const int64_t t = (p.tile_first + tix % tiles_per_seq) * 8 + slot % 8;
-      const bool ok = tix < p.seqs * tiles_per_seq && t >= p.t0 && t < p.t0 + p.n;
-      h8 v0 = h8{0, 0, 0, 0, 0, 0, 0, 0}, v1 = v0;
-      if (ok) {
-        const _Float16* src = p.x + (s * p.n + (t - p.t0)) * D + part * 16;
-        v0 = *reinterpret_cast<const h8*>(src);
-        v1 = *reinterpret_cast<const h8*>(src + 8);
-      }
-      *reinterpret_cast<h8*>(&xs[slot][part * 16]) = v0;
-      *reinterpret_cast<h8*>(&xs[slot][part * 16 + 8]) = v1;
+      const h8 v0 = nx0, v1 = nx1;
+      *reinterpret_cast<h8*>(&xs[lslot][lpart * 16]) = v0;
+      *reinterpret_cast<h8*>(&xs[lslot][lpart * 16 + 8]) = v1;
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf((float)v0[e], (float)v0[e], fmaf((float)v1[e], (float)v1[e], ss));
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
       ss += __shfl_xor(ss, 4);
-      if (part == 0) nrm[slot] = sqrtf(ss);
+      if (lpart == 0) nrm[lslot] = sqrtf(ss);
+      load_x(grp + (int)gridDim.x, nx0, nx1);
     }
     __syncthreads();
 
@@ -166,10 +182,13 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
     }
 
     if constexpr (!VALUES) {
+      uint8_t* idx_s = p.idx + s * p.cap * rowb;
       // Lane (g4, l16) holds coordinates 32w + 8g4 + 4ct + r of token slot 16tt + l16.
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int slot = 16 * tt + l16;
+        const int t = ((int)p.tile_first + gt + slot / 8) * 8 + slot % 8;
+        const bool ok = gt + slot / 8 < tiles && t >= t0 && t < tend;
         const float nn = nrm[slot];
         const float inv = nn > 0.f ? inv_sqrt_d / nn : 0.f;
         uint32_t packed = 0;
@@ -186,14 +205,11 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
             r[4 * ct + q] = y - c;
             rr = fmaf(r[4 * ct + q], r[4 * ct + q], rr);
           }
-        const int64_t tix = grp * 4 + slot / 8;
-        const int64_t s = tix / tiles_per_seq;
-        const int64_t t = (p.tile_first + tix % tiles_per_seq) * 8 + slot % 8;
-        const bool ok = tix < p.seqs * tiles_per_seq && t >= p.t0 && t < p.t0 + p.n;
         if (ok) {
-          uint8_t* dst = p.idx + (s * p.cap + t) * (D * BITS / 8) + (4 * w + g4) * BITS;
+          uint8_t* dst = idx_s + t * rowb + (4 * w + g4) * BITS;
 #pragma unroll
           for (int b = 0; b < BITS; ++b) dst[b] = (uint8_t)(packed >> (8 * b));
+          if (w == 0 && g4 == 0) p.norm[s * p.cap + t] = nn;
         }
         if constexpr (QJL) {
           h8 hi, lo;
@@ -207,7 +223,6 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
           *reinterpret_cast<h8*>(&rs[1][slot][32 * w + 8 * g4]) = lo;
           rsq[slot][4 * w + g4] = rr;
         }
-        if (w == 0 && g4 == 0 && ok) p.norm[s * p.cap + t] = nn;
       }
       if constexpr (QJL) {
         __syncthreads();
@@ -231,25 +246,26 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
             }
           }
         }
+        uint8_t* sign_s = p.sign + s * p.cap * (D / 8);
+        float* rn_s = p.rnorm + s * p.cap;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int slot = 16 * tt + l16;
+          const int t = ((int)p.tile_first + gt + slot / 8) * 8 + slot % 8;
+          const bool ok = gt + slot / 8 < tiles && t >= t0 && t < tend;
           uint32_t bits = 0;
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bits |= (pacc[ct][tt][q] >= 0.f ? 1u : 0u) << (4 * ct + q);
-          const int64_t tix = grp * 4 + slot / 8;
-          const int64_t s = tix / tiles_per_seq;
-          const int64_t t = (p.tile_first + tix % tiles_per_seq) * 8 + slot % 8;
-          const bool ok = tix < p.seqs * tiles_per_seq && t >= p.t0 && t < p.t0 + p.n;
+            for (int q = 0; q < 4; ++q)  // sign bit of the float, inverted: 1 for >= +0
+              bits |= ((__float_as_uint(pacc[ct][tt][q]) >> 31) ^ 1u) << (4 * ct + q);
           if (ok) {
-            p.sign[(s * p.cap + t) * (D / 8) + 4 * w + g4] = (uint8_t)bits;
+            sign_s[t * (D / 8) + 4 * w + g4] = (uint8_t)bits;
             if (w == 0 && g4 == 0) {
               float g = 0.f;
 #pragma unroll
               for (int i = 0; i < 16; ++i) g += rsq[slot][i];
-              p.rnorm[s * p.cap + t] = sqrtf(g);
+              rn_s[t] = sqrtf(g);
             }
           }
         }
@@ -257,21 +273,20 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
     } else {
       // Lane (g4, l16) holds, for coordinate tile ct, coordinate out_coord(w, ct, l16)
       // of the 8 tokens of value tile g4 (token 4 tt + r in D row 4 g4 + r of tile tt).
-      const int64_t tix = grp * 4 + g4;
-      const bool tile_ok = tix < p.seqs * tiles_per_seq;
-      const int64_t s = tile_ok ? tix / tiles_per_seq : 0;
-      const int64_t tile = p.tile_first + (tile_ok ? tix % tiles_per_seq : 0);
+      const bool tile_ok = gt + g4 < tiles;
+      const int tile = (int)p.tile_first + gt + g4;
       uint32_t keep = 0;  // code bits of tokens outside [t0, t0+n) are left unchanged
       float inv[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int64_t t = tile * 8 + k;
-        const bool ok = t >= p.t0 && t < p.t0 + p.n;
+        const int t = tile * 8 + k;
+        const bool ok = t >= t0 && t < tend;
         if (!ok) keep |= ((1u << BITS) - 1u) << (BITS * k);
         const float nn = nrm[8 * g4 + k];
         inv[k] = nn > 0.f ? inv_sqrt_d / nn : 0.f;
         if (ok && tile_ok && w == 0 && l16 == 0) p.norm[s * p.cap + t] = nn;
       }
+      uint8_t* tile_base = p.idx + s * (p.cap / 8) * (D * BITS) + tile * (D * BITS);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         uint32_t packed = 0;
@@ -284,7 +299,7 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
             packed |= qz.code(acc[ct][tt][q] * inv[k], c) << (BITS * k);
           }
         if (tile_ok) {
-          uint8_t* dst = p.idx + (s * (p.cap / 8) + tile) * (D * BITS) + out_coord(w, ct, l16) * BITS;
+          uint8_t* dst = tile_base + out_coord(w, ct, l16) * BITS;
           if (keep) {
             uint32_t old = 0;
 #pragma unroll
@@ -346,7 +361,7 @@ hipError_t launch_quantize_mfma(const QuantizeArgs& a, hipStream_t st) {
   p.sign = a.sign;
   p.norm = a.norm;
   p.rnorm = a.rnorm;
-  const int64_t groups = (a.seqs * (p.tile_last - p.tile_first + 1) + 3) / 4;
+  const int64_t groups = a.seqs * ((p.tile_last - p.tile_first + 1 + 3) / 4);
   if (a.value_layout) return dispatch_bits<0, 1>(p, a.bits, groups, st);
   if (a.qjl) return dispatch_bits<1, 0>(p, a.bits, groups, st);
   return dispatch_bits<0, 0>(p, a.bits, groups, st);
