@@ -14,7 +14,6 @@ Printed (one JSON line on stdout):
   cpu_baseline       the fp64 oracle on a bounded sample of the same workload
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -37,17 +36,6 @@ def packed_bytes_per_token(cfg):
     return k, v
 
 
-def kernel_sources_digest():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "compressed_attention_turboquant_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def traffic_from_profile(kernel_tag, workload, digest, per_launch_units):
     """HBM bytes per launch from committed rocprofv3 counter summaries, or None
     if there are none or the kernels changed since they were taken."""
@@ -61,8 +49,14 @@ def traffic_from_profile(kernel_tag, workload, digest, per_launch_units):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, K_dev, V_dev, q_dev):
-    """Time the fp64 oracle (as it stands) on one (batch, KV head) sequence."""
+def cpu_baseline(cfg, K_dev, V_dev, q_dev, budget_s=8.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload.
+
+    Decode: whole (batch 0, KV head h) sequences, decoded from packed bytes for
+    the G query heads that share them, one after another until `budget_s` has
+    passed.  Quantize: chunks of 8192 K rows and 8192 V rows taken from the
+    sequences in order, until `budget_s` has passed.  Rates are scaled to the
+    metric's units (packed-KV GB/s, vectors/s)."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_info
@@ -71,41 +65,61 @@ def cpu_baseline(cfg, K_dev, V_dev, q_dev):
         cores = os.cpu_count() or 1
     from oracle import attention, codebook, codec, transforms
 
-    d, N = cfg.d, cfg.N
+    d, N, G = cfg.d, cfg.N, cfg.G
     R = transforms.rotation(d, cfg.rot, cfg.layer_seed)
     S = transforms.gaussian_projection(d, cfg.layer_seed)
     ck, bk = codebook.codebook(cfg.k_bits, d)
     cv, bv = codebook.codebook(cfg.v_bits, d)
-    xk = K_dev[0, 0, :N].float().cpu().numpy()
-    xv = V_dev[0, 0, :N].float().cpu().numpy()
-    q = q_dev[:1, : cfg.G].float().cpu().numpy()          # the G query heads of KV head 0
-    nq = 16384
-    t0 = time.perf_counter()
-    codec.encode_rows(xk[:nq], R, ck, bk, S if cfg.k_qjl else None)
-    codec.encode_rows(xv[:nq], R, cv, bv)
-    t_quant = time.perf_counter() - t0
-    # encode the whole sequence (untimed) and decode it from packed bytes (timed)
-    ek = codec.encode_rows(xk, R, ck, bk, S if cfg.k_qjl else None)
-    ev = codec.encode_rows(xv, R, cv, bv)
-    packed = {"k_idx": codec.pack_key_codes(ek["idx"], cfg.k_bits), "k_norm": ek["norm"].astype(np.float32),
-              "v_idx": codec.pack_value_codes(ev["idx"].reshape(1, N, d), cfg.v_bits),
-              "v_norm": ev["norm"].astype(np.float32)}
-    if cfg.k_qjl:
-        packed["k_sign"] = codec.pack_key_codes(ek["sign"].astype(np.int64), 1)
-        packed["k_rnorm"] = ek["rnorm"].astype(np.float32)
-    t0 = time.perf_counter()
-    cache = attention.unpack_cache(packed, 1, 1, N, d, cfg.k_bits, cfg.v_bits, cfg.k_qjl)
-    attention.decode(q, R, S, ck, cv, cache, N, bool(cfg.causal))
-    t_dec = time.perf_counter() - t0
+    Sk = S if cfg.k_qjl else None
+    seqs = [(b, h) for b in range(cfg.B) for h in range(cfg.Hkv)]
+
+    # quantize: 8192-row chunks until the budget is spent
+    chunk, nq = 8192, 0
+    t_quant = 0.0
+    for b, h in seqs:
+        for t0 in range(0, N, chunk):
+            xk = K_dev[b, h, t0:t0 + chunk].double().cpu().numpy()
+            xv = V_dev[b, h, t0:t0 + chunk].double().cpu().numpy()
+            t = time.perf_counter()
+            codec.encode_rows(xk, R, ck, bk, Sk)
+            codec.encode_rows(xv, R, cv, bv)
+            t_quant += time.perf_counter() - t
+            nq += xk.shape[0]
+            if t_quant >= budget_s:
+                break
+        if t_quant >= budget_s:
+            break
+
+    # decode: whole sequences (packed untimed, unpack + decode timed)
+    t_dec, nseq = 0.0, 0
+    for b, h in seqs:
+        xk = K_dev[b, h, :N].double().cpu().numpy()
+        xv = V_dev[b, h, :N].double().cpu().numpy()
+        q = q_dev[b:b + 1, h * G:(h + 1) * G].double().cpu().numpy()
+        ek = codec.encode_rows(xk, R, ck, bk, Sk)
+        ev = codec.encode_rows(xv, R, cv, bv)
+        packed = {"k_idx": codec.pack_key_codes(ek["idx"], cfg.k_bits), "k_norm": ek["norm"].astype(np.float32),
+                  "v_idx": codec.pack_value_codes(ev["idx"].reshape(1, N, d), cfg.v_bits),
+                  "v_norm": ev["norm"].astype(np.float32)}
+        if cfg.k_qjl:
+            packed["k_sign"] = codec.pack_key_codes(ek["sign"].astype(np.int64), 1)
+            packed["k_rnorm"] = ek["rnorm"].astype(np.float32)
+        t = time.perf_counter()
+        cache = attention.unpack_cache(packed, 1, 1, N, d, cfg.k_bits, cfg.v_bits, cfg.k_qjl)
+        attention.decode(q, R, S, ck, cv, cache, N, bool(cfg.causal))
+        t_dec += time.perf_counter() - t
+        nseq += 1
+        if t_dec >= budget_s:
+            break
     kb, vb = packed_bytes_per_token(cfg)
     return {
-        "value": round((kb + vb) * N / t_dec / 1e9, 4),
+        "value": round((kb + vb) * N * nseq / t_dec / 1e9, 4),
         "unit": "GB/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"decode of 1 of {cfg.B * cfg.Hkv} (batch, KV head) sequences ({cfg.G} query heads x "
-                  f"{N} keys, from packed bytes) in {t_dec:.2f} s; quantize of {nq} K + {nq} V rows "
-                  f"in {t_quant:.2f} s",
+        "sample": f"decode of {nseq} of {len(seqs)} (batch, KV head) sequences ({G * cfg.Tq} query rows x "
+                  f"{N} keys each, unpacked from packed bytes) in {t_dec:.2f} s; quantize of {nq} K + "
+                  f"{nq} V rows in {t_quant:.2f} s",
         "quantize_vectors_per_s": round(2 * nq / t_quant, 1),
     }
 
@@ -128,6 +142,7 @@ def main():
     import torch
     import workloads
     from compressed_attention_turboquant_amd import binding as B
+    from compressed_attention_turboquant_amd.profsummary import kernel_sources_digest
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = workloads.CONFIGS[args.workload]

@@ -1,0 +1,180 @@
+"""Turn rocprofv3 CSV output of a bench.py run into short text summaries.
+
+Usage (on the machine that ran the profiles):
+
+    python -m compressed_attention_turboquant_amd.profsummary \
+        --workload C3 --trace DIR_T --fetch DIR_F --write DIR_W \
+        --trace-cmd "..." --fetch-cmd "..." --write-cmd "..." --out profiles
+
+DIR_T holds `<prefix>_kernel_stats.csv` from `rocprofv3 --kernel-trace --stats
+--output-format csv`; DIR_F / DIR_W hold `<prefix>_counter_collection.csv`
+from `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
+`bench.py --copy-calibration`.  The 1 GiB device copy that bench.py runs after
+its timed region (the runtime's copy-buffer kernel, dispatched after the last
+library kernel) calibrates both counters: its known byte count divided by what
+the counter reports gives the factor that turns a counter reading into bytes.
+
+Writes `kernels_<workload>.md` (per-kernel durations), `traffic_<workload>.md`
+(per-dispatch HBM bytes next to the algorithmic bytes) and, for bench.py,
+`traffic_decode_<workload>.json` and `traffic_quantize_<workload>.json`, each
+stamped with the digest of the kernel sources they were measured on.
+"""
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+
+# (tag, substring of the kernel name) for the launches one library call makes
+DECODE_KERNELS = ("prerotate", "decode_mfma_kernel", "decode_split_ref", "decode_combine")
+QUANT_KERNELS = ("quantize_mfma_kernel", "quantize_tile_ref", "quantize_fwht")
+
+
+def kernel_sources_digest():
+    """sha256 over the library's kernel and host sources (file names and bytes)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _one(directory, suffix):
+    hits = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return hits[0]
+
+
+def _short(name):
+    name = name.replace("tq::(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0] if "(" in name and "<" not in name.split("(")[0][-2:] else name[:80]
+
+
+def kernel_stats(directory):
+    rows = list(csv.DictReader(open(_one(directory, "kernel_stats.csv"))))
+    return [r for r in rows if "tq::" in r["Name"]]
+
+
+def counters(directory, counter):
+    """Per-kernel list of counter values (KiB per dispatch) in dispatch order,
+    plus the copy-buffer dispatches that follow the last library dispatch."""
+    rows = [r for r in csv.DictReader(open(_one(directory, "counter_collection.csv")))
+            if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    last_tq = max(int(r["Dispatch_Id"]) for r in rows if "tq::" in r["Kernel_Name"])
+    per = collections.defaultdict(list)
+    copy = 0.0
+    for r in rows:
+        v = float(r["Counter_Value"])
+        if "tq::" in r["Kernel_Name"]:
+            per[r["Kernel_Name"]].append(v)
+        elif int(r["Dispatch_Id"]) > last_tq and "copyBuffer" in r["Kernel_Name"]:
+            copy += v
+    if copy <= 0:
+        raise SystemExit(f"{counter}: no calibration copy after the library kernels")
+    return per, COPY_BYTES / (copy * 1024.0)
+
+
+def packed_bytes(cfg):
+    k = cfg.d * cfg.k_bits // 8 + 4 + (cfg.d // 8 + 4 if cfg.k_qjl else 0)
+    v = cfg.d * cfg.v_bits // 8 + 4
+    return k, v
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--trace-cmd", required=True)
+    ap.add_argument("--fetch-cmd", required=True)
+    ap.add_argument("--write-cmd", required=True)
+    ap.add_argument("--out", default="profiles")
+    a = ap.parse_args()
+
+    import sys
+    sys.path.insert(0, os.path.dirname(PKG))
+    import workloads
+    cfg = workloads.CONFIGS[a.workload]
+    digest = kernel_sources_digest()
+    os.makedirs(a.out, exist_ok=True)
+
+    stats = kernel_stats(a.trace)
+    lines = [f"# Kernel durations, workload {cfg.name}", "",
+             f"{workloads.WORKLOAD_TEXT[cfg.name]}", "",
+             f"Kernel sources digest: `{digest}`", "", "Command (from the repository root, TMPDIR=/tmp):", "", "```",
+             a.trace_cmd, "```", "", "Summary written by `python -m compressed_attention_turboquant_amd.profsummary`.", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    dec_sum = 0.0
+    for r in stats:
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {avg:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {r['Percentage']}% |")
+        if any(k in r["Name"] for k in DECODE_KERNELS):
+            dec_sum += avg
+    kb, vb = packed_bytes(cfg)
+    rows = cfg.B * cfg.Hkv * cfg.N
+    lines += ["", f"Sum of the decode call's kernel averages: {dec_sum:.1f} us; packed KV read "
+              f"{(kb + vb) * rows / 1e9:.4f} GB, i.e. {(kb + vb) * rows / dec_sum / 1e3:.0f} GB/s "
+              "over the kernels alone."]
+    with open(os.path.join(a.out, f"kernels_{cfg.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    fetch, ff = counters(a.fetch, "FETCH_SIZE")
+    write, fw = counters(a.write, "WRITE_SIZE")
+    in_b = 2 if cfg.dtype == "f16" else 4
+    algo = {"decode": (kb + vb) * rows,
+            "quantize K": rows * (cfg.d * in_b + kb), "quantize V": rows * (cfg.d * in_b + vb)}
+    t = [f"# HBM traffic per dispatch, workload {cfg.name}", "",
+         f"Kernel sources digest: `{digest}`", "", "Commands (from the repository root, TMPDIR=/tmp):", "",
+         "```", a.fetch_cmd, a.write_cmd, "```", "",
+         "Summary written by `python -m compressed_attention_turboquant_amd.profsummary`.", "",
+         f"Calibration with the 1 GiB device copy bench.py runs after its timed region: "
+         f"FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {fw:.4f} give bytes.", "",
+         "| kernel | dispatches | read (MB) | written (MB) |", "|---|---:|---:|---:|"]
+    per_kernel = {}
+    for name in sorted(set(fetch) | set(write)):
+        fr = fetch.get(name, [0.0])
+        wr = write.get(name, [0.0])
+        rb = sum(fr) / len(fr) * 1024 * ff
+        wb = sum(wr) / len(wr) * 1024 * fw
+        per_kernel[name] = (rb, wb)
+        t.append(f"| `{_short(name)}` | {len(fr)} | {rb / 1e6:.2f} | {wb / 1e6:.2f} |")
+
+    def total(keys, which=None):
+        tot = 0.0
+        for name, (rb, wb) in per_kernel.items():
+            if any(k in name for k in keys) and (which is None or which(name)):
+                tot += rb + wb
+        return tot
+
+    dec = total(DECODE_KERNELS)
+    quant = total(QUANT_KERNELS)
+    t += ["", f"Decode call (all its launches): {dec / 1e9:.4f} GB moved vs {algo['decode'] / 1e9:.4f} GB "
+          "of packed KV (algorithmic).",
+          f"Quantize K + V calls: {quant / 1e9:.4f} GB moved vs "
+          f"{(algo['quantize K'] + algo['quantize V']) / 1e9:.4f} GB (input rows in, packed rows out)."]
+    with open(os.path.join(a.out, f"traffic_{cfg.name}.md"), "w") as f:
+        f.write("\n".join(t) + "\n")
+    for tag, val, alg in (("decode", dec, algo["decode"]),
+                          ("quantize", quant, algo["quantize K"] + algo["quantize V"])):
+        with open(os.path.join(a.out, f"traffic_{tag}_{cfg.name}.json"), "w") as f:
+            json.dump({"workload": cfg.name, "sources_digest": digest, "bytes_per_launch": round(val),
+                       "algorithmic_bytes_per_launch": alg, "fetch_factor": round(ff, 4),
+                       "write_factor": round(fw, 4), "commands": [a.fetch_cmd, a.write_cmd]}, f, indent=1)
+    print("\n".join(lines + [""] + t))
+
+
+if __name__ == "__main__":
+    main()
