@@ -64,6 +64,10 @@ def compare_codes(gpu_idx, enc, boundaries, what):
 
 
 def compare_key_extras(gpu_sign, gpu_rnorm, enc, flipped, what):
+    """Check sign bits (exact outside the band) and residual norms of the rows
+    whose codes matched.  Returns a boolean per row: True where a sign bit
+    differed (legally, inside the band) -- such a key's score differs by
+    gamma sqrt(pi/2)/d * 2 |(S q)_i|, so score comparisons leave it out."""
     keep = ~flipped
     sdiff = (gpu_sign != enc["sign"]) & keep[:, None]
     sband = np.abs(enc["proj"]) < BAND
@@ -71,6 +75,7 @@ def compare_key_extras(gpu_sign, gpu_rnorm, enc, flipped, what):
     assert not bad.any(), f"{what}: {int(bad.sum())} sign bits differ outside the band"
     np.testing.assert_allclose(gpu_rnorm[keep], enc["rnorm"][keep], rtol=1e-5, atol=1e-6,
                                err_msg=f"{what}: residual norms")
+    return sdiff.any(axis=1)
 
 
 def score_scale(q, R, S, ck, cache, N, G, qjl):

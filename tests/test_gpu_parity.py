@@ -103,7 +103,7 @@ def test_decode_on_random_cache(name):
 @pytest.mark.parametrize("name", list(REDUCED))
 def test_end_to_end_from_raw_inputs(name):
     """Quantize K and V and decode on the GPU; the oracle encodes the same raw
-    inputs itself.  Keys whose code differs inside the boundary band are left
+    inputs itself.  Keys whose code or sign bit differs inside the boundary band are left
     out of the score comparison; the output must still be within 2e-3."""
     cfg = REDUCED[name]
     H.log(f"[end to end] {name}")
@@ -115,6 +115,9 @@ def test_end_to_end_from_raw_inputs(name):
     _, _, V, ev, _ = H.run_quantize_both(cfg, xv, B.TQ_VALUES, layer, ol)
     rows = np.array([s * cap + t for s in range(S) for t in range(N)])
     kflip = H.compare_codes(H.gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), ek, ol.bk, "K")
+    if cfg.k_qjl:
+        kflip = kflip | H.compare_key_extras(H.gpu_signs(K, S, cap, d, rows), K["rnorm"].cpu().numpy()[rows],
+                                             ek, kflip, "K")
     q_np = workloads.q_numpy(cfg, seed=2)
     q = torch.from_numpy(q_np).cuda()
     out, scores = B.attn_decode(layer, q, K, V, N, cfg.Hkv, cfg.causal, want_scores=True)
@@ -210,6 +213,9 @@ def test_edge_shapes_single_key_zero_rows_and_head_dims():
         S, N, d = xk.shape
         rows = np.array([s * cap + t for s in range(S) for t in range(N)])
         kflip = H.compare_codes(H.gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), ek, ol.bk, "K")
+        if cfg.k_qjl:
+            kflip = kflip | H.compare_key_extras(H.gpu_signs(K, S, cap, d, rows),
+                                                 K["rnorm"].cpu().numpy()[rows], ek, kflip, "K")
         assert K["norm"].view(S, cap)[:, 0].abs().max().item() == 0.0
         q_np = workloads.q_numpy(cfg, seed=5)
         out, scores = B.attn_decode(layer, torch.from_numpy(q_np).cuda(), K, V, N, cfg.Hkv,
