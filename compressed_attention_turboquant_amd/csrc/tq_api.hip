@@ -224,6 +224,8 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
   a.bits = which == TQ_KEYS ? layer->k_bits : layer->v_bits;
   a.qjl = which == TQ_KEYS ? layer->k_qjl : 0;
   a.value_layout = which == TQ_VALUES;
+  a.rot = layer->rot;
+  a.dsign = blob_f(layer, BL.signs);
   a.R = blob_f(layer, BL.rot);
   a.SR = blob_f(layer, BL.projr);
   a.cent = blob_f(layer, BL.codebook) + (which == TQ_KEYS ? 0 : 2 * kMaxLevels);
@@ -237,6 +239,7 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
   a.norm = cache->norm;
   a.rnorm = cache->rnorm;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fwht_quantize_supports(a.d, a.rot, a.qjl)) return hip_status(launch_quantize_fwht(a, st), "quantize launch");
   if (mfma_quantize_supports(a.d, a.dtype)) return hip_status(launch_quantize_mfma(a, st), "quantize launch");
   return hip_status(launch_quantize_ref(a, st), "quantize launch");
 }

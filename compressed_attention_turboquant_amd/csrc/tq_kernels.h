@@ -11,8 +11,9 @@ struct QuantizeArgs {
   const void* x;
   int dtype;
   int64_t seqs, n, t0, cap;
-  int d, bits, qjl, value_layout;
+  int d, bits, qjl, value_layout, rot;
   const float *R, *SR, *cent, *bnd;  // rotation, S R^T, codebook
+  const float* dsign;                // [d] +-1 signs D of the Hadamard rotation
   const void *rot_hi, *rot_lo, *projr_hi, *projr_lo;  // half splits for MFMA
   uint8_t *idx, *sign;
   float *norm, *rnorm;
@@ -86,6 +87,8 @@ struct QuantMfmaParams {
 hipError_t launch_quantize_ref(const QuantizeArgs& a, hipStream_t st);
 bool mfma_quantize_supports(int d, int dtype);
 hipError_t launch_quantize_mfma(const QuantizeArgs& a, hipStream_t st);
+bool fwht_quantize_supports(int d, int rot, int qjl);
+hipError_t launch_quantize_fwht(const QuantizeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 bool mfma_decode_supports(int d, int rows);
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st);

@@ -1,0 +1,321 @@
+// Key/value compression with the randomized Hadamard rotation, without QJL
+// (gfx950, vector ALU).
+//
+// Per token x ([Mobilint] "How JL Matrices Evolved": the rotation H D with a
+// normalised Sylvester H and random signs D; "Designing the Optimal Codebook
+// Without Data" and "TurboQuant: Theoretical Optimality via Scalar
+// Quantization" for the scalar quantizer):
+//   n = ||x||;  y = H (D x) / n  (H with entries +-1/sqrt(d));
+//   idx_j = #{i : beta_i < y_j};  pack idx.
+// The rotation is a fast Walsh-Hadamard transform: d log2(d) adds per row,
+// no matrix multiply, so the kernel is bound by HBM (d fp16 in, d*b/8 bytes +
+// a norm out per row).
+//
+// Mapping to CDNA4 (one 64-lane wave per 8-token tile):
+//  * Lane l works on token t = (l>>2 & 1) | (l>>3 & 6) of the tile and holds the
+//    coordinates j = 8k + 64c + e (e < 8, c < d/64) with k = (l & 3) | (l>>1 & 4):
+//    8 lanes share a token.  Index bits 0-2 and 6-7 of j live in registers,
+//    bits 3, 4 and 5 in lane bits 0, 1 and 3, so every cross-lane butterfly is
+//    one DPP move (quad_perm for lane xor 1 and 2, row_ror:8 for lane xor 8)
+//    plus one FMA with a +-1 factor.
+//  * Each chunk of 8 coordinates is one 16-byte load of fp16 input (a token's
+//    8 lanes read 128 contiguous bytes per load).
+//  * Codes go through LDS as bytes ([token][coordinate]) and leave as whole
+//    dwords: keys as 32-coordinate pieces of a token's stream, values as
+//    4-coordinate x 8-token pieces of the tile's coordinate-major stream.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cmath>
+#include <type_traits>
+
+#include "tq_kernels.h"
+
+namespace tq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppXor8 = 0x128; // row_ror:8 (within a row of 16 lanes: lane ^ 8)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int BITS>
+struct Codes {
+  static constexpr int K = (1 << (BITS - 1)) - 1;  // positive boundaries
+  float beta[K > 0 ? K : 1];
+  __device__ void init(const float* bnd) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) beta[i] = bnd[K + 1 + i];
+  }
+  // #{i : boundary_i < y} for the symmetric boundaries (middle one 0).
+  __device__ __forceinline__ uint32_t code(float y) const {
+    const float a = fabsf(y);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < K; ++i) cnt += a > beta[i] ? 1u : 0u;
+    return y > 0.f ? (uint32_t)(K + 1) + cnt : (uint32_t)K - cnt;
+  }
+};
+
+// Bytes per LDS code row: a multiple of 16 words plus 16 (mod 64 words), so the
+// 8-byte writes of the 32 lanes of a half wave fall in distinct banks.
+template <int D>
+constexpr int lds_row() { return (D / 4) % 32 == 0 ? D + 64 : D; }
+
+struct FwhtParams {
+  const void* x;
+  int64_t seqs, n, t0, cap;
+  int64_t tile_first, tiles;  // tiles touched per sequence
+  const float *dsign, *bnd;
+  uint8_t* idx;
+  float* norm;
+};
+
+template <int D, int BITS, int VALUES, typename Tin>
+__global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
+  constexpr int NC = D / 64, V = 8 * NC, ROW = lds_row<D>();
+  __shared__ __align__(16) uint8_t codes[kWaves][8][ROW];
+
+  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int k = (lane & 3) | ((lane >> 1) & 4);
+  const int tl = ((lane >> 2) & 1) | ((lane >> 3) & 6);
+
+  // D signs of this lane's coordinates, as sign-bit masks.
+  uint32_t dmask[V];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dmask[8 * c + e] = p.dsign[8 * k + 64 * c + e] < 0.f ? 0x80000000u : 0u;
+  // +1 where this lane is the lower partner of a cross-lane butterfly.
+  const float s1 = (lane & 1) ? -1.f : 1.f, s2 = (lane & 2) ? -1.f : 1.f, s8 = (lane & 8) ? -1.f : 1.f;
+  Codes<BITS> cq;
+  cq.init(p.bnd);
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+
+  const int64_t items = p.seqs * p.tiles;
+  const int64_t wstride = (int64_t)gridDim.x * kWaves;
+  const int64_t t0 = p.t0, tend = p.t0 + p.n;
+  constexpr int kRowB = D * BITS / 8;  // key stream bytes per token
+
+  const bool small = items <= 0x7FFFFFFF;
+  auto split = [&](int64_t item, int64_t& s, int64_t& tile) {  // item -> (sequence, tile)
+    if (small) {
+      const uint32_t q = (uint32_t)item / (uint32_t)p.tiles;
+      s = q;
+      tile = p.tile_first + ((uint32_t)item - q * (uint32_t)p.tiles);
+    } else {
+      s = item / p.tiles;
+      tile = p.tile_first + item % p.tiles;
+    }
+  };
+  // Raw input of one tile for this lane: NC chunks of 8 values.
+  typedef typename std::conditional<std::is_same<Tin, _Float16>::value, h8, f8>::type Raw;
+  auto load = [&](int64_t item, Raw (&raw)[NC]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) raw[c] = Raw{};
+    if (item >= items) return;
+    int64_t s, tile;
+    split(item, s, tile);
+    const int64_t t = tile * 8 + tl;
+    if (t < t0 || t >= tend) return;
+    const Tin* src = static_cast<const Tin*>(p.x) + (s * p.n + (t - t0)) * D + 8 * k;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) raw[c] = *reinterpret_cast<const Raw*>(src + 64 * c);
+  };
+
+  int64_t item = (int64_t)blockIdx.x * kWaves + w;
+  Raw nx[NC];
+  load(item, nx);
+  for (; item < items; item += wstride) {
+    float x[V];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * c + e] = (float)nx[c][e];
+    load(item + wstride, nx);
+
+    int64_t s, tile;
+    split(item, s, tile);
+
+    // ---- norm (8 lanes per token) ----
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) ss = fmaf(x[v], x[v], ss);
+    ss += dpp<kDppXor1>(ss);
+    ss += dpp<kDppXor2>(ss);
+    ss += dpp<kDppXor8>(ss);
+    const float nn = sqrtf(ss);
+    const float inv = nn > 0.f ? inv_sqrt_d / nn : 0.f;
+
+    // ---- D, then the unnormalised Walsh-Hadamard transform ----
+#pragma unroll
+    for (int v = 0; v < V; ++v) x[v] = __uint_as_float(__float_as_uint(x[v]) ^ dmask[v]);
+#pragma unroll
+    for (int b = 1; b < V; b <<= 1) {  // register bits: e (1, 2, 4) then c (8, 16)
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        if (v & b) continue;
+        const float u = x[v], z = x[v + b];
+        x[v] = u + z;
+        x[v + b] = u - z;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) x[v] = fmaf(s1, x[v], dpp<kDppXor1>(x[v]));
+#pragma unroll
+    for (int v = 0; v < V; ++v) x[v] = fmaf(s2, x[v], dpp<kDppXor2>(x[v]));
+#pragma unroll
+    for (int v = 0; v < V; ++v) x[v] = fmaf(s8, x[v], dpp<kDppXor8>(x[v]));
+
+    // ---- codes into LDS, [token][coordinate] ----
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wd[e / 4] |= cq.code(x[8 * c + e] * inv) << (8 * (e % 4));
+      *reinterpret_cast<uint2*>(&codes[w][tl][8 * k + 64 * c]) = make_uint2(wd[0], wd[1]);
+    }
+    const int64_t tok = tile * 8 + tl;
+    if (k == 0 && tok >= t0 && tok < tend) p.norm[s * p.cap + tok] = nn;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- pack 32 codes per lane into BITS dwords and store ----
+    if (lane < D / 4) {
+      uint32_t cw[8];  // 32 code bytes, in stream order
+      if constexpr (!VALUES) {
+        const int t = lane / (D / 32), jb = lane % (D / 32);
+        const u4 a = *reinterpret_cast<const u4*>(&codes[w][t][32 * jb]);
+        const u4 b = *reinterpret_cast<const u4*>(&codes[w][t][32 * jb + 16]);
+        cw[0] = a[0]; cw[1] = a[1]; cw[2] = a[2]; cw[3] = a[3];
+        cw[4] = b[0]; cw[5] = b[1]; cw[6] = b[2]; cw[7] = b[3];
+      } else {
+        // positions 8 j + t for j = 4 lane .. 4 lane + 3: byte i of word t holds (j = 4 lane + i, t)
+        uint32_t r[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) r[t] = *reinterpret_cast<const uint32_t*>(&codes[w][t][4 * lane]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // stream bytes 8i .. 8i+7 = coordinate 4 lane + i, tokens 0..7
+          uint32_t lo = 0, hi = 0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) lo |= ((r[t] >> (8 * i)) & 0xFFu) << (8 * t);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) hi |= ((r[4 + t] >> (8 * i)) & 0xFFu) << (8 * t);
+          cw[2 * i] = lo;
+          cw[2 * i + 1] = hi;
+        }
+      }
+      uint32_t out[BITS];
+#pragma unroll
+      for (int q = 0; q < BITS; ++q) out[q] = 0u;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t cd = (cw[i / 4] >> (8 * (i % 4))) & 0xFFu;
+        const int bit = BITS * i;
+        out[bit / 32] |= cd << (bit % 32);
+        if (bit % 32 + BITS > 32) out[bit / 32 + 1] |= cd >> (32 - bit % 32);
+      }
+      if constexpr (!VALUES) {
+        const int t = lane / (D / 32), jb = lane % (D / 32);
+        const int64_t tk = tile * 8 + t;
+        if (tk >= t0 && tk < tend) {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(p.idx + (s * p.cap + tk) * kRowB + jb * 4 * BITS);
+#pragma unroll
+          for (int q = 0; q < BITS; ++q) dst[q] = out[q];
+        }
+      } else {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(p.idx + (s * (p.cap / 8) + tile) * (D * BITS) + lane * 4 * BITS);
+        const int64_t first = tile * 8;
+        if (first < t0 || first + 8 > tend) {
+          // partial tile: keep the codes of tokens outside [t0, t0 + n)
+          uint32_t keep[BITS];
+#pragma unroll
+          for (int q = 0; q < BITS; ++q) keep[q] = 0u;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const int64_t tk = first + (i % 8);
+            if (tk < t0 || tk >= tend) {
+              const uint32_t m = (1u << BITS) - 1u;
+              const int bit = BITS * i;
+              keep[bit / 32] |= m << (bit % 32);
+              if (bit % 32 + BITS > 32) keep[bit / 32 + 1] |= m >> (32 - bit % 32);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < BITS; ++q) out[q] = (out[q] & ~keep[q]) | (dst[q] & keep[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < BITS; ++q) dst[q] = out[q];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int D, int VALUES, typename Tin>
+hipError_t launch_bits(const FwhtParams& p, int bits, unsigned grid, hipStream_t st) {
+  switch (bits) {
+    case 1: hipLaunchKernelGGL((quantize_fwht_kernel<D, 1, VALUES, Tin>), dim3(grid), dim3(kThreads), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((quantize_fwht_kernel<D, 2, VALUES, Tin>), dim3(grid), dim3(kThreads), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((quantize_fwht_kernel<D, 3, VALUES, Tin>), dim3(grid), dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((quantize_fwht_kernel<D, 4, VALUES, Tin>), dim3(grid), dim3(kThreads), 0, st, p); break;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwhtParams& p, const QuantizeArgs& a, unsigned grid, hipStream_t st) {
+  if (a.dtype == TQ_F16)
+    return a.value_layout ? launch_bits<D, 1, _Float16>(p, a.bits, grid, st) : launch_bits<D, 0, _Float16>(p, a.bits, grid, st);
+  return a.value_layout ? launch_bits<D, 1, float>(p, a.bits, grid, st) : launch_bits<D, 0, float>(p, a.bits, grid, st);
+}
+
+}  // namespace
+
+bool fwht_quantize_supports(int d, int rot, int qjl) {
+  return rot == TQ_ROT_HADAMARD && !qjl && (d == 64 || d == 128 || d == 256);
+}
+
+hipError_t launch_quantize_fwht(const QuantizeArgs& a, hipStream_t st) {
+  if (a.n == 0 || a.seqs == 0) return hipSuccess;
+  FwhtParams p{};
+  p.x = a.x;
+  p.seqs = a.seqs;
+  p.n = a.n;
+  p.t0 = a.t0;
+  p.cap = a.cap;
+  p.tile_first = a.t0 / 8;
+  p.tiles = (a.t0 + a.n - 1) / 8 - p.tile_first + 1;
+  p.dsign = a.dsign;
+  p.bnd = a.bnd;
+  p.idx = a.idx;
+  p.norm = a.norm;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const int64_t items = p.seqs * p.tiles;
+  int64_t grid = (items + kWaves - 1) / kWaves;
+  if (grid > (int64_t)cus * 8) grid = (int64_t)cus * 8;
+  switch (a.d) {
+    case 64: return launch_d<64>(p, a, (unsigned)grid, st);
+    case 128: return launch_d<128>(p, a, (unsigned)grid, st);
+    default: return launch_d<256>(p, a, (unsigned)grid, st);
+  }
+}
+
+}  // namespace tq

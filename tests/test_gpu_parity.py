@@ -161,10 +161,19 @@ def test_dequantize_parity(name, which):
     np.testing.assert_allclose(half[~flipped], got[~flipped], rtol=2e-3, atol=1e-3)
 
 
-def test_append_in_pieces_matches_one_call():
+APPEND_CASES = {
+    "haar-d128-f16": workloads.CONFIGS["C2"].with_(N=40),
+    "hadamard-d256-f16": workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=40),
+    "hadamard-d64-f32": workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=40, d=64, dtype="f32",
+                                                       k_bits=2, v_bits=3),
+}
+
+
+@pytest.mark.parametrize("case", list(APPEND_CASES))
+def test_append_in_pieces_matches_one_call(case):
     """Quantizing tokens in several calls (starting inside a value tile) gives
     the same bytes as one call, and leaves other tokens untouched."""
-    cfg = workloads.CONFIGS["C2"].with_(N=40)
+    cfg = APPEND_CASES[case]
     layer = H.gpu_layer(cfg)
     x = torch.from_numpy(_kv(cfg, "V", seed=4)).cuda()
     S = x.shape[0]
@@ -243,3 +252,28 @@ def test_decode_is_deterministic():
     b, _ = B.attn_decode(layer, q, K, V, cfg.N, cfg.Hkv)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_hadamard_quantize_all_widths(d, dtype):
+    """Randomized-Hadamard rotation without QJL (the transform path): every code
+    width, head dimension and input dtype, keys and values, ragged length."""
+    for bits in (1, 2, 3, 4):
+        cfg = workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=77, d=d, dtype=dtype, k_bits=bits,
+                                            v_bits=5 - bits)
+        H.log(f"[hadamard quantize] d={d} {dtype} k_bits={bits} v_bits={5 - bits}")
+        for which, bnd_bits in ((B.TQ_KEYS, cfg.k_bits), (B.TQ_VALUES, cfg.v_bits)):
+            x = _kv(cfg, "K" if which == B.TQ_KEYS else "V", seed=7)
+            S, n, _ = x.shape
+            layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, which)
+            rows = np.array([s * cap + t for s in range(S) for t in range(n)])
+            if which == B.TQ_KEYS:
+                gidx = H.gpu_codes_key(cache, S, cap, d, bnd_bits, rows)
+                bnd = ol.bk
+            else:
+                gidx = H.gpu_codes_value(cache, S, cap, d, bnd_bits)[rows]
+                bnd = ol.bv
+            flipped = H.compare_codes(gidx, enc, bnd, f"d={d} {dtype} bits={bnd_bits}")
+            assert flipped.mean() < 0.02
+            np.testing.assert_allclose(cache["norm"].cpu().numpy()[rows], enc["norm"], rtol=2e-6)
