@@ -28,9 +28,11 @@ Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
   p.mfma = mfma_decode_supports(d, Hq / Hkv * Tq);
   if (p.mfma) {
     // Work in blocks of 32 keys; aim for ~2048 workgroups (8 per CU) while
-    // giving each of a workgroup's 4 waves at least 4 blocks.
+    // giving each of a workgroup's 4 waves at least 4 blocks.  A workgroup
+    // serves up to 4 query rows of one KV head.
     const int64_t blocks = (N + 31) / 32;
-    int64_t want = (2048 + seqs - 1) / seqs;
+    const int64_t groups = seqs * ((Hq / Hkv * Tq + 3) / 4);
+    int64_t want = (2048 + groups - 1) / groups;
     const int64_t max_split = (blocks + 15) / 16;
     if (want > max_split) want = max_split;
     if (want > 1024) want = 1024;  // the combine kernel keeps one weight per split in LDS

@@ -357,13 +357,18 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
   const int l16 = lane % 16, g4 = lane / 16;
-  const int64_t seq = blockIdx.x;
+  // Workgroup = (sequence, group of up to 4 of its query rows, key split).
+  const int64_t seq = blockIdx.x / p.rgroups;
+  const int r0 = 4 * (int)(blockIdx.x % p.rgroups);
   const int split = blockIdx.y;
   const int64_t b_ = seq / p.Hkv;
   const int hkv = (int)(seq % p.Hkv);
   const int G = p.Hq / p.Hkv;
-  const int rows = G * p.Tq;
-  auto qrow_of = [&](int r) -> int64_t { return (b_ * p.Hq + (int64_t)hkv * G + r / p.Tq) * p.Tq + r % p.Tq; };
+  const int rows = min(4, G * p.Tq - r0);  // query rows of this workgroup
+  auto qrow_of = [&](int r) -> int64_t {
+    const int rr = r0 + r;  // row within the KV head's G * Tq rows
+    return (b_ * p.Hq + (int64_t)hkv * G + rr / p.Tq) * p.Tq + rr % p.Tq;
+  };
 
   SeqBuffers sb;
   sb.kidx = make_rsrc(p.kidx + seq * p.cap * S::KROW, p.cap * S::KROW);
@@ -420,7 +425,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
     ws.ca = rc[0] * inv_sqrt_d * kLog2e;
     ws.c2 = rc[1] * cq;
     ws.c0 = rc[2] * cq;
-    ws.limit = (int)(p.causal ? p.N - p.Tq + (g4 % p.Tq) + 1 : p.N);
+    ws.limit = (int)(p.causal ? p.N - p.Tq + ((r0 + g4) % p.Tq) + 1 : p.N);
   }
 #pragma unroll
   for (int i = 0; i < S::CB; ++i) ws.acc[i] = f4{0.f, 0.f, 0.f, 0.f};
@@ -463,7 +468,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
 #pragma unroll
   for (int cb = 0; cb < S::CB; ++cb) mrg_acc[wave][g4][l16 * S::CB + cb] = (ws.acc[cb][0] + ws.acc[cb][1]) * inv_sv;
   __syncthreads();
-  const int64_t rows_total = (int64_t)gridDim.x / p.Hkv * p.Hq * p.Tq;
+  const int64_t rows_total = (int64_t)(gridDim.x / p.rgroups) / p.Hkv * p.Hq * p.Tq;
   for (int idx = tid; idx < rows * D; idx += kThreads) {
     const int r = idx / D, j = idx % D;
     float M = -INFINITY;
@@ -604,7 +609,7 @@ hipError_t dispatch_d(const DecodeMfmaParams& p, int kb, int qjl, int vb, dim3 g
 
 }  // namespace
 
-bool mfma_decode_supports(int d, int rows) { return (d == 128 || d == 256) && rows >= 1 && rows <= 4; }
+bool mfma_decode_supports(int d, int rows) { return (d == 128 || d == 256) && rows >= 1; }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st) {
   PrerotateParams pr{};
@@ -647,7 +652,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   p.keys_per_split = a.keys_per_split;
   p.part = a.part;
   p.scores = a.scores;
-  const dim3 grid((unsigned)(a.B * a.Hkv), (unsigned)a.nsplit);
+  p.rgroups = (a.Hq / a.Hkv * a.Tq + 3) / 4;
+  const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * p.rgroups), (unsigned)a.nsplit);
   const hipError_t e = a.d == 128 ? dispatch_d<128>(p, a.kb, a.qjl, a.vb, grid, st)
                                   : dispatch_d<256>(p, a.kb, a.qjl, a.vb, grid, st);
   if (e != hipSuccess) return e;

@@ -55,6 +55,7 @@ struct DecodeMfmaParams {
   float* out;
   int* counters;                    // per sequence: workgroups finished (reset to 0 after use)
   int Hq, Hkv, Tq, causal;
+  int rgroups;                      // groups of up to 4 query rows per KV head
   int64_t N, cap, keys_per_split;
   float *part, *scores;
 };

@@ -48,26 +48,49 @@ constexpr int kDppXor8 = 0x128; // row_ror:8 (within a row of 16 lanes: lane ^ 8
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
+// Magnitude index m = #{i : t_i < a} over the K = 2^(BITS-1) - 1 positive
+// boundaries t (sorted), by a branchless binary search (value selects only).
 template <int BITS>
-struct Codes {
-  static constexpr int K = (1 << (BITS - 1)) - 1;  // positive boundaries
-  float beta[K > 0 ? K : 1];
-  __device__ void init(const float* bnd) {
-#pragma unroll
-    for (int i = 0; i < K; ++i) beta[i] = bnd[K + 1 + i];
+__device__ __forceinline__ uint32_t magnitude(float a, const float (&t)[BITS > 1 ? (1 << (BITS - 1)) - 1 : 1]) {
+  if constexpr (BITS == 1) {
+    return 0u;
+  } else if constexpr (BITS == 2) {
+    return a > t[0] ? 1u : 0u;
+  } else if constexpr (BITS == 3) {
+    const float t0 = t[0], t1 = t[1], t2 = t[2];
+    const bool c1 = a > t1;
+    const float h = c1 ? t2 : t0;
+    const bool c0 = a > h;
+    return (c1 ? 2u : 0u) + (c0 ? 1u : 0u);
+  } else {
+    const float t0 = t[0], t1 = t[1], t2 = t[2], t3 = t[3], t4 = t[4], t5 = t[5], t6 = t[6];
+    const bool c2 = a > t3;
+    const float h1 = c2 ? t5 : t1;
+    const float h04 = c2 ? t4 : t0;
+    const float h26 = c2 ? t6 : t2;
+    const bool c1 = a > h1;
+    const float h0 = c1 ? h26 : h04;
+    const bool c0 = a > h0;
+    return (c2 ? 4u : 0u) + (c1 ? 2u : 0u) + (c0 ? 1u : 0u);
   }
-  // #{i : boundary_i < y} for the symmetric boundaries (middle one 0).
-  __device__ __forceinline__ uint32_t code(float y) const {
-    const float a = fabsf(y);
-    uint32_t cnt = 0;
+}
+
+// BITS consecutive dwords to a 4-byte aligned address (16-byte aligned when
+// BITS is 4), as one vector store.
+template <int BITS>
+__device__ __forceinline__ void store_words(uint8_t* dst, const uint32_t (&w)[BITS]) {
+  if constexpr (BITS == 4) {
+    *reinterpret_cast<u4*>(dst) = u4{w[0], w[1], w[2], w[3]};
+  } else if constexpr (BITS == 2) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else {
 #pragma unroll
-    for (int i = 0; i < K; ++i) cnt += a > beta[i] ? 1u : 0u;
-    return y > 0.f ? (uint32_t)(K + 1) + cnt : (uint32_t)K - cnt;
+    for (int q = 0; q < BITS; ++q) reinterpret_cast<uint32_t*>(dst)[q] = w[q];
   }
-};
+}
 
 // Bytes per LDS code row: a multiple of 16 words plus 16 (mod 64 words), so the
 // 8-byte writes of the 32 lanes of a half wave fall in distinct banks.
@@ -86,31 +109,43 @@ struct FwhtParams {
 template <int D, int BITS, int VALUES, typename Tin>
 __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
   constexpr int NC = D / 64, V = 8 * NC, ROW = lds_row<D>();
+  constexpr int KB = (1 << (BITS - 1)) - 1;  // positive boundaries
+  constexpr int K = KB > 0 ? KB : 1;          // their array size
+  constexpr bool kHalf = std::is_same<Tin, _Float16>::value;
+  constexpr int RW = kHalf ? 4 : 8;  // dwords per chunk of 8 inputs
+  typedef uint32_t Raw __attribute__((ext_vector_type(RW)));
   __shared__ __align__(16) uint8_t codes[kWaves][8][ROW];
 
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int k = (lane & 3) | ((lane >> 1) & 4);
   const int tl = ((lane >> 2) & 1) | ((lane >> 3) & 6);
 
-  // D signs of this lane's coordinates, as sign-bit masks.
-  uint32_t dmask[V];
+  // D as sign-bit masks on the raw input words of this lane's coordinates.
+  Raw dm[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dmask[8 * c + e] = p.dsign[8 * k + 64 * c + e] < 0.f ? 0x80000000u : 0u;
+    for (int q = 0; q < RW; ++q) {
+      if constexpr (kHalf) {
+        const float* sg = p.dsign + 8 * k + 64 * c + 2 * q;
+        dm[c][q] = (sg[0] < 0.f ? 0x8000u : 0u) | (sg[1] < 0.f ? 0x80000000u : 0u);
+      } else {
+        dm[c][q] = p.dsign[8 * k + 64 * c + q] < 0.f ? 0x80000000u : 0u;
+      }
+    }
   // +1 where this lane is the lower partner of a cross-lane butterfly.
   const float s1 = (lane & 1) ? -1.f : 1.f, s2 = (lane & 2) ? -1.f : 1.f, s8 = (lane & 8) ? -1.f : 1.f;
-  Codes<BITS> cq;
-  cq.init(p.bnd);
-  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  float beta[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) beta[i] = BITS > 1 ? p.bnd[(1 << (BITS - 1)) + i] : 0.f;
+  const float sqrt_d = sqrtf((float)D);
 
   const int64_t items = p.seqs * p.tiles;
   const int64_t wstride = (int64_t)gridDim.x * kWaves;
   const int64_t t0 = p.t0, tend = p.t0 + p.n;
   constexpr int kRowB = D * BITS / 8;  // key stream bytes per token
-
   const bool small = items <= 0x7FFFFFFF;
-  auto split = [&](int64_t item, int64_t& s, int64_t& tile) {  // item -> (sequence, tile)
+  auto split = [&](int64_t item, int64_t& s, int64_t& tile) {  // item -> (sequence, tile), uniform
     if (small) {
       const uint32_t q = (uint32_t)item / (uint32_t)p.tiles;
       s = q;
@@ -120,8 +155,7 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
       tile = p.tile_first + item % p.tiles;
     }
   };
-  // Raw input of one tile for this lane: NC chunks of 8 values.
-  typedef typename std::conditional<std::is_same<Tin, _Float16>::value, h8, f8>::type Raw;
+  const int lane_off = tl * D + 8 * k;  // this lane's first input, relative to the tile's first row
   auto load = [&](int64_t item, Raw (&raw)[NC]) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) raw[c] = Raw{};
@@ -130,26 +164,32 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
     split(item, s, tile);
     const int64_t t = tile * 8 + tl;
     if (t < t0 || t >= tend) return;
-    const Tin* src = static_cast<const Tin*>(p.x) + (s * p.n + (t - t0)) * D + 8 * k;
+    const Tin* src = static_cast<const Tin*>(p.x) + (s * p.n + tile * 8 - t0) * D + lane_off;
 #pragma unroll
     for (int c = 0; c < NC; ++c) raw[c] = *reinterpret_cast<const Raw*>(src + 64 * c);
   };
 
-  int64_t item = (int64_t)blockIdx.x * kWaves + w;
-  Raw nx[NC];
-  load(item, nx);
-  for (; item < items; item += wstride) {
-    float x[V];
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[8 * c + e] = (float)nx[c][e];
-    load(item + wstride, nx);
-
+  // Converts this tile's raw input, refills `raw` with the tile two steps
+  // ahead (so its loads are in flight for two tiles of work), then quantizes.
+  auto process = [&](int64_t item, Raw (&raw)[NC]) {
     int64_t s, tile;
     split(item, s, tile);
-
-    // ---- norm (8 lanes per token) ----
+    float x[V];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const Raw r = raw[c] ^ dm[c];  // D applied to the input's sign bits
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (kHalf) {
+          const uint32_t h = e % 2 ? r[e / 2] >> 16 : r[e / 2] & 0xFFFFu;
+          x[8 * c + e] = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+        } else {
+          x[8 * c + e] = __uint_as_float(r[e]);
+        }
+      }
+    }
+    load(item + 2 * wstride, raw);
+    // norm over the token's 8 lanes (D does not change it)
     float ss = 0.f;
 #pragma unroll
     for (int v = 0; v < V; ++v) ss = fmaf(x[v], x[v], ss);
@@ -157,13 +197,14 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
     ss += dpp<kDppXor2>(ss);
     ss += dpp<kDppXor8>(ss);
     const float nn = sqrtf(ss);
-    const float inv = nn > 0.f ? inv_sqrt_d / nn : 0.f;
+    // thresholds in the unnormalised transform's units: beta * n * sqrt(d)
+    float th[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) th[i] = beta[i] * (nn * sqrt_d);
 
-    // ---- D, then the unnormalised Walsh-Hadamard transform ----
+    // unnormalised Walsh-Hadamard transform: register bits, then lane bits
 #pragma unroll
-    for (int v = 0; v < V; ++v) x[v] = __uint_as_float(__float_as_uint(x[v]) ^ dmask[v]);
-#pragma unroll
-    for (int b = 1; b < V; b <<= 1) {  // register bits: e (1, 2, 4) then c (8, 16)
+    for (int b = 1; b < V; b <<= 1) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         if (v & b) continue;
@@ -179,12 +220,17 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
 #pragma unroll
     for (int v = 0; v < V; ++v) x[v] = fmaf(s8, x[v], dpp<kDppXor8>(x[v]));
 
-    // ---- codes into LDS, [token][coordinate] ----
+    // codes into LDS, [token][coordinate]: code = #{i : beta_i < y}
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       uint32_t wd[2] = {0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) wd[e / 4] |= cq.code(x[8 * c + e] * inv) << (8 * (e % 4));
+      for (int e = 0; e < 8; ++e) {
+        const float z = x[8 * c + e];
+        const uint32_t m = magnitude<BITS>(fabsf(z), th);
+        const uint32_t code = m ^ (z > 0.f ? (uint32_t)(KB + 1) : (uint32_t)KB);
+        wd[e / 4] |= code << (8 * (e % 4));
+      }
       *reinterpret_cast<uint2*>(&codes[w][tl][8 * k + 64 * c]) = make_uint2(wd[0], wd[1]);
     }
     const int64_t tok = tile * 8 + tl;
@@ -193,7 +239,7 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- pack 32 codes per lane into BITS dwords and store ----
+    // pack 32 codes per lane into BITS dwords and store
     if (lane < D / 4) {
       uint32_t cw[8];  // 32 code bytes, in stream order
       if constexpr (!VALUES) {
@@ -203,12 +249,12 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
         cw[0] = a[0]; cw[1] = a[1]; cw[2] = a[2]; cw[3] = a[3];
         cw[4] = b[0]; cw[5] = b[1]; cw[6] = b[2]; cw[7] = b[3];
       } else {
-        // positions 8 j + t for j = 4 lane .. 4 lane + 3: byte i of word t holds (j = 4 lane + i, t)
+        // stream positions 8 j + t, j = 4 lane + i: byte i of r[t] is code (j, t)
         uint32_t r[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) r[t] = *reinterpret_cast<const uint32_t*>(&codes[w][t][4 * lane]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {  // stream bytes 8i .. 8i+7 = coordinate 4 lane + i, tokens 0..7
+        for (int i = 0; i < 4; ++i) {
           uint32_t lo = 0, hi = 0;
 #pragma unroll
           for (int t = 0; t < 4; ++t) lo |= ((r[t] >> (8 * i)) & 0xFFu) << (8 * t);
@@ -232,9 +278,7 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
         const int t = lane / (D / 32), jb = lane % (D / 32);
         const int64_t tk = tile * 8 + t;
         if (tk >= t0 && tk < tend) {
-          uint32_t* dst = reinterpret_cast<uint32_t*>(p.idx + (s * p.cap + tk) * kRowB + jb * 4 * BITS);
-#pragma unroll
-          for (int q = 0; q < BITS; ++q) dst[q] = out[q];
+          store_words<BITS>(p.idx + (s * p.cap + tile * 8) * kRowB + t * kRowB + jb * 4 * BITS, out);
         }
       } else {
         uint32_t* dst = reinterpret_cast<uint32_t*>(p.idx + (s * (p.cap / 8) + tile) * (D * BITS) + lane * 4 * BITS);
@@ -257,11 +301,23 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
 #pragma unroll
           for (int q = 0; q < BITS; ++q) out[q] = (out[q] & ~keep[q]) | (dst[q] & keep[q]);
         }
-#pragma unroll
-        for (int q = 0; q < BITS; ++q) dst[q] = out[q];
+        store_words<BITS>(reinterpret_cast<uint8_t*>(dst), out);
       }
     }
     __builtin_amdgcn_wave_barrier();
+  };
+
+  // Two tiles of loads in flight per wave.
+  int64_t item = (int64_t)blockIdx.x * kWaves + w;
+  Raw ra[NC], rb[NC];
+  load(item, ra);
+  load(item + wstride, rb);
+  while (item < items) {
+    process(item, ra);
+    item += wstride;
+    if (item >= items) break;
+    process(item, rb);
+    item += wstride;
   }
 }
 
