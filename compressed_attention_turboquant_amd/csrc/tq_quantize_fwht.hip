@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "tq_kernels.h"
+#include "tq_quant_common.h"
 
 namespace tq {
 namespace {
@@ -49,33 +50,6 @@ constexpr int kDppXor8 = 0x128; // row_ror:8 (within a row of 16 lanes: lane ^ 8
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-
-// Magnitude index m = #{i : t_i < a} over the K = 2^(BITS-1) - 1 positive
-// boundaries t (sorted), by a branchless binary search (value selects only).
-template <int BITS>
-__device__ __forceinline__ uint32_t magnitude(float a, const float (&t)[BITS > 1 ? (1 << (BITS - 1)) - 1 : 1]) {
-  if constexpr (BITS == 1) {
-    return 0u;
-  } else if constexpr (BITS == 2) {
-    return a > t[0] ? 1u : 0u;
-  } else if constexpr (BITS == 3) {
-    const float t0 = t[0], t1 = t[1], t2 = t[2];
-    const bool c1 = a > t1;
-    const float h = c1 ? t2 : t0;
-    const bool c0 = a > h;
-    return (c1 ? 2u : 0u) + (c0 ? 1u : 0u);
-  } else {
-    const float t0 = t[0], t1 = t[1], t2 = t[2], t3 = t[3], t4 = t[4], t5 = t[5], t6 = t[6];
-    const bool c2 = a > t3;
-    const float h1 = c2 ? t5 : t1;
-    const float h04 = c2 ? t4 : t0;
-    const float h26 = c2 ? t6 : t2;
-    const bool c1 = a > h1;
-    const float h0 = c1 ? h26 : h04;
-    const bool c0 = a > h0;
-    return (c2 ? 4u : 0u) + (c1 ? 2u : 0u) + (c0 ? 1u : 0u);
-  }
 }
 
 // BITS consecutive dwords to a 4-byte aligned address (16-byte aligned when
@@ -109,8 +83,7 @@ struct FwhtParams {
 template <int D, int BITS, int VALUES, typename Tin>
 __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
   constexpr int NC = D / 64, V = 8 * NC, ROW = lds_row<D>();
-  constexpr int KB = (1 << (BITS - 1)) - 1;  // positive boundaries
-  constexpr int K = KB > 0 ? KB : 1;          // their array size
+  constexpr int K = BITS > 1 ? (1 << (BITS - 1)) - 1 : 1;  // positive boundaries (array size)
   constexpr bool kHalf = std::is_same<Tin, _Float16>::value;
   constexpr int RW = kHalf ? 4 : 8;  // dwords per chunk of 8 inputs
   typedef uint32_t Raw __attribute__((ext_vector_type(RW)));
@@ -226,10 +199,7 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
       uint32_t wd[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float z = x[8 * c + e];
-        const uint32_t m = magnitude<BITS>(fabsf(z), th);
-        const uint32_t code = m ^ (z > 0.f ? (uint32_t)(KB + 1) : (uint32_t)KB);
-        wd[e / 4] |= code << (8 * (e % 4));
+        wd[e / 4] |= symmetric_code<BITS>(x[8 * c + e], th) << (8 * (e % 4));
       }
       *reinterpret_cast<uint2*>(&codes[w][tl][8 * k + 64 * c]) = make_uint2(wd[0], wd[1]);
     }

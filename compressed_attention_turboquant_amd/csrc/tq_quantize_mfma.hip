@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "tq_kernels.h"
+#include "tq_quant_common.h"
 
 namespace tq {
 namespace {
@@ -50,34 +51,6 @@ __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
 __device__ __forceinline__ int out_coord(int w, int ct, int rho) {
   return 32 * w + 8 * (rho / 4) + 4 * ct + (rho % 4);
 }
-
-template <int BITS>
-struct Quantizer {
-  static constexpr int K = (1 << (BITS - 1)) - 1;  // positive boundaries
-  float beta[K > 0 ? K : 1];
-  float mag[K + 1];
-  __device__ void init(const float* cent, const float* bnd) {
-#pragma unroll
-    for (int i = 0; i < K; ++i) beta[i] = bnd[K + 1 + i];
-#pragma unroll
-    for (int i = 0; i <= K; ++i) mag[i] = cent[K + 1 + i];
-  }
-  // code = #{i : boundary_i < y}; c = centroid of that code.
-  __device__ __forceinline__ uint32_t code(float y, float& c) const {
-    const float a = fabsf(y);
-    uint32_t cnt = 0;
-    float m = mag[0];
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-      const bool gt = a > beta[i];
-      cnt += gt ? 1u : 0u;
-      m = gt ? mag[i + 1] : m;
-    }
-    const bool pos = y > 0.f;
-    c = pos ? m : -m;
-    return pos ? (uint32_t)(K + 1) + cnt : (uint32_t)K - cnt;
-  }
-};
 
 template <int BITS, int QJL, int VALUES>
 __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams p) {
@@ -106,8 +79,13 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
       }
     }
   }
-  Quantizer<BITS> qz;
-  qz.init(p.cent, p.bnd);
+  // Positive half of the symmetric boundaries, and the centroids as a register
+  // table (lane i holds c[i mod 16]) read with ds_bpermute.
+  constexpr int KP = BITS > 1 ? (1 << (BITS - 1)) - 1 : 1;
+  float beta[KP];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) beta[i] = BITS > 1 ? p.bnd[(1 << (BITS - 1)) + i] : 0.f;
+  const int ctab = __float_as_int(p.cent[lane % 16]);
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
   // Work unit: 4 consecutive value tiles (32 token slots) of one sequence.
@@ -190,7 +168,7 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
         const int t = ((int)p.tile_first + gt + slot / 8) * 8 + slot % 8;
         const bool ok = gt + slot / 8 < tiles && t >= t0 && t < tend;
         const float nn = nrm[slot];
-        const float inv = nn > 0.f ? inv_sqrt_d / nn : 0.f;
+        const float inv = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
         uint32_t packed = 0;
         float r[8];
         float rr = 0.f;
@@ -199,8 +177,8 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float y = acc[ct][tt][q] * inv;
-            float c;
-            const uint32_t code = qz.code(y, c);
+            const uint32_t code = symmetric_code<BITS>(y, beta);
+            const float c = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(code << 2), ctab));
             packed |= code << (BITS * (4 * ct + q));
             r[4 * ct + q] = y - c;
             rr = fmaf(r[4 * ct + q], r[4 * ct + q], rr);
@@ -283,7 +261,7 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
         const bool ok = t >= t0 && t < tend;
         if (!ok) keep |= ((1u << BITS) - 1u) << (BITS * k);
         const float nn = nrm[8 * g4 + k];
-        inv[k] = nn > 0.f ? inv_sqrt_d / nn : 0.f;
+        inv[k] = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
         if (ok && tile_ok && w == 0 && l16 == 0) p.norm[s * p.cap + t] = nn;
       }
       uint8_t* tile_base = p.idx + s * (p.cap / 8) * (D * BITS) + tile * (D * BITS);
@@ -295,8 +273,7 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int k = 4 * tt + q;
-            float c;
-            packed |= qz.code(acc[ct][tt][q] * inv[k], c) << (BITS * k);
+            packed |= symmetric_code<BITS>(acc[ct][tt][q] * inv[k], beta) << (BITS * k);
           }
         if (tile_ok) {
           uint8_t* dst = tile_base + out_coord(w, ct, l16) * BITS;
