@@ -1,8 +1,8 @@
 // Decode attention on the compressed cache with the matrix cores (gfx950).
 //
 // What is computed is the asymmetric estimator and softmax of [cuTile]
-// "Asymmetric estimator: term1 (MSE dot) + term2 (QJL correction)" and "Fused
-// attention + online softmax, decompresses ... V on-chip", with the query
+// listing (asymmetric score estimator; fused attention function with online
+// softmax and values decoded on chip), with the query
 // rotated once ([Mobilint] "Two-Stage Approach": <q, x~> = <Pi q, y~>):
 //   s_t = n_t * (<R q, c_k[idx_t]> + gamma_t sqrt(pi/2)/d <S q, sigma_t>) / sqrt(d)
 //   out = R^T (sum_t softmax(s)_t * nv_t * c_v[idxv_t]).

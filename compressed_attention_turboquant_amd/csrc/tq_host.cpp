@@ -6,8 +6,7 @@
 //   start + k * 0x9E3779B97F4A7C15.  Uniforms are ((z >> 11) + 0.5) / 2^53;
 //   normals come from Box-Muller on consecutive uniform pairs (cos, then sin);
 //   signs are +1 when the top bit is 0.  Tags: 0 rotation, 1 projection, 2 signs.
-// * Haar rotation ([cuTile] "Haar-distributed random orthogonal matrix via QR
-//   of Gaussian"): Householder QR of the row-major Gaussian G, Q formed
+// * Haar rotation ([cuTile] listing, Haar rotation function): Householder QR of the row-major Gaussian G, Q formed
 //   explicitly, columns signed so that diag(R) > 0 (the unique, Haar Q).
 // * Randomized Hadamard ([Mobilint] "How JL Matrices Evolved"): R = H D with
 //   H[i][j] = (-1)^popcount(i&j) / sqrt(d) (Sylvester order) and D the signs.

@@ -3,13 +3,13 @@
 // indexing over speed and serve the shapes the tuned kernels do not cover.
 //
 // Method steps and where the pages define them:
-//   quantize  [cuTile] "K: (seq_k, head_dim) -> compressed dict", "V: ... MSE
-//             only"; [Mobilint] "Two-Stage Approach" (stage 1 codes, stage 2
+//   quantize  [cuTile] listing, key and value compression functions
+//             (values without QJL); [Mobilint] "Two-Stage Approach" (stage 1 codes, stage 2
 //             sign(S r) and ||r||).
-//   decode    [cuTile] "Asymmetric estimator", "Full pipeline: scores ->
-//             softmax -> weighted V sum", "Fused attention + online softmax";
+//   decode    [cuTile] listing, asymmetric score estimator, attention
+//             pipeline and fused attention with online softmax;
 //             [Mobilint] "Two-Stage Approach" (<q, x~> = <Pi q, y~>).
-//   dequant   [cuTile] "indices -> centroids -> un-rotate -> rescale".
+//   dequant   [cuTile] listing, decompression function.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 

@@ -1,7 +1,7 @@
 // Key/value compression on the matrix cores (gfx950), head dimension 128.
 //
-// Per token x ([cuTile] "K: (seq_k, head_dim) -> compressed dict", "V: ... MSE
-// only, no QJL"; [Mobilint] "Coordinates Become Predictable After Rotation",
+// Per token x ([cuTile] listing, key and value compression functions, values
+// without QJL; [Mobilint] "Coordinates Become Predictable After Rotation",
 // "Designing the Optimal Codebook Without Data", "Two-Stage Approach"):
 //   n = ||x||;  y = R x / n;  idx_j = #{i : beta_i < y_j};  pack idx;
 //   keys with QJL: r = y - c[idx] (rotated residual), gamma = ||r||,

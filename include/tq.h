@@ -115,12 +115,11 @@ tq_status tq_cache_bytes(const tq_layer* layer, int32_t which, int64_t seqs, int
                          size_t out[4]);
 
 /* Set up a layer: draws the Haar rotation Pi (QR of a seeded Gaussian with a
- * positive R diagonal; [cuTile] "Haar-distributed random orthogonal matrix via
- * QR of Gaussian") or the randomized Hadamard H*D ([Mobilint] "How JL Matrices
+ * positive R diagonal; [cuTile] listing, Haar rotation function) or the randomized Hadamard H*D ([Mobilint] "How JL Matrices
  * Evolved"), the QJL projection S with i.i.d. N(0,1) entries ([Mobilint]
  * "Two-Stage Approach", stage 2), and the Lloyd-Max codebooks for the N(0,1/d)
  * coordinate law ([Mobilint] "Designing the Optimal Codebook Without Data";
- * [cuTile] "Returns (centroids, boundaries) as sorted float32").  The random
+ * [cuTile] listing, codebook function: both tables sorted, float32).  The random
  * matrices come from the SplitMix64 stream with Box-Muller normals, tags
  * 0 (Pi), 1 (S), 2 (D).  Builds the tables on the host in float64, copies them
  * into `dev_blob` (tq_layer_blob_bytes(d) bytes, caller-owned) on `stream` and
@@ -139,9 +138,9 @@ tq_status tq_host_tables(int32_t d, int32_t rot, uint64_t seed, double* rotation
  * centroids and 2^bits-1 sorted boundaries ([cuTile] codebook function). */
 tq_status tq_get_codebook(int32_t d, int32_t bits, float* centroids, float* boundaries);
 
-/* Compress tokens t0..t0+n-1 of every sequence into `cache` ([cuTile] "K:
- * (seq_k, head_dim) -> compressed dict" and "V: ... MSE only, no QJL";
- * [Mobilint] "Two-Stage Approach").  Per token: store n = ||x||; rotate
+/* Compress tokens t0..t0+n-1 of every sequence into `cache` ([cuTile] listing,
+ * key and value compression functions, values without QJL; [Mobilint]
+ * "Two-Stage Approach").  Per token: store n = ||x||; rotate
  * u = x/n (u = 0 when n = 0); code each coordinate as #{i : beta_i < y_j};
  * bit-pack.  Keys with QJL also store gamma = ||r|| and sign(S r) for the
  * residual r = u - R^T c[idx] (sign(0) = +1).  x is [seqs][n][d] of `dtype`
@@ -155,10 +154,9 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
 size_t tq_decode_workspace_bytes(const tq_layer* layer, int32_t B, int32_t Hq, int32_t Hkv,
                                  int32_t Tq, int64_t N);
 
-/* Decode attention on the compressed cache ([cuTile] "Asymmetric estimator:
- * term1 (MSE dot) + term2 (QJL correction)", "Full pipeline: scores -> softmax
- * -> weighted V sum", "Fused attention + online softmax, decompresses ... V
- * on-chip"; [Mobilint] "Two-Stage Approach": <q, x~> = <Pi q, y~>).  For each
+/* Decode attention on the compressed cache ([cuTile] listing,
+ * asymmetric score estimator, the attention pipeline and the fused attention
+ * function with online softmax and values decoded on chip; [Mobilint] "Two-Stage Approach": <q, x~> = <Pi q, y~>).  For each
  * query row the query is rotated once (R q, S q); key t scores
  *   s_t = n_t * (<R q, c_k[idx_t]> + gamma_t*sqrt(pi/2)/d * <S q, sigma_t>) / sqrt(d);
  * softmax over keys 0..N-1 (with `causal`, query i of Tq sees keys
@@ -174,7 +172,7 @@ tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, 
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Reconstruct tokens 0..n-1 of every sequence: x_hat = n * R^T c[idx]
- * ([cuTile] "indices -> centroids -> un-rotate -> rescale").  out is
+ * ([cuTile] listing, decompression function).  out is
  * [seqs][n][d] of out_dtype (TQ_F32 or TQ_F16). */
 tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,
                         void* out, int32_t out_dtype, void* stream);

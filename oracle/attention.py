@@ -1,8 +1,8 @@
 """Decode attention over a TurboQuant-compressed cache (fp64).
 
-[cuTile] listing: "Asymmetric estimator: term1 (MSE dot) + term2 (QJL
-correction)", "Full pipeline: scores -> softmax -> weighted V sum", "Scores
-should be scaled by 1/sqrt(d)".  [Mobilint], "Two-Stage Approach": the query
+[cuTile] listing: the asymmetric score estimator (an MSE inner product plus
+a QJL correction term), the attention pipeline (scores, softmax, weighted sum
+of values) and its test that scores carry the 1/sqrt(d) scale.  [Mobilint], "Two-Stage Approach": the query
 is rotated once, <q, x~> = <Pi q, y~>, so each cached token costs one O(d)
 inner product; the QJL term uses S q against the stored signs with the
 factor sqrt(pi/2)/d.  Per key t and query q:

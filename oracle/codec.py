@@ -2,8 +2,8 @@
 
 Encoding of one row x ([Mobilint], sections "Coordinates Become Predictable
 After Rotation", "Designing the Optimal Codebook Without Data" and
-"Two-Stage Approach"; [cuTile] listing, "K: (seq_k, head_dim) -> compressed
-dict" and "V: ... MSE only, no QJL"):
+"Two-Stage Approach"; [cuTile] listing, key and value compression functions, values without
+QJL):
   1. n = ||x||_2 is stored; u = x / n (u = 0 when n = 0).
   2. y = R u with R the Haar rotation Pi or the randomized Hadamard H D.
   3. idx_j = #{i : beta_i < y_j} over the sorted float32 boundaries.
@@ -65,8 +65,8 @@ def encode_rows(x, R, centroids, boundaries, S=None) -> dict:
 
 
 def reconstruct_mse(idx, norm, R, centroids) -> np.ndarray:
-    """x_hat = n * R^T c[idx] ([cuTile] listing: indices -> centroids ->
-    un-rotate -> rescale)."""
+    """x_hat = n * R^T c[idx] ([cuTile] listing, decompression function:
+    centroid lookup, inverse rotation, norm rescale)."""
     c = np.asarray(centroids, dtype=np.float64)
     return np.asarray(norm, dtype=np.float64)[:, None] * (c[idx] @ np.asarray(R, np.float64))
 

@@ -3,9 +3,8 @@
 The pages fix only the distributions: a Gaussian matrix whose QR factor is
 the Haar rotation, a Gaussian projection S, and random +-1 signs D for the
 randomized Hadamard transform ([Mobilint], sections "How JL Matrices Evolved"
-and "Two-Stage Approach"; [cuTile] listing, "Random Gaussian projection
-matrix for QJL" and "Haar-distributed random orthogonal matrix via QR of
-Gaussian").  Which generator produces them is not on the pages, so this
+and "Two-Stage Approach"; [cuTile] listing, the QJL projection and Haar
+rotation functions).  Which generator produces them is not on the pages, so this
 stream is a contract of this project (parity unpinned by the pages).
 
 Definition (SplitMix64, Steele, Lea and Flood, "Fast splittable pseudorandom

@@ -1,8 +1,7 @@
 """Random rotation, QJL projection and randomized Hadamard transform (fp64).
 
 * Haar rotation Pi: the Q factor of the QR factorisation of a d x d standard
-  Gaussian matrix ([cuTile] listing, "Haar-distributed random orthogonal
-  matrix via QR of Gaussian"; [Mobilint], "Two-Stage Approach", where the
+  Gaussian matrix ([cuTile] listing, Haar rotation function; [Mobilint], "Two-Stage Approach", where the
   sample code rotates by the QR factor).  Reading: the columns of Q are signed
   so that diag(R) > 0, which makes Q unique and exactly Haar distributed.
   A unit vector u is rotated as y = Pi u.

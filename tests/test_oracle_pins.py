@@ -226,8 +226,8 @@ def test_encode_matches_nearest_centroid_bruteforce():
 
 
 def test_centroid_round_trip_and_nearby_values():
-    # [cuTile] tests: "Quantize -> dequantize should map each centroid exactly
-    # to itself" and "values close to a centroid map to that index".
+    # [cuTile] tests: a centroid survives a quantize/dequantize round trip
+    # unchanged, and a value near a centroid takes that centroid's index.
     d = 128
     for b in (1, 2, 3, 4):
         c, beta = codebook.codebook(b, d)
