@@ -35,15 +35,42 @@ DECODE_KERNELS = ("prerotate", "decode_mfma_kernel", "decode_split_ref", "decode
 QUANT_KERNELS = ("quantize_mfma_kernel", "quantize_tile_ref", "quantize_fwht")
 
 
-def kernel_sources_digest():
-    """sha256 over the library's kernel and host sources (file names and bytes)."""
+def strip_comments(src):
+    """C/C++ source text without its comments and with runs of whitespace
+    collapsed (string and character literals are kept as they are)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_sources_digest(csrc=None):
+    """sha256 over the library's kernel and host sources (file names and code,
+    comments left out), so that a profile stays matched to the code it was
+    measured on across edits that change only comments."""
     h = hashlib.sha256()
-    csrc = os.path.join(PKG, "csrc")
+    csrc = csrc or os.path.join(PKG, "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
                 h.update(name.encode())
-                h.update(f.read())
+                h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 
