@@ -86,9 +86,14 @@ def _short(name):
     return name.split("(")[0] if "(" in name and "<" not in name.split("(")[0][-2:] else name[:80]
 
 
+def _is_lib(name):
+    """True for the library's kernels, demangled (tq::...) or not (_ZN2tq...)."""
+    return "tq::" in name or "_ZN2tq" in name
+
+
 def kernel_stats(directory):
     rows = list(csv.DictReader(open(_one(directory, "kernel_stats.csv"))))
-    return [r for r in rows if "tq::" in r["Name"]]
+    return [r for r in rows if _is_lib(r["Name"])]
 
 
 def counters(directory, counter):
@@ -97,12 +102,12 @@ def counters(directory, counter):
     rows = [r for r in csv.DictReader(open(_one(directory, "counter_collection.csv")))
             if r["Counter_Name"] == counter]
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-    last_tq = max(int(r["Dispatch_Id"]) for r in rows if "tq::" in r["Kernel_Name"])
+    last_tq = max(int(r["Dispatch_Id"]) for r in rows if _is_lib(r["Kernel_Name"]))
     per = collections.defaultdict(list)
     copy = 0.0
     for r in rows:
         v = float(r["Counter_Value"])
-        if "tq::" in r["Kernel_Name"]:
+        if _is_lib(r["Kernel_Name"]):
             per[r["Kernel_Name"]].append(v)
         elif int(r["Dispatch_Id"]) > last_tq and "copyBuffer" in r["Kernel_Name"]:
             copy += v
