@@ -18,11 +18,11 @@
 //    used as fp16 copies of s*c with a per-codebook factor s chosen at set-up so
 //    every s*c_i is within 2e-5 (3-bit) / 1e-4 (4-bit) of an fp16 value; 1/s is
 //    folded into the query side.
-//  * Code -> fp16 decode is a table lookup through ds_bpermute: each lane holds
-//    one table entry (the fp16 pair for a pair of codes), and the packed stream
-//    shifted so the pair lands in address bits [2, 8) selects it (the
-//    instruction ignores the other address bits; tables are replicated when
-//    the index is shorter).  One VALU op + one bpermute per fp16 pair.
+//  * Code -> fp16 decode is a table lookup in LDS: for widths 1-3 the packed
+//    stream's next four codes form the index of an 8-byte entry holding their
+//    four fp16 values (4-bit codes: pairs, 4-byte entries).  Two VALU ops (an
+//    align and a mask) and one 64-bit LDS read per four codes; the workgroup
+//    fills the table (32 KB for 3-bit codes) once at start.
 //  * Sign bits become fp16 B-operand halves by masking: a half whose only set
 //    bit is exponent bit p is the power of two 2^(2^(p-10)-15); rotating the
 //    32 sign bits by 0/4/8/12 and masking bits p and p+16 (p = 10..13) yields
@@ -55,6 +55,7 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -71,54 +72,91 @@ __device__ __forceinline__ void sfor(F&& f) {
   }
 }
 
-// Bits [O, ...) of the little-endian stream in w[], moved to bit 2 of the
-// result (bits above the field are don't-care): a ds_bpermute byte address.
-template <int O, int NW>
-__device__ __forceinline__ uint32_t at2(const uint32_t (&w)[NW]) {
-  if constexpr (O == 0) {
-    return w[0] << 2;
+// Code -> fp16 operand tables in LDS.  Widths 1-3 look codes up four at a time:
+// a 4*BITS-bit index selects an 8-byte entry holding the four fp16 centroids, one
+// 64-bit LDS read per four codes.  4-bit codes go in pairs: an 8-bit index
+// selects a 4-byte entry of two fp16 centroids.  (A random 64-bit read from such
+// a table costs about as much LDS time as a 32-bit cross-lane permute, so four
+// codes per read halve the LDS time of two codes per permute.)
+template <int BITS>
+struct Lut {
+  static constexpr int kCodes = BITS < 4 ? 4 : 2;   // codes per lookup
+  static constexpr int kIdx = BITS * kCodes;        // index bits
+  static constexpr int kEntries = 1 << kIdx;
+  static constexpr int kShift = kCodes == 4 ? 3 : 2;  // log2 of the entry bytes
+  static constexpr int kDwords = kEntries << (kShift - 2);
+};
+
+// Bits [O, O+N) of the little-endian stream in w[], moved to bits [SH, SH+N) of
+// the result, every other bit zero: a byte offset into a table of 2^SH-byte
+// entries.
+template <int O, int N, int SH, int NW>
+__device__ __forceinline__ uint32_t field(const uint32_t (&w)[NW]) {
+  constexpr uint32_t mask = ((1u << N) - 1u) << SH;
+  constexpr int b = O - SH;
+  if constexpr (b < 0) {
+    return (w[0] << (-b)) & mask;
   } else {
-    constexpr int b = O - 2, wi = b / 32, sh = b % 32;
+    constexpr int wi = b / 32, sh = b % 32;
+    static_assert(wi < NW && (wi + 1 < NW || sh + SH + N <= 32), "field outside the stream");
     if constexpr (sh == 0)
-      return w[wi];
+      return w[wi] & mask;
     else if constexpr (wi + 1 < NW)
-      return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh);
+      return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & mask;
     else
-      return w[wi] >> sh;
+      return (w[wi] >> sh) & mask;
   }
 }
 
-__device__ __forceinline__ uint32_t bperm(uint32_t addr, uint32_t table) {
-  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)addr, (int)table);
-}
-
-// fp16 pair of centroids for codes 2i, 2i+1 of the stream (bit offset O0 + 2*BITS*i).
-template <int BITS, int O0, int I, int NW>
-__device__ __forceinline__ uint32_t decode_pair(const uint32_t (&w)[NW], uint32_t t0, uint32_t t1) {
-  if constexpr (BITS < 4) {
-    return bperm(at2<O0 + 2 * BITS * I>(w), t0);
+// The eight fp16 centroids (s * c[code]) of the codes at stream bit offsets
+// O, O+BITS, ..., O+7*BITS, in order, as one MFMA operand.
+template <int BITS, int O, int NW>
+__device__ __forceinline__ u4 decode8(const uint32_t (&w)[NW], const uint32_t* tab) {
+  using L = Lut<BITS>;
+  const char* base = reinterpret_cast<const char*>(tab);
+  u4 r;
+  if constexpr (L::kCodes == 4) {
+    const u2 lo = *reinterpret_cast<const u2*>(base + field<O, L::kIdx, 3>(w));
+    const u2 hi = *reinterpret_cast<const u2*>(base + field<O + 4 * BITS, L::kIdx, 3>(w));
+    r[0] = lo[0];
+    r[1] = lo[1];
+    r[2] = hi[0];
+    r[3] = hi[1];
   } else {
-    return bperm(at2<O0 + 8 * I>(w), t0) | bperm(at2<O0 + 8 * I + 4>(w), t1);
+    sfor<0, 4>([&](auto i) {
+      r[decltype(i)::value] = *reinterpret_cast<const uint32_t*>(base + field<O + 8 * decltype(i)::value, 8, 2>(w));
+    });
   }
+  return r;
 }
 
 __device__ __forceinline__ uint32_t half_bits(float x) {
   return (uint32_t)__half_as_ushort(__float2half_rn(x));
 }
 
-// This lane's entries of the code -> fp16 tables (see decode_pair).
+// Every thread of the workgroup: fill the table for centroids c scaled by s.
 template <int BITS>
-__device__ __forceinline__ void make_tables(const float* c, float s, int lane, uint32_t& t0,
-                                            uint32_t& t1) {
-  if constexpr (BITS == 4) {
-    const uint32_t h = half_bits(s * c[lane & 15]);
-    t0 = h;
-    t1 = h << 16;
-  } else {
-    constexpr int L = 1 << BITS;
-    const int idx = lane & (L * L - 1);
-    t0 = half_bits(s * c[idx % L]) | (half_bits(s * c[idx / L]) << 16);
-    t1 = 0;
+__device__ __forceinline__ void fill_lut(uint32_t* tab, const float* c, float s, int tid) {
+  using L = Lut<BITS>;
+  constexpr uint32_t m = (1u << BITS) - 1u;
+  // Lane j holds fp16(s * c[j % 2^BITS]); entries gather it with permutes.
+  const uint32_t h = half_bits(s * c[tid & m]);
+  auto lv = [&](uint32_t code) { return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(code << 2), (int)h); };
+  // Whole waves run every iteration (the permutes need their source lanes).
+  for (int i0 = 0; i0 < L::kEntries; i0 += kThreads) {
+    const int i = i0 + tid;
+    const uint32_t u = (uint32_t)i;
+    if constexpr (L::kCodes == 4) {
+      const uint32_t e0 = lv(u & m) | (lv((u >> BITS) & m) << 16);
+      const uint32_t e1 = lv((u >> (2 * BITS)) & m) | (lv((u >> (3 * BITS)) & m) << 16);
+      if (i < L::kEntries) {
+        tab[2 * i] = e0;
+        tab[2 * i + 1] = e1;
+      }
+    } else {
+      const uint32_t e = lv(u & m) | (lv((u >> 4) & m) << 16);
+      if (i < L::kEntries) tab[i] = e;
+    }
   }
 }
 
@@ -242,7 +280,7 @@ struct WaveState {
   float ca, c2, c0;
   int limit;
   int64_t srow;
-  uint32_t kt0, kt1, vt0, vt1;
+  const uint32_t *ktab, *vtab;  // code -> fp16 tables in LDS
 };
 
 template <int D, int KB, int QJL, int VB, int SCORES>
@@ -251,15 +289,11 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, con
                                               int l16, int g4, int rows) {
   using S = Shape<D, KB, QJL, VB>;
   // Phase 1: all key-code lookups of both 16-key tiles go out before any MFMA
-  // needs one, so the bpermute latency overlaps instead of serialising.
+  // needs one, so the LDS latency overlaps instead of serialising.
   u4 bk[2][S::KBLK];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
-    sfor<0, S::KBLK>([&](auto kb) {
-      sfor<0, 4>([&](auto w) {
-        bk[t][kb][decltype(w)::value] = decode_pair<KB, 0, 4 * kb + w>(cur.kw[t], ws.kt0, ws.kt1);
-      });
-    });
+    sfor<0, S::KBLK>([&](auto kb) { bk[t][kb] = decode8<KB, 8 * KB * kb>(cur.kw[t], ws.ktab); });
   __builtin_amdgcn_sched_barrier(0);
   // Phase 2: score MFMAs.  Separate accumulators for the centroid and sign parts
   // halve the dependency chains; each fills only its own rows (parts 0,1 / 2,3).
@@ -287,11 +321,7 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, con
   });
   // Phase 3: value-code lookups, in flight while the softmax arithmetic runs.
   u4 bv[S::CB];
-  sfor<0, S::CB>([&](auto cb) {
-    sfor<0, 4>([&](auto w) {
-      bv[cb][decltype(w)::value] = decode_pair<VB, 8 * VB * cb, w>(cur.vw, ws.vt0, ws.vt1);
-    });
-  });
+  sfor<0, S::CB>([&](auto cb) { bv[cb] = decode8<VB, 8 * VB * cb>(cur.vw, ws.vtab); });
   __builtin_amdgcn_sched_barrier(0);
   // Phase 4: scores of lane (query row g4, key l16), online softmax.
   float st[2];
@@ -350,12 +380,19 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, con
 template <int D, int KB, int QJL, int VB, int SCORES>
 __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams p) {
   using S = Shape<D, KB, QJL, VB>;
+  // One table serves keys and values when their widths match (the codebook and
+  // its fp16 factor depend only on the width and the head dimension).
+  constexpr int kKtab = Lut<KB>::kDwords, kVtab = KB == VB ? 0 : Lut<VB>::kDwords;
+  __shared__ __align__(16) uint32_t lut[kKtab + kVtab];
   __shared__ __align__(16) _Float16 pbuf[kWaves][2][4][32];
   __shared__ float mrg_m[kWaves][4], mrg_l[kWaves][4];
   __shared__ float mrg_acc[kWaves][4][D];
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  // The wave index is uniform across the wave; saying so keeps the key loop's
+  // control flow scalar (a per-lane loop exit would copy the accumulators out
+  // of the matrix-core registers on every block).
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int l16 = lane % 16, g4 = lane / 16;
   // Workgroup = (sequence, group of up to 4 of its query rows, key split).
   const int64_t seq = blockIdx.x / p.rgroups;
@@ -379,9 +416,11 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   sb.vnorm = make_rsrc(p.vnorm + seq * p.cap, p.N * 4);
 
   WaveState<D, KB, QJL, VB> ws;
-  const float scale_k = p.scales[0], scale_v = p.scales[1];
-  make_tables<KB>(p.cb, scale_k, lane, ws.kt0, ws.kt1);
-  make_tables<VB>(p.cb + 2 * kMaxLevels, scale_v, lane, ws.vt0, ws.vt1);
+  const float scale_k = p.scales[0], scale_v = KB == VB ? scale_k : p.scales[1];
+  fill_lut<KB>(lut, p.cb, scale_k, tid);
+  if constexpr (KB != VB) fill_lut<VB>(lut + kKtab, p.cb + 2 * kMaxLevels, scale_v, tid);
+  ws.ktab = lut;
+  ws.vtab = KB == VB ? lut : lut + kKtab;
 
   // Query operands: lane (row rho = l16, k-group g4).
   {
@@ -445,6 +484,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   int blk = blk0 + wave;
   load_block(b0, sb, blk * 32, l16, g4);
   load_block(b1, sb, (blk + kWaves) * 32, l16, g4);
+  __syncthreads();  // the code tables are filled
   for (; blk < blk1; blk += 3 * kWaves) {
     load_block(b2, sb, (blk + 2 * kWaves) * 32, l16, g4);
     process_block<D, KB, QJL, VB, SCORES>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
