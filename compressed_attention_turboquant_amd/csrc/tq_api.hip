@@ -19,7 +19,7 @@ struct Plan {  // split-K plan of one decode call
   int nsplit;
   int64_t keys_per_split;
   int64_t rows_total;
-  size_t off_qrot, off_qproj, off_rowc, off_count, off_part, total;
+  size_t off_qrot, off_qproj, off_rowc, off_part, total;
 };
 
 Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
@@ -54,8 +54,7 @@ Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
   p.off_qrot = o;  o = align_up(o + (size_t)p.rows_total * d * sizeof(float), 256);
   p.off_qproj = o; o = align_up(o + (size_t)p.rows_total * d * sizeof(float), 256);
   p.off_rowc = o;  o = align_up(o + (size_t)p.rows_total * 4 * sizeof(float), 256);
-  p.off_count = o; o = align_up(o + (size_t)seqs * sizeof(int), 256);
-  p.off_part = o;  o = align_up(o + (size_t)p.nsplit * p.rows_total * (d + 2) * sizeof(float), 256);
+  p.off_part = o;  o = align_up(o + (size_t)p.nsplit * p.rows_total * (d + kPartPad) * sizeof(float), 256);
   p.total = o;
   return p;
 }
@@ -322,7 +321,6 @@ tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, 
     x.St = blob_f(layer, BL.proj_t);
     x.scales = blob_f(layer, BL.scales);
     x.rowc = reinterpret_cast<float*>(ws + P.off_rowc);
-    x.counters = reinterpret_cast<int*>(ws + P.off_count);
     return hip_status(launch_decode_mfma(a, x, st), "decode launch");
   }
   return hip_status(launch_decode_ref(a, st), "decode launch");

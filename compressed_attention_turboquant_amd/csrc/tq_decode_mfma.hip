@@ -523,7 +523,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
         L = fmaf(f, mrg_l[w][r], L);
       }
     }
-    float* dst = p.part + ((int64_t)split * rows_total + qrow_of(r)) * (D + 2);
+    float* dst = p.part + ((int64_t)split * rows_total + qrow_of(r)) * (D + kPartPad);
     dst[j] = a;
     if (j == 0) {
       dst[D] = M * kLn2;  // natural-log units, as the combine kernel expects
@@ -532,62 +532,87 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   }
 }
 
-// One block per query row: rotates it once (R q, S q, reading R^T and S^T so
-// that neighbouring threads read neighbouring addresses) and normalises it for
-// the fp16 operand split: qa = (R q) / (s_k c1), qb = (S q) 2 / c2 with c1, c2
-// powers of two bringing the largest entry into [1, 2); rowc = {c1, c2,
-// -sum(S q), 0}.  The first row of each KV head also clears its split counter.
-__global__ void __launch_bounds__(256) prerotate_mfma_kernel(PrerotateParams p) {
-  __shared__ float qs[256];
-  __shared__ float part[2][2][256];
+// Matrix-vector products with 256 threads: thread (jq, sl) owns outputs
+// 4jq..4jq+3 and the k-slice sl, reading one float4 of a matrix row per k (so
+// a wave reads whole rows) with every load of the slice in flight at once.
+template <int D>
+struct MatVec {
+  static constexpr int kJ = D / 4;           // threads per k-slice
+  static constexpr int kSlices = 256 / kJ;   // 8 (D = 128) or 4 (D = 256)
+  static constexpr int kSpan = D / kSlices;  // k per slice
+};
+
+// sum over the thread's k-slice of M[k][4jq..4jq+3] * x[k]; M row-major D x D
+// (global), x in LDS.
+template <int D>
+__device__ __forceinline__ f4 matvec_part(const float* __restrict__ M, const float* x, int jq, int sl) {
+  using V = MatVec<D>;
+  const f4* m = reinterpret_cast<const f4*>(M) + jq;
+  f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+  for (int kk = 0; kk < V::kSpan; kk += 2) {
+    const int k = sl * V::kSpan + kk;
+    acc0 += m[(size_t)k * V::kJ] * x[k];
+    acc1 += m[(size_t)(k + 1) * V::kJ] * x[k + 1];
+  }
+  return acc0 + acc1;
+}
+
+// Output j (thread j < D) of the slices' partial sums.
+template <int D>
+__device__ __forceinline__ float matvec_sum(const f4 (*part)[D / 4], int j) {
+  float v = 0.f;
+#pragma unroll
+  for (int s = 0; s < MatVec<D>::kSlices; ++s) v += part[s][j / 4][j % 4];
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// One block per query row: rotates it once (R q, S q, reading R^T and S^T) and
+// normalises it for the fp16 operand split: qa = (R q) / (s_k c1), qb = (S q) 2
+// / c2 with c1, c2 powers of two bringing the largest entry into [1, 2); rowc =
+// {c1, c2, -sum(S q), 0}.
+template <int D, int QJL>
+__global__ void __launch_bounds__(256) prerotate_kernel(PrerotateParams p) {
+  using V = MatVec<D>;
+  __shared__ float qs[D];
+  __shared__ f4 part[2][V::kSlices][V::kJ];
   __shared__ float red[3][4];
   const int64_t row = blockIdx.x;  // = (b * Hq + h) * Tq + t
-  const int tid = threadIdx.x;
-  const int d = p.d;
-  if (tid < d)
-    qs[tid] = p.qdt == TQ_F16 ? __half2float(static_cast<const __half*>(p.q)[row * d + tid])
-                              : static_cast<const float*>(p.q)[row * d + tid];
-  {
-    const int64_t h = (row / p.Tq) % p.Hq, t = row % p.Tq, b = row / ((int64_t)p.Tq * p.Hq);
-    const int G = p.Hq / p.Hkv;
-    if (tid == 0 && h % G == 0 && t == 0) p.counters[b * p.Hkv + h / G] = 0;
-  }
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  if (tid < D)
+    qs[tid] = p.qdt == TQ_F16 ? __half2float(static_cast<const __half*>(p.q)[row * D + tid])
+                              : static_cast<const float*>(p.q)[row * D + tid];
   __syncthreads();
-  // thread -> output j, k-range half hk (d = 128: two halves of 64; d = 256: one)
-  const int j = tid % d, hk = tid / d, nk = 256 / d, kspan = d / nk;
-  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
-  for (int k = hk * kspan; k < (hk + 1) * kspan; k += 2) {
-    a0 = fmaf(p.Rt[(size_t)k * d + j], qs[k], a0);
-    a1 = fmaf(p.Rt[(size_t)(k + 1) * d + j], qs[k + 1], a1);
-    if (p.qjl) {
-      b0 = fmaf(p.St[(size_t)k * d + j], qs[k], b0);
-      b1 = fmaf(p.St[(size_t)(k + 1) * d + j], qs[k + 1], b1);
-    }
-  }
-  part[0][hk][j] = a0 + a1;
-  part[1][hk][j] = b0 + b1;
+  const int jq = tid % V::kJ, sl = tid / V::kJ;
+  part[0][sl][jq] = matvec_part<D>(p.Rt, qs, jq, sl);
+  if constexpr (QJL) part[1][sl][jq] = matvec_part<D>(p.St, qs, jq, sl);
   __syncthreads();
   float a = 0.f, b = 0.f;
-  if (tid < d) {
-    for (int h = 0; h < nk; ++h) {
-      a += part[0][h][tid];
-      b += part[1][h][tid];
-    }
-    a /= p.scales[0];
+  if (tid < D) {
+    a = matvec_sum<D>(part[0], tid) / p.scales[0];
+    if constexpr (QJL) b = matvec_sum<D>(part[1], tid);
   }
-  float x = tid < d ? fabsf(a) : 0.f, y = tid < d ? fabsf(b) : 0.f, z = tid < d ? b : 0.f;
-  for (int o = 32; o > 0; o >>= 1) {
-    x = fmaxf(x, __shfl_xor(x, o));
-    y = fmaxf(y, __shfl_xor(y, o));
-    z += __shfl_xor(z, o);
-  }
-  if (tid % 64 == 0) {
-    red[0][tid / 64] = x;
-    red[1][tid / 64] = y;
-    red[2][tid / 64] = z;
+  const float x = wave_max(fabsf(a)), y = wave_max(fabsf(b)), z = wave_sum(b);
+  if (lane == 0) {
+    red[0][wave] = x;
+    red[1][wave] = y;
+    red[2][wave] = z;
   }
   __syncthreads();
+  if (tid >= D) return;
   float ma = 0.f, mb = 0.f, sbv = 0.f;
+#pragma unroll
   for (int w = 0; w < 4; ++w) {
     ma = fmaxf(ma, red[0][w]);
     mb = fmaxf(mb, red[1][w]);
@@ -598,16 +623,61 @@ __global__ void __launch_bounds__(256) prerotate_mfma_kernel(PrerotateParams p) 
   frexpf(mb, &e2);
   const float c1 = ma > 0.f ? ldexpf(1.f, e1 - 1) : 1.f;
   const float c2 = mb > 0.f ? ldexpf(1.f, e2) : 2.f;
-  if (tid < d) {
-    p.qa[row * d + tid] = a / c1;
-    p.qb[row * d + tid] = b * 2.f / c2;
-  }
+  p.qa[row * D + tid] = a / c1;
+  p.qb[row * D + tid] = b * 2.f / c2;
   if (tid == 0) {
     p.rowc[row * 4 + 0] = c1;
     p.rowc[row * 4 + 1] = c2;
     p.rowc[row * 4 + 2] = -sbv;
     p.rowc[row * 4 + 3] = 0.f;
   }
+}
+
+// One block per query row: merges the splits' partial softmax sums (rows of D +
+// kPartPad floats: accumulator, maximum in natural-log units, sum) and
+// un-rotates the result, out = R^T (sum_s w_s acc_s / sum_s w_s L_s) with w_s =
+// exp(m_s - max_s m_s).
+template <int D>
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ part, int nsplit,
+                                                      int64_t rows_total, const float* __restrict__ R,
+                                                      float* __restrict__ out) {
+  using V = MatVec<D>;
+  constexpr int kStride = D + kPartPad;
+  __shared__ float wts[1024];  // the plan keeps nsplit <= 1024
+  __shared__ float os[D];
+  __shared__ f4 acc[V::kSlices][V::kJ];
+  __shared__ float red[2][4];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const float* base = part + row * kStride;
+  const int64_t sstride = rows_total * kStride;
+  float M = -INFINITY;
+  for (int s = tid; s < nsplit; s += 256) M = fmaxf(M, base[s * sstride + D]);
+  M = wave_max(M);
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  float L = 0.f;
+  for (int s = tid; s < nsplit; s += 256) {
+    const float m = base[s * sstride + D];
+    const float w = m == -INFINITY ? 0.f : expf(m - M);
+    wts[s] = w;
+    L = fmaf(w, base[s * sstride + D + 1], L);
+  }
+  L = wave_sum(L);
+  if (lane == 0) red[1][wave] = L;
+  __syncthreads();
+  const float invL = 1.0f / (red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+  const int jq = tid % V::kJ, sl = tid / V::kJ;
+  f4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s = sl; s < nsplit; s += V::kSlices) o += reinterpret_cast<const f4*>(base + s * sstride)[jq] * wts[s];
+  acc[sl][jq] = o;
+  __syncthreads();
+  if (tid < D) os[tid] = matvec_sum<D>(acc, tid) * invL;
+  __syncthreads();
+  acc[sl][jq] = matvec_part<D>(R, os, jq, sl);
+  __syncthreads();
+  if (tid < D) out[row * D + tid] = matvec_sum<D>(acc, tid);
 }
 
 template <int D, int KB, int QJL, int VB>
@@ -666,8 +736,15 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   pr.qa = a.q_rot;
   pr.qb = a.q_proj;
   pr.rowc = x.rowc;
-  pr.counters = x.counters;
-  hipLaunchKernelGGL(prerotate_mfma_kernel, dim3((unsigned)((int64_t)a.B * a.Hq * a.Tq)), dim3(256), 0, st, pr);
+  const int64_t qrows = (int64_t)a.B * a.Hq * a.Tq;
+  const dim3 rgrid((unsigned)qrows);
+  if (a.d == 128) {
+    if (a.qjl) hipLaunchKernelGGL((prerotate_kernel<128, 1>), rgrid, dim3(256), 0, st, pr);
+    else hipLaunchKernelGGL((prerotate_kernel<128, 0>), rgrid, dim3(256), 0, st, pr);
+  } else {
+    if (a.qjl) hipLaunchKernelGGL((prerotate_kernel<256, 1>), rgrid, dim3(256), 0, st, pr);
+    else hipLaunchKernelGGL((prerotate_kernel<256, 0>), rgrid, dim3(256), 0, st, pr);
+  }
   DecodeMfmaParams p{};
   p.qa = a.q_rot;
   p.qb = a.q_proj;
@@ -682,7 +759,6 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   p.cb = a.cb;
   p.R = a.R;
   p.out = a.out;
-  p.counters = x.counters;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.Tq = a.Tq;
@@ -694,10 +770,14 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   p.scores = a.scores;
   p.rgroups = (a.Hq / a.Hkv * a.Tq + 3) / 4;
   const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * p.rgroups), (unsigned)a.nsplit);
-  const hipError_t e = a.d == 128 ? dispatch_d<128>(p, a.kb, a.qjl, a.vb, grid, st)
-                                  : dispatch_d<256>(p, a.kb, a.qjl, a.vb, grid, st);
+  hipError_t e = a.d == 128 ? dispatch_d<128>(p, a.kb, a.qjl, a.vb, grid, st)
+                            : dispatch_d<256>(p, a.kb, a.qjl, a.vb, grid, st);
   if (e != hipSuccess) return e;
-  return launch_decode_combine(a, st);
+  if (a.d == 128)
+    hipLaunchKernelGGL(combine_kernel<128>, rgrid, dim3(256), 0, st, a.part, a.nsplit, qrows, a.R, a.out);
+  else
+    hipLaunchKernelGGL(combine_kernel<256>, rgrid, dim3(256), 0, st, a.part, a.nsplit, qrows, a.R, a.out);
+  return hipGetLastError();
 }
 
 }  // namespace tq

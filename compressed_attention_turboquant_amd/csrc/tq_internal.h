@@ -10,6 +10,10 @@
 namespace tq {
 
 constexpr int kMaxLevels = 16;  // 4-bit codes
+// Decode split partials: one row of d + kPartPad floats per (split, query row):
+// the rotated-domain accumulator (d), the running maximum (natural log), the
+// sum of weights and padding to a 16-byte multiple.
+constexpr int kPartPad = 4;
 
 // Offsets (bytes) of the tables inside a layer blob.  All float32 unless noted.
 struct BlobLayout {

@@ -53,7 +53,6 @@ struct DecodeMfmaParams {
   const float* scales;              // blob: fp16 table factors for key and value centroids
   const float* R;                   // rotation (row-major) for the final un-rotation
   float* out;
-  int* counters;                    // per sequence: workgroups finished (reset to 0 after use)
   int Hq, Hkv, Tq, causal;
   int rgroups;                      // groups of up to 4 query rows per KV head
   int64_t N, cap, keys_per_split;
@@ -65,14 +64,12 @@ struct PrerotateParams {
   int qdt, d, Hq, Hkv, Tq, qjl;
   const float *Rt, *St, *scales;
   float *qa, *qb, *rowc;
-  int* counters;
 };
 
 // Blob and workspace pieces the matrix-core decode needs besides DecodeArgs.
 struct DecodeMfmaExtra {
   const float *Rt, *St, *scales;
   float* rowc;
-  int* counters;
 };
 
 // Arguments of the matrix-core quantize kernel (tq_quantize_mfma.hip, d = 128, fp16 input).

@@ -310,19 +310,19 @@ __global__ void __launch_bounds__(kThreads) decode_split_ref(
       const int p = tid + a * kThreads;
       if (p < rows * d) {
         const int r = p / d, j = p % d;
-        part[((int64_t)split * rows_total + qrow_of(r)) * (d + 2) + j] = acc[a];
+        part[((int64_t)split * rows_total + qrow_of(r)) * (d + kPartPad) + j] = acc[a];
       }
     }
   }
   for (int r = tid; r < rows; r += kThreads) {
-    float* dst = part + ((int64_t)split * rows_total + qrow_of(r)) * (d + 2) + d;
+    float* dst = part + ((int64_t)split * rows_total + qrow_of(r)) * (d + kPartPad) + d;
     dst[0] = mrow[r];
     dst[1] = lrow[r];
   }
 }
 
 // Merge the per-split partial softmax sums and un-rotate once per query row.
-// Partial rows are [acc (d) | max (natural log) | sum].
+// Partial rows are [acc (d) | max (natural log) | sum | padding], d + kPartPad floats.
 __global__ void __launch_bounds__(kThreads) decode_combine_ref(const float* __restrict__ part,
                                                                int nsplit, int64_t rows_total,
                                                                int d, const float* __restrict__ R,
@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(kThreads) decode_combine_ref(const float* __re
   // max over splits, then weights: one thread per split (looping if more splits than threads)
   __shared__ float red[kThreads];
   float M = -INFINITY;
-  for (int s = j; s < nsplit; s += kThreads) M = fmaxf(M, part[((int64_t)s * rows_total + row) * (d + 2) + d]);
+  for (int s = j; s < nsplit; s += kThreads) M = fmaxf(M, part[((int64_t)s * rows_total + row) * (d + kPartPad) + d]);
   red[j] = M;
   __syncthreads();
   for (int off = kThreads / 2; off > 0; off >>= 1) {
@@ -346,7 +346,7 @@ __global__ void __launch_bounds__(kThreads) decode_combine_ref(const float* __re
   __syncthreads();
   float lsum = 0.f;
   for (int s = j; s < nsplit; s += kThreads) {
-    const float* p = part + ((int64_t)s * rows_total + row) * (d + 2);
+    const float* p = part + ((int64_t)s * rows_total + row) * (d + kPartPad);
     const float w = p[d] == -INFINITY ? 0.f : expf(p[d] - M);
     if (s < 1024) wts[0][s] = w;
     lsum = fmaf(w, p[d + 1], lsum);
@@ -364,10 +364,10 @@ __global__ void __launch_bounds__(kThreads) decode_combine_ref(const float* __re
     int s = 0;
     for (; s + 1 < nsplit; s += 2) {
       const float w0 = s < 1024 ? wts[0][s] : 0.f, w1 = s + 1 < 1024 ? wts[0][s + 1] : 0.f;
-      a0 = fmaf(w0, part[((int64_t)s * rows_total + row) * (d + 2) + j], a0);
-      a1 = fmaf(w1, part[((int64_t)(s + 1) * rows_total + row) * (d + 2) + j], a1);
+      a0 = fmaf(w0, part[((int64_t)s * rows_total + row) * (d + kPartPad) + j], a0);
+      a1 = fmaf(w1, part[((int64_t)(s + 1) * rows_total + row) * (d + kPartPad) + j], a1);
     }
-    for (; s < nsplit; ++s) a0 = fmaf(s < 1024 ? wts[0][s] : 0.f, part[((int64_t)s * rows_total + row) * (d + 2) + j], a0);
+    for (; s < nsplit; ++s) a0 = fmaf(s < 1024 ? wts[0][s] : 0.f, part[((int64_t)s * rows_total + row) * (d + kPartPad) + j], a0);
     o[j] = (a0 + a1) * invL;
   }
   __syncthreads();
