@@ -19,7 +19,7 @@ struct Plan {  // split-K plan of one decode call
   int nsplit;
   int64_t keys_per_split;
   int64_t rows_total;
-  size_t off_qrot, off_qproj, off_rowc, off_part, total;
+  size_t off_qrot, off_qproj, off_part, total;
 };
 
 Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
@@ -27,12 +27,15 @@ Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
   const int64_t seqs = (int64_t)B * Hkv;
   p.mfma = mfma_decode_supports(d, Hq / Hkv * Tq);
   if (p.mfma) {
-    // Work in blocks of 32 keys; aim for ~2048 workgroups (8 per CU) while
-    // giving each of a workgroup's 4 waves at least 4 blocks.  A workgroup
-    // serves up to 4 query rows of one KV head.
+    // Work in blocks of 32 keys.  A workgroup serves up to 4 query rows of one
+    // KV head; split the keys so that the workgroups fill the chip once (2 per
+    // CU at d = 128, 1 at d = 256: their register use allows no more) -- a
+    // second round of workgroups costs more in set-up and tail than it gains
+    // -- while giving each of a workgroup's 4 waves at least 4 blocks.
     const int64_t blocks = (N + 31) / 32;
     const int64_t groups = seqs * ((Hq / Hkv * Tq + 3) / 4);
-    int64_t want = (2048 + groups - 1) / groups;
+    const int64_t target = d == 128 ? 512 : 256;
+    int64_t want = (target + groups - 1) / groups;
     const int64_t max_split = (blocks + 15) / 16;
     if (want > max_split) want = max_split;
     if (want > 1024) want = 1024;  // the combine kernel keeps one weight per split in LDS
@@ -51,9 +54,11 @@ Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
   }
   p.rows_total = (int64_t)B * Hq * Tq;
   size_t o = 0;
-  p.off_qrot = o;  o = align_up(o + (size_t)p.rows_total * d * sizeof(float), 256);
-  p.off_qproj = o; o = align_up(o + (size_t)p.rows_total * d * sizeof(float), 256);
-  p.off_rowc = o;  o = align_up(o + (size_t)p.rows_total * 4 * sizeof(float), 256);
+  // The reference path rotates the query rows into the workspace first; the
+  // matrix-core kernel does it on chip.
+  const size_t qbytes = p.mfma ? 0 : (size_t)p.rows_total * d * sizeof(float);
+  p.off_qrot = o;  o = align_up(o + qbytes, 256);
+  p.off_qproj = o; o = align_up(o + qbytes, 256);
   p.off_part = o;  o = align_up(o + (size_t)p.nsplit * p.rows_total * (d + kPartPad) * sizeof(float), 256);
   p.total = o;
   return p;
@@ -320,7 +325,6 @@ tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, 
     x.Rt = blob_f(layer, BL.rot_t);
     x.St = blob_f(layer, BL.proj_t);
     x.scales = blob_f(layer, BL.scales);
-    x.rowc = reinterpret_cast<float*>(ws + P.off_rowc);
     return hip_status(launch_decode_mfma(a, x, st), "decode launch");
   }
   return hip_status(launch_decode_ref(a, st), "decode launch");

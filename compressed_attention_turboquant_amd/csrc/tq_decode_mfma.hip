@@ -377,6 +377,39 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, con
   __builtin_amdgcn_wave_barrier();
 }
 
+// The workgroup's query rows rotated once: rq[0][r][j] = (R q_r)_j / s_k and
+// rq[1][r][j] = (S q_r)_j, from the rows in qs (LDS) and R^T, S^T (global,
+// row-major, so that neighbouring threads read neighbouring addresses).  Each
+// workgroup starts at its own row k0 of the matrices, so that the workgroups,
+// which all read the same few hundred KB at once, spread over the L2 channels.
+template <int D, int QJL>
+__device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const float* __restrict__ St,
+                                            float s_k, const float (*qs)[D], float (*rq)[4][D], int tid,
+                                            int k0) {
+  constexpr int kMats = D == 128 ? 2 : 1;  // matrices handled side by side by the 256 threads
+#pragma unroll
+  for (int pass = 0; pass < 2 / kMats; ++pass) {
+    const int m = D == 128 ? tid / 128 : pass, j = tid % D;
+    if (m == 1 && !QJL) continue;
+    const float* M = (m == 0 ? Rt : St) + j;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 16
+    for (int kk = 0; kk < D; ++kk) {
+      const int k = (kk + k0) & (D - 1);
+      const float x = M[(size_t)k * D];
+      a0 = fmaf(x, qs[0][k], a0);
+      a1 = fmaf(x, qs[1][k], a1);
+      a2 = fmaf(x, qs[2][k], a2);
+      a3 = fmaf(x, qs[3][k], a3);
+    }
+    const float f = m == 0 ? 1.0f / s_k : 1.0f;
+    rq[m][0][j] = a0 * f;
+    rq[m][1][j] = a1 * f;
+    rq[m][2][j] = a2 * f;
+    rq[m][3][j] = a3 * f;
+  }
+}
+
 template <int D, int KB, int QJL, int VB, int SCORES>
 __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams p) {
   using S = Shape<D, KB, QJL, VB>;
@@ -387,6 +420,9 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   __shared__ __align__(16) _Float16 pbuf[kWaves][2][4][32];
   __shared__ float mrg_m[kWaves][4], mrg_l[kWaves][4];
   __shared__ float mrg_acc[kWaves][4][D];
+  __shared__ float qsh[4][D];      // the workgroup's query rows
+  __shared__ float qrs[2][4][D];   // R q / s_k and S q of those rows
+  __shared__ float qcon[4][4];     // per row: c1, c2, -sum(S q)
 
   const int tid = threadIdx.x;
   // The wave index is uniform across the wave; saying so keeps the key loop's
@@ -415,6 +451,15 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   sb.vidx = make_rsrc(p.vidx + seq * (p.cap / 8) * S::VTILE, (p.cap / 8) * S::VTILE);
   sb.vnorm = make_rsrc(p.vnorm + seq * p.cap, p.N * 4);
 
+  // The first two key blocks start loading before the set-up below.
+  const int nblk = (int)((p.N + 31) / 32);
+  const int blk0 = (int)(split * (p.keys_per_split / 32));
+  const int blk1 = min(nblk, blk0 + (int)(p.keys_per_split / 32));
+  Block<D, KB, QJL, VB> b0, b1, b2;
+  int blk = blk0 + wave;
+  load_block(b0, sb, blk * 32, l16, g4);
+  load_block(b1, sb, (blk + kWaves) * 32, l16, g4);
+
   WaveState<D, KB, QJL, VB> ws;
   const float scale_k = p.scales[0], scale_v = KB == VB ? scale_k : p.scales[1];
   fill_lut<KB>(lut, p.cb, scale_k, tid);
@@ -422,17 +467,61 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   ws.ktab = lut;
   ws.vtab = KB == VB ? lut : lut + kKtab;
 
+  // Rotate the query rows once (R q, S q) and normalise them for the fp16
+  // operand split: qa = (R q) / (s_k c1), qb = 2 (S q) / c2 with c1, c2 powers of
+  // two that bring the largest entry into [1, 2).
+  for (int i = tid; i < 4 * D; i += kThreads) {
+    const int r = i / D, k = i % D;
+    float v = 0.f;
+    if (r < rows) {
+      const int64_t o = qrow_of(r) * D + k;
+      v = p.qdt == TQ_F16 ? __half2float(static_cast<const __half*>(p.q)[o]) : static_cast<const float*>(p.q)[o];
+    }
+    qsh[r][k] = v;
+  }
+  __syncthreads();  // also publishes the code tables
+  rotate_rows<D, QJL>(p.Rt, p.St, scale_k, qsh, qrs, tid, (int)((blockIdx.x * 5 + blockIdx.y * 3) * 16) & (D - 1));
+  __syncthreads();
+  {
+    const int r = wave;  // wave r normalises row r
+    float ma = 0.f, mb = 0.f, sbv = 0.f;
+#pragma unroll
+    for (int j = lane; j < D; j += 64) {
+      ma = fmaxf(ma, fabsf(qrs[0][r][j]));
+      if constexpr (QJL) {
+        mb = fmaxf(mb, fabsf(qrs[1][r][j]));
+        sbv += qrs[1][r][j];
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      ma = fmaxf(ma, __shfl_xor(ma, o));
+      mb = fmaxf(mb, __shfl_xor(mb, o));
+      sbv += __shfl_xor(sbv, o);
+    }
+    if (lane == 0) {
+      int e1 = 0, e2 = 0;
+      frexpf(ma, &e1);
+      frexpf(mb, &e2);
+      qcon[r][0] = ma > 0.f ? ldexpf(1.f, e1 - 1) : 1.f;
+      qcon[r][1] = mb > 0.f ? ldexpf(1.f, e2) : 2.f;
+      qcon[r][2] = QJL ? -sbv : 0.f;
+    }
+  }
+  __syncthreads();
+
   // Query operands: lane (row rho = l16, k-group g4).
   {
     const int qr = l16 / 4, part = l16 % 4;
     const bool ok = qr < rows;
-    const float* qa = p.qa + (ok ? qrow_of(qr) : 0) * D + (D / 4) * g4;
-    const float* qb = p.qb + (ok ? qrow_of(qr) : 0) * D + (D / 4) * g4;
+    const float fa = 1.0f / qcon[qr][0], fb = 2.0f / qcon[qr][1];  // powers of two: exact
+    const float* qa = &qrs[0][qr][(D / 4) * g4];
+    const float* qb = &qrs[1][qr][(D / 4) * g4];
     sfor<0, S::KBLK>([&](auto kb) {
       h8 a;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = (ok && part < 2) ? qa[8 * kb + e] : 0.f;
+        const float x = (ok && part < 2) ? qa[8 * kb + e] * fa : 0.f;
         const _Float16 hi = (_Float16)x;
         const _Float16 lo = (_Float16)(x - (float)hi);
         a[e] = part == 0 ? hi : (part == 1 ? lo : (_Float16)0.f);
@@ -443,7 +532,8 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int w = e / 2, h = e % 2;
-          const float x = (ok && part >= 2) ? qb[32 * (kb / 4) + sign_coord(kb % 4, w, h)] * sign_comp(w) : 0.f;
+          const float x =
+              (ok && part >= 2) ? qb[32 * (kb / 4) + sign_coord(kb % 4, w, h)] * fb * sign_comp(w) : 0.f;
           const _Float16 hi = (_Float16)x;
           const _Float16 lo = (_Float16)(x - (float)hi);
           s[e] = part == 2 ? hi : (part == 3 ? lo : (_Float16)0.f);
@@ -458,7 +548,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   ws.srow = 0;
   if (g4 < rows) {
     ws.srow = qrow_of(g4);
-    const float* rc = p.rowc + ws.srow * 4;
+    const float* rc = qcon[g4];
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
     const float cq = sqrtf(0.5f * (float)M_PI) / (float)D * inv_sqrt_d * kLog2e;
     ws.ca = rc[0] * inv_sqrt_d * kLog2e;
@@ -472,19 +562,10 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   ws.msafe = 0.f;
   ws.lsum = 0.f;
 
-  const int nblk = (int)((p.N + 31) / 32);
-  const int blk0 = (int)(split * (p.keys_per_split / 32));
-  const int blk1 = min(nblk, blk0 + (int)(p.keys_per_split / 32));
-
   // Three register sets rotate so two blocks are in flight while one is used.
   // The prefetches are unconditional (reads past the split land in the same
   // sequence, reads past its capacity return 0), which keeps the loop body
   // straight-line and lets the compiler count outstanding loads exactly.
-  Block<D, KB, QJL, VB> b0, b1, b2;
-  int blk = blk0 + wave;
-  load_block(b0, sb, blk * 32, l16, g4);
-  load_block(b1, sb, (blk + kWaves) * 32, l16, g4);
-  __syncthreads();  // the code tables are filled
   for (; blk < blk1; blk += 3 * kWaves) {
     load_block(b2, sb, (blk + 2 * kWaves) * 32, l16, g4);
     process_block<D, KB, QJL, VB, SCORES>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
@@ -543,15 +624,16 @@ struct MatVec {
 };
 
 // sum over the thread's k-slice of M[k][4jq..4jq+3] * x[k]; M row-major D x D
-// (global), x in LDS.
+// (global), x in LDS.  Slices start at row k0 (even), which blocks vary so that
+// they do not all read the same rows at once.
 template <int D>
-__device__ __forceinline__ f4 matvec_part(const float* __restrict__ M, const float* x, int jq, int sl) {
+__device__ __forceinline__ f4 matvec_part(const float* __restrict__ M, const float* x, int jq, int sl, int k0) {
   using V = MatVec<D>;
   const f4* m = reinterpret_cast<const f4*>(M) + jq;
   f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
   for (int kk = 0; kk < V::kSpan; kk += 2) {
-    const int k = sl * V::kSpan + kk;
+    const int k = (sl * V::kSpan + kk + k0) & (D - 1);
     acc0 += m[(size_t)k * V::kJ] * x[k];
     acc1 += m[(size_t)(k + 1) * V::kJ] * x[k + 1];
   }
@@ -576,61 +658,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
-}
-
-// One block per query row: rotates it once (R q, S q, reading R^T and S^T) and
-// normalises it for the fp16 operand split: qa = (R q) / (s_k c1), qb = (S q) 2
-// / c2 with c1, c2 powers of two bringing the largest entry into [1, 2); rowc =
-// {c1, c2, -sum(S q), 0}.
-template <int D, int QJL>
-__global__ void __launch_bounds__(256) prerotate_kernel(PrerotateParams p) {
-  using V = MatVec<D>;
-  __shared__ float qs[D];
-  __shared__ f4 part[2][V::kSlices][V::kJ];
-  __shared__ float red[3][4];
-  const int64_t row = blockIdx.x;  // = (b * Hq + h) * Tq + t
-  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  if (tid < D)
-    qs[tid] = p.qdt == TQ_F16 ? __half2float(static_cast<const __half*>(p.q)[row * D + tid])
-                              : static_cast<const float*>(p.q)[row * D + tid];
-  __syncthreads();
-  const int jq = tid % V::kJ, sl = tid / V::kJ;
-  part[0][sl][jq] = matvec_part<D>(p.Rt, qs, jq, sl);
-  if constexpr (QJL) part[1][sl][jq] = matvec_part<D>(p.St, qs, jq, sl);
-  __syncthreads();
-  float a = 0.f, b = 0.f;
-  if (tid < D) {
-    a = matvec_sum<D>(part[0], tid) / p.scales[0];
-    if constexpr (QJL) b = matvec_sum<D>(part[1], tid);
-  }
-  const float x = wave_max(fabsf(a)), y = wave_max(fabsf(b)), z = wave_sum(b);
-  if (lane == 0) {
-    red[0][wave] = x;
-    red[1][wave] = y;
-    red[2][wave] = z;
-  }
-  __syncthreads();
-  if (tid >= D) return;
-  float ma = 0.f, mb = 0.f, sbv = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    ma = fmaxf(ma, red[0][w]);
-    mb = fmaxf(mb, red[1][w]);
-    sbv += red[2][w];
-  }
-  int e1 = 0, e2 = 0;
-  frexpf(ma, &e1);
-  frexpf(mb, &e2);
-  const float c1 = ma > 0.f ? ldexpf(1.f, e1 - 1) : 1.f;
-  const float c2 = mb > 0.f ? ldexpf(1.f, e2) : 2.f;
-  p.qa[row * D + tid] = a / c1;
-  p.qb[row * D + tid] = b * 2.f / c2;
-  if (tid == 0) {
-    p.rowc[row * 4 + 0] = c1;
-    p.rowc[row * 4 + 1] = c2;
-    p.rowc[row * 4 + 2] = -sbv;
-    p.rowc[row * 4 + 3] = 0.f;
-  }
 }
 
 // One block per query row: merges the splits' partial softmax sums (rows of D +
@@ -675,7 +702,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   __syncthreads();
   if (tid < D) os[tid] = matvec_sum<D>(acc, tid) * invL;
   __syncthreads();
-  acc[sl][jq] = matvec_part<D>(R, os, jq, sl);
+  acc[sl][jq] = matvec_part<D>(R, os, jq, sl, (int)(blockIdx.x * 6) & (D - 1));
   __syncthreads();
   if (tid < D) out[row * D + tid] = matvec_sum<D>(acc, tid);
 }
@@ -722,33 +749,13 @@ hipError_t dispatch_d(const DecodeMfmaParams& p, int kb, int qjl, int vb, dim3 g
 bool mfma_decode_supports(int d, int rows) { return (d == 128 || d == 256) && rows >= 1; }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st) {
-  PrerotateParams pr{};
-  pr.q = a.q;
-  pr.qdt = a.q_dtype;
-  pr.d = a.d;
-  pr.Hq = a.Hq;
-  pr.Hkv = a.Hkv;
-  pr.Tq = a.Tq;
-  pr.qjl = a.qjl;
-  pr.Rt = x.Rt;
-  pr.St = x.St;
-  pr.scales = x.scales;
-  pr.qa = a.q_rot;
-  pr.qb = a.q_proj;
-  pr.rowc = x.rowc;
   const int64_t qrows = (int64_t)a.B * a.Hq * a.Tq;
   const dim3 rgrid((unsigned)qrows);
-  if (a.d == 128) {
-    if (a.qjl) hipLaunchKernelGGL((prerotate_kernel<128, 1>), rgrid, dim3(256), 0, st, pr);
-    else hipLaunchKernelGGL((prerotate_kernel<128, 0>), rgrid, dim3(256), 0, st, pr);
-  } else {
-    if (a.qjl) hipLaunchKernelGGL((prerotate_kernel<256, 1>), rgrid, dim3(256), 0, st, pr);
-    else hipLaunchKernelGGL((prerotate_kernel<256, 0>), rgrid, dim3(256), 0, st, pr);
-  }
   DecodeMfmaParams p{};
-  p.qa = a.q_rot;
-  p.qb = a.q_proj;
-  p.rowc = x.rowc;
+  p.q = a.q;
+  p.qdt = a.q_dtype;
+  p.Rt = x.Rt;
+  p.St = x.St;
   p.scales = x.scales;
   p.kidx = a.kidx;
   p.ksign = a.ksign;

@@ -47,7 +47,9 @@ struct DequantArgs {
 
 // Arguments of the matrix-core decode split kernel (tq_decode_mfma.hip).
 struct DecodeMfmaParams {
-  const float *qa, *qb, *rowc;      // normalised R q and S q rows, per-row constants
+  const void* q;                    // query rows [B][Hq][Tq][d]
+  int qdt;                          // TQ_F16 or TQ_F32
+  const float *Rt, *St;             // R^T and S^T (row-major) for the query rotation
   const uint8_t *kidx, *ksign, *vidx;
   const float *knorm, *krnorm, *vnorm, *cb;
   const float* scales;              // blob: fp16 table factors for key and value centroids
@@ -59,17 +61,9 @@ struct DecodeMfmaParams {
   float *part, *scores;
 };
 
-struct PrerotateParams {
-  const void* q;
-  int qdt, d, Hq, Hkv, Tq, qjl;
-  const float *Rt, *St, *scales;
-  float *qa, *qb, *rowc;
-};
-
 // Blob and workspace pieces the matrix-core decode needs besides DecodeArgs.
 struct DecodeMfmaExtra {
   const float *Rt, *St, *scales;
-  float* rowc;
 };
 
 // Arguments of the matrix-core quantize kernel (tq_quantize_mfma.hip, d = 128, fp16 input).
