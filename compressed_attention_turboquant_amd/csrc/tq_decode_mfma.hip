@@ -135,27 +135,30 @@ __device__ __forceinline__ uint32_t half_bits(float x) {
 }
 
 // Every thread of the workgroup: fill the table for centroids c scaled by s.
+// Lane l holds the fp16 pair of the codes in the low and high half of its lane
+// index (one code per half for 4-bit tables).  A wave fills 64 consecutive
+// entries, so an entry's low half is the lane's own value and its high half
+// comes from the lane its high index bits name (one cross-lane read).
 template <int BITS>
 __device__ __forceinline__ void fill_lut(uint32_t* tab, const float* c, float s, int tid) {
   using L = Lut<BITS>;
   constexpr uint32_t m = (1u << BITS) - 1u;
-  // Lane j holds fp16(s * c[j % 2^BITS]); entries gather it with permutes.
-  const uint32_t h = half_bits(s * c[tid & m]);
-  auto lv = [&](uint32_t code) { return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(code << 2), (int)h); };
-  // Whole waves run every iteration (the permutes need their source lanes).
-  for (int i0 = 0; i0 < L::kEntries; i0 += kThreads) {
-    const int i = i0 + tid;
-    const uint32_t u = (uint32_t)i;
-    if constexpr (L::kCodes == 4) {
-      const uint32_t e0 = lv(u & m) | (lv((u >> BITS) & m) << 16);
-      const uint32_t e1 = lv((u >> (2 * BITS)) & m) | (lv((u >> (3 * BITS)) & m) << 16);
-      if (i < L::kEntries) {
-        tab[2 * i] = e0;
-        tab[2 * i + 1] = e1;
-      }
-    } else {
-      const uint32_t e = lv(u & m) | (lv((u >> 4) & m) << 16);
-      if (i < L::kEntries) tab[i] = e;
+  const int lane = tid % 64;
+  if constexpr (L::kCodes == 4) {
+    constexpr int pb = 2 * BITS;  // bits of a pair index; 2^pb divides 64
+    constexpr uint32_t pm = (1u << pb) - 1u;
+    const uint32_t P = half_bits(s * c[lane & m]) | (half_bits(s * c[(lane >> BITS) & m]) << 16);
+    for (int i0 = 0; i0 < L::kEntries; i0 += kThreads) {
+      const uint32_t i = (uint32_t)(i0 + tid);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((i >> pb) & pm) << 2), (int)P);
+      if (i < (uint32_t)L::kEntries) *reinterpret_cast<u2*>(tab + 2 * i) = u2{P, hi};
+    }
+  } else {
+    const uint32_t h = half_bits(s * c[lane & m]);
+    for (int i0 = 0; i0 < L::kEntries; i0 += kThreads) {
+      const uint32_t i = (uint32_t)(i0 + tid);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((i >> BITS) & m) << 2), (int)h);
+      if (i < (uint32_t)L::kEntries) tab[i] = h | (hi << 16);
     }
   }
 }
@@ -379,39 +382,62 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, con
 
 // The workgroup's query rows rotated once: rq[0][r][j] = (R q_r)_j / s_k and
 // rq[1][r][j] = (S q_r)_j, from the rows in qs (LDS) and R^T, S^T (global,
-// row-major, so that neighbouring threads read neighbouring addresses).  Each
-// workgroup starts at its own row k0 of the matrices, so that the workgroups,
-// which all read the same few hundred KB at once, spread over the L2 channels.
+// row-major).  Thread (matrix, jq, slice) reads float4 rows M[k][4jq..4jq+3]
+// over its quarter of k for all four query rows; the slices' partial sums meet
+// in part (LDS).  Each workgroup starts its slices at its own row offset k0, so
+// that the workgroups, which all read the same few hundred KB at once, spread
+// over the L2 channels.
 template <int D, int QJL>
 __device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const float* __restrict__ St,
-                                            float s_k, const float (*qs)[D], float (*rq)[4][D], int tid,
-                                            int k0) {
-  constexpr int kMats = D == 128 ? 2 : 1;  // matrices handled side by side by the 256 threads
+                                            float s_k, const float (*qs)[D], float (*rq)[4][D],
+                                            f4 (*part)[4][D / 4], int tid, int k0) {
+  constexpr int kJ = D / 4;                   // float4 columns per matrix row
+  constexpr int kMats = D == 128 ? 2 : 1;     // matrices handled side by side
+  constexpr int kSl = 256 / (kJ * kMats);     // k-slices: 4
+  constexpr int kSpan = D / kSl;
 #pragma unroll
   for (int pass = 0; pass < 2 / kMats; ++pass) {
-    const int m = D == 128 ? tid / 128 : pass, j = tid % D;
-    if (m == 1 && !QJL) continue;
-    const float* M = (m == 0 ? Rt : St) + j;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    const int m = kMats == 2 ? tid / (kJ * kSl) : pass;
+    const int jq = tid % kJ, sl = (tid / kJ) % kSl;
+    if (QJL || m == 0) {
+      const f4* M = reinterpret_cast<const f4*>(m == 0 ? Rt : St) + jq;
+      f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
 #pragma unroll 16
-    for (int kk = 0; kk < D; ++kk) {
-      const int k = (kk + k0) & (D - 1);
-      const float x = M[(size_t)k * D];
-      a0 = fmaf(x, qs[0][k], a0);
-      a1 = fmaf(x, qs[1][k], a1);
-      a2 = fmaf(x, qs[2][k], a2);
-      a3 = fmaf(x, qs[3][k], a3);
+      for (int kk = 0; kk < kSpan; ++kk) {
+        const int k = (sl * kSpan + kk + k0) & (D - 1);
+        const f4 x = M[(size_t)k * kJ];
+        a0 += x * qs[0][k];
+        a1 += x * qs[1][k];
+        a2 += x * qs[2][k];
+        a3 += x * qs[3][k];
+      }
+      const int ps = (kMats == 2 ? m * kSl : 0) + sl;
+      part[ps][0][jq] = a0;
+      part[ps][1][jq] = a1;
+      part[ps][2][jq] = a2;
+      part[ps][3][jq] = a3;
     }
-    const float f = m == 0 ? 1.0f / s_k : 1.0f;
-    rq[m][0][j] = a0 * f;
-    rq[m][1][j] = a1 * f;
-    rq[m][2][j] = a2 * f;
-    rq[m][3][j] = a3 * f;
+    // part holds one matrix per pass at d = 256; at d = 128 the two matrices
+    // use its two halves (slices 0-3 for R, 4-7 for S).
+    __syncthreads();
+    for (int o = tid; o < kMats * 4 * D; o += 256) {
+      const int mm = kMats == 2 ? o / (4 * D) : pass, r = (o / D) % 4, j = o % D;
+      float v = 0.f;
+      if (QJL || mm == 0) {
+#pragma unroll
+        for (int t = 0; t < kSl; ++t) v += part[(kMats == 2 ? mm * kSl : 0) + t][r][j / 4][j % 4];
+      }
+      rq[mm][r][j] = mm == 0 ? v / s_k : v;
+    }
+    if (pass + 1 < 2 / kMats) __syncthreads();
   }
 }
 
+// Two workgroups per CU at d = 128 (the registers of two waves per SIMD), one
+// at d = 256; the bound keeps a code change from silently halving occupancy.
 template <int D, int KB, int QJL, int VB, int SCORES>
-__global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams p) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
+decode_mfma_kernel(DecodeMfmaParams p) {
   using S = Shape<D, KB, QJL, VB>;
   // One table serves keys and values when their widths match (the codebook and
   // its fp16 factor depend only on the width and the head dimension).
@@ -423,6 +449,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
   __shared__ float qsh[4][D];      // the workgroup's query rows
   __shared__ float qrs[2][4][D];   // R q / s_k and S q of those rows
   __shared__ float qcon[4][4];     // per row: c1, c2, -sum(S q)
+  __shared__ f4 rpart[D == 128 ? 8 : 4][4][D / 4];  // k-slice partial sums of the rotation
 
   const int tid = threadIdx.x;
   // The wave index is uniform across the wave; saying so keeps the key loop's
@@ -480,7 +507,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeMfmaParams 
     qsh[r][k] = v;
   }
   __syncthreads();  // also publishes the code tables
-  rotate_rows<D, QJL>(p.Rt, p.St, scale_k, qsh, qrs, tid, (int)((blockIdx.x * 5 + blockIdx.y * 3) * 16) & (D - 1));
+  rotate_rows<D, QJL>(p.Rt, p.St, scale_k, qsh, qrs, rpart, tid, (int)((blockIdx.x * 5 + blockIdx.y * 3) * 16) & (D - 1));
   __syncthreads();
   {
     const int r = wave;  // wave r normalises row r
