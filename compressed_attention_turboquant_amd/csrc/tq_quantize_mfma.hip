@@ -121,13 +121,21 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
       const h8 v0 = nx0, v1 = nx1;
       *reinterpret_cast<h8*>(&xs[lslot][lpart * 16]) = v0;
       *reinterpret_cast<h8*>(&xs[lslot][lpart * 16 + 8]) = v1;
-      float ss = 0.f;
+      // Sum of squares: fp16 products are exact in fp32; two independent
+      // chains of packed dot products.
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf((float)v0[e], (float)v0[e], fmaf((float)v1[e], (float)v1[e], ss));
+      for (int e = 0; e < 8; e += 2) {
+        const h2 a{v0[e], v0[e + 1]}, b{v1[e], v1[e + 1]};
+        s0 = __builtin_amdgcn_fdot2(a, a, s0, false);
+        s1 = __builtin_amdgcn_fdot2(b, b, s1, false);
+      }
+      float ss = s0 + s1;
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
       ss += __shfl_xor(ss, 4);
-      if (lpart == 0) nrm[lslot] = sqrtf(ss);
+      if (lpart == 0) nrm[lslot] = __builtin_amdgcn_sqrtf(ss);
       load_x(grp + (int)gridDim.x, nx0, nx1);
     }
     __syncthreads();
@@ -243,7 +251,7 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
               float g = 0.f;
 #pragma unroll
               for (int i = 0; i < 16; ++i) g += rsq[slot][i];
-              rn_s[t] = sqrtf(g);
+              rn_s[t] = __builtin_amdgcn_sqrtf(g);
             }
           }
         }
@@ -262,7 +270,11 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
         if (!ok) keep |= ((1u << BITS) - 1u) << (BITS * k);
         const float nn = nrm[8 * g4 + k];
         inv[k] = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
-        if (ok && tile_ok && w == 0 && l16 == 0) p.norm[s * p.cap + t] = nn;
+      }
+      // Norms: lane l16 < 8 of wave 0 stores token l16 of value tile g4.
+      if (w == 0 && l16 < 8 && tile_ok) {
+        const int t = tile * 8 + l16;
+        if (t >= t0 && t < tend) p.norm[s * p.cap + t] = nrm[8 * g4 + l16];
       }
       uint8_t* tile_base = p.idx + s * (p.cap / 8) * (D * BITS) + tile * (D * BITS);
 #pragma unroll
@@ -292,14 +304,20 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
   }
 }
 
+// Persistent grid: as many workgroups as the CUs hold at once (a second,
+// partial round of workgroups would run the last share at low occupancy).
 template <int BITS, int QJL, int VALUES>
 hipError_t launch(const QuantMfmaParams& p, int64_t groups, hipStream_t st) {
-  int dev = 0, cus = 256;
+  int dev = 0, cus = 256, per_cu = 0;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
-  const int64_t grid = groups < (int64_t)cus * 4 ? groups : (int64_t)cus * 4;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_mfma_kernel<BITS, QJL, VALUES>, kThreads, 0) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int64_t slots = (int64_t)cus * per_cu;
+  const int64_t grid = groups < slots ? groups : slots;
   hipLaunchKernelGGL((quantize_mfma_kernel<BITS, QJL, VALUES>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
