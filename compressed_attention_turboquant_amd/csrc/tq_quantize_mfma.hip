@@ -146,26 +146,41 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) acc[ct][tt] = f4{0.f, 0.f, 0.f, 0.f};
+    // token operand: keys read slot 16 tt + l16; values read the slot that makes
+    // lane group g4 hold value tile g4 (slot 8 (l16/4) + 4 tt + l16 % 4).  Steps
+    // (kb, tt) run in order; each step's operand is read from LDS one step
+    // ahead, so that the read overlaps the previous step's MFMAs.
+    auto x_operand = [&](int st) {
+      const int kb = st / 2, tt = st % 2;
+      const int slot = VALUES ? 8 * (l16 / 4) + 4 * tt + (l16 % 4) : 16 * tt + l16;
+      return *reinterpret_cast<const h8*>(&xs[slot][32 * kb + 8 * g4]);
+    };
+    h8 xv = x_operand(0);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int st = 0; st < 8; ++st) {
+      const int kb = st / 2, tt = st % 2;
+      const h8 xn = st < 7 ? x_operand(st + 1) : xv;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        // token operand: keys read slot 16 tt + l16; values read the slot that makes
-        // lane group g4 hold value tile g4 (slot 8 (l16/4) + 4 tt + l16 % 4).
-        const int slot = VALUES ? 8 * (l16 / 4) + 4 * tt + (l16 % 4) : 16 * tt + l16;
-        const h8 xv = *reinterpret_cast<const h8*>(&xs[slot][32 * kb + 8 * g4]);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          if constexpr (VALUES) {
-            acc[ct][tt] = mfma(xv, wr[ct][kb][0], acc[ct][tt]);
-            acc[ct][tt] = mfma(xv, wr[ct][kb][1], acc[ct][tt]);
-          } else {
-            acc[ct][tt] = mfma(wr[ct][kb][0], xv, acc[ct][tt]);
-            acc[ct][tt] = mfma(wr[ct][kb][1], xv, acc[ct][tt]);
-          }
+      for (int ct = 0; ct < 2; ++ct) {
+        if constexpr (VALUES) {
+          acc[ct][tt] = mfma(xv, wr[ct][kb][0], acc[ct][tt]);
+          acc[ct][tt] = mfma(xv, wr[ct][kb][1], acc[ct][tt]);
+        } else {
+          acc[ct][tt] = mfma(wr[ct][kb][0], xv, acc[ct][tt]);
+          acc[ct][tt] = mfma(wr[ct][kb][1], xv, acc[ct][tt]);
         }
       }
+      xv = xn;
     }
+    // Order for the scheduler: two reads, then per step its four MFMAs and
+    // the next read.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int st = 0; st < 7; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (st < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
     if constexpr (!VALUES) {
       uint8_t* idx_s = p.idx + s * p.cap * rowb;
@@ -217,21 +232,33 @@ __global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) pacc[ct][tt] = f4{0.f, 0.f, 0.f, 0.f};
+        // Same one-step-ahead operand reads as the rotation.
+        auto r_operand = [&](int st, int part) {
+          const int kb = st / 2, tt = st % 2;
+          return *reinterpret_cast<const h8*>(&rs[part][16 * tt + l16][32 * kb + 8 * g4]);
+        };
+        h8 rh = r_operand(0, 0), rl = r_operand(0, 1);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int st = 0; st < 8; ++st) {
+          const int kb = st / 2, tt = st % 2;
+          const h8 nh = st < 7 ? r_operand(st + 1, 0) : rh;
+          const h8 nl = st < 7 ? r_operand(st + 1, 1) : rl;
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int slot = 16 * tt + l16;
-            const h8 rh = *reinterpret_cast<const h8*>(&rs[0][slot][32 * kb + 8 * g4]);
-            const h8 rl = *reinterpret_cast<const h8*>(&rs[1][slot][32 * kb + 8 * g4]);
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-              pacc[ct][tt] = mfma(wp[ct][kb][0], rh, pacc[ct][tt]);
-              pacc[ct][tt] = mfma(wp[ct][kb][0], rl, pacc[ct][tt]);
-              pacc[ct][tt] = mfma(wp[ct][kb][1], rh, pacc[ct][tt]);
-            }
+          for (int ct = 0; ct < 2; ++ct) {
+            pacc[ct][tt] = mfma(wp[ct][kb][0], rh, pacc[ct][tt]);
+            pacc[ct][tt] = mfma(wp[ct][kb][0], rl, pacc[ct][tt]);
+            pacc[ct][tt] = mfma(wp[ct][kb][1], rh, pacc[ct][tt]);
           }
+          rh = nh;
+          rl = nl;
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int st = 0; st < 7; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+          if (st < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         uint8_t* sign_s = p.sign + s * p.cap * (D / 8);
         float* rn_s = p.rnorm + s * p.cap;
 #pragma unroll
