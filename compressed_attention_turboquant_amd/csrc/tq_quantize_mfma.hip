@@ -52,8 +52,11 @@ __device__ __forceinline__ int out_coord(int w, int ct, int rho) {
   return 32 * w + 8 * (rho / 4) + 4 * ct + (rho % 4);
 }
 
+// Two waves per SIMD for keys (the stationary weights of the rotation and the
+// projection take half the registers), three for values.
 template <int BITS, int QJL, int VALUES>
-__global__ void __launch_bounds__(kThreads) quantize_mfma_kernel(QuantMfmaParams p) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(VALUES ? 3 : 2)))
+quantize_mfma_kernel(QuantMfmaParams p) {
   __shared__ __align__(16) _Float16 xs[kSlots][D + 8];       // token rows (padded)
   __shared__ __align__(16) _Float16 rs[2][kSlots][D + 8];    // residual hi / lo
   __shared__ float nrm[kSlots];
