@@ -27,13 +27,14 @@ Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
   const int64_t seqs = (int64_t)B * Hkv;
   p.mfma = mfma_decode_supports(d, Hq / Hkv * Tq);
   if (p.mfma) {
-    // Work in blocks of 32 keys.  A workgroup serves up to 4 query rows of one
-    // KV head; split the keys so that the workgroups fill the chip once (2 per
+    // Work in blocks of 32 keys.  A workgroup serves up to 4 (or 8) query rows
+    // of one KV head; split the keys so that the workgroups fill the chip once (2 per
     // CU at d = 128, 1 at d = 256: their register use allows no more) -- a
     // second round of workgroups costs more in set-up and tail than it gains
     // -- while giving each of a workgroup's 4 waves at least 4 blocks.
     const int64_t blocks = (N + 31) / 32;
-    const int64_t groups = seqs * ((Hq / Hkv * Tq + 3) / 4);
+    const int rw = decode_rows_per_group(Hq / Hkv * Tq);
+    const int64_t groups = seqs * ((Hq / Hkv * Tq + rw - 1) / rw);
     const int64_t target = d == 128 ? 512 : 256;
     int64_t want = (target + groups - 1) / groups;
     const int64_t max_split = (blocks + 15) / 16;

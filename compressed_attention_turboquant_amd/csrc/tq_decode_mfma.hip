@@ -273,22 +273,25 @@ __device__ __forceinline__ void load_block(Block<D, KB, QJL, VB>& b, const SeqBu
   buf_load(b.vw, sb.vidx, (k0 / 8 + g4) * S::VTILE + l16 * (S::VTILE / 16));
 }
 
-// Per-wave state of the running softmax and the query operands.
-template <int D, int KB, int QJL, int VB>
+// Per-wave state of the running softmax and the query operands.  A lane holds
+// NR query rows (NR = 1: the 16 MFMA rows are 4 query rows x {R q hi, R q lo,
+// S q hi, S q lo}; NR = 2: they are 8 query rows x {hi, lo}, the centroid and
+// sign terms having separate A operands).
+template <int D, int KB, int QJL, int VB, int NR>
 struct WaveState {
   using S = Shape<D, KB, QJL, VB>;
   h8 Ak[S::KBLK], As[QJL ? S::KBLK : 1];
   f4 acc[S::CB];
-  float m, msafe, lsum;
-  float ca, c2, c0;
-  int limit;
-  int64_t srow;
+  float m[NR], msafe[NR], lsum[NR];
+  float ca[NR], c2[NR], c0[NR];
+  int limit[NR];
+  int64_t srow[NR];
   const uint32_t *ktab, *vtab;  // code -> fp16 tables in LDS
 };
 
-template <int D, int KB, int QJL, int VB, int SCORES>
-__device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, const Block<D, KB, QJL, VB>& cur,
-                                              int k0, const DecodeMfmaParams& p, _Float16 (*pb)[4][32],
+template <int D, int KB, int QJL, int VB, int SCORES, int NR>
+__device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws, const Block<D, KB, QJL, VB>& cur,
+                                              int k0, const DecodeMfmaParams& p, _Float16 (*pb)[4 * NR][32],
                                               int l16, int g4, int rows) {
   using S = Shape<D, KB, QJL, VB>;
   // Phase 1: all key-code lookups of both 16-key tiles go out before any MFMA
@@ -299,7 +302,8 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, con
     sfor<0, S::KBLK>([&](auto kb) { bk[t][kb] = decode8<KB, 8 * KB * kb>(cur.kw[t], ws.ktab); });
   __builtin_amdgcn_sched_barrier(0);
   // Phase 2: score MFMAs.  Separate accumulators for the centroid and sign parts
-  // halve the dependency chains; each fills only its own rows (parts 0,1 / 2,3).
+  // halve the dependency chains (with NR = 1 each fills only its own rows, parts
+  // 0,1 / 2,3).
   f4 sk[2], ss[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -326,52 +330,75 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, con
   u4 bv[S::CB];
   sfor<0, S::CB>([&](auto cb) { bv[cb] = decode8<VB, 8 * VB * cb>(cur.vw, ws.vtab); });
   __builtin_amdgcn_sched_barrier(0);
-  // Phase 4: scores of lane (query row g4, key l16), online softmax.
-  float st[2];
+  // Phase 4: scores of lane (query rows NR g4 + j, key l16), online softmax.
+  float st[NR][2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    float s = (cur.kn[t] * ws.ca) * (sk[t][0] + sk[t][1]);
-    if constexpr (QJL) s = fmaf(cur.kn[t] * cur.kg[t], fmaf(ws.c2, ss[t][2] + ss[t][3], ws.c0), s);
-    const int key = k0 + 16 * t + l16;
-    s = key < ws.limit ? s : -INFINITY;
-    if constexpr (SCORES) {
-      if (g4 < rows && key < p.N) p.scores[ws.srow * p.N + key] = s * kLn2;
+  for (int j = 0; j < NR; ++j)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float cent = NR == 1 ? sk[t][0] + sk[t][1] : sk[t][2 * j] + sk[t][2 * j + 1];
+      float s = (cur.kn[t] * ws.ca[j]) * cent;
+      if constexpr (QJL) {
+        const float sgn = NR == 1 ? ss[t][2] + ss[t][3] : ss[t][2 * j] + ss[t][2 * j + 1];
+        s = fmaf(cur.kn[t] * cur.kg[t], fmaf(ws.c2[j], sgn, ws.c0[j]), s);
+      }
+      const int key = k0 + 16 * t + l16;
+      s = key < ws.limit[j] ? s : -INFINITY;
+      if constexpr (SCORES) {
+        if (NR * g4 + j < rows && key < p.N) p.scores[ws.srow[j] * p.N + key] = s * kLn2;
+      }
+      st[j][t] = s;
     }
-    st[t] = s;
-  }
   // The reference maximum only moves when a score exceeds it by more than
   // kSlack (log2 units): weights stay <= 2^kSlack, and the rare rescale keeps
   // the sum exact (every term is relative to the same reference).
-  const float mx = fmaxf(st[0], st[1]);
-  if (__any(mx > ws.m + kSlack)) {
-    float rmax = mx;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
-    const float mnew = fmaxf(ws.m, rmax);
-    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(ws.m - mnew);
-    ws.lsum *= alpha;
+  for (int j = 0; j < NR; ++j) {
+    const float mx = fmaxf(st[j][0], st[j][1]);
+    if (__any(mx > ws.m[j] + kSlack)) {
+      float rmax = mx;
 #pragma unroll
-    for (int i = 0; i < S::CB; ++i) ws.acc[i] *= alpha;
-    ws.m = mnew;
-    ws.msafe = mnew == -INFINITY ? 0.f : mnew;
+      for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
+      const float mnew = fmaxf(ws.m[j], rmax);
+      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(ws.m[j] - mnew);
+      ws.lsum[j] *= alpha;
+#pragma unroll
+      for (int i = 0; i < S::CB; ++i) {
+        if constexpr (NR == 1) {
+          ws.acc[i] *= alpha;
+        } else {
+          ws.acc[i][2 * j] *= alpha;
+          ws.acc[i][2 * j + 1] *= alpha;
+        }
+      }
+      ws.m[j] = mnew;
+      ws.msafe[j] = mnew == -INFINITY ? 0.f : mnew;
+    }
   }
-  // v_exp_f32 directly: weights below 2^-126 of the running maximum become 0.
-  const float p0 = __builtin_amdgcn_exp2f(st[0] - ws.msafe), p1 = __builtin_amdgcn_exp2f(st[1] - ws.msafe);
-  ws.lsum += p0 + p1;
-  // P carries 2^-kSlack so p * ||v|| keeps the fp16 range of ||v||.
-  const float q0 = p0 * cur.vn[0] * kInvSlack, q1 = p1 * cur.vn[1] * kInvSlack;
-  const _Float16 h0 = (_Float16)q0, h1 = (_Float16)q1;
-  pb[0][g4][l16] = h0;
-  pb[0][g4][16 + l16] = h1;
-  pb[1][g4][l16] = (_Float16)(q0 - (float)h0);
-  pb[1][g4][16 + l16] = (_Float16)(q1 - (float)h1);
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    // v_exp_f32 directly: weights below 2^-126 of the running maximum become 0.
+    const float p0 = __builtin_amdgcn_exp2f(st[j][0] - ws.msafe[j]);
+    const float p1 = __builtin_amdgcn_exp2f(st[j][1] - ws.msafe[j]);
+    ws.lsum[j] += p0 + p1;
+    // P carries 2^-kSlack so p * ||v|| keeps the fp16 range of ||v||.
+    const float q0 = p0 * cur.vn[0] * kInvSlack, q1 = p1 * cur.vn[1] * kInvSlack;
+    const _Float16 h0 = (_Float16)q0, h1 = (_Float16)q1;
+    const int qr = NR * g4 + j;
+    pb[0][qr][l16] = h0;
+    pb[0][qr][16 + l16] = h1;
+    pb[1][qr][l16] = (_Float16)(q0 - (float)h0);
+    pb[1][qr][16 + l16] = (_Float16)(q1 - (float)h1);
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   h8 ap = h8{0, 0, 0, 0, 0, 0, 0, 0};
-  {
+  if constexpr (NR == 1) {
     const int part = l16 % 4, qr = l16 / 4;
     if (part < 2) ap = *reinterpret_cast<const h8*>(&pb[part][qr][8 * g4]);
+  } else {
+    ap = *reinterpret_cast<const h8*>(&pb[l16 % 2][l16 / 2][8 * g4]);
   }
   // Phase 5: P.V.
   sfor<0, S::CB>([&](auto cb) {
@@ -380,17 +407,17 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB>& ws, con
   __builtin_amdgcn_wave_barrier();
 }
 
-// The workgroup's query rows rotated once: rq[0][r][j] = (R q_r)_j / s_k and
-// rq[1][r][j] = (S q_r)_j, from the rows in qs (LDS) and R^T, S^T (global,
-// row-major).  Thread (matrix, jq, slice) reads float4 rows M[k][4jq..4jq+3]
-// over its quarter of k for all four query rows; the slices' partial sums meet
-// in part (LDS).  Each workgroup starts its slices at its own row offset k0, so
-// that the workgroups, which all read the same few hundred KB at once, spread
-// over the L2 channels.
-template <int D, int QJL>
+// Four of the workgroup's query rows (rb..rb+3) rotated once: rq[0][r][j] =
+// (R q_r)_j / s_k and rq[1][r][j] = (S q_r)_j, from the rows in qs (LDS) and
+// R^T, S^T (global, row-major).  Thread (matrix, jq, slice) reads float4 rows
+// M[k][4jq..4jq+3] over its quarter of k for the four rows; the slices' partial
+// sums meet in part (LDS).  Each workgroup starts its slices at its own row
+// offset k0, so that the workgroups, which all read the same few hundred KB at
+// once, spread over the L2 channels.
+template <int D, int QJL, int RW>
 __device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const float* __restrict__ St,
-                                            float s_k, const float (*qs)[D], float (*rq)[4][D],
-                                            f4 (*part)[4][D / 4], int tid, int k0) {
+                                            float s_k, const float (*qs)[D], float (*rq)[RW][D],
+                                            f4 (*part)[4][D / 4], int tid, int k0, int rb) {
   constexpr int kJ = D / 4;                   // float4 columns per matrix row
   constexpr int kMats = D == 128 ? 2 : 1;     // matrices handled side by side
   constexpr int kSl = 256 / (kJ * kMats);     // k-slices: 4
@@ -406,10 +433,10 @@ __device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const 
       for (int kk = 0; kk < kSpan; ++kk) {
         const int k = (sl * kSpan + kk + k0) & (D - 1);
         const f4 x = M[(size_t)k * kJ];
-        a0 += x * qs[0][k];
-        a1 += x * qs[1][k];
-        a2 += x * qs[2][k];
-        a3 += x * qs[3][k];
+        a0 += x * qs[rb][k];
+        a1 += x * qs[rb + 1][k];
+        a2 += x * qs[rb + 2][k];
+        a3 += x * qs[rb + 3][k];
       }
       const int ps = (kMats == 2 ? m * kSl : 0) + sl;
       part[ps][0][jq] = a0;
@@ -427,7 +454,7 @@ __device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const 
 #pragma unroll
         for (int t = 0; t < kSl; ++t) v += part[(kMats == 2 ? mm * kSl : 0) + t][r][j / 4][j % 4];
       }
-      rq[mm][r][j] = mm == 0 ? v / s_k : v;
+      rq[mm][rb + r][j] = mm == 0 ? v / s_k : v;
     }
     if (pass + 1 < 2 / kMats) __syncthreads();
   }
@@ -435,21 +462,26 @@ __device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const 
 
 // Two workgroups per CU at d = 128 (the registers of two waves per SIMD), one
 // at d = 256; the bound keeps a code change from silently halving occupancy.
-template <int D, int KB, int QJL, int VB, int SCORES>
+template <int D, int KB, int QJL, int VB, int SCORES, int NR>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
 decode_mfma_kernel(DecodeMfmaParams p) {
   using S = Shape<D, KB, QJL, VB>;
+  constexpr int RW = 4 * NR;  // query rows per workgroup
   // One table serves keys and values when their widths match (the codebook and
   // its fp16 factor depend only on the width and the head dimension).
   constexpr int kKtab = Lut<KB>::kDwords, kVtab = KB == VB ? 0 : Lut<VB>::kDwords;
   __shared__ __align__(16) uint32_t lut[kKtab + kVtab];
-  __shared__ __align__(16) _Float16 pbuf[kWaves][2][4][32];
-  __shared__ float mrg_m[kWaves][4], mrg_l[kWaves][4];
-  __shared__ float mrg_acc[kWaves][4][D];
-  __shared__ float qsh[4][D];      // the workgroup's query rows
-  __shared__ float qrs[2][4][D];   // R q / s_k and S q of those rows
-  __shared__ float qcon[4][4];     // per row: c1, c2, -sum(S q)
-  __shared__ f4 rpart[D == 128 ? 8 : 4][4][D / 4];  // k-slice partial sums of the rotation
+  __shared__ __align__(16) _Float16 pbuf[kWaves][2][RW][32];
+  __shared__ float mrg_m[kWaves][RW], mrg_l[kWaves][RW];
+  __shared__ float qsh[RW][D];     // the workgroup's query rows
+  __shared__ float qrs[2][RW][D];  // R q / s_k and S q of those rows
+  __shared__ float qcon[RW][4];    // per row: c1, c2, -sum(S q)
+  // The rotation's k-slice partial sums (set-up) and the waves' accumulators
+  // (merge, after the key loop) share one buffer.
+  constexpr int kRpart = (D == 128 ? 8 : 4) * 4 * (D / 4) * 16, kMrg = kWaves * RW * D * 4;
+  __shared__ __align__(16) char scratch[kRpart > kMrg ? kRpart : kMrg];
+  auto rpart = reinterpret_cast<f4 (*)[4][D / 4]>(scratch);
+  auto mrg_acc = reinterpret_cast<float (*)[RW][D]>(scratch);
 
   const int tid = threadIdx.x;
   // The wave index is uniform across the wave; saying so keeps the key loop's
@@ -457,14 +489,14 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   // of the matrix-core registers on every block).
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int l16 = lane % 16, g4 = lane / 16;
-  // Workgroup = (sequence, group of up to 4 of its query rows, key split).
+  // Workgroup = (sequence, group of up to RW of its query rows, key split).
   const int64_t seq = blockIdx.x / p.rgroups;
-  const int r0 = 4 * (int)(blockIdx.x % p.rgroups);
+  const int r0 = RW * (int)(blockIdx.x % p.rgroups);
   const int split = blockIdx.y;
   const int64_t b_ = seq / p.Hkv;
   const int hkv = (int)(seq % p.Hkv);
   const int G = p.Hq / p.Hkv;
-  const int rows = min(4, G * p.Tq - r0);  // query rows of this workgroup
+  const int rows = min(RW, G * p.Tq - r0);  // query rows of this workgroup
   auto qrow_of = [&](int r) -> int64_t {
     const int rr = r0 + r;  // row within the KV head's G * Tq rows
     return (b_ * p.Hq + (int64_t)hkv * G + rr / p.Tq) * p.Tq + rr % p.Tq;
@@ -487,7 +519,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   load_block(b0, sb, blk * 32, l16, g4);
   load_block(b1, sb, (blk + kWaves) * 32, l16, g4);
 
-  WaveState<D, KB, QJL, VB> ws;
+  WaveState<D, KB, QJL, VB, NR> ws;
   const float scale_k = p.scales[0], scale_v = KB == VB ? scale_k : p.scales[1];
   fill_lut<KB>(lut, p.cb, scale_k, tid);
   if constexpr (KB != VB) fill_lut<VB>(lut + kKtab, p.cb + 2 * kMaxLevels, scale_v, tid);
@@ -497,7 +529,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   // Rotate the query rows once (R q, S q) and normalise them for the fp16
   // operand split: qa = (R q) / (s_k c1), qb = 2 (S q) / c2 with c1, c2 powers of
   // two that bring the largest entry into [1, 2).
-  for (int i = tid; i < 4 * D; i += kThreads) {
+  for (int i = tid; i < RW * D; i += kThreads) {
     const int r = i / D, k = i % D;
     float v = 0.f;
     if (r < rows) {
@@ -507,10 +539,17 @@ decode_mfma_kernel(DecodeMfmaParams p) {
     qsh[r][k] = v;
   }
   __syncthreads();  // also publishes the code tables
-  rotate_rows<D, QJL>(p.Rt, p.St, scale_k, qsh, qrs, rpart, tid, (int)((blockIdx.x * 5 + blockIdx.y * 3) * 16) & (D - 1));
-  __syncthreads();
   {
-    const int r = wave;  // wave r normalises row r
+    const int k0 = (int)((blockIdx.x * 5 + blockIdx.y * 3) * 16) & (D - 1);
+#pragma unroll
+    for (int rb = 0; rb < RW; rb += 4) {
+      if (rb > 0) __syncthreads();  // rpart is reused
+      rotate_rows<D, QJL, RW>(p.Rt, p.St, scale_k, qsh, qrs, rpart, tid, k0, rb);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = wave; r < RW; r += kWaves) {  // wave w normalises rows w, w + 4
     float ma = 0.f, mb = 0.f, sbv = 0.f;
 #pragma unroll
     for (int j = lane; j < D; j += 64) {
@@ -537,9 +576,11 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   }
   __syncthreads();
 
-  // Query operands: lane (row rho = l16, k-group g4).
+  // Query operands: lane (row rho = l16, k-group g4).  NR = 1: rho = 4 qr + part,
+  // parts {R q hi, R q lo} in Ak and {S q hi, S q lo} in As; NR = 2: rho = 2 qr +
+  // part, parts {hi, lo} in both.
   {
-    const int qr = l16 / 4, part = l16 % 4;
+    const int qr = NR == 1 ? l16 / 4 : l16 / 2, part = NR == 1 ? l16 % 4 : l16 % 2;
     const bool ok = qr < rows;
     const float fa = 1.0f / qcon[qr][0], fb = 2.0f / qcon[qr][1];  // powers of two: exact
     const float* qa = &qrs[0][qr][(D / 4) * g4];
@@ -548,7 +589,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
       h8 a;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = (ok && part < 2) ? qa[8 * kb + e] * fa : 0.f;
+        const float x = (ok && part < 2) ? qa[8 * kb + e] * fa : 0.f;  // NR = 2: part < 2 always
         const _Float16 hi = (_Float16)x;
         const _Float16 lo = (_Float16)(x - (float)hi);
         a[e] = part == 0 ? hi : (part == 1 ? lo : (_Float16)0.f);
@@ -559,35 +600,40 @@ decode_mfma_kernel(DecodeMfmaParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int w = e / 2, h = e % 2;
-          const float x =
-              (ok && part >= 2) ? qb[32 * (kb / 4) + sign_coord(kb % 4, w, h)] * fb * sign_comp(w) : 0.f;
+          const bool sp = NR == 1 ? part >= 2 : true;  // rows of the sign term
+          const float x = (ok && sp) ? qb[32 * (kb / 4) + sign_coord(kb % 4, w, h)] * fb * sign_comp(w) : 0.f;
           const _Float16 hi = (_Float16)x;
           const _Float16 lo = (_Float16)(x - (float)hi);
-          s[e] = part == 2 ? hi : (part == 3 ? lo : (_Float16)0.f);
+          const int sp_part = NR == 1 ? part - 2 : part;
+          s[e] = sp_part == 0 ? hi : (sp_part == 1 ? lo : (_Float16)0.f);
         }
         ws.As[kb] = s;
       }
     });
   }
-  // Score-side constants of this lane's query row g4 (log2 domain).
-  ws.ca = ws.c2 = ws.c0 = 0.f;
-  ws.limit = -1;
-  ws.srow = 0;
-  if (g4 < rows) {
-    ws.srow = qrow_of(g4);
-    const float* rc = qcon[g4];
-    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    const float cq = sqrtf(0.5f * (float)M_PI) / (float)D * inv_sqrt_d * kLog2e;
-    ws.ca = rc[0] * inv_sqrt_d * kLog2e;
-    ws.c2 = rc[1] * cq;
-    ws.c0 = rc[2] * cq;
-    ws.limit = (int)(p.causal ? p.N - p.Tq + ((r0 + g4) % p.Tq) + 1 : p.N);
+  // Score-side constants of this lane's query rows NR g4 + j (log2 domain).
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int q = NR * g4 + j;
+    ws.ca[j] = ws.c2[j] = ws.c0[j] = 0.f;
+    ws.limit[j] = -1;
+    ws.srow[j] = 0;
+    if (q < rows) {
+      ws.srow[j] = qrow_of(q);
+      const float* rc = qcon[q];
+      const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+      const float cq = sqrtf(0.5f * (float)M_PI) / (float)D * inv_sqrt_d * kLog2e;
+      ws.ca[j] = rc[0] * inv_sqrt_d * kLog2e;
+      ws.c2[j] = rc[1] * cq;
+      ws.c0[j] = rc[2] * cq;
+      ws.limit[j] = (int)(p.causal ? p.N - p.Tq + ((r0 + q) % p.Tq) + 1 : p.N);
+    }
+    ws.m[j] = -INFINITY;
+    ws.msafe[j] = 0.f;
+    ws.lsum[j] = 0.f;
   }
 #pragma unroll
   for (int i = 0; i < S::CB; ++i) ws.acc[i] = f4{0.f, 0.f, 0.f, 0.f};
-  ws.m = -INFINITY;
-  ws.msafe = 0.f;
-  ws.lsum = 0.f;
 
   // Three register sets rotate so two blocks are in flight while one is used.
   // The prefetches are unconditional (reads past the split land in the same
@@ -595,26 +641,31 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   // straight-line and lets the compiler count outstanding loads exactly.
   for (; blk < blk1; blk += 3 * kWaves) {
     load_block(b2, sb, (blk + 2 * kWaves) * 32, l16, g4);
-    process_block<D, KB, QJL, VB, SCORES>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
+    process_block<D, KB, QJL, VB, SCORES, NR>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
     if (blk + kWaves >= blk1) break;
     load_block(b0, sb, (blk + 3 * kWaves) * 32, l16, g4);
-    process_block<D, KB, QJL, VB, SCORES>(ws, b1, (blk + kWaves) * 32, p, pbuf[wave], l16, g4, rows);
+    process_block<D, KB, QJL, VB, SCORES, NR>(ws, b1, (blk + kWaves) * 32, p, pbuf[wave], l16, g4, rows);
     if (blk + 2 * kWaves >= blk1) break;
     load_block(b1, sb, (blk + 4 * kWaves) * 32, l16, g4);
-    process_block<D, KB, QJL, VB, SCORES>(ws, b2, (blk + 2 * kWaves) * 32, p, pbuf[wave], l16, g4, rows);
+    process_block<D, KB, QJL, VB, SCORES, NR>(ws, b2, (blk + 2 * kWaves) * 32, p, pbuf[wave], l16, g4, rows);
   }
 
   // Merge the waves of this workgroup.
-  float lsum = ws.lsum;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) lsum += __shfl_xor(lsum, o);
-  if (l16 == 0) {
-    mrg_m[wave][g4] = ws.m;
-    mrg_l[wave][g4] = lsum;
-  }
+  __syncthreads();  // mrg_acc shares its memory with the set-up's rotation buffer
   const float inv_sv = 16.f / scale_v;  // undoes 2^-kSlack and the fp16 table factor
 #pragma unroll
-  for (int cb = 0; cb < S::CB; ++cb) mrg_acc[wave][g4][l16 * S::CB + cb] = (ws.acc[cb][0] + ws.acc[cb][1]) * inv_sv;
+  for (int j = 0; j < NR; ++j) {
+    float lsum = ws.lsum[j];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) lsum += __shfl_xor(lsum, o);
+    if (l16 == 0) {
+      mrg_m[wave][NR * g4 + j] = ws.m[j];
+      mrg_l[wave][NR * g4 + j] = lsum;
+    }
+#pragma unroll
+    for (int cb = 0; cb < S::CB; ++cb)
+      mrg_acc[wave][NR * g4 + j][l16 * S::CB + cb] = (ws.acc[cb][2 * j] + ws.acc[cb][2 * j + 1]) * inv_sv;
+  }
   __syncthreads();
   const int64_t rows_total = (int64_t)(gridDim.x / p.rgroups) / p.Hkv * p.Hq * p.Tq;
   for (int idx = tid; idx < rows * D; idx += kThreads) {
@@ -736,10 +787,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 
 template <int D, int KB, int QJL, int VB>
 hipError_t launch_split(const DecodeMfmaParams& p, dim3 grid, hipStream_t st) {
-  if (p.scores)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 1>), grid, dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 0>), grid, dim3(kThreads), 0, st, p);
+  const bool r8 = decode_rows_per_group(p.Hq / p.Hkv * p.Tq) == 8;
+  if (p.scores) {
+    if (r8)
+      hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 1, 2>), grid, dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 1, 1>), grid, dim3(kThreads), 0, st, p);
+  } else {
+    if (r8)
+      hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 0, 2>), grid, dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 0, 1>), grid, dim3(kThreads), 0, st, p);
+  }
   return hipGetLastError();
 }
 
@@ -802,7 +861,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   p.keys_per_split = a.keys_per_split;
   p.part = a.part;
   p.scores = a.scores;
-  p.rgroups = (a.Hq / a.Hkv * a.Tq + 3) / 4;
+  const int rw = decode_rows_per_group(a.Hq / a.Hkv * a.Tq);
+  p.rgroups = (a.Hq / a.Hkv * a.Tq + rw - 1) / rw;
   const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * p.rgroups), (unsigned)a.nsplit);
   hipError_t e = a.d == 128 ? dispatch_d<128>(p, a.kb, a.qjl, a.vb, grid, st)
                             : dispatch_d<256>(p, a.kb, a.qjl, a.vb, grid, st);

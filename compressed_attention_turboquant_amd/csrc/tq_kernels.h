@@ -83,6 +83,9 @@ bool fwht_quantize_supports(int d, int rot, int qjl);
 hipError_t launch_quantize_fwht(const QuantizeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 bool mfma_decode_supports(int d, int rows);
+// Query rows one decode workgroup serves (4, or 8 when a KV head has more than
+// 4 query rows: the matrix-core rows then carry 8 query rows x {hi, lo}).
+inline int decode_rows_per_group(int rows_per_head) { return rows_per_head > 4 ? 8 : 4; }
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st);
 hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_dequant_ref(const DequantArgs& a, hipStream_t st);

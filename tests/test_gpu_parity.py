@@ -100,6 +100,36 @@ def test_decode_on_random_cache(name):
     H.log(f"  score rel err {rel:.2e}  out abs err {err:.2e}")
 
 
+# Query rows per KV head (G * Tq) around the decode kernel's row groups of 4
+# and 8: one partial group, exactly one group, a full group plus a partial one,
+# several groups; causal chunks take Tq > 1.
+ROW_GROUP_CASES = {
+    "5 rows (G=5)": workloads.CONFIGS["C2"].with_(Hq=5, Hkv=1, N=300),
+    "8 rows (G=8)": workloads.CONFIGS["C2"].with_(Hq=16, Hkv=2, N=300),
+    "12 rows (G=4, Tq=3, causal)": workloads.CONFIGS["C4"].with_(B=1, Hq=8, Hkv=2, Tq=3, N=300),
+    "20 rows (G=4, Tq=5, causal, d=256)": workloads.CONFIGS["C5"].with_(B=1, Hq=8, Hkv=2, Tq=5, N=300,
+                                                                      causal=1, k_qjl=1, k_bits=2,
+                                                                      v_bits=3),
+}
+
+
+@pytest.mark.parametrize("name", list(ROW_GROUP_CASES))
+def test_decode_row_groups(name):
+    """Decode of heads whose query rows fill the kernel's row groups partly,
+    exactly and over several groups: every score and output against the oracle."""
+    cfg = ROW_GROUP_CASES[name]
+    N = cfg.N
+    cap = (N + 7) // 8 * 8
+    H.log(f"[decode row groups] {name}")
+    packed = workloads.random_packed_numpy(cfg, cfg.B * cfg.Hkv, cap, seed=7)
+    q = workloads.q_numpy(cfg, seed=7)
+    out, scores, ref_out, ref_scores, cache, ol = _decode_both(cfg, packed, q, N)
+    scale = H.score_scale(q, ol.R, ol.S, ol.ck, cache, N, cfg.G, cfg.k_qjl)
+    rel = H.compare_scores(scores, ref_scores, scale, name)
+    err = H.compare_out(out, ref_out, name)
+    H.log(f"  score rel err {rel:.2e}  out abs err {err:.2e}")
+
+
 @pytest.mark.parametrize("name", list(REDUCED))
 def test_end_to_end_from_raw_inputs(name):
     """Quantize K and V and decode on the GPU; the oracle encodes the same raw
