@@ -22,20 +22,21 @@ struct Plan {  // split-K plan of one decode call
   size_t off_qrot, off_qproj, off_part, total;
 };
 
-Plan decode_plan(int d, int B, int Hq, int Hkv, int Tq, int64_t N) {
+Plan decode_plan(int d, int qjl, int B, int Hq, int Hkv, int Tq, int64_t N) {
   Plan p{};
   const int64_t seqs = (int64_t)B * Hkv;
   p.mfma = mfma_decode_supports(d, Hq / Hkv * Tq);
   if (p.mfma) {
     // Work in blocks of 32 keys.  A workgroup serves up to 4 (or 8) query rows
-    // of one KV head; split the keys so that the workgroups fill the chip once (2 per
-    // CU at d = 128, 1 at d = 256: their register use allows no more) -- a
-    // second round of workgroups costs more in set-up and tail than it gains
-    // -- while giving each of a workgroup's 4 waves at least 4 blocks.
+    // of one KV head; split the keys so that the workgroups fill the chip's 256
+    // CUs once (decode_wgs_per_cu workgroups each: what their registers allow)
+    // -- a second round of workgroups costs more in set-up and tail than it
+    // gains -- while giving each of a workgroup's 4 waves at least 4 blocks.
+    // The plan depends on the shape only, so the workspace size does too.
     const int64_t blocks = (N + 31) / 32;
     const int rw = decode_rows_per_group(Hq / Hkv * Tq);
     const int64_t groups = seqs * ((Hq / Hkv * Tq + rw - 1) / rw);
-    const int64_t target = d == 128 ? 512 : 256;
+    const int64_t target = 256 * decode_wgs_per_cu(d, qjl, rw);
     int64_t want = (target + groups - 1) / groups;
     const int64_t max_split = (blocks + 15) / 16;
     if (want > max_split) want = max_split;
@@ -254,7 +255,7 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
 size_t tq_decode_workspace_bytes(const tq_layer* layer, int32_t B, int32_t Hq, int32_t Hkv,
                                  int32_t Tq, int64_t N) {
   if (!layer || !supported_d(layer->d) || B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || N < 1) return 0;
-  return decode_plan(layer->d, B, Hq, Hkv, Tq, N).total;
+  return decode_plan(layer->d, layer->k_qjl, B, Hq, Hkv, Tq, N).total;
 }
 
 tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, int32_t B,
@@ -282,7 +283,7 @@ tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, 
   if (!mfma_decode_supports(layer->d, rows) && !ref_decode_supports(layer->d, rows))
     return fail(TQ_ERR_UNSUPPORTED, "(Hq/Hkv)*Tq too large for this head dimension");
   if ((int64_t)B * Hkv > 0x7FFFFFFF) return fail(TQ_ERR_UNSUPPORTED, "too many sequences");
-  const Plan P = decode_plan(layer->d, B, Hq, Hkv, Tq, N);
+  const Plan P = decode_plan(layer->d, layer->k_qjl, B, Hq, Hkv, Tq, N);
   if (P.nsplit > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many key splits");
   if (!workspace) return fail(TQ_ERR_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)workspace & 255u) != 0) return fail(TQ_ERR_ALIGNMENT, "workspace must be 256-byte aligned");

@@ -294,41 +294,58 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
                                               int k0, const DecodeMfmaParams& p, _Float16 (*pb)[4 * NR][32],
                                               int l16, int g4, int rows) {
   using S = Shape<D, KB, QJL, VB>;
-  // Phase 1: all key-code lookups of both 16-key tiles go out before any MFMA
-  // needs one, so the LDS latency overlaps instead of serialising.
-  u4 bk[2][S::KBLK];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    sfor<0, S::KBLK>([&](auto kb) { bk[t][kb] = decode8<KB, 8 * KB * kb>(cur.kw[t], ws.ktab); });
-  __builtin_amdgcn_sched_barrier(0);
-  // Phase 2: score MFMAs.  Separate accumulators for the centroid and sign parts
-  // halve the dependency chains (with NR = 1 each fills only its own rows, parts
-  // 0,1 / 2,3).
+  // At d = 256 the decoded operands of a whole block would not fit next to two
+  // waves' worth of other state, so keys are decoded one 16-key tile at a time
+  // and values in two halves (kLean); the second wave on the SIMD covers the
+  // LDS latency this exposes.
+  constexpr bool kLean = D == 256;
+  constexpr int kVParts = kLean ? 2 : 1, kCBp = S::CB / kVParts;
   f4 sk[2], ss[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     sk[t] = f4{0.f, 0.f, 0.f, 0.f};
     ss[t] = sk[t];
   }
-  sfor<0, S::KBLK>([&](auto kb) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      sk[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ws.Ak[kb], __builtin_bit_cast(h8, bk[t][kb]), sk[t], 0, 0, 0);
-    if constexpr (QJL) {
-      constexpr int r = kb % 4;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
+  // Score MFMAs of tile t from its decoded keys.  Separate accumulators for the
+  // centroid and sign parts halve the dependency chains (with NR = 1 each fills
+  // only its own rows, parts 0,1 / 2,3).
+  auto score_tile = [&](int t, const u4 (&bkt)[S::KBLK]) {
+    sfor<0, S::KBLK>([&](auto kb) {
+      sk[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ws.Ak[kb], __builtin_bit_cast(h8, bkt[kb]), sk[t], 0, 0, 0);
+      if constexpr (QJL) {
+        constexpr int r = kb % 4;
         const uint32_t word = cur.sw[t][kb / 4];
         const uint32_t rot = r == 0 ? word : __builtin_amdgcn_alignbit(word, word, 32 - 4 * r);
         u4 bw;
         sfor<0, 4>([&](auto w) { bw[decltype(w)::value] = sign_dword<decltype(w)::value>(rot); });
         ss[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ws.As[kb], __builtin_bit_cast(h8, bw), ss[t], 0, 0, 0);
       }
+    });
+  };
+  if constexpr (!kLean) {
+    // Phase 1: all key-code lookups of both 16-key tiles go out before any MFMA
+    // needs one, so the LDS latency overlaps instead of serialising.
+    u4 bk[2][S::KBLK];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      sfor<0, S::KBLK>([&](auto kb) { bk[t][kb] = decode8<KB, 8 * KB * kb>(cur.kw[t], ws.ktab); });
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 2: score MFMAs.
+    score_tile(0, bk[0]);
+    score_tile(1, bk[1]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      u4 bk[S::KBLK];
+      sfor<0, S::KBLK>([&](auto kb) { bk[kb] = decode8<KB, 8 * KB * kb>(cur.kw[t], ws.ktab); });
+      __builtin_amdgcn_sched_barrier(0);
+      score_tile(t, bk);
     }
-  });
-  // Phase 3: value-code lookups, in flight while the softmax arithmetic runs.
-  u4 bv[S::CB];
-  sfor<0, S::CB>([&](auto cb) { bv[cb] = decode8<VB, 8 * VB * cb>(cur.vw, ws.vtab); });
+  }
+  // Phase 3: value-code lookups (the first part at d = 256), in flight while the
+  // softmax arithmetic runs.
+  u4 bv[kCBp];
+  sfor<0, kCBp>([&](auto cb) { bv[cb] = decode8<VB, 8 * VB * cb>(cur.vw, ws.vtab); });
   __builtin_amdgcn_sched_barrier(0);
   // Phase 4: scores of lane (query rows NR g4 + j, key l16), online softmax.
   float st[NR][2];
@@ -400,10 +417,18 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
   } else {
     ap = *reinterpret_cast<const h8*>(&pb[l16 % 2][l16 / 2][8 * g4]);
   }
-  // Phase 5: P.V.
-  sfor<0, S::CB>([&](auto cb) {
+  // Phase 5: P.V (at d = 256 the second half of the values is decoded after
+  // the first half's MFMAs are issued).
+  sfor<0, kCBp>([&](auto cb) {
     ws.acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(h8, bv[cb]), ws.acc[cb], 0, 0, 0);
   });
+  if constexpr (kLean) {
+    sfor<0, kCBp>([&](auto cb) { bv[cb] = decode8<VB, 8 * VB * (cb + kCBp)>(cur.vw, ws.vtab); });
+    sfor<0, kCBp>([&](auto cb) {
+      ws.acc[cb + kCBp] =
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(h8, bv[cb]), ws.acc[cb + kCBp], 0, 0, 0);
+    });
+  }
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -460,10 +485,11 @@ __device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const 
   }
 }
 
-// Two workgroups per CU at d = 128 (the registers of two waves per SIMD), one
-// at d = 256; the bound keeps a code change from silently halving occupancy.
+// Workgroups per CU as decode_wgs_per_cu gives (two waves per SIMD where the
+// registers allow); the bound keeps a code change from silently halving
+// occupancy.
 template <int D, int KB, int QJL, int VB, int SCORES, int NR>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_wgs_per_cu(D, QJL, 4 * NR))))
 decode_mfma_kernel(DecodeMfmaParams p) {
   using S = Shape<D, KB, QJL, VB>;
   constexpr int RW = 4 * NR;  // query rows per workgroup
@@ -510,14 +536,15 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   sb.vidx = make_rsrc(p.vidx + seq * (p.cap / 8) * S::VTILE, (p.cap / 8) * S::VTILE);
   sb.vnorm = make_rsrc(p.vnorm + seq * p.cap, p.N * 4);
 
-  // The first two key blocks start loading before the set-up below.
+  // The first key blocks start loading before the set-up below (two at d = 128,
+  // one at d = 256, whose loop keeps two register sets).
   const int nblk = (int)((p.N + 31) / 32);
   const int blk0 = (int)(split * (p.keys_per_split / 32));
   const int blk1 = min(nblk, blk0 + (int)(p.keys_per_split / 32));
   Block<D, KB, QJL, VB> b0, b1, b2;
   int blk = blk0 + wave;
   load_block(b0, sb, blk * 32, l16, g4);
-  load_block(b1, sb, (blk + kWaves) * 32, l16, g4);
+  if constexpr (D == 128) load_block(b1, sb, (blk + kWaves) * 32, l16, g4);
 
   WaveState<D, KB, QJL, VB, NR> ws;
   const float scale_k = p.scales[0], scale_v = KB == VB ? scale_k : p.scales[1];
@@ -635,19 +662,29 @@ decode_mfma_kernel(DecodeMfmaParams p) {
 #pragma unroll
   for (int i = 0; i < S::CB; ++i) ws.acc[i] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // Three register sets rotate so two blocks are in flight while one is used.
-  // The prefetches are unconditional (reads past the split land in the same
+  // Three register sets rotate so two blocks are in flight while one is used
+  // (d = 256: two sets, one block in flight).  The prefetches are unconditional (reads past the split land in the same
   // sequence, reads past its capacity return 0), which keeps the loop body
   // straight-line and lets the compiler count outstanding loads exactly.
-  for (; blk < blk1; blk += 3 * kWaves) {
-    load_block(b2, sb, (blk + 2 * kWaves) * 32, l16, g4);
-    process_block<D, KB, QJL, VB, SCORES, NR>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
-    if (blk + kWaves >= blk1) break;
-    load_block(b0, sb, (blk + 3 * kWaves) * 32, l16, g4);
-    process_block<D, KB, QJL, VB, SCORES, NR>(ws, b1, (blk + kWaves) * 32, p, pbuf[wave], l16, g4, rows);
-    if (blk + 2 * kWaves >= blk1) break;
-    load_block(b1, sb, (blk + 4 * kWaves) * 32, l16, g4);
-    process_block<D, KB, QJL, VB, SCORES, NR>(ws, b2, (blk + 2 * kWaves) * 32, p, pbuf[wave], l16, g4, rows);
+  if constexpr (D == 128) {
+    for (; blk < blk1; blk += 3 * kWaves) {
+      load_block(b2, sb, (blk + 2 * kWaves) * 32, l16, g4);
+      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
+      if (blk + kWaves >= blk1) break;
+      load_block(b0, sb, (blk + 3 * kWaves) * 32, l16, g4);
+      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b1, (blk + kWaves) * 32, p, pbuf[wave], l16, g4, rows);
+      if (blk + 2 * kWaves >= blk1) break;
+      load_block(b1, sb, (blk + 4 * kWaves) * 32, l16, g4);
+      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b2, (blk + 2 * kWaves) * 32, p, pbuf[wave], l16, g4, rows);
+    }
+  } else {
+    for (; blk < blk1; blk += 2 * kWaves) {
+      load_block(b1, sb, (blk + kWaves) * 32, l16, g4);
+      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
+      if (blk + kWaves >= blk1) break;
+      load_block(b0, sb, (blk + 2 * kWaves) * 32, l16, g4);
+      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b1, (blk + kWaves) * 32, p, pbuf[wave], l16, g4, rows);
+    }
   }
 
   // Merge the waves of this workgroup.

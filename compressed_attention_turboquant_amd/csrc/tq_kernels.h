@@ -86,6 +86,12 @@ bool mfma_decode_supports(int d, int rows);
 // Query rows one decode workgroup serves (4, or 8 when a KV head has more than
 // 4 query rows: the matrix-core rows then carry 8 query rows x {hi, lo}).
 inline int decode_rows_per_group(int rows_per_head) { return rows_per_head > 4 ? 8 : 4; }
+
+// Decode workgroups one CU runs at once: 2 (two waves per SIMD), except at
+// d = 256 with QJL keys or row groups of 8, whose register use allows one.
+constexpr int decode_wgs_per_cu(int d, int qjl, int rows_per_group) {
+  return d == 256 && (qjl || rows_per_group == 8) ? 1 : 2;
+}
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st);
 hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_dequant_ref(const DequantArgs& a, hipStream_t st);
