@@ -8,12 +8,17 @@
 //   out = R^T (sum_t softmax(s)_t * nv_t * c_v[idxv_t]).
 //
 // How it maps to CDNA4 (one 64-lane wave works on 32 keys at a time):
-//  * Both contractions run on v_mfma_f32_16x16x32_f16.  Scores: the 16 MFMA rows
-//    are 4 query rows x {R q hi, R q lo, S q hi, S q lo}; the key operand stacks
-//    the decoded centroids (d values) over the sign bits (d values), so one
-//    accumulator holds, per (query row, key), the hi/lo parts of both terms in
-//    the 4 registers of a single lane.  P.V: rows are {p hi, p lo} per query row
-//    against the decoded value centroids; the sum stays in the rotated domain.
+//  * Set-up per workgroup: the first key blocks start loading; the code tables
+//    are filled; the workgroup's query rows are rotated once (R q, S q in fp32)
+//    and normalised for the fp16 operand split.
+//  * Both contractions run on v_mfma_f32_16x16x32_f16.  Scores: with row groups
+//    of 4 the 16 MFMA rows are 4 query rows x {R q hi, R q lo, S q hi, S q lo}
+//    (the centroid term's A operand fills the first two parts, the sign term's
+//    the other two); with row groups of 8 (heads with more than 4 query rows)
+//    they are 8 query rows x {hi, lo} in both operands.  The B operands are the
+//    decoded centroids and the sign values of 16 keys.  P.V: rows are {p hi,
+//    p lo} per query row against the decoded value centroids; the sum stays in
+//    the rotated domain.
 //  * The fp32 query splits into hi + lo halves (exact to ~2^-22).  Centroids are
 //    used as fp16 copies of s*c with a per-codebook factor s chosen at set-up so
 //    every s*c_i is within 2e-5 (3-bit) / 1e-4 (4-bit) of an fp16 value; 1/s is
@@ -32,9 +37,11 @@
 //  * Softmax runs in the log2 domain with a lazily updated running maximum: the
 //    accumulators are rescaled only in the (rare) blocks where a score exceeds
 //    the current maximum of its row.
-//  * Split-K over keys: grid (sequence, split); 4 waves per workgroup take every
-//    4th block of 32 keys, each keeping two blocks of loads in flight (three
-//    rotating register sets); the waves' partial (max, sum, acc) merge in LDS
+//  * Split-K over keys: grid (sequence x row group, split), sized so the
+//    workgroups fill the chip once; 4 waves per workgroup take every 4th block
+//    of 32 keys, each keeping two blocks of loads in flight (three rotating
+//    register sets; d = 256 keeps two sets and decodes in smaller pieces so that
+//    two waves fit per SIMD); the waves' partial (max, sum, acc) merge in LDS
 //    and one partial per split goes to the workspace; a small kernel merges the
 //    splits and un-rotates.  (Merging in the last workgroup instead needs an
 //    agent-scope fence per workgroup, which writes back the L2 of its XCD and
