@@ -800,14 +800,38 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const float* base = part + row * kStride;
   const int64_t sstride = rows_total * kStride;
-  float M = -INFINITY;
-  for (int s = tid; s < nsplit; s += 256) M = fmaxf(M, base[s * sstride + D]);
+  const int jq = tid % V::kJ, sl = tid / V::kJ;
+  const int k0 = (int)(blockIdx.x * 6) & (D - 1);
+  // The loads that do not depend on one another go out first: this thread's
+  // (max, sum) of split tid, its first accumulator slice and, at d = 128, its
+  // rows of R (16 float4) -- one memory round trip instead of three.
+  float m_own = -INFINITY, l_own = 0.f;
+  if (tid < nsplit) {
+    m_own = base[tid * sstride + D];
+    l_own = base[tid * sstride + D + 1];
+  }
+  f4 a_first = {0.f, 0.f, 0.f, 0.f};
+  if (sl < nsplit) a_first = reinterpret_cast<const f4*>(base + sl * sstride)[jq];
+  constexpr bool kPre = D == 128;
+  f4 rrow[kPre ? V::kSpan : 1];
+  if constexpr (kPre) {
+    const f4* m = reinterpret_cast<const f4*>(R) + jq;
+#pragma unroll
+    for (int kk = 0; kk < V::kSpan; ++kk) rrow[kk] = m[(size_t)((sl * V::kSpan + kk + k0) & (D - 1)) * V::kJ];
+  }
+  float M = m_own;
+  for (int s = tid + 256; s < nsplit; s += 256) M = fmaxf(M, base[s * sstride + D]);
   M = wave_max(M);
   if (lane == 0) red[0][wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
   float L = 0.f;
-  for (int s = tid; s < nsplit; s += 256) {
+  if (tid < nsplit) {
+    const float w = m_own == -INFINITY ? 0.f : expf(m_own - M);
+    wts[tid] = w;
+    L = w * l_own;
+  }
+  for (int s = tid + 256; s < nsplit; s += 256) {
     const float m = base[s * sstride + D];
     const float w = m == -INFINITY ? 0.f : expf(m - M);
     wts[s] = w;
@@ -817,14 +841,24 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   if (lane == 0) red[1][wave] = L;
   __syncthreads();
   const float invL = 1.0f / (red[1][0] + red[1][1] + red[1][2] + red[1][3]);
-  const int jq = tid % V::kJ, sl = tid / V::kJ;
-  f4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s = sl; s < nsplit; s += V::kSlices) o += reinterpret_cast<const f4*>(base + s * sstride)[jq] * wts[s];
+  f4 o = sl < nsplit ? a_first * wts[sl] : f4{0.f, 0.f, 0.f, 0.f};
+  for (int s = sl + V::kSlices; s < nsplit; s += V::kSlices)
+    o += reinterpret_cast<const f4*>(base + s * sstride)[jq] * wts[s];
   acc[sl][jq] = o;
   __syncthreads();
   if (tid < D) os[tid] = matvec_sum<D>(acc, tid) * invL;
   __syncthreads();
-  acc[sl][jq] = matvec_part<D>(R, os, jq, sl, (int)(blockIdx.x * 6) & (D - 1));
+  if constexpr (kPre) {
+    f4 r0 = {0.f, 0.f, 0.f, 0.f}, r1 = r0;
+#pragma unroll
+    for (int kk = 0; kk < V::kSpan; kk += 2) {
+      r0 += rrow[kk] * os[(sl * V::kSpan + kk + k0) & (D - 1)];
+      r1 += rrow[kk + 1] * os[(sl * V::kSpan + kk + 1 + k0) & (D - 1)];
+    }
+    acc[sl][jq] = r0 + r1;
+  } else {
+    acc[sl][jq] = matvec_part<D>(R, os, jq, sl, k0);
+  }
   __syncthreads();
   if (tid < D) out[row * D + tid] = matvec_sum<D>(acc, tid);
 }
