@@ -20,6 +20,9 @@
  *  Streams     `stream` is a hipStream_t passed as void* (NULL = the default
  *              stream).  Compute calls only enqueue work: results are valid in
  *              stream order, and no call synchronises except tq_make_rotation.
+ *              tq_quantize_kv, tq_attn_decode and tq_dequantize enqueue kernels
+ *              only (no allocation, copy or memset), so a stream capture of
+ *              them replays as a HIP graph.
  *  Errors      Every argument is validated on the host before any HIP call; on
  *              an invalid argument nothing is written and nothing is enqueued.
  *              tq_last_error() returns a message for the calling thread's most
