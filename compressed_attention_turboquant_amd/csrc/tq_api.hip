@@ -17,6 +17,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 struct Plan {  // split-K plan of one decode call
   bool mfma;     // matrix-core kernel (else the reference kernels)
   int nsplit;
+  int waves;     // per workgroup (matrix-core kernel)
   int64_t keys_per_split;
   int64_t rows_total;
   size_t off_qrot, off_qproj, off_part, total;
@@ -29,22 +30,34 @@ Plan decode_plan(int d, int qjl, int B, int Hq, int Hkv, int Tq, int64_t N) {
   if (p.mfma) {
     // Work in blocks of 32 keys.  A workgroup serves up to 4 (or 8) query rows
     // of one KV head; split the keys so that the workgroups fill the chip's 256
-    // CUs once (decode_wgs_per_cu workgroups each: what their registers allow)
-    // -- a second round of workgroups costs more in set-up and tail than it
-    // gains -- while giving each of a workgroup's 4 waves at least 4 blocks.
-    // The plan depends on the shape only, so the workspace size does too.
+    // CUs once (as many waves on each as the registers allow) -- a second round
+    // of workgroups costs more in set-up and tail than it gains -- while giving
+    // each wave at least 4 blocks.  The plan depends on the shape only, so the
+    // workspace size does too.
     const int64_t blocks = (N + 31) / 32;
     const int rw = decode_rows_per_group(Hq / Hkv * Tq);
     const int64_t groups = seqs * ((Hq / Hkv * Tq + rw - 1) / rw);
-    const int64_t target = 256 * decode_wgs_per_cu(d, qjl, rw);
-    int64_t want = (target + groups - 1) / groups;
-    const int64_t max_split = (blocks + 15) / 16;
-    if (want > max_split) want = max_split;
-    if (want > 1024) want = 1024;  // the combine kernel keeps one weight per split in LDS
-    if (want < 1) want = 1;
-    const int64_t bps = (blocks + want - 1) / want;
-    p.keys_per_split = bps * 32;
-    p.nsplit = (int)((blocks + bps - 1) / bps);
+    const int simd_waves = decode_simd_waves(d, qjl, rw);
+    auto split_keys = [&](int waves) {
+      const int64_t target = 256 * 4 * simd_waves / waves;
+      int64_t want = (target + groups - 1) / groups;
+      const int64_t max_split = (blocks + 4 * waves - 1) / (4 * waves);
+      if (want > max_split) want = max_split;
+      if (want > 1024) want = 1024;  // the combine kernel keeps one weight per split in LDS
+      if (want < 1) want = 1;
+      const int64_t bps = (blocks + want - 1) / want;
+      p.waves = waves;
+      p.keys_per_split = bps * 32;
+      p.nsplit = (int)((blocks + bps - 1) / bps);
+    };
+    // Workgroups of 4 waves, two per CU where the registers allow.  When they
+    // fill every CU but leave each wave fewer than 16 blocks, the set-up (code
+    // tables and query rotation, once per workgroup) weighs on the short key
+    // loop, and one 8-wave workgroup per CU, which does it once with twice the
+    // threads, is faster (4-row groups only).
+    split_keys(4);
+    if (simd_waves == 2 && rw == 4 && groups <= 256 && groups * p.nsplit >= 512 && p.keys_per_split < 4 * 16 * 32)
+      split_keys(8);
   } else {
     int64_t want = (2048 + seqs - 1) / seqs;
     const int64_t max_split = (N + 63) / 64;
@@ -320,6 +333,7 @@ tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, 
   a.q_proj = reinterpret_cast<float*>(ws + P.off_qproj);
   a.part = reinterpret_cast<float*>(ws + P.off_part);
   a.nsplit = P.nsplit;
+  a.waves = P.waves;
   a.keys_per_split = P.keys_per_split;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (P.mfma) {

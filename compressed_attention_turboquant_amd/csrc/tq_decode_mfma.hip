@@ -175,10 +175,13 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   p.rgroups = (a.Hq / a.Hkv * a.Tq + rw - 1) / rw;
   const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * p.rgroups), (unsigned)a.nsplit);
   hipError_t e;
+  const int w = a.waves;
   if (a.d == 128)
-    e = a.qjl ? launch_decode_split_d128_q1(p, a.kb, a.vb, grid, st) : launch_decode_split_d128_q0(p, a.kb, a.vb, grid, st);
+    e = a.qjl ? launch_decode_split_d128_q1(p, a.kb, a.vb, w, grid, st)
+              : launch_decode_split_d128_q0(p, a.kb, a.vb, w, grid, st);
   else
-    e = a.qjl ? launch_decode_split_d256_q1(p, a.kb, a.vb, grid, st) : launch_decode_split_d256_q0(p, a.kb, a.vb, grid, st);
+    e = a.qjl ? launch_decode_split_d256_q1(p, a.kb, a.vb, w, grid, st)
+              : launch_decode_split_d256_q0(p, a.kb, a.vb, w, grid, st);
   if (e != hipSuccess) return e;
   if (a.d == 128)
     hipLaunchKernelGGL(combine_kernel<128>, rgrid, dim3(256), 0, st, a.part, a.nsplit, qrows, a.R, a.out);

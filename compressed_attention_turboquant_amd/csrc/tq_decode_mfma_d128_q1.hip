@@ -5,41 +5,45 @@
 namespace tq {
 namespace {
 
-template <int D, int KB, int QJL, int VB>
-hipError_t launch_split(const DecodeMfmaParams& p, dim3 grid, hipStream_t st) {
-  const bool r8 = decode_rows_per_group(p.Hq / p.Hkv * p.Tq) == 8;
-  if (p.scores) {
-    if (r8)
-      hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 1, 2>), grid, dim3(kThreads), 0, st, p);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 1, 1>), grid, dim3(kThreads), 0, st, p);
-  } else {
-    if (r8)
-      hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 0, 2>), grid, dim3(kThreads), 0, st, p);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, 0, 1>), grid, dim3(kThreads), 0, st, p);
-  }
+template <int D, int KB, int QJL, int VB, int SCORES, int NR, int W>
+hipError_t launch(const DecodeMfmaParams& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((decode_mfma_kernel<D, KB, QJL, VB, SCORES, NR, W>), grid, dim3(64 * W), 0, st, p);
   return hipGetLastError();
 }
 
+// Where the plan asks for 8-wave workgroups (4-row groups with two waves per
+// SIMD), calls without score output get them; calls that also write the scores
+// run 4-wave workgroups on the same grid.
+template <int D, int KB, int QJL, int VB>
+hipError_t launch_split(const DecodeMfmaParams& p, int waves, dim3 grid, hipStream_t st) {
+  const bool r8 = decode_rows_per_group(p.Hq / p.Hkv * p.Tq) == 8;
+  if (p.scores) return r8 ? launch<D, KB, QJL, VB, 1, 2, 4>(p, grid, st) : launch<D, KB, QJL, VB, 1, 1, 4>(p, grid, st);
+  if (r8) return launch<D, KB, QJL, VB, 0, 2, 4>(p, grid, st);
+  if constexpr (decode_simd_waves(D, QJL, 4) == 2) {
+    if (waves == 8) return launch<D, KB, QJL, VB, 0, 1, 8>(p, grid, st);
+  }
+  return launch<D, KB, QJL, VB, 0, 1, 4>(p, grid, st);
+}
+
 template <int D, int KB, int QJL>
-hipError_t dispatch_vb(const DecodeMfmaParams& p, int vb, dim3 grid, hipStream_t st) {
+hipError_t dispatch_vb(const DecodeMfmaParams& p, int vb, int waves, dim3 grid, hipStream_t st) {
   switch (vb) {
-    case 1: return launch_split<D, KB, QJL, 1>(p, grid, st);
-    case 2: return launch_split<D, KB, QJL, 2>(p, grid, st);
-    case 3: return launch_split<D, KB, QJL, 3>(p, grid, st);
-    default: return launch_split<D, KB, QJL, 4>(p, grid, st);
+    case 1: return launch_split<D, KB, QJL, 1>(p, waves, grid, st);
+    case 2: return launch_split<D, KB, QJL, 2>(p, waves, grid, st);
+    case 3: return launch_split<D, KB, QJL, 3>(p, waves, grid, st);
+    default: return launch_split<D, KB, QJL, 4>(p, waves, grid, st);
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_split_d128_q1(const DecodeMfmaParams& p, int kb, int vb, dim3 grid, hipStream_t st) {
+hipError_t launch_decode_split_d128_q1(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid,
+                                       hipStream_t st) {
   switch (kb) {
-    case 1: return dispatch_vb<128, 1, 1>(p, vb, grid, st);
-    case 2: return dispatch_vb<128, 2, 1>(p, vb, grid, st);
-    case 3: return dispatch_vb<128, 3, 1>(p, vb, grid, st);
-    default: return dispatch_vb<128, 4, 1>(p, vb, grid, st);
+    case 1: return dispatch_vb<128, 1, 1>(p, vb, waves, grid, st);
+    case 2: return dispatch_vb<128, 2, 1>(p, vb, waves, grid, st);
+    case 3: return dispatch_vb<128, 3, 1>(p, vb, waves, grid, st);
+    default: return dispatch_vb<128, 4, 1>(p, vb, waves, grid, st);
   }
 }
 

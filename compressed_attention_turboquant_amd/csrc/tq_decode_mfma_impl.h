@@ -68,8 +68,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kSlack = 4.f;            // log2 headroom of the lazily updated maximum
@@ -150,7 +148,7 @@ __device__ __forceinline__ uint32_t half_bits(float x) {
 // index (one code per half for 4-bit tables).  A wave fills 64 consecutive
 // entries, so an entry's low half is the lane's own value and its high half
 // comes from the lane its high index bits name (one cross-lane read).
-template <int BITS>
+template <int BITS, int T>
 __device__ __forceinline__ void fill_lut(uint32_t* tab, const float* c, float s, int tid) {
   using L = Lut<BITS>;
   constexpr uint32_t m = (1u << BITS) - 1u;
@@ -159,14 +157,14 @@ __device__ __forceinline__ void fill_lut(uint32_t* tab, const float* c, float s,
     constexpr int pb = 2 * BITS;  // bits of a pair index; 2^pb divides 64
     constexpr uint32_t pm = (1u << pb) - 1u;
     const uint32_t P = half_bits(s * c[lane & m]) | (half_bits(s * c[(lane >> BITS) & m]) << 16);
-    for (int i0 = 0; i0 < L::kEntries; i0 += kThreads) {
+    for (int i0 = 0; i0 < L::kEntries; i0 += T) {
       const uint32_t i = (uint32_t)(i0 + tid);
       const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((i >> pb) & pm) << 2), (int)P);
       if (i < (uint32_t)L::kEntries) *reinterpret_cast<u2*>(tab + 2 * i) = u2{P, hi};
     }
   } else {
     const uint32_t h = half_bits(s * c[lane & m]);
-    for (int i0 = 0; i0 < L::kEntries; i0 += kThreads) {
+    for (int i0 = 0; i0 < L::kEntries; i0 += T) {
       const uint32_t i = (uint32_t)(i0 + tid);
       const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((i >> BITS) & m) << 2), (int)h);
       if (i < (uint32_t)L::kEntries) tab[i] = h | (hi << 16);
@@ -446,17 +444,17 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
 // Four of the workgroup's query rows (rb..rb+3) rotated once: rq[0][r][j] =
 // (R q_r)_j / s_k and rq[1][r][j] = (S q_r)_j, from the rows in qs (LDS) and
 // R^T, S^T (global, row-major).  Thread (matrix, jq, slice) reads float4 rows
-// M[k][4jq..4jq+3] over its quarter of k for the four rows; the slices' partial
+// M[k][4jq..4jq+3] over its slice of k for the four rows; the slices' partial
 // sums meet in part (LDS).  Each workgroup starts its slices at its own row
 // offset k0, so that the workgroups, which all read the same few hundred KB at
 // once, spread over the L2 channels.
-template <int D, int QJL, int RW>
+template <int D, int QJL, int RW, int T>
 __device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const float* __restrict__ St,
                                             float s_k, const float (*qs)[D], float (*rq)[RW][D],
                                             f4 (*part)[4][D / 4], int tid, int k0, int rb) {
   constexpr int kJ = D / 4;                   // float4 columns per matrix row
   constexpr int kMats = D == 128 ? 2 : 1;     // matrices handled side by side
-  constexpr int kSl = 256 / (kJ * kMats);     // k-slices: 4
+  constexpr int kSl = T / (kJ * kMats);       // k-slices: 4 per 256 threads
   constexpr int kSpan = D / kSl;
 #pragma unroll
   for (int pass = 0; pass < 2 / kMats; ++pass) {
@@ -483,7 +481,7 @@ __device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const 
     // part holds one matrix per pass at d = 256; at d = 128 the two matrices
     // use its two halves (slices 0-3 for R, 4-7 for S).
     __syncthreads();
-    for (int o = tid; o < kMats * 4 * D; o += 256) {
+    for (int o = tid; o < kMats * 4 * D; o += T) {
       const int mm = kMats == 2 ? o / (4 * D) : pass, r = (o / D) % 4, j = o % D;
       float v = 0.f;
       if (QJL || mm == 0) {
@@ -496,26 +494,27 @@ __device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const 
   }
 }
 
-// Workgroups per CU as decode_wgs_per_cu gives (two waves per SIMD where the
-// registers allow); the bound keeps a code change from silently halving
-// occupancy.
-template <int D, int KB, int QJL, int VB, int SCORES, int NR>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_wgs_per_cu(D, QJL, 4 * NR))))
+// W waves per workgroup; the SIMDs hold two waves each where
+// decode_simd_waves allows (the bound keeps a code change from silently
+// halving occupancy).
+template <int D, int KB, int QJL, int VB, int SCORES, int NR, int W>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(decode_simd_waves(D, QJL, 4 * NR))))
 decode_mfma_kernel(DecodeMfmaParams p) {
   using S = Shape<D, KB, QJL, VB>;
+  constexpr int T = 64 * W;   // threads
   constexpr int RW = 4 * NR;  // query rows per workgroup
   // One table serves keys and values when their widths match (the codebook and
   // its fp16 factor depend only on the width and the head dimension).
   constexpr int kKtab = Lut<KB>::kDwords, kVtab = KB == VB ? 0 : Lut<VB>::kDwords;
   __shared__ __align__(16) uint32_t lut[kKtab + kVtab];
-  __shared__ __align__(16) _Float16 pbuf[kWaves][2][RW][32];
-  __shared__ float mrg_m[kWaves][RW], mrg_l[kWaves][RW];
+  __shared__ __align__(16) _Float16 pbuf[W][2][RW][32];
+  __shared__ float mrg_m[W][RW], mrg_l[W][RW];
   __shared__ float qsh[RW][D];     // the workgroup's query rows
   __shared__ float qrs[2][RW][D];  // R q / s_k and S q of those rows
   __shared__ float qcon[RW][4];    // per row: c1, c2, -sum(S q)
   // The rotation's k-slice partial sums (set-up) and the waves' accumulators
   // (merge, after the key loop) share one buffer.
-  constexpr int kRpart = (D == 128 ? 8 : 4) * 4 * (D / 4) * 16, kMrg = kWaves * RW * D * 4;
+  constexpr int kRpart = (T / (D / 4)) * 4 * (D / 4) * 16, kMrg = W * RW * D * 4;
   __shared__ __align__(16) char scratch[kRpart > kMrg ? kRpart : kMrg];
   auto rpart = reinterpret_cast<f4 (*)[4][D / 4]>(scratch);
   auto mrg_acc = reinterpret_cast<float (*)[RW][D]>(scratch);
@@ -547,27 +546,28 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   sb.vidx = make_rsrc(p.vidx + seq * (p.cap / 8) * S::VTILE, (p.cap / 8) * S::VTILE);
   sb.vnorm = make_rsrc(p.vnorm + seq * p.cap, p.N * 4);
 
-  // The first key blocks start loading before the set-up below (two at d = 128,
-  // one at d = 256, whose loop keeps two register sets).
+  // The split's key blocks [blk0, blk1): wave w takes blocks blk0 + w + W j.
+  // The first ones start loading before the set-up below (two at d = 128, one
+  // at d = 256, whose loop keeps two register sets).
   const int nblk = (int)((p.N + 31) / 32);
   const int blk0 = (int)(split * (p.keys_per_split / 32));
   const int blk1 = min(nblk, blk0 + (int)(p.keys_per_split / 32));
   Block<D, KB, QJL, VB> b0, b1, b2;
   int blk = blk0 + wave;
   load_block(b0, sb, blk * 32, l16, g4);
-  if constexpr (D == 128) load_block(b1, sb, (blk + kWaves) * 32, l16, g4);
+  if constexpr (D == 128) load_block(b1, sb, (blk + W) * 32, l16, g4);
 
   WaveState<D, KB, QJL, VB, NR> ws;
   const float scale_k = p.scales[0], scale_v = KB == VB ? scale_k : p.scales[1];
-  fill_lut<KB>(lut, p.cb, scale_k, tid);
-  if constexpr (KB != VB) fill_lut<VB>(lut + kKtab, p.cb + 2 * kMaxLevels, scale_v, tid);
+  fill_lut<KB, T>(lut, p.cb, scale_k, tid);
+  if constexpr (KB != VB) fill_lut<VB, T>(lut + kKtab, p.cb + 2 * kMaxLevels, scale_v, tid);
   ws.ktab = lut;
   ws.vtab = KB == VB ? lut : lut + kKtab;
 
   // Rotate the query rows once (R q, S q) and normalise them for the fp16
   // operand split: qa = (R q) / (s_k c1), qb = 2 (S q) / c2 with c1, c2 powers of
   // two that bring the largest entry into [1, 2).
-  for (int i = tid; i < RW * D; i += kThreads) {
+  for (int i = tid; i < RW * D; i += T) {
     const int r = i / D, k = i % D;
     float v = 0.f;
     if (r < rows) {
@@ -582,12 +582,12 @@ decode_mfma_kernel(DecodeMfmaParams p) {
 #pragma unroll
     for (int rb = 0; rb < RW; rb += 4) {
       if (rb > 0) __syncthreads();  // rpart is reused
-      rotate_rows<D, QJL, RW>(p.Rt, p.St, scale_k, qsh, qrs, rpart, tid, k0, rb);
+      rotate_rows<D, QJL, RW, T>(p.Rt, p.St, scale_k, qsh, qrs, rpart, tid, k0, rb);
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int r = wave; r < RW; r += kWaves) {  // wave w normalises rows w, w + 4
+  for (int r = wave; r < RW; r += W) {  // wave w normalises rows w, w + W, ...
     float ma = 0.f, mb = 0.f, sbv = 0.f;
 #pragma unroll
     for (int j = lane; j < D; j += 64) {
@@ -674,27 +674,28 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   for (int i = 0; i < S::CB; ++i) ws.acc[i] = f4{0.f, 0.f, 0.f, 0.f};
 
   // Three register sets rotate so two blocks are in flight while one is used
-  // (d = 256: two sets, one block in flight).  The prefetches are unconditional (reads past the split land in the same
-  // sequence, reads past its capacity return 0), which keeps the loop body
-  // straight-line and lets the compiler count outstanding loads exactly.
+  // (d = 256: two sets, one block in flight).  The prefetches are
+  // unconditional (reads past the split land in the same sequence, reads past
+  // its capacity return 0), which keeps the loop body straight-line and lets
+  // the compiler count outstanding loads exactly.
   if constexpr (D == 128) {
-    for (; blk < blk1; blk += 3 * kWaves) {
-      load_block(b2, sb, (blk + 2 * kWaves) * 32, l16, g4);
+    for (; blk < blk1; blk += 3 * W) {
+      load_block(b2, sb, (blk + 2 * W) * 32, l16, g4);
       process_block<D, KB, QJL, VB, SCORES, NR>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
-      if (blk + kWaves >= blk1) break;
-      load_block(b0, sb, (blk + 3 * kWaves) * 32, l16, g4);
-      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b1, (blk + kWaves) * 32, p, pbuf[wave], l16, g4, rows);
-      if (blk + 2 * kWaves >= blk1) break;
-      load_block(b1, sb, (blk + 4 * kWaves) * 32, l16, g4);
-      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b2, (blk + 2 * kWaves) * 32, p, pbuf[wave], l16, g4, rows);
+      if (blk + W >= blk1) break;
+      load_block(b0, sb, (blk + 3 * W) * 32, l16, g4);
+      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b1, (blk + W) * 32, p, pbuf[wave], l16, g4, rows);
+      if (blk + 2 * W >= blk1) break;
+      load_block(b1, sb, (blk + 4 * W) * 32, l16, g4);
+      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b2, (blk + 2 * W) * 32, p, pbuf[wave], l16, g4, rows);
     }
   } else {
-    for (; blk < blk1; blk += 2 * kWaves) {
-      load_block(b1, sb, (blk + kWaves) * 32, l16, g4);
+    for (; blk < blk1; blk += 2 * W) {
+      load_block(b1, sb, (blk + W) * 32, l16, g4);
       process_block<D, KB, QJL, VB, SCORES, NR>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
-      if (blk + kWaves >= blk1) break;
-      load_block(b0, sb, (blk + 2 * kWaves) * 32, l16, g4);
-      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b1, (blk + kWaves) * 32, p, pbuf[wave], l16, g4, rows);
+      if (blk + W >= blk1) break;
+      load_block(b0, sb, (blk + 2 * W) * 32, l16, g4);
+      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b1, (blk + W) * 32, p, pbuf[wave], l16, g4, rows);
     }
   }
 
@@ -716,15 +717,15 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   }
   __syncthreads();
   const int64_t rows_total = (int64_t)(gridDim.x / p.rgroups) / p.Hkv * p.Hq * p.Tq;
-  for (int idx = tid; idx < rows * D; idx += kThreads) {
+  for (int idx = tid; idx < rows * D; idx += T) {
     const int r = idx / D, j = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg_m[w][r]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, mrg_m[w][r]);
     float a = 0.f, L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float f = exp2f(mrg_m[w][r] - M);
         a = fmaf(f, mrg_acc[w][r][j], a);
         L = fmaf(f, mrg_l[w][r], L);

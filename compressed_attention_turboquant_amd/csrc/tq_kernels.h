@@ -32,6 +32,7 @@ struct DecodeArgs {
   // workspace pieces
   float *q_rot, *q_proj, *part;
   int nsplit;
+  int waves;  // waves per decode workgroup (matrix-core kernel)
   int64_t keys_per_split;
 };
 
@@ -84,19 +85,24 @@ hipError_t launch_quantize_fwht(const QuantizeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 bool mfma_decode_supports(int d, int rows);
 // The split kernel for one head dimension and key kind (tq_decode_mfma_d*.hip).
-hipError_t launch_decode_split_d128_q0(const DecodeMfmaParams& p, int kb, int vb, dim3 grid, hipStream_t st);
-hipError_t launch_decode_split_d128_q1(const DecodeMfmaParams& p, int kb, int vb, dim3 grid, hipStream_t st);
-hipError_t launch_decode_split_d256_q0(const DecodeMfmaParams& p, int kb, int vb, dim3 grid, hipStream_t st);
-hipError_t launch_decode_split_d256_q1(const DecodeMfmaParams& p, int kb, int vb, dim3 grid, hipStream_t st);
+hipError_t launch_decode_split_d128_q0(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid,
+                                       hipStream_t st);
+hipError_t launch_decode_split_d128_q1(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid,
+                                       hipStream_t st);
+hipError_t launch_decode_split_d256_q0(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid,
+                                       hipStream_t st);
+hipError_t launch_decode_split_d256_q1(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid,
+                                       hipStream_t st);
 // Query rows one decode workgroup serves (4, or 8 when a KV head has more than
 // 4 query rows: the matrix-core rows then carry 8 query rows x {hi, lo}).
 inline int decode_rows_per_group(int rows_per_head) { return rows_per_head > 4 ? 8 : 4; }
 
-// Decode workgroups one CU runs at once: 2 (two waves per SIMD), except at
-// d = 256 with QJL keys or row groups of 8, whose register use allows one.
-constexpr int decode_wgs_per_cu(int d, int qjl, int rows_per_group) {
+// Decode waves one SIMD runs at once: 2, except at d = 256 with QJL keys or row
+// groups of 8, whose register use allows one.
+constexpr int decode_simd_waves(int d, int qjl, int rows_per_group) {
   return d == 256 && (qjl || rows_per_group == 8) ? 1 : 2;
 }
+
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st);
 hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_dequant_ref(const DequantArgs& a, hipStream_t st);
