@@ -1,8 +1,8 @@
 """Benchmark of the TurboQuant KV-cache path on one MI355X.
 
-One step = quantize the layer's keys, quantize its values, and run decode
-attention over the compressed cache, on synthetic inputs already resident in
-HBM.  The default workload is the Llama-3-8B-shaped layer (batch 16, 32 query
+One step = quantize the layer's keys, quantize its values, run decode
+attention over the compressed cache, and dequantize both caches (into the
+input's dtype), on synthetic inputs already resident in HBM.  The default workload is the Llama-3-8B-shaped layer (batch 16, 32 query
 / 8 KV heads, d=128, 131072 keys, fp16 inputs with per-channel LogNormal(0,
 0.5) scales, keys 3-bit MSE + 1-bit QJL, values 3-bit, Haar rotation).
 
@@ -11,6 +11,7 @@ Printed (one JSON line on stdout):
   quantize_vectors_per_s   (K rows + V rows) / duration of the two quantize calls
   roofline           decode kernel vs the 8 TB/s HBM peak
   roofline_quantize  quantize kernel vs its bound
+  roofline_dequantize  dequantize kernel vs its bound
   cpu_baseline       the fp64 oracle on a bounded sample of the same workload
 """
 import argparse
@@ -163,6 +164,7 @@ def main():
     out = torch.empty((cfg.B, cfg.Hq, cfg.Tq, d), dtype=torch.float32, device=dev)
     ws = torch.empty(max(B.decode_workspace_bytes(layer, cfg.B, cfg.Hq, cfg.Hkv, cfg.Tq, cfg.N), 1),
                      dtype=torch.uint8, device=dev)
+    xhat = torch.empty((S, cfg.N, d), dtype=torch.float16 if cfg.dtype == "f16" else torch.float32, device=dev)
 
     def step(ev=None):
         if ev: ev[0].record(stream)
@@ -172,12 +174,15 @@ def main():
         if ev: ev[2].record(stream)
         B.attn_decode(layer, q, Kc, Vc, cfg.N, cfg.Hkv, cfg.causal, out=out, workspace=ws)
         if ev: ev[3].record(stream)
+        B.dequantize(layer, B.TQ_KEYS, Kc, cfg.N, out=xhat)
+        B.dequantize(layer, B.TQ_VALUES, Vc, cfg.N, out=xhat)
+        if ev: ev[4].record(stream)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -188,6 +193,7 @@ def main():
     qk_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     qv_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     dec_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    dq_ms = sum(e[3].elapsed_time(e[4]) for e in events) / args.steps
     kb, vb = packed_bytes_per_token(cfg)
     rows = cfg.B * cfg.Hkv * cfg.N
     packed = (kb + vb) * rows
@@ -196,8 +202,12 @@ def main():
     in_bytes = 2 if cfg.dtype == "f16" else 4
     q_bytes = rows * (d * in_bytes * 2) + packed            # fp16 K and V in, packed cache out
     q_gbs = q_bytes / ((qk_ms + qv_ms) * 1e-3) / 1e9
+    # dequantize: codes and norm in, rows of the input's dtype out, for K and V
+    dq_bytes = rows * (d * (cfg.k_bits + cfg.v_bits) // 8 + 8 + 2 * d * in_bytes)
+    dq_gbs = dq_bytes / (dq_ms * 1e-3) / 1e9
     digest = kernel_sources_digest()
-    log(f"decode {dec_ms:.3f} ms ({dec_gbs:.0f} GB/s), quantize K {qk_ms:.3f} ms, V {qv_ms:.3f} ms")
+    log(f"decode {dec_ms:.3f} ms ({dec_gbs:.0f} GB/s), quantize K {qk_ms:.3f} ms, V {qv_ms:.3f} ms, "
+        f"dequantize K + V {dq_ms:.3f} ms ({dq_gbs:.0f} GB/s)")
 
     res = {
         "metric": METRIC,
@@ -221,6 +231,7 @@ def main():
         "quantize_k_ms": round(qk_ms, 4),
         "quantize_v_ms": round(qv_ms, 4),
         "quantize_vectors_per_s": round(vec_s, 1),
+        "dequantize_ms": round(dq_ms, 4),
         "packed_kv_bytes": packed,
         "roofline": {"kernel": "tq_attn_decode (all launches of one call)", "bound": "hbm",
                      "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -230,6 +241,10 @@ def main():
                               "achieved": round(q_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(q_gbs / HBM_PEAK_GBS, 4),
                               "traffic": traffic_from_profile("quantize", cfg.name, digest, 1)},
+        "roofline_dequantize": {"kernel": "tq_dequantize (K and V calls)", "bound": "hbm",
+                                "achieved": round(dq_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(dq_gbs / HBM_PEAK_GBS, 4),
+                                "traffic": traffic_from_profile("dequantize", cfg.name, digest, 1)},
         "sources_digest": digest,
     }
     if args.copy_calibration:

@@ -195,10 +195,14 @@ def attn_decode(layer: Layer, q, K: Cache, V: Cache, N: int, Hkv: int, causal: i
     return out, scores
 
 
-def dequantize(layer: Layer, which: int, cache: Cache, n: int, out_dtype=None, stream=None):
+def dequantize(layer: Layer, which: int, cache: Cache, n: int, out_dtype=None, stream=None, out=None):
+    """tq_dequantize into out ([seqs][n][d], float32 or float16; allocated when
+    not given, of out_dtype, default float32)."""
     import torch
-    out_dtype = out_dtype or torch.float32
-    out = torch.empty((cache.c.seqs, n, layer.d), dtype=out_dtype, device=cache["idx"].device)
+    if out is None:
+        out = torch.empty((cache.c.seqs, n, layer.d), dtype=out_dtype or torch.float32, device=cache["idx"].device)
+    elif tuple(out.shape) != (cache.c.seqs, n, layer.d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [seqs][n][d] tensor")
     check(load().tq_dequantize(ctypes.byref(layer.c), which, ctypes.byref(cache.c), n,
                                out.data_ptr(), _dtype_code(out), _stream(stream)))
     return out

@@ -373,10 +373,11 @@ tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* ca
   a.bits = which == TQ_KEYS ? layer->k_bits : layer->v_bits;
   a.value_layout = which == TQ_VALUES;
   a.R = blob_f(layer, BL.rot);
+  a.Rt = blob_f(layer, BL.rot_t);
   a.cent = blob_f(layer, BL.codebook) + (which == TQ_KEYS ? 0 : 2 * kMaxLevels);
   a.out = out;
   a.out_dtype = out_dtype;
-  return hip_status(launch_dequant_ref(a, static_cast<hipStream_t>(stream)), "dequantize launch");
+  return hip_status(launch_dequant_mfma(a, static_cast<hipStream_t>(stream)), "dequantize launch");
 }
 
 }  // extern "C"

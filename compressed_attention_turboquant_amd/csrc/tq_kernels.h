@@ -41,7 +41,7 @@ struct DequantArgs {
   const float* norm;
   int64_t seqs, n, cap;
   int d, bits, value_layout;
-  const float *R, *cent;
+  const float *R, *Rt, *cent;  // R and R^T row-major
   void* out;
   int out_dtype;
 };
@@ -105,7 +105,7 @@ constexpr int decode_simd_waves(int d, int qjl, int rows_per_group) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st);
 hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st);
-hipError_t launch_dequant_ref(const DequantArgs& a, hipStream_t st);
+hipError_t launch_dequant_mfma(const DequantArgs& a, hipStream_t st);
 bool ref_decode_supports(int d, int rows);
 
 }  // namespace tq

@@ -9,7 +9,6 @@
 //   decode    [cuTile] listing, asymmetric score estimator, attention
 //             pipeline and fused attention with online softmax;
 //             [Mobilint] "Two-Stage Approach" (<q, x~> = <Pi q, y~>).
-//   dequant   [cuTile] listing, decompression function.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -382,46 +381,6 @@ __global__ void __launch_bounds__(kThreads) decode_combine_ref(const float* __re
   out[row * d + j] = (v0 + v1) + (v2 + v3);
 }
 
-// ------------------------------------------------------------- dequantize --
-__global__ void __launch_bounds__(kThreads) dequant_tile_ref(
-    const uint8_t* __restrict__ idx, const float* __restrict__ norm, int64_t n, int64_t cap,
-    int d, int bits, int value_layout, const float* __restrict__ R,
-    const float* __restrict__ cent, void* __restrict__ out, int odt) {
-  extern __shared__ float smem[];
-  float* c = smem;  // [8][d]
-  __shared__ float nn[8];
-  const int64_t s = blockIdx.y;
-  const int64_t tile = blockIdx.x;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < 8 * d; e += kThreads) {
-    const int i = e / d, j = e % d;
-    const int64_t t = tile * 8 + i;
-    float v = 0.f;
-    if (t < n) {
-      const uint32_t code =
-          value_layout ? stream_code(idx + (s * (cap / 8) + tile) * (d * bits), 8 * j + i, bits)
-                       : stream_code(idx + (s * cap + t) * (d * bits / 8), j, bits);
-      v = cent[code];
-    }
-    c[e] = v;
-  }
-  if (tid < 8) nn[tid] = tile * 8 + tid < n ? norm[s * cap + tile * 8 + tid] : 0.f;
-  __syncthreads();
-  for (int e = tid; e < 8 * d; e += kThreads) {
-    const int i = e / d, j = e % d;
-    const int64_t t = tile * 8 + i;
-    if (t >= n) continue;
-    float v = 0.f;
-    for (int k = 0; k < d; ++k) v = fmaf(R[(size_t)k * d + j], c[i * d + k], v);
-    v *= nn[i];
-    const int64_t o = (s * n + t) * d + j;
-    if (odt == TQ_F16)
-      static_cast<__half*>(out)[o] = __float2half(v);
-    else
-      static_cast<float*>(out)[o] = v;
-  }
-}
-
 }  // namespace
 
 // ------------------------------------------------------------- launchers --
@@ -474,15 +433,6 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
   const int64_t qrows = (int64_t)a.B * a.Hq * a.Tq;
   hipLaunchKernelGGL(decode_combine_ref, dim3((unsigned)qrows), dim3(kThreads), 0, st, a.part,
                      a.nsplit, qrows, a.d, a.R, a.out);
-  return hipGetLastError();
-}
-
-hipError_t launch_dequant_ref(const DequantArgs& a, hipStream_t st) {
-  if (a.n == 0 || a.seqs == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.n + 7) / 8), (unsigned)a.seqs);
-  hipLaunchKernelGGL(dequant_tile_ref, grid, dim3(kThreads), (size_t)8 * a.d * sizeof(float), st,
-                     a.idx, a.norm, a.n, a.cap, a.d, a.bits, a.value_layout, a.R, a.cent, a.out,
-                     a.out_dtype);
   return hipGetLastError();
 }
 

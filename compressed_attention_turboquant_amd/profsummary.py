@@ -34,6 +34,7 @@ COPY_BYTES = 1 << 30
 DECODE_KERNELS = ("prerotate_ref", "decode_mfma_kernel", "decode_split_ref", "decode_combine_ref",
                   "combine_kernel")
 QUANT_KERNELS = ("quantize_mfma_kernel", "quantize_tile_ref", "quantize_fwht")
+DEQUANT_KERNELS = ("dequant_mfma_kernel",)
 
 
 def strip_comments(src):
@@ -168,7 +169,9 @@ def main():
     write, fw = counters(a.write, "WRITE_SIZE")
     in_b = 2 if cfg.dtype == "f16" else 4
     algo = {"decode": (kb + vb) * rows,
-            "quantize K": rows * (cfg.d * in_b + kb), "quantize V": rows * (cfg.d * in_b + vb)}
+            "quantize K": rows * (cfg.d * in_b + kb), "quantize V": rows * (cfg.d * in_b + vb),
+            # codes and norm in, rows of the input's dtype out (QJL signs are not read)
+            "dequantize": rows * (cfg.d * (cfg.k_bits + cfg.v_bits) // 8 + 8 + 2 * cfg.d * in_b)}
     t = [f"# HBM traffic per dispatch, workload {cfg.name}", "",
          f"Kernel sources digest: `{digest}`", "", "Commands (from the repository root, TMPDIR=/tmp):", "",
          "```", a.fetch_cmd, a.write_cmd, "```", "",
@@ -194,14 +197,18 @@ def main():
 
     dec = total(DECODE_KERNELS)
     quant = total(QUANT_KERNELS)
+    deq = total(DEQUANT_KERNELS)
     t += ["", f"Decode call (all its launches): {dec / 1e9:.4f} GB moved vs {algo['decode'] / 1e9:.4f} GB "
           "of packed KV (algorithmic).",
           f"Quantize K + V calls: {quant / 1e9:.4f} GB moved vs "
-          f"{(algo['quantize K'] + algo['quantize V']) / 1e9:.4f} GB (input rows in, packed rows out)."]
+          f"{(algo['quantize K'] + algo['quantize V']) / 1e9:.4f} GB (input rows in, packed rows out).",
+          f"Dequantize K + V calls: {deq / 1e9:.4f} GB moved vs {algo['dequantize'] / 1e9:.4f} GB "
+          "(codes and norms in, rows out)."]
     with open(os.path.join(a.out, f"traffic_{cfg.name}.md"), "w") as f:
         f.write("\n".join(t) + "\n")
     for tag, val, alg in (("decode", dec, algo["decode"]),
-                          ("quantize", quant, algo["quantize K"] + algo["quantize V"])):
+                          ("quantize", quant, algo["quantize K"] + algo["quantize V"]),
+                          ("dequantize", deq, algo["dequantize"])):
         with open(os.path.join(a.out, f"traffic_{tag}_{cfg.name}.json"), "w") as f:
             json.dump({"workload": cfg.name, "sources_digest": digest, "bytes_per_launch": round(val),
                        "algorithmic_bytes_per_launch": alg, "fetch_factor": round(ff, 4),

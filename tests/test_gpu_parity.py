@@ -169,26 +169,57 @@ def test_end_to_end_from_raw_inputs(name):
     H.log(f"  flipped keys {int(kflip.sum())}  score rel {rel:.2e}  out abs {err:.2e}")
 
 
+def _check_dequantize(cfg, which, n_out=None):
+    """Quantize cfg's rows, dequantize the first n_out tokens of each sequence
+    and compare with the oracle's reconstruction n * R^T c[idx]."""
+    x = _kv(cfg, "K" if which == B.TQ_KEYS else "V", seed=3)
+    S, n, d = x.shape
+    n_out = n if n_out is None else n_out
+    layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, which)
+    got = B.dequantize(layer, which, cache, n_out).cpu().numpy().reshape(-1, d)
+    c, bnd = (ol.ck, ol.bk) if which == B.TQ_KEYS else (ol.cv, ol.bv)
+    keep = np.array([s * n + t for s in range(S) for t in range(n_out)], dtype=np.int64)
+    ref = codec.reconstruct_mse(enc["idx"][keep], enc["norm"][keep], ol.R, c)
+    rows = np.array([s * cap + t for s in range(S) for t in range(n)])
+    bits = cfg.k_bits if which == B.TQ_KEYS else cfg.v_bits
+    gidx = (H.gpu_codes_key(cache, S, cap, d, bits, rows) if which == B.TQ_KEYS
+            else H.gpu_codes_value(cache, S, cap, d, bits)[rows])
+    flipped = H.compare_codes(gidx, enc, bnd, "codes")[keep]
+    scale = enc["norm"][keep][:, None]
+    err = np.abs(got - ref) / np.maximum(scale, 1e-30)
+    assert err[~flipped].max() < 2e-6
+    half = B.dequantize(layer, which, cache, n_out, out_dtype=torch.float16).cpu().numpy().reshape(-1, d)
+    np.testing.assert_allclose(half[~flipped], got[~flipped], rtol=2e-3, atol=1e-3)
+    return err[~flipped].max()
+
+
 @pytest.mark.parametrize("name", ["C1", "C3", "C5"])
 @pytest.mark.parametrize("which", [B.TQ_KEYS, B.TQ_VALUES])
 def test_dequantize_parity(name, which):
-    cfg = REDUCED[name]
     H.log(f"[dequantize] {name} which={which}")
-    x = _kv(cfg, "K" if which == B.TQ_KEYS else "V", seed=3)
-    S, n, d = x.shape
-    layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, which)
-    got = B.dequantize(layer, which, cache, n).cpu().numpy().reshape(-1, d)
-    c, bnd = (ol.ck, ol.bk) if which == B.TQ_KEYS else (ol.cv, ol.bv)
-    ref = codec.reconstruct_mse(enc["idx"], enc["norm"], ol.R, c)
-    rows = np.array([s * cap + t for s in range(S) for t in range(n)])
-    gidx = (H.gpu_codes_key(cache, S, cap, d, cfg.k_bits, rows) if which == B.TQ_KEYS
-            else H.gpu_codes_value(cache, S, cap, d, cfg.v_bits)[rows])
-    flipped = H.compare_codes(gidx, enc, bnd, "codes")
-    scale = enc["norm"][:, None]
-    err = np.abs(got - ref) / np.maximum(scale, 1e-30)
-    assert err[~flipped].max() < 2e-6
-    half = B.dequantize(layer, which, cache, n, out_dtype=torch.float16).cpu().numpy().reshape(-1, d)
-    np.testing.assert_allclose(half[~flipped], got[~flipped], rtol=2e-3, atol=1e-3)
+    _check_dequantize(REDUCED[name], which)
+
+
+# Head dimensions, widths and token counts the workloads above leave out:
+# d = 64, 1-bit codes, fewer tokens than one 8-token value tile, an exact
+# multiple of the kernel's 64-token step, and a prefix of the stored tokens.
+DEQUANT_SHAPES = {
+    "hadamard d64 K1 V2, 70 tokens": (workloads.CONFIGS["C5"].with_(B=1, Hq=2, Hkv=2, N=70, d=64, dtype="f32",
+                                                                     k_bits=1, v_bits=2), None),
+    "haar d128 K4 V1, 5 tokens": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=5, k_bits=4, v_bits=1), None),
+    "haar d128 K2 V3, 128 tokens": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=128), None),
+    "hadamard d256 K3 V2, first 67 of 200": (workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=200, k_bits=3,
+                                                                            v_bits=2), 67),
+}
+
+
+@pytest.mark.parametrize("name", list(DEQUANT_SHAPES))
+@pytest.mark.parametrize("which", [B.TQ_KEYS, B.TQ_VALUES])
+def test_dequantize_shapes(name, which):
+    cfg, n_out = DEQUANT_SHAPES[name]
+    H.log(f"[dequantize] {name} which={which}")
+    err = _check_dequantize(cfg, which, n_out)
+    H.log(f"  max error / norm {err:.2e}")
 
 
 APPEND_CASES = {
