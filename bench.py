@@ -137,7 +137,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path is "
-              "measured on one GPU's share, see DESIGN.md for how it would shard)", file=sys.stderr)
+              "measured on one GPU's share of the sequences)", file=sys.stderr)
         sys.exit(2)
 
     import torch

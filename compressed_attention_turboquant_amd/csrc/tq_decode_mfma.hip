@@ -142,6 +142,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
+// Key blocks of a CU's first-dispatched workgroup per block of its second one
+// (x 1024), from the key-loop times of the two (split_blocks).
+constexpr int kFirstShare = 1331;
+
 bool mfma_decode_supports(int d, int rows) { return (d == 128 || d == 256) && rows >= 1; }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st) {
@@ -174,6 +178,14 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   const int rw = decode_rows_per_group(a.Hq / a.Hkv * a.Tq);
   p.rgroups = (a.Hq / a.Hkv * a.Tq + rw - 1) / rw;
   const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * p.rgroups), (unsigned)a.nsplit);
+  // Unequal splits when the grid is exactly two 4-wave workgroups per CU.
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  const bool two_per_cu = a.waves == 4 && decode_simd_waves(a.d, a.qjl, rw) == 2 &&
+                          (int64_t)grid.x * grid.y == 2 * (int64_t)cus;
+  p.first_wgs = two_per_cu ? cus : 0;
+  p.first_share = kFirstShare;
   hipError_t e;
   const int w = a.waves;
   if (a.d == 128)

@@ -494,6 +494,36 @@ __device__ __forceinline__ void rotate_rows(const float* __restrict__ Rt, const 
   }
 }
 
+// Key blocks [b0, b1) of split `split` of this workgroup's row group.  Blocks
+// are dispatched in linear order (x fastest), so with two workgroups per CU
+// the first first_wgs of them share no CU and each CU's second workgroup
+// arrives later; the later one runs its key loop about 11% slower (the SIMDs'
+// issue arbitration favours the older waves) and, with equal splits, runs alone
+// at the end while the first has finished.  Giving the first-dispatched splits
+// (those with x + gx y < first_wgs, the lowest y of each row group) first_share
+// / 1024 times the blocks of the others makes both end together.  The layout
+// depends only on the grid, so the results do not depend on timing; a split can
+// come out empty (b0 >= b1), which the merge and the combine treat as weight 0.
+__device__ __forceinline__ void split_blocks(const DecodeMfmaParams& p, int split, int& b0, int& b1) {
+  const int nblk = (int)((p.N + 31) / 32), ns = (int)gridDim.y, per = (int)(p.keys_per_split / 32);
+  const int x = (int)blockIdx.x, gx = (int)gridDim.x;
+  int nf = x < p.first_wgs ? (p.first_wgs - x + gx - 1) / gx : 0;
+  nf = min(nf, ns);
+  if (nf > 0 && nf < ns) {
+    const int64_t S = p.first_share;
+    const int big = (int)(((int64_t)nblk * S + nf * S + (int64_t)(ns - nf) * 1024 - 1) / (nf * S + (int64_t)(ns - nf) * 1024));
+    const int rest = nblk - nf * big;
+    const int small = (rest + ns - nf - 1) / (ns - nf);
+    if (rest > 0 && small > 0) {
+      b0 = split < nf ? split * big : nf * big + (split - nf) * small;
+      b1 = min(nblk, b0 + (split < nf ? big : small));
+      return;
+    }
+  }
+  b0 = split * per;
+  b1 = min(nblk, b0 + per);
+}
+
 // W waves per workgroup; the SIMDs hold two waves each where
 // decode_simd_waves allows (the bound keeps a code change from silently
 // halving occupancy).
@@ -549,9 +579,8 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   // The split's key blocks [blk0, blk1): wave w takes blocks blk0 + w + W j.
   // The first ones start loading before the set-up below (two at d = 128, one
   // at d = 256, whose loop keeps two register sets).
-  const int nblk = (int)((p.N + 31) / 32);
-  const int blk0 = (int)(split * (p.keys_per_split / 32));
-  const int blk1 = min(nblk, blk0 + (int)(p.keys_per_split / 32));
+  int blk0, blk1;
+  split_blocks(p, split, blk0, blk1);
   Block<D, KB, QJL, VB> b0, b1, b2;
   int blk = blk0 + wave;
   load_block(b0, sb, blk * 32, l16, g4);

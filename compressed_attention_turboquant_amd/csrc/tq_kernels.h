@@ -59,6 +59,10 @@ struct DecodeMfmaParams {
   int Hq, Hkv, Tq, causal;
   int rgroups;                      // groups of up to 4 query rows per KV head
   int64_t N, cap, keys_per_split;
+  // Unequal splits (see split_blocks): workgroups with a linear index below
+  // first_wgs get first_share / 1024 times the key blocks of the others; 0: all
+  // splits of a row group have keys_per_split keys.
+  int first_wgs, first_share;
   float *part, *scores;
 };
 

@@ -130,6 +130,29 @@ def test_decode_row_groups(name):
     H.log(f"  score rel err {rel:.2e}  out abs err {err:.2e}")
 
 
+# Grids of exactly two 4-wave workgroups per CU on a 256-CU part (128 row
+# groups x 4 key splits of more than 64 blocks), where the splits dispatched
+# first get more key blocks than the others; N = 8500 leaves a ragged last block.
+SPLIT_CASES = {
+    "128 heads x 4 unequal splits, 8500 keys": workloads.CONFIGS["C3"].with_(B=16, N=8500, dist="normal"),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_decode_unequal_splits(name):
+    cfg = SPLIT_CASES[name]
+    N = cfg.N
+    cap = (N + 7) // 8 * 8
+    H.log(f"[decode unequal splits] {name}")
+    packed = workloads.random_packed_numpy(cfg, cfg.B * cfg.Hkv, cap, seed=9)
+    q = workloads.q_numpy(cfg, seed=9)
+    out, scores, ref_out, ref_scores, cache, ol = _decode_both(cfg, packed, q, N)
+    scale = H.score_scale(q, ol.R, ol.S, ol.ck, cache, N, cfg.G, cfg.k_qjl)
+    rel = H.compare_scores(scores, ref_scores, scale, name)
+    err = H.compare_out(out, ref_out, name)
+    H.log(f"  score rel err {rel:.2e}  out abs err {err:.2e}")
+
+
 @pytest.mark.parametrize("name", list(REDUCED))
 def test_end_to_end_from_raw_inputs(name):
     """Quantize K and V and decode on the GPU; the oracle encodes the same raw
