@@ -1,12 +1,13 @@
 """Stream capture of the hot path into a HIP graph.
 
-The quantize and decode calls allocate nothing, wait for nothing and record no
-memset, so one stream capture of (quantize K, quantize V, decode) must replay
-to the same bytes as the same calls made eagerly.  Each replay runs after
-eager work on the same buffers (the outputs are cleared and a differently
-seeded decode runs in between), and every replay is compared with the eager
-results: packed caches and norms byte for byte, the attention output exactly
-(the kernels are deterministic).
+The quantize, decode and dequantize calls allocate nothing, wait for nothing
+and record no memset, so one stream capture of (quantize K, quantize V,
+decode, dequantize K and V) must replay to the same bytes as the same calls
+made eagerly.  Each replay runs after eager work on the same buffers (the
+outputs are cleared and a differently seeded decode runs in between), and
+every replay is compared with the eager results: packed caches and norms byte
+for byte, the attention output and the reconstructed rows exactly (the kernels
+are deterministic).
 """
 import numpy as np
 import pytest
@@ -51,15 +52,20 @@ def test_graph_replays_match_eager(name):
     out = torch.empty((cfg.B, cfg.Hq, cfg.Tq, d), dtype=torch.float32, device=dev)
     ws = torch.zeros(max(B.decode_workspace_bytes(layer, cfg.B, cfg.Hq, cfg.Hkv, cfg.Tq, N), 1),
                      dtype=torch.uint8, device=dev)
+    xk_hat = torch.empty((S, N, d), dtype=torch.float32, device=dev)
+    xv_hat = torch.empty((S, N, d), dtype=torch.float16, device=dev)
 
     def step():
         B.quantize_kv(layer, B.TQ_KEYS, xk, K)
         B.quantize_kv(layer, B.TQ_VALUES, xv, V)
         B.attn_decode(layer, q, K, V, N, cfg.Hkv, cfg.causal, out=out, workspace=ws)
+        B.dequantize(layer, B.TQ_KEYS, K, N, out=xk_hat)
+        B.dequantize(layer, B.TQ_VALUES, V, N, out=xv_hat)
 
     step()
     torch.cuda.synchronize()
     ref_k, ref_v, ref_out = _snapshot(K), _snapshot(V), out.clone()
+    ref_xk, ref_xv = xk_hat.clone(), xv_hat.clone()
 
     # Capture on a side stream (torch's graph capture requires one).
     g = torch.cuda.CUDAGraph()
@@ -84,6 +90,8 @@ def test_graph_replays_match_eager(name):
         _clear(K)
         _clear(V)
         out.zero_()
+        xk_hat.zero_()
+        xv_hat.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -94,5 +102,7 @@ def test_graph_replays_match_eager(name):
         assert torch.equal(out, ref_out), (
             f"{name}: replay {replay}: output differs by "
             f"{float((out - ref_out).abs().max()):.3e}")
-        H.log(f"  replay {replay}: caches and output identical to the eager call")
+        assert torch.equal(xk_hat, ref_xk), f"{name}: replay {replay}: dequantized keys differ"
+        assert torch.equal(xv_hat, ref_xv), f"{name}: replay {replay}: dequantized values differ"
+        H.log(f"  replay {replay}: caches, output and dequantized rows identical to the eager calls")
     assert np.isfinite(ref_out.cpu().numpy()).all()
