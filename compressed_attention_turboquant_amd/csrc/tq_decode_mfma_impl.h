@@ -279,7 +279,10 @@ __device__ __forceinline__ void load_block(Block<D, KB, QJL, VB>& b, const SeqBu
     if constexpr (QJL) b.kg[t] = buf_f32(sb.krnorm, key * 4);
     b.vn[t] = buf_f32(sb.vnorm, key * 4);
   }
-  buf_load(b.vw, sb.vidx, (k0 / 8 + g4) * S::VTILE + l16 * (S::VTILE / 16));
+  // The tile index is below 2^24 (buffer offsets are 32-bit), so a 24-bit
+  // multiply is exact; a 32-bit one compiles to a 64-bit multiply-add whose
+  // unused high operand can make the loop wait for every load in flight.
+  buf_load(b.vw, sb.vidx, (int)__umul24((unsigned)(k0 / 8 + g4), (unsigned)S::VTILE) + l16 * (S::VTILE / 16));
 }
 
 // Per-wave state of the running softmax and the query operands.  A lane holds
@@ -645,7 +648,10 @@ decode_mfma_kernel(DecodeMfmaParams p) {
 
   // Query operands: lane (row rho = l16, k-group g4).  NR = 1: rho = 4 qr + part,
   // parts {R q hi, R q lo} in Ak and {S q hi, S q lo} in As; NR = 2: rho = 2 qr +
-  // part, parts {hi, lo} in both.
+  // part, parts {hi, lo} in both.  Every lane reads and scales its values (qr <
+  // RW keeps the reads inside qrs, whose rows are finite), the factor being 0
+  // for lanes outside the rows and parts: a read used only under that condition
+  // compiles into one branch and one full LDS wait per element.
   {
     const int qr = NR == 1 ? l16 / 4 : l16 / 2, part = NR == 1 ? l16 % 4 : l16 % 2;
     const bool ok = qr < rows;
@@ -656,7 +662,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
       h8 a;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = (ok && part < 2) ? qa[8 * kb + e] * fa : 0.f;  // NR = 2: part < 2 always
+        const float x = qa[8 * kb + e] * ((ok && part < 2) ? fa : 0.f);  // NR = 2: part < 2 always
         const _Float16 hi = (_Float16)x;
         const _Float16 lo = (_Float16)(x - (float)hi);
         a[e] = part == 0 ? hi : (part == 1 ? lo : (_Float16)0.f);
@@ -668,7 +674,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
         for (int e = 0; e < 8; ++e) {
           const int w = e / 2, h = e % 2;
           const bool sp = NR == 1 ? part >= 2 : true;  // rows of the sign term
-          const float x = (ok && sp) ? qb[32 * (kb / 4) + sign_coord(kb % 4, w, h)] * fb * sign_comp(w) : 0.f;
+          const float x = qb[32 * (kb / 4) + sign_coord(kb % 4, w, h)] * ((ok && sp) ? fb * sign_comp(w) : 0.f);
           const _Float16 hi = (_Float16)x;
           const _Float16 lo = (_Float16)(x - (float)hi);
           const int sp_part = NR == 1 ? part - 2 : part;
