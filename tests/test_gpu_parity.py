@@ -153,6 +153,31 @@ def test_decode_unequal_splits(name):
     H.log(f"  score rel err {rel:.2e}  out abs err {err:.2e}")
 
 
+def test_decode_eight_wave_workgroups():
+    """8 heads x 32768 keys: the 4-wave plan fills the chip with short key
+    loops, so the call runs one 8-wave workgroup per CU (64 splits of 512 keys
+    become 32 of 1024).  The score-free call (8-wave kernel) is compared with
+    the oracle and with the call that also writes the scores (4-wave kernel on
+    the same grid)."""
+    cfg = workloads.CONFIGS["C2"]
+    N = cfg.N
+    cap = (N + 7) // 8 * 8
+    H.log("[decode 8-wave workgroups] C2 shape")
+    packed = workloads.random_packed_numpy(cfg, cfg.B * cfg.Hkv, cap, seed=11)
+    q = workloads.q_numpy(cfg, seed=11)
+    out, scores, ref_out, ref_scores, cache, ol = _decode_both(cfg, packed, q, N)
+    scale = H.score_scale(q, ol.R, ol.S, ol.ck, cache, N, cfg.G, cfg.k_qjl)
+    H.compare_scores(scores, ref_scores, scale, "C2 scores")
+    H.compare_out(out, ref_out, "C2 with scores")
+    layer = H.gpu_layer(cfg)
+    K, V = H.upload_packed(layer, cfg, packed, cfg.B * cfg.Hkv, cap)
+    out8, _ = B.attn_decode(layer, torch.from_numpy(q).cuda(), K, V, N, cfg.Hkv, cfg.causal)
+    torch.cuda.synchronize()
+    err = H.compare_out(out8.cpu().numpy(), ref_out, "C2 without scores")
+    assert np.abs(out8.cpu().numpy() - out).max() <= 2e-3
+    H.log(f"  out abs err {err:.2e}")
+
+
 @pytest.mark.parametrize("name", list(REDUCED))
 def test_end_to_end_from_raw_inputs(name):
     """Quantize K and V and decode on the GPU; the oracle encodes the same raw
