@@ -61,7 +61,8 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   constexpr int NKB = D / 32;         // k-blocks of the MFMA
   constexpr int PITCH = D + 8;        // LDS row pitch (halves): rows 16 bytes apart in the banks
   constexpr int kPairs = 1 << (2 * BITS);
-  __shared__ uint32_t thi[kPairs], tlo[kPairs];  // code pair -> two fp16 (first code low)
+  // code pair -> {two fp16 hi parts, two fp16 lo parts} (first code in the low halves)
+  __shared__ __align__(8) u2 tpair[kPairs];
   __shared__ __align__(16) _Float16 bhi[kTile][PITCH], blo[kTile][PITCH];
   __shared__ float nsh[kTile];
 
@@ -73,8 +74,7 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
     const float c0 = a.cent[i & ((1 << BITS) - 1)] * kFactor, c1 = a.cent[i >> BITS] * kFactor;
     const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
     const _Float16 e0 = (_Float16)(c0 - (float)h0), e1 = (_Float16)(c1 - (float)h1);
-    thi[i] = hbits(h0) | (hbits(h1) << 16);
-    tlo[i] = hbits(e0) | (hbits(e1) << 16);
+    tpair[i] = u2{hbits(h0) | (hbits(h1) << 16), hbits(e0) | (hbits(e1) << 16)};
   }
 
   // This wave's rows of 16 R^T: row j = 32 wave + 16 jb + l16, k = 32 kb + 8 g4 + e.
@@ -133,9 +133,9 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
     {
       uint32_t ph[16], pl[16];
       sfor<0, 16>([&](auto p) {
-        const uint32_t v = bits_at<2 * BITS * p, 2 * BITS>(w);
-        ph[p] = thi[v];
-        pl[p] = tlo[v];
+        const u2 e = tpair[bits_at<2 * BITS * p, 2 * BITS>(w)];
+        ph[p] = e[0];
+        pl[p] = e[1];
       });
       if constexpr (VALUES) {
         // Token i of the tile: pairs p = 4 kk + i / 2 (kk = 0..3), its half i % 2.
