@@ -32,7 +32,7 @@ COPY_BYTES = 1 << 30
 
 # (tag, substring of the kernel name) for the launches one library call makes
 DECODE_KERNELS = ("prerotate_ref", "decode_mfma_kernel", "decode_split_ref", "decode_combine_ref",
-                  "combine_kernel")
+                  "combine_kernel", "combine_rows128_kernel")
 QUANT_KERNELS = ("quantize_mfma_kernel", "quantize_tile_ref", "quantize_fwht")
 DEQUANT_KERNELS = ("dequant_mfma_kernel",)
 

@@ -110,6 +110,9 @@ ROW_GROUP_CASES = {
     "20 rows (G=4, Tq=5, causal, d=256)": workloads.CONFIGS["C5"].with_(B=1, Hq=8, Hkv=2, Tq=5, N=300,
                                                                       causal=1, k_qjl=1, k_bits=2,
                                                                       v_bits=3),
+    # 2048 query rows in all: the combine merges 4 rows per block.
+    "16 rows x 128 heads (G=4, Tq=4, causal)": workloads.CONFIGS["C3"].with_(B=16, Tq=4, N=203, causal=1,
+                                                                             dist="normal"),
 }
 
 
