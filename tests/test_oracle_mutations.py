@@ -11,6 +11,7 @@ import pytest
 
 import oracle.attention as attention
 import oracle.codec as codec
+import oracle.transforms as transforms
 from tests import test_oracle_pins as pins
 
 
@@ -53,6 +54,14 @@ def _reconstruct_prod_wrong_kappa(idx, norm, sign, rnorm, R, centroids, S):
 _orig_encode = codec.encode_rows
 
 
+def _hadamard_signs_after(d, seed):
+    """D H instead of H D: the signs scale the rows of the transform."""
+    return transforms.rademacher_signs(d, seed)[:, None] * transforms.sylvester_hadamard(d)
+
+
+MODULES = {"codec": codec, "transforms": transforms}
+
+
 def _decode_variant(mutation):
     orig = attention.decode
 
@@ -88,10 +97,12 @@ def _decode_variant(mutation):
      [pins.test_zero_row_is_lower_middle_index]),
     ("QJL factor pi/2 instead of sqrt(pi/2)", ("codec", "reconstruct_prod", _reconstruct_prod_wrong_kappa),
      [pins.test_slopes_mse_only_biased_qjl_unbiased, pins.test_unbiased_and_variance_bound]),
+    ("Hadamard signs applied after the transform", ("transforms", "hadamard_rotation", _hadamard_signs_after),
+     [lambda: pins.test_hadamard_applies_signs_before_transform(64)]),
 ])
 def test_planted_codec_mistake_is_caught(monkeypatch, mutation, patch, checks):
     mod, name, fn = patch
-    monkeypatch.setattr(codec, name, fn)
+    monkeypatch.setattr(MODULES[mod], name, fn)
     assert any(_fails(check) for check in checks), mutation
 
 

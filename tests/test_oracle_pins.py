@@ -9,6 +9,8 @@ Parity status per oracle function:
                         (Which generator is used: parity unpinned by the pages.)
   transforms.haar_*     orthogonality, R-factor sign rule, Haar law (KS).
   transforms.sylvester  scipy.linalg.hadamard, printed H_4, 1/sqrt(d) spread.
+  transforms.hadamard_rotation  signs before the transform (H D, not D H):
+                        D e_k -> column k of H.
   codebook.*            printed 1-/2-bit codebooks and MSEs, Max (1960) table,
                         conditional-mean fixed point by quadrature,
                         Panter-Dite bound, monotone in b.
@@ -126,6 +128,23 @@ def test_hadamard_spreads_one_hot():
     assert np.allclose(np.abs(y), 1 / np.sqrt(d))
     assert round(float(np.abs(y).max()), 3) == 0.088
     assert np.abs(HD.T @ HD - np.eye(d)).max() < 1e-14
+
+
+@pytest.mark.parametrize("d", [16, 64, 256])
+def test_hadamard_applies_signs_before_transform(d):
+    # [Mobilint], "How JL Matrices Evolved": f(x) = P H D x, the random signs act
+    # on the input before the transform.  Since D D = I, the input D e_k must
+    # come out as column k of H (a Walsh function), and D 1 / sqrt(d) as e_0.
+    # With the signs applied after the transform (D H) neither holds unless
+    # every sign is equal, which the seed below rules out.
+    seed = 21
+    D = np.array(rng.signs(seed, rng.TAG_SIGNS, d), dtype=np.float64)
+    assert 0 < (D > 0).sum() < d
+    HD = transforms.hadamard_rotation(d, seed)
+    H = scipy_hadamard(d) / np.sqrt(d)
+    assert np.allclose(HD @ (D / np.sqrt(d)), np.eye(d)[0], atol=1e-14)
+    for k in (0, 1, d // 2 + 3, d - 1):
+        assert np.allclose(HD @ (D * np.eye(d)[k]), H[:, k], atol=1e-14)
 
 
 def test_fwht_op_count_at_128():
