@@ -25,20 +25,32 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include")]
 
 
+# Sources compiled more than once, each time with its own defines: the decode
+# split kernel's instantiations, one object per (head dimension, key kind).
+MULTI = {
+    "tq_decode_mfma_inst.hip": [(f"d{d}_q{q}", [f"-DTQ_INST_D={d}", f"-DTQ_INST_QJL={q}"])
+                                for d in (128, 256) for q in (0, 1)],
+}
+
+
 def _sources():
+    """(source, object name, extra flags) for every compilation."""
     out = []
     for name in sorted(os.listdir(CSRC)):
         if name.endswith(".hip") or name.endswith(".cpp"):
-            out.append(os.path.join(CSRC, name))
+            src = os.path.join(CSRC, name)
+            for tag, defs in MULTI.get(name, [("", [])]):
+                out.append((src, name + (f".{tag}" if tag else "") + ".o", defs))
     return out
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(job):
+    src, objname, defs = job
+    obj = os.path.join(BUILD, objname)
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", "-c", src, "-o", obj] + HIP_FLAGS
+        cmd = [HIPCC, "-x", "hip", "-c", src, "-o", obj] + HIP_FLAGS + defs
     else:
-        cmd = ["g++", "-c", src, "-o", obj] + CXX_FLAGS
+        cmd = ["g++", "-c", src, "-o", obj] + CXX_FLAGS + defs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -14,6 +14,14 @@ thread_local std::string g_last_error;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The kernels address one sequence of a cache array through 32-bit byte
+// offsets (buffer descriptors, with a few hundred keys of read-ahead past the
+// last block), so each array of a sequence must stay below 2^31 bytes with
+// margin.  The code array is the largest (d * bits / 8 bytes per token, at
+// least the d / 8 of the sign bits).
+constexpr int64_t kSeqBytesMax = ((int64_t)1 << 31) - ((int64_t)1 << 20);
+bool seq_bytes_ok(int d, int bits, int64_t cap) { return cap <= kSeqBytesMax / ((int64_t)d * bits / 8); }
+
 struct Plan {  // split-K plan of one decode call
   bool mfma;     // matrix-core kernel (else the reference kernels)
   int nsplit;
@@ -103,6 +111,8 @@ tq_status check_cache(const tq_layer* L, int which, const tq_cache* c, const cha
     return fail(TQ_ERR_INVALID_ARG, n + ": keys with QJL need sign and rnorm");
   if (!aligned16(c->idx) || !aligned16(c->norm) || (qjl && (!aligned16(c->sign) || !aligned16(c->rnorm))))
     return fail(TQ_ERR_ALIGNMENT, n + ": cache pointers must be 16-byte aligned");
+  if (!seq_bytes_ok(L->d, which == TQ_KEYS ? L->k_bits : L->v_bits, c->cap))
+    return fail(TQ_ERR_UNSUPPORTED, n + ": cap * d * bits / 8 must stay below 2^31 - 2^20 bytes per sequence");
   return TQ_OK;
 }
 
@@ -156,6 +166,8 @@ tq_status tq_cache_bytes(const tq_layer* layer, int32_t which, int64_t seqs, int
   if (seqs < 0 || cap <= 0 || cap % 8) return fail(TQ_ERR_INVALID_ARG, "need seqs >= 0 and cap a positive multiple of 8");
   const int bits = which == TQ_KEYS ? layer->k_bits : layer->v_bits;
   if (bits < 1 || bits > 4) return fail(TQ_ERR_INVALID_ARG, "bit widths must be 1..4");
+  if (!seq_bytes_ok(layer->d, bits, cap))
+    return fail(TQ_ERR_UNSUPPORTED, "cap * d * bits / 8 must stay below 2^31 - 2^20 bytes per sequence");
   const bool qjl = which == TQ_KEYS && layer->k_qjl;
   const size_t tokens = (size_t)seqs * (size_t)cap;
   out[0] = tokens * layer->d * bits / 8;
@@ -358,6 +370,8 @@ tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* ca
   if (!aligned16(cache->idx) || !aligned16(cache->norm)) return fail(TQ_ERR_ALIGNMENT, "cache pointers must be 16-byte aligned");
   if (n < 0 || n > cache->cap) return fail(TQ_ERR_INVALID_ARG, "n must be in [0, cap]");
   if (cache->seqs > 65535) return fail(TQ_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (!seq_bytes_ok(layer->d, which == TQ_KEYS ? layer->k_bits : layer->v_bits, cache->cap))
+    return fail(TQ_ERR_UNSUPPORTED, "cap * d * bits / 8 must stay below 2^31 - 2^20 bytes per sequence");
   if (n > 0 && cache->seqs > 0) {
     if (!out) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
     if (!aligned16(out)) return fail(TQ_ERR_ALIGNMENT, "out must be 16-byte aligned");

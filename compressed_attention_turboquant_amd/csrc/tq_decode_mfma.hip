@@ -1,5 +1,5 @@
 // Decode on the matrix cores: the combine kernel and the launcher.  The split
-// kernel (tq_decode_mfma_impl.h) is instantiated in tq_decode_mfma_d*.hip.
+// kernel (tq_decode_mfma_impl.h) is instantiated by tq_decode_mfma_inst.hip.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -296,11 +296,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   hipError_t e;
   const int w = a.waves;
   if (a.d == 128)
-    e = a.qjl ? launch_decode_split_d128_q1(p, a.kb, a.vb, w, grid, st)
-              : launch_decode_split_d128_q0(p, a.kb, a.vb, w, grid, st);
+    e = a.qjl ? launch_decode_split<128, 1>(p, a.kb, a.vb, w, grid, st)
+              : launch_decode_split<128, 0>(p, a.kb, a.vb, w, grid, st);
   else
-    e = a.qjl ? launch_decode_split_d256_q1(p, a.kb, a.vb, w, grid, st)
-              : launch_decode_split_d256_q0(p, a.kb, a.vb, w, grid, st);
+    e = a.qjl ? launch_decode_split<256, 1>(p, a.kb, a.vb, w, grid, st)
+              : launch_decode_split<256, 0>(p, a.kb, a.vb, w, grid, st);
   if (e != hipSuccess) return e;
   // Many query rows: 4 per block (R read a quarter as often; C4's 16384 rows,
   // -1.5%).  Fewer than 2048: one per block, which keeps more blocks in flight

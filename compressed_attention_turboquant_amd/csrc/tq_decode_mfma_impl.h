@@ -1,8 +1,8 @@
 #pragma once
 // Decode attention on the compressed cache with the matrix cores (gfx950):
-// the split kernel and its device helpers.  Included by the files that
-// instantiate it (tq_decode_mfma_d*.hip), one head dimension and key kind each,
-// so that they compile in parallel.
+// the split kernel and its device helpers.  Included by tq_decode_mfma_inst.hip,
+// which the build compiles once per head dimension and key kind, so that the
+// instantiations compile in parallel.
 //
 // What is computed is the asymmetric estimator and softmax of [cuTile]
 // listing (asymmetric score estimator; fused attention function with online
@@ -72,6 +72,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kSlack = 4.f;            // log2 headroom of the lazily updated maximum
 constexpr float kInvSlack = 1.f / 16.f;  // 2^-kSlack
+// The P.V operand p * ||v|| * vsc is kept below 2^15 (fp16 holds up to 65504):
+// with p <= 2^kSlack that needs ||v|| * vsc <= 2^kVExp.
+constexpr int kVExp = 11;
 
 template <int I, int N, class F>
 __device__ __forceinline__ void sfor(F&& f) {
@@ -295,6 +298,7 @@ struct WaveState {
   h8 Ak[S::KBLK], As[QJL ? S::KBLK : 1];
   f4 acc[S::CB];
   float m[NR], msafe[NR], lsum[NR];
+  float vsc, vlim;  // value-norm factor of the P operand (a power of two) and 2^kVExp / vsc
   float ca[NR], c2[NR], c0[NR];
   int limit[NR];
   int64_t srow[NR];
@@ -404,14 +408,34 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
       ws.msafe[j] = mnew == -INFINITY ? 0.f : mnew;
     }
   }
+  // The value norms enter the fp16 P operand scaled by vsc.  It starts at
+  // 2^-kSlack; a block whose largest norm exceeds vlim lowers it to the power of
+  // two that brings that norm below 2^kVExp, and the accumulators are scaled by
+  // the same exact factor (every term of the sum keeps one common scale).  The
+  // block maximum is the same in every 16-lane group (they hold the same keys).
+  {
+    const float vl = fmaxf(cur.vn[0], cur.vn[1]);
+    if (__any(vl > ws.vlim)) {
+      float vm = vl;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) vm = fmaxf(vm, __shfl_xor(vm, o));
+      int e = 0;
+      frexpf(vm, &e);  // vm < 2^e
+      const float nsc = fminf(ws.vsc, ldexpf(1.f, kVExp - e));
+      const float ratio = nsc / ws.vsc;
+#pragma unroll
+      for (int i = 0; i < S::CB; ++i) ws.acc[i] *= ratio;
+      ws.vsc = nsc;
+      ws.vlim = ldexpf(1.f, kVExp) / nsc;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
     // v_exp_f32 directly: weights below 2^-126 of the running maximum become 0.
     const float p0 = __builtin_amdgcn_exp2f(st[j][0] - ws.msafe[j]);
     const float p1 = __builtin_amdgcn_exp2f(st[j][1] - ws.msafe[j]);
     ws.lsum[j] += p0 + p1;
-    // P carries 2^-kSlack so p * ||v|| keeps the fp16 range of ||v||.
-    const float q0 = p0 * cur.vn[0] * kInvSlack, q1 = p1 * cur.vn[1] * kInvSlack;
+    const float q0 = p0 * cur.vn[0] * ws.vsc, q1 = p1 * cur.vn[1] * ws.vsc;
     const _Float16 h0 = (_Float16)q0, h1 = (_Float16)q1;
     const int qr = NR * g4 + j;
     pb[0][qr][l16] = h0;
@@ -707,6 +731,8 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   }
 #pragma unroll
   for (int i = 0; i < S::CB; ++i) ws.acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+  ws.vsc = kInvSlack;
+  ws.vlim = ldexpf(1.f, kVExp) / kInvSlack;
 
   // Three register sets rotate so two blocks are in flight while one is used
   // (d = 256: two sets, one block in flight).  The prefetches are
@@ -736,7 +762,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
 
   // Merge the waves of this workgroup.
   __syncthreads();  // mrg_acc shares its memory with the set-up's rotation buffer
-  const float inv_sv = 16.f / scale_v;  // undoes 2^-kSlack and the fp16 table factor
+  const float inv_sv = 1.f / (ws.vsc * scale_v);  // undoes the value-norm and fp16 table factors
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
     float lsum = ws.lsum[j];

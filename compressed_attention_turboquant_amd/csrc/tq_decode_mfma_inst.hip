@@ -1,6 +1,12 @@
-// Decode split kernel instantiations for head dimension 128, keys with QJL
-// signs: every (key bits, value bits, scores output, rows per group).
+// Decode split kernel instantiations for one head dimension and key kind:
+// every (key bits, value bits, scores output, rows per group).  The build
+// compiles this file once per (TQ_INST_D, TQ_INST_QJL) pair -- (128, 0),
+// (128, 1), (256, 0), (256, 1) -- so that the four sets compile in parallel.
 #include "tq_decode_mfma_impl.h"
+
+#if !defined(TQ_INST_D) || !defined(TQ_INST_QJL)
+#error "compile with -DTQ_INST_D=<128|256> -DTQ_INST_QJL=<0|1>"
+#endif
 
 namespace tq {
 namespace {
@@ -37,13 +43,14 @@ hipError_t dispatch_vb(const DecodeMfmaParams& p, int vb, int waves, dim3 grid, 
 
 }  // namespace
 
-hipError_t launch_decode_split_d128_q1(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid,
-                                       hipStream_t st) {
+template <>
+hipError_t launch_decode_split<TQ_INST_D, TQ_INST_QJL>(const DecodeMfmaParams& p, int kb, int vb, int waves,
+                                                       dim3 grid, hipStream_t st) {
   switch (kb) {
-    case 1: return dispatch_vb<128, 1, 1>(p, vb, waves, grid, st);
-    case 2: return dispatch_vb<128, 2, 1>(p, vb, waves, grid, st);
-    case 3: return dispatch_vb<128, 3, 1>(p, vb, waves, grid, st);
-    default: return dispatch_vb<128, 4, 1>(p, vb, waves, grid, st);
+    case 1: return dispatch_vb<TQ_INST_D, 1, TQ_INST_QJL>(p, vb, waves, grid, st);
+    case 2: return dispatch_vb<TQ_INST_D, 2, TQ_INST_QJL>(p, vb, waves, grid, st);
+    case 3: return dispatch_vb<TQ_INST_D, 3, TQ_INST_QJL>(p, vb, waves, grid, st);
+    default: return dispatch_vb<TQ_INST_D, 4, TQ_INST_QJL>(p, vb, waves, grid, st);
   }
 }
 

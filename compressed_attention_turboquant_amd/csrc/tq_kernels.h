@@ -88,15 +88,10 @@ bool fwht_quantize_supports(int d, int rot, int qjl);
 hipError_t launch_quantize_fwht(const QuantizeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 bool mfma_decode_supports(int d, int rows);
-// The split kernel for one head dimension and key kind (tq_decode_mfma_d*.hip).
-hipError_t launch_decode_split_d128_q0(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid,
-                                       hipStream_t st);
-hipError_t launch_decode_split_d128_q1(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid,
-                                       hipStream_t st);
-hipError_t launch_decode_split_d256_q0(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid,
-                                       hipStream_t st);
-hipError_t launch_decode_split_d256_q1(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid,
-                                       hipStream_t st);
+// The split kernel for one head dimension and key kind; each (D, QJL) pair is
+// instantiated by its own compilation of tq_decode_mfma_inst.hip.
+template <int D, int QJL>
+hipError_t launch_decode_split(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid, hipStream_t st);
 // Query rows one decode workgroup serves (4, or 8 when a KV head has more than
 // 4 query rows: the matrix-core rows then carry 8 query rows x {hi, lo}).
 inline int decode_rows_per_group(int rows_per_head) { return rows_per_head > 4 ? 8 : 4; }

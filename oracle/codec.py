@@ -39,9 +39,10 @@ KAPPA_NUM = math.sqrt(math.pi / 2.0)      # QJL correction sqrt(pi/2); divided b
 def encode_rows(x, R, centroids, boundaries, S=None) -> dict:
     """Encode rows of x [rows, d].  Returns unpacked fields plus diagnostics.
 
-    idx [rows, d] int64; norm [rows] fp64; y [rows, d] the rotated unit
-    vectors (to locate coordinates near a boundary); with S: sign [rows, d]
-    bool (True means +1), rnorm [rows] fp64 and proj [rows, d] = S r.
+    idx [rows, d] int64; norm [rows] fp64; u [rows, d] the unit rows; y
+    [rows, d] the rotated unit vectors (to locate coordinates near a
+    boundary); with S: sign [rows, d] bool (True means +1), rnorm [rows] fp64
+    and proj [rows, d] = S r (see qjl_stage).
     """
     x = np.asarray(x, dtype=np.float64)
     R = np.asarray(R, dtype=np.float64)
@@ -53,15 +54,25 @@ def encode_rows(x, R, centroids, boundaries, S=None) -> dict:
     u = np.where(norm[:, None] > 0.0, x / safe[:, None], 0.0)
     y = u @ R.T                                   # row form of y = R u
     idx = (y[..., None] > beta).sum(axis=-1)      # #{i : beta_i < y_j}
-    out = {"idx": idx, "norm": norm, "y": y}
+    out = {"idx": idx, "norm": norm, "y": y, "u": u}
     if S is not None:
-        x_mse = c[idx] @ R                        # row form of R^T c[idx]
-        r = u - x_mse
-        proj = r @ np.asarray(S, dtype=np.float64).T
-        out["sign"] = proj >= 0.0
-        out["rnorm"] = np.sqrt(np.sum(r * r, axis=1))
-        out["proj"] = proj
+        out.update(qjl_stage(u, idx, R, c, S))
     return out
+
+
+def qjl_stage(u, idx, R, centroids, S) -> dict:
+    """Stage 2 of [Mobilint], "Two-Stage Approach", for unit rows u [rows, d]
+    whose stage-1 codes are idx: residual r = u - R^T c[idx], gamma = ||r||_2,
+    sign bits sigma_i = sign((S r)_i) with sign(0) = +1.
+
+    Returns sign [rows, d] bool (True means +1), rnorm [rows] and proj = S r
+    [rows, d].  Any codes may be given, so a row can be re-derived from codes
+    other than its nearest-centroid ones."""
+    c = np.asarray(centroids, dtype=np.float64)
+    x_mse = c[np.asarray(idx)] @ np.asarray(R, dtype=np.float64)   # row form of R^T c[idx]
+    r = np.asarray(u, dtype=np.float64) - x_mse
+    proj = r @ np.asarray(S, dtype=np.float64).T
+    return {"sign": proj >= 0.0, "rnorm": np.sqrt(np.sum(r * r, axis=1)), "proj": proj}
 
 
 def reconstruct_mse(idx, norm, R, centroids) -> np.ndarray:

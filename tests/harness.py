@@ -3,8 +3,12 @@ and the fp64 oracle on the same seeded inputs, and compare them at the
 tolerances the method's target states:
   * codes and sign bits bit-exact, except coordinates whose rotated value lies
     within 1e-5 of a boundary (resp. |(S r)_i| < 1e-5), where either adjacent
-    code is accepted; a row with such a code difference has a different
-    residual, so its sign bits and residual norm are not compared;
+    code (either sign) is accepted.  A row whose codes differ inside the band
+    has a different residual: the oracle recomputes its residual, gamma and
+    S r from the GPU's codes, and its sign bits and gamma are compared with
+    those.  The decode checks then run the oracle on the cache the GPU wrote
+    (its validated codes and signs, the oracle's own norms and gammas), so
+    every key takes part in every score comparison;
   * scores within 1e-4 relative to the score's Cauchy-Schwarz scale
     n_k (||q|| ||c[idx]|| + gamma sqrt(pi/2)/d ||S q||_1) / sqrt(d);
   * attention output within 2e-3 max absolute error.
@@ -63,19 +67,58 @@ def compare_codes(gpu_idx, enc, boundaries, what):
     return diff.any(axis=1)
 
 
-def compare_key_extras(gpu_sign, gpu_rnorm, enc, flipped, what):
-    """Check sign bits (exact outside the band) and residual norms of the rows
-    whose codes matched.  Returns a boolean per row: True where a sign bit
-    differed (legally, inside the band) -- such a key's score differs by
-    gamma sqrt(pi/2)/d * 2 |(S q)_i|, so score comparisons leave it out."""
-    keep = ~flipped
-    sdiff = (gpu_sign != enc["sign"]) & keep[:, None]
-    sband = np.abs(enc["proj"]) < BAND
-    bad = sdiff & ~sband
-    assert not bad.any(), f"{what}: {int(bad.sum())} sign bits differ outside the band"
-    np.testing.assert_allclose(gpu_rnorm[keep], enc["rnorm"][keep], rtol=1e-5, atol=1e-6,
-                               err_msg=f"{what}: residual norms")
-    return sdiff.any(axis=1)
+def check_keys(gpu_idx, gpu_norm, enc, ol, what, gpu_sign=None, gpu_rnorm=None):
+    """Validate the GPU's key fields against the oracle's encoding `enc` of the
+    same rows and return the oracle's view of those keys as decode inputs.
+
+    Codes: exact outside the band (compare_codes).  Norms: within 2e-6.  With
+    QJL, expected signs and gamma come from the oracle's own codes for rows
+    whose codes matched, and from codec.qjl_stage on the GPU's codes for rows
+    whose codes differed inside the band; sign bits must then match outside
+    |(S r)_i| < BAND and gamma within 1e-5 relative.
+
+    Returns (fields, stats): fields = {"idx", "norm"[, "sign", "rnorm"]} per
+    row -- the GPU's codes and signs (validated, so any difference from the
+    oracle's is a legal band choice) and the oracle's fp64 norms and gammas;
+    stats counts rows with a band code difference and with a band sign
+    difference."""
+    flipped = compare_codes(gpu_idx, enc, ol.bk, what + " codes")
+    np.testing.assert_allclose(gpu_norm, enc["norm"], rtol=2e-6, atol=0, err_msg=what + ": norms")
+    fields = {"idx": gpu_idx, "norm": enc["norm"]}
+    stats = {"code_rows": int(flipped.sum()), "sign_rows": 0}
+    if gpu_sign is not None:
+        sign, rnorm, proj = enc["sign"].copy(), enc["rnorm"].copy(), enc["proj"].copy()
+        if flipped.any():
+            redo = codec.qjl_stage(enc["u"][flipped], gpu_idx[flipped], ol.R, ol.ck, ol.S)
+            sign[flipped], rnorm[flipped], proj[flipped] = redo["sign"], redo["rnorm"], redo["proj"]
+        sdiff = gpu_sign != sign
+        bad = sdiff & ~(np.abs(proj) < BAND)
+        assert not bad.any(), f"{what}: {int(bad.sum())} sign bits differ outside the band " \
+                              f"(first at {np.argwhere(bad)[0].tolist()})"
+        np.testing.assert_allclose(gpu_rnorm, rnorm, rtol=1e-5, atol=1e-6, err_msg=what + ": residual norms")
+        fields["sign"] = gpu_sign
+        fields["rnorm"] = rnorm
+        stats["sign_rows"] = int(sdiff.any(axis=1).sum())
+    return fields, stats
+
+
+def check_values(gpu_idx, gpu_norm, enc, ol, what):
+    """Validate the GPU's value codes and norms; return the decode inputs
+    (the GPU's validated codes, the oracle's norms) and the count of rows with
+    a band code difference."""
+    flipped = compare_codes(gpu_idx, enc, ol.bv, what + " codes")
+    np.testing.assert_allclose(gpu_norm, enc["norm"], rtol=2e-6, atol=0, err_msg=what + ": norms")
+    return {"idx": gpu_idx, "norm": enc["norm"]}, int(flipped.sum())
+
+
+def oracle_cache(kf, vf, B, Hkv, N, d):
+    """Decode inputs [B, Hkv, N, ...] from per-row key and value fields."""
+    cache = {"k_idx": kf["idx"].reshape(B, Hkv, N, d), "k_norm": kf["norm"].reshape(B, Hkv, N),
+             "v_idx": vf["idx"].reshape(B, Hkv, N, d), "v_norm": vf["norm"].reshape(B, Hkv, N)}
+    if "sign" in kf:
+        cache["k_sign"] = kf["sign"].reshape(B, Hkv, N, d)
+        cache["k_rnorm"] = kf["rnorm"].reshape(B, Hkv, N)
+    return cache
 
 
 def score_scale(q, R, S, ck, cache, N, G, qjl):
@@ -95,21 +138,23 @@ def score_scale(q, R, S, ck, cache, N, G, qjl):
     return out
 
 
-def compare_scores(gpu, ref, scale, what, key_mask=None):
+def compare_scores(gpu, ref, scale, what):
     finite = np.isfinite(ref)
     assert np.array_equal(finite, np.isfinite(gpu)), f"{what}: mask pattern differs"
     with np.errstate(invalid="ignore"):
         err = np.abs(np.where(finite, gpu - ref, 0.0)) / np.where(finite, scale, 1.0)
-    if key_mask is not None:
-        err = err * key_mask
     worst = float(err.max()) if err.size else 0.0
     assert worst <= SCORE_RTOL, f"{what}: score relative error {worst:.3e} > {SCORE_RTOL}"
     return worst
 
 
-def compare_out(gpu, ref, what):
+def compare_out(gpu, ref, what, scale=1.0):
+    """Max absolute error within OUT_ATOL * scale.  scale is 1 for the
+    workloads' inputs (output coordinates of order one); rows of much larger
+    norm pass their output scale (fp32 cannot hold 2e-3 absolute at 1e4)."""
+    assert np.isfinite(gpu).all(), f"{what}: output not finite"
     err = float(np.abs(gpu - ref).max()) if gpu.size else 0.0
-    assert err <= OUT_ATOL, f"{what}: output max abs error {err:.3e} > {OUT_ATOL}"
+    assert err <= OUT_ATOL * scale, f"{what}: output max abs error {err:.3e} > {OUT_ATOL * scale:.3e}"
     return err
 
 
@@ -156,3 +201,25 @@ def run_quantize_both(cfg, x_np, which, layer=None, olayer=None):
     Sm = olayer.S if (which == B.TQ_KEYS and cfg.k_qjl) else None
     enc = codec.encode_rows(x_np.reshape(-1, d), olayer.R, c, bnd, Sm)
     return layer, olayer, cache, enc, cap
+
+
+def quantize_and_check(cfg, xk, xv, layer=None, ol=None, what=""):
+    """Quantize K and V rows [S, N, d] (host arrays) on the GPU into caches of
+    capacity N rounded up to 8 and in the oracle; validate every GPU field
+    (check_keys, check_values) and return (layer, ol, K, V, cache, stats) with
+    `cache` the oracle's decode inputs [B, Hkv, N, ...] for those keys."""
+    layer = layer or gpu_layer(cfg)
+    ol = ol or OracleLayer(cfg)
+    _, _, K, ek, cap = run_quantize_both(cfg, xk, B.TQ_KEYS, layer, ol)
+    _, _, V, ev, _ = run_quantize_both(cfg, xv, B.TQ_VALUES, layer, ol)
+    S, N, d = xk.shape
+    rows = np.array([s * cap + t for s in range(S) for t in range(N)], dtype=np.int64)
+    kn = K["norm"].cpu().numpy()[rows]
+    if cfg.k_qjl:
+        kf, st = check_keys(gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), kn, ek, ol, what + " K",
+                            gpu_signs(K, S, cap, d, rows), K["rnorm"].cpu().numpy()[rows])
+    else:
+        kf, st = check_keys(gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), kn, ek, ol, what + " K")
+    vf, st["value_rows"] = check_values(gpu_codes_value(V, S, cap, d, cfg.v_bits)[rows],
+                                        V["norm"].cpu().numpy()[rows], ev, ol, what + " V")
+    return layer, ol, K, V, oracle_cache(kf, vf, cfg.B, cfg.Hkv, N, d), st

@@ -31,6 +31,10 @@ def _kv(cfg, which, seed=0):
     return x.reshape(cfg.B * cfg.Hkv, cfg.N, cfg.d)
 
 
+def _rows(S, cap, n):
+    return np.array([s * cap + t for s in range(S) for t in range(n)], dtype=np.int64)
+
+
 @pytest.mark.parametrize("name", list(REDUCED))
 def test_quantize_keys_parity(name):
     cfg = REDUCED[name]
@@ -38,20 +42,22 @@ def test_quantize_keys_parity(name):
     x = _kv(cfg, "K")
     S, n, d = x.shape
     layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, B.TQ_KEYS)
-    rows = np.array([s * cap + t for s in range(S) for t in range(n)])
+    rows = _rows(S, cap, n)
     gidx = H.gpu_codes_key(cache, S, cap, d, cfg.k_bits, rows)
-    flipped = H.compare_codes(gidx, enc, ol.bk, f"{name} K codes")
-    assert flipped.mean() < 0.01
-    np.testing.assert_allclose(cache["norm"].cpu().numpy()[rows], enc["norm"], rtol=2e-6)
+    gnorm = cache["norm"].cpu().numpy()[rows]
+    if cfg.k_qjl:
+        gsign = H.gpu_signs(cache, S, cap, d, rows)
+        _, st = H.check_keys(gidx, gnorm, enc, ol, f"{name} K", gsign, cache["rnorm"].cpu().numpy()[rows])
+    else:
+        _, st = H.check_keys(gidx, gnorm, enc, ol, f"{name} K")
+    assert st["code_rows"] < 0.01 * len(rows)
     # packed bytes are identical for every row without a band difference
+    flipped = (gidx != enc["idx"]).any(axis=1)
     rb = d * cfg.k_bits // 8
     gbytes = cache["idx"].cpu().numpy().reshape(S * cap, rb)[rows]
     obytes = codec.pack_key_codes(enc["idx"], cfg.k_bits)
     assert np.array_equal(gbytes[~flipped], obytes[~flipped])
-    if cfg.k_qjl:
-        gs = H.gpu_signs(cache, S, cap, d, rows)
-        H.compare_key_extras(gs, cache["rnorm"].cpu().numpy()[rows], enc, flipped, f"{name} K")
-    H.log(f"  rows={len(rows)} band-flipped rows={int(flipped.sum())}")
+    H.log(f"  rows={len(rows)} band-flipped code rows={st['code_rows']} sign rows={st['sign_rows']}")
 
 
 @pytest.mark.parametrize("name", list(REDUCED))
@@ -61,11 +67,10 @@ def test_quantize_values_parity(name):
     x = _kv(cfg, "V")
     S, n, d = x.shape
     layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, B.TQ_VALUES)
-    rows = np.array([s * cap + t for s in range(S) for t in range(n)])
+    rows = _rows(S, cap, n)
     gidx = H.gpu_codes_value(cache, S, cap, d, cfg.v_bits)[rows]
-    flipped = H.compare_codes(gidx, enc, ol.bv, f"{name} V codes")
-    assert flipped.mean() < 0.01
-    np.testing.assert_allclose(cache["norm"].cpu().numpy()[rows], enc["norm"], rtol=2e-6)
+    _, flips = H.check_values(gidx, cache["norm"].cpu().numpy()[rows], enc, ol, f"{name} V")
+    assert flips < 0.01 * len(rows)
 
 
 def _decode_both(cfg, packed, q_np, N, want_scores=True):
@@ -181,43 +186,176 @@ def test_decode_eight_wave_workgroups():
     H.log(f"  out abs err {err:.2e}")
 
 
-@pytest.mark.parametrize("name", list(REDUCED))
-def test_end_to_end_from_raw_inputs(name):
+def _end_to_end(cfg, what, seed=2, out_scale=1.0):
     """Quantize K and V and decode on the GPU; the oracle encodes the same raw
-    inputs itself.  Keys whose code or sign bit differs inside the boundary band are left
-    out of the score comparison; the output must still be within 2e-3."""
-    cfg = REDUCED[name]
-    H.log(f"[end to end] {name}")
-    xk, xv = _kv(cfg, "K", seed=2), _kv(cfg, "V", seed=2)
-    S, N, d = xk.shape
-    layer = H.gpu_layer(cfg)
-    ol = H.OracleLayer(cfg)
-    _, _, K, ek, cap = H.run_quantize_both(cfg, xk, B.TQ_KEYS, layer, ol)
-    _, _, V, ev, _ = H.run_quantize_both(cfg, xv, B.TQ_VALUES, layer, ol)
-    rows = np.array([s * cap + t for s in range(S) for t in range(N)])
-    kflip = H.compare_codes(H.gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), ek, ol.bk, "K")
-    if cfg.k_qjl:
-        kflip = kflip | H.compare_key_extras(H.gpu_signs(K, S, cap, d, rows), K["rnorm"].cpu().numpy()[rows],
-                                             ek, kflip, "K")
-    q_np = workloads.q_numpy(cfg, seed=2)
-    q = torch.from_numpy(q_np).cuda()
-    out, scores = B.attn_decode(layer, q, K, V, N, cfg.Hkv, cfg.causal, want_scores=True)
+    inputs itself, validates every GPU field and decodes the cache the GPU
+    wrote (its codes and signs, the oracle's norms and gammas); every score
+    and output is compared."""
+    xk, xv = _kv(cfg, "K", seed=seed), _kv(cfg, "V", seed=seed)
+    return _decode_check(cfg, xk, xv, workloads.q_numpy(cfg, seed=seed), what, out_scale)
+
+
+def _decode_check(cfg, xk, xv, q_np, what, out_scale=1.0):
+    N = xk.shape[1]
+    layer, ol, K, V, cache, st = H.quantize_and_check(cfg, xk, xv, what=what)
+    out, scores = B.attn_decode(layer, torch.from_numpy(q_np).cuda(), K, V, N, cfg.Hkv, cfg.causal,
+                                want_scores=True)
     torch.cuda.synchronize()
-    pk = {"k_idx": codec.pack_key_codes(ek["idx"], cfg.k_bits),
-          "k_norm": ek["norm"].astype(np.float32),
-          "v_idx": codec.pack_value_codes(ev["idx"].reshape(S, N, d), cfg.v_bits) if N % 8 == 0 else None}
-    cache = {"k_idx": ek["idx"].reshape(cfg.B, cfg.Hkv, N, d), "k_norm": ek["norm"].reshape(cfg.B, cfg.Hkv, N),
-             "v_idx": ev["idx"].reshape(cfg.B, cfg.Hkv, N, d), "v_norm": ev["norm"].reshape(cfg.B, cfg.Hkv, N)}
-    if cfg.k_qjl:
-        cache["k_sign"] = ek["sign"].reshape(cfg.B, cfg.Hkv, N, d)
-        cache["k_rnorm"] = ek["rnorm"].reshape(cfg.B, cfg.Hkv, N)
     ref_out, ref_scores = attention.decode(q_np, ol.R, ol.S, ol.ck, ol.cv, cache, N, cfg.causal)
     scale = H.score_scale(q_np, ol.R, ol.S, ol.ck, cache, N, cfg.G, cfg.k_qjl)
-    keep = (~kflip).reshape(cfg.B, cfg.Hkv, N)
-    key_mask = np.repeat(keep, cfg.G, axis=1)[:, :, None, :]
-    rel = H.compare_scores(scores.cpu().numpy(), ref_scores, scale, name, key_mask)
-    err = H.compare_out(out.cpu().numpy(), ref_out, name)
-    H.log(f"  flipped keys {int(kflip.sum())}  score rel {rel:.2e}  out abs {err:.2e}")
+    rel = H.compare_scores(scores.cpu().numpy(), ref_scores, np.maximum(scale, 1e-30), what)
+    err = H.compare_out(out.cpu().numpy(), ref_out, what, out_scale)
+    H.log(f"  band rows: codes K {st['code_rows']} V {st['value_rows']}, signs {st['sign_rows']}; "
+          f"score rel {rel:.2e}  out abs {err:.2e}")
+    return rel, err
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_end_to_end_from_raw_inputs(name):
+    cfg = REDUCED[name]
+    H.log(f"[end to end] {name}")
+    _end_to_end(cfg, name)
+
+
+# Every key width through the matrix-core quantize and decode kernels at
+# d = 128 (Haar, fp16), with and without QJL (MSE-only keys), value widths
+# chosen so that every value width occurs too.
+@pytest.mark.parametrize("qjl", [0, 1])
+@pytest.mark.parametrize("kb", [1, 2, 3, 4])
+def test_key_widths_d128(kb, qjl):
+    cfg = workloads.CONFIGS["C2"].with_(Hq=8, Hkv=2, N=301, k_bits=kb, k_qjl=qjl, v_bits=5 - kb)
+    H.log(f"[key widths d128] k_bits={kb} k_qjl={qjl} v_bits={5 - kb}")
+    _end_to_end(cfg, f"d128 K{kb}{'+QJL' if qjl else ''} V{5 - kb}", seed=8)
+
+
+@pytest.mark.parametrize("qjl", [0, 1])
+@pytest.mark.parametrize("d", [128, 256])
+def test_decode_all_width_pairs(d, qjl):
+    """Decode alone on seeded random caches for all 16 (key bits, value bits)
+    pairs of the matrix-core kernel, with and without QJL keys."""
+    worst = 0.0
+    for kb in (1, 2, 3, 4):
+        for vb in (1, 2, 3, 4):
+            cfg = workloads.CONFIGS["C2"].with_(d=d, Hq=8, Hkv=2, N=211, k_bits=kb, v_bits=vb, k_qjl=qjl)
+            cap = (cfg.N + 7) // 8 * 8
+            packed = workloads.random_packed_numpy(cfg, cfg.B * cfg.Hkv, cap, seed=20 + kb * 4 + vb)
+            q = workloads.q_numpy(cfg, seed=20 + kb * 4 + vb)
+            out, scores, ref_out, ref_scores, cache, ol = _decode_both(cfg, packed, q, cfg.N)
+            scale = H.score_scale(q, ol.R, ol.S, ol.ck, cache, cfg.N, cfg.G, cfg.k_qjl)
+            what = f"d={d} qjl={qjl} K{kb} V{vb}"
+            worst = max(worst, H.compare_scores(scores, ref_scores, scale, what))
+            H.compare_out(out, ref_out, what)
+    H.log(f"[decode width pairs] d={d} qjl={qjl}: worst score rel {worst:.2e}")
+
+
+# Rows with norms far above the fp16 range of the P.V operand: fp32 inputs
+# (reference quantize kernel) and fp16 inputs (matrix-core kernel), keys and
+# values of norm > 1e5.  The outputs are of order max ||v|| / sqrt(d), so the
+# 2e-3 output bound is applied relative to that scale.
+LARGE_NORM_CASES = {
+    "fp32 d128 QJL, |k| ~ 3.4e5, |v| ~ 2.3e5": (workloads.CONFIGS["C1"].with_(N=300, Hq=4, Hkv=2), 3e4, 2e4),
+    "fp16 d128 QJL, |k| ~ 1.1e5, |v| ~ 1.1e5": (workloads.CONFIGS["C2"].with_(Hq=8, Hkv=2, N=300), 1e4, 1e4),
+    "fp16 d256 Hadamard, |v| ~ 1.6e5": (workloads.CONFIGS["C5"].with_(B=1, Hq=8, Hkv=2, N=300, dist="normal"),
+                                        1.0, 1e4),
+}
+
+
+@pytest.mark.parametrize("name", list(LARGE_NORM_CASES))
+def test_large_norms(name):
+    cfg, ks, vs = LARGE_NORM_CASES[name]
+    H.log(f"[large norms] {name}")
+    dt = np.float16 if cfg.dtype == "f16" else np.float32
+    xk = (_kv(cfg, "K", seed=12).astype(np.float64) * ks).astype(dt)
+    xv = (_kv(cfg, "V", seed=12).astype(np.float64) * vs).astype(dt)
+    assert np.isfinite(xk).all() and np.isfinite(xv).all()
+    vmax = float(np.linalg.norm(xv.astype(np.float64), axis=-1).max())
+    assert vmax > 1e5
+    _decode_check(cfg, xk, xv, workloads.q_numpy(cfg, seed=12), name, out_scale=vmax / math.sqrt(cfg.d))
+
+
+def test_decode_random_cache_huge_value_norms():
+    """Value norms from 1 to 1e7 in one sequence (the decode's value scale is
+    lowered as larger norms arrive, mid-loop)."""
+    cfg = workloads.CONFIGS["C3"].with_(B=2, N=1500, dist="normal")
+    cap = (cfg.N + 7) // 8 * 8
+    packed = workloads.random_packed_numpy(cfg, cfg.B * cfg.Hkv, cap, seed=13)
+    ramp = np.logspace(0, 7, cap, dtype=np.float64)
+    packed["v_norm"] = (packed["v_norm"].reshape(-1, cap) * ramp[None, :]).astype(np.float32).reshape(-1)
+    q = workloads.q_numpy(cfg, seed=13)
+    out, scores, ref_out, ref_scores, cache, ol = _decode_both(cfg, packed, q, cfg.N)
+    scale = H.score_scale(q, ol.R, ol.S, ol.ck, cache, cfg.N, cfg.G, cfg.k_qjl)
+    H.compare_scores(scores, ref_scores, scale, "huge value norms")
+    vmax = float(packed["v_norm"].max())
+    err = H.compare_out(out, ref_out, "huge value norms", vmax / math.sqrt(cfg.d))
+    H.log(f"[huge value norms] out abs err {err:.2e} (scale {vmax / math.sqrt(cfg.d):.2e})")
+
+
+# Append one token per step into a preallocated cache and decode after every
+# step ([tq-kv] page: single-key compression appended to a growing compressed
+# cache; [cuTile] listing: decode with one query token over the cache).  The
+# cache starts with a bulk-quantized prefix; the appended tokens cross 8-token
+# value tiles; the capacity exceeds the last length.
+APPEND_LOOP_CASES = {
+    "haar d128 K2+QJL V3": workloads.CONFIGS["C2"].with_(B=2, Hq=8, Hkv=2, N=37),
+    "haar d128 MSE-only K4 V2": workloads.CONFIGS["C2"].with_(B=2, Hq=8, Hkv=2, N=37, k_bits=4, k_qjl=0,
+                                                               v_bits=2),
+    "hadamard d256 K4 V4": workloads.CONFIGS["C5"].with_(B=1, Hq=8, Hkv=2, N=37),
+}
+
+
+@pytest.mark.parametrize("name", list(APPEND_LOOP_CASES))
+def test_append_decode_loop(name):
+    cfg = APPEND_LOOP_CASES[name]
+    steps, cap = 14, 64
+    H.log(f"[append + decode loop] {name}: prefix {cfg.N}, {steps} single-token steps, capacity {cap}")
+    S, d = cfg.B * cfg.Hkv, cfg.d
+    total = cfg.N + steps
+    xk = _kv(cfg.with_(N=total), "K", seed=14)
+    xv = _kv(cfg.with_(N=total), "V", seed=14)
+    q_all = workloads.q_numpy(cfg.with_(Tq=steps), seed=14)       # query of step i: token i
+    layer = H.gpu_layer(cfg)
+    ol = H.OracleLayer(cfg)
+    K = B.Cache(layer, B.TQ_KEYS, S, cap)
+    V = B.Cache(layer, B.TQ_VALUES, S, cap)
+    dk, dv = torch.from_numpy(xk).cuda(), torch.from_numpy(xv).cuda()
+    B.quantize_kv(layer, B.TQ_KEYS, dk[:, :cfg.N].contiguous(), K)
+    B.quantize_kv(layer, B.TQ_VALUES, dv[:, :cfg.N].contiguous(), V)
+    Sk = ol.S if cfg.k_qjl else None
+    ek = codec.encode_rows(xk.reshape(-1, d), ol.R, ol.ck, ol.bk, Sk)
+    ev = codec.encode_rows(xv.reshape(-1, d), ol.R, ol.cv, ol.bv)
+    wsb = max(B.decode_workspace_bytes(layer, cfg.B, cfg.Hq, cfg.Hkv, 1, n) for n in range(cfg.N + 1, total + 1))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    worst_rel, worst_out = 0.0, 0.0
+    for i in range(steps):
+        t = cfg.N + i
+        B.quantize_kv(layer, B.TQ_KEYS, dk[:, t:t + 1].contiguous(), K, t0=t)
+        B.quantize_kv(layer, B.TQ_VALUES, dv[:, t:t + 1].contiguous(), V, t0=t)
+        q_np = np.ascontiguousarray(q_all[:, :, i:i + 1])
+        out, scores = B.attn_decode(layer, torch.from_numpy(q_np).cuda(), K, V, t + 1, cfg.Hkv,
+                                    want_scores=True, workspace=ws)
+        torch.cuda.synchronize()
+        n = t + 1
+        rows = _rows(S, cap, n)
+        orow = np.array([s * total + u for s in range(S) for u in range(n)], dtype=np.int64)
+        sub = lambda e: {k: v[orow] for k, v in e.items()}
+        ekn, evn = sub(ek), sub(ev)
+        if cfg.k_qjl:
+            kf, _ = H.check_keys(H.gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), K["norm"].cpu().numpy()[rows],
+                                 ekn, ol, f"step {i} K", H.gpu_signs(K, S, cap, d, rows),
+                                 K["rnorm"].cpu().numpy()[rows])
+        else:
+            kf, _ = H.check_keys(H.gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), K["norm"].cpu().numpy()[rows],
+                                 ekn, ol, f"step {i} K")
+        vf, _ = H.check_values(H.gpu_codes_value(V, S, cap, d, cfg.v_bits)[rows], V["norm"].cpu().numpy()[rows],
+                               evn, ol, f"step {i} V")
+        cache = H.oracle_cache(kf, vf, cfg.B, cfg.Hkv, n, d)
+        ref_out, ref_scores = attention.decode(q_np, ol.R, ol.S, ol.ck, ol.cv, cache, n, False)
+        scale = H.score_scale(q_np, ol.R, ol.S, ol.ck, cache, n, cfg.G, cfg.k_qjl)
+        worst_rel = max(worst_rel, H.compare_scores(scores.cpu().numpy(), ref_scores, scale, f"step {i}"))
+        worst_out = max(worst_out, H.compare_out(out.cpu().numpy(), ref_out, f"step {i}"))
+    # tokens past the last one were never written
+    assert float(K["norm"].view(S, cap)[:, total:].abs().max()) == 0.0
+    H.log(f"  worst score rel {worst_rel:.2e}, worst out abs {worst_out:.2e}")
 
 
 def _check_dequantize(cfg, which, n_out=None):
@@ -327,30 +465,7 @@ def test_edge_shapes_single_key_zero_rows_and_head_dims():
         H.log(f"[edge] {cfg}")
         xk, xv = _kv(cfg, "K", seed=5), _kv(cfg, "V", seed=5)
         xk[:, 0] = 0  # a zero key row
-        layer = H.gpu_layer(cfg)
-        ol = H.OracleLayer(cfg)
-        _, _, K, ek, cap = H.run_quantize_both(cfg, xk, B.TQ_KEYS, layer, ol)
-        _, _, V, ev, _ = H.run_quantize_both(cfg, xv, B.TQ_VALUES, layer, ol)
-        S, N, d = xk.shape
-        rows = np.array([s * cap + t for s in range(S) for t in range(N)])
-        kflip = H.compare_codes(H.gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), ek, ol.bk, "K")
-        if cfg.k_qjl:
-            kflip = kflip | H.compare_key_extras(H.gpu_signs(K, S, cap, d, rows),
-                                                 K["rnorm"].cpu().numpy()[rows], ek, kflip, "K")
-        assert K["norm"].view(S, cap)[:, 0].abs().max().item() == 0.0
-        q_np = workloads.q_numpy(cfg, seed=5)
-        out, scores = B.attn_decode(layer, torch.from_numpy(q_np).cuda(), K, V, N, cfg.Hkv,
-                                    cfg.causal, want_scores=True)
-        cache = {"k_idx": ek["idx"].reshape(cfg.B, cfg.Hkv, N, d), "k_norm": ek["norm"].reshape(cfg.B, cfg.Hkv, N),
-                 "v_idx": ev["idx"].reshape(cfg.B, cfg.Hkv, N, d), "v_norm": ev["norm"].reshape(cfg.B, cfg.Hkv, N)}
-        if cfg.k_qjl:
-            cache["k_sign"] = ek["sign"].reshape(cfg.B, cfg.Hkv, N, d)
-            cache["k_rnorm"] = ek["rnorm"].reshape(cfg.B, cfg.Hkv, N)
-        ref_out, ref_scores = attention.decode(q_np, ol.R, ol.S, ol.ck, ol.cv, cache, N, cfg.causal)
-        scale = H.score_scale(q_np, ol.R, ol.S, ol.ck, cache, N, cfg.G, cfg.k_qjl)
-        keep = np.repeat((~kflip).reshape(cfg.B, cfg.Hkv, N), cfg.G, axis=1)[:, :, None, :]
-        H.compare_scores(scores.cpu().numpy(), ref_scores, np.maximum(scale, 1e-30), str(cfg), keep)
-        H.compare_out(out.cpu().numpy(), ref_out, str(cfg))
+        rel, err = _decode_check(cfg, xk, xv, workloads.q_numpy(cfg, seed=5), str(cfg))
 
 
 def test_decode_is_deterministic():

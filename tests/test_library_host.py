@@ -175,3 +175,31 @@ def test_product_code_does_not_touch_the_oracle():
         if f.endswith(".py"):
             with open(os.path.join(ROOT, "oracle", f)) as fh:
                 assert "compressed_attention_turboquant_amd" not in fh.read(), f
+
+
+def test_cache_size_limit_is_rejected_before_any_gpu_call(lib):
+    """Each cache array of one sequence is addressed with 32-bit offsets, so
+    cap * d * bits / 8 must stay below 2^31 - 2^20 bytes: at d = 256 with
+    4-bit codes, cap = 2^24 - 2^13 is the largest accepted capacity."""
+    L = _layer(d=256, kb=4, qjl=0, vb=4)
+    out = (ctypes.c_size_t * 4)()
+    ok_cap, bad_cap = (1 << 24) - (1 << 13), 1 << 24
+    assert lib.tq_cache_bytes(ctypes.byref(L), B.TQ_KEYS, 1, ok_cap, out) == B.TQ_OK
+    assert out[0] == ok_cap * 128
+    assert lib.tq_cache_bytes(ctypes.byref(L), B.TQ_KEYS, 1, bad_cap, out) == B.TQ_ERR_UNSUPPORTED
+    assert lib.tq_cache_bytes(ctypes.byref(L), B.TQ_VALUES, 1, bad_cap, out) == B.TQ_ERR_UNSUPPORTED
+    big_k = B.tq_cache(1 << 20, None, 3 << 20, None, 1, bad_cap)
+    big_v = B.tq_cache(5 << 20, None, 6 << 20, None, 1, bad_cap)
+    ws = 1 << 16
+    st = lib.tq_attn_decode(ctypes.byref(L), 4096, 1, 1, 4, 1, 1, 16, 0, ctypes.byref(big_k),
+                            ctypes.byref(big_v), 8192, None, ws, 1 << 30, None)
+    assert st == B.TQ_ERR_UNSUPPORTED and "2^31" in _err(lib)
+    assert lib.tq_quantize_kv(ctypes.byref(L), B.TQ_KEYS, 4096, 1, 1, 8, 0, ctypes.byref(big_k),
+                              None) == B.TQ_ERR_UNSUPPORTED
+    assert lib.tq_dequantize(ctypes.byref(L), B.TQ_VALUES, ctypes.byref(big_v), 8, 4096, 0,
+                             None) == B.TQ_ERR_UNSUPPORTED
+    # d = 128, 3-bit keys: 48 bytes per token allow caps up to 44,717,568.
+    L3 = _layer(d=128, kb=3, qjl=1, vb=3)
+    limit = ((1 << 31) - (1 << 20)) // 48
+    assert lib.tq_cache_bytes(ctypes.byref(L3), B.TQ_KEYS, 1, limit // 8 * 8, out) == B.TQ_OK
+    assert lib.tq_cache_bytes(ctypes.byref(L3), B.TQ_KEYS, 1, limit // 8 * 8 + 8, out) == B.TQ_ERR_UNSUPPORTED
