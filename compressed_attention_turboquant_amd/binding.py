@@ -20,7 +20,9 @@ TQ_KEYS, TQ_VALUES = 0, 1
 
 EXPORTS = ["tq_abi_version", "tq_status_string", "tq_last_error", "tq_layer_blob_bytes",
            "tq_cache_bytes", "tq_make_rotation", "tq_host_tables", "tq_get_codebook",
-           "tq_quantize_kv", "tq_decode_workspace_bytes", "tq_attn_decode", "tq_dequantize"]
+           "tq_quantize_kv", "tq_decode_workspace_bytes", "tq_attn_decode", "tq_attn_decode_static",
+           "tq_dequantize"]
+DECODE_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class tq_layer(ctypes.Structure):
@@ -67,6 +69,7 @@ def load(path: Optional[str] = None):
         "tq_quantize_kv": (i32, [L, i32, vp, i32, i64, i64, i64, C, vp]),
         "tq_decode_workspace_bytes": (sz, [L, i32, i32, i32, i32, i64]),
         "tq_attn_decode": (i32, [L, vp, i32, i32, i32, i32, i32, i64, i32, C, C, vp, vp, vp, sz, vp]),
+        "tq_attn_decode_static": (i32, [L, vp, i32, i32, i32, i32, i32, i64, i32, C, C, vp, vp, vp]),
         "tq_dequantize": (i32, [L, i32, C, i64, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
@@ -192,6 +195,24 @@ def attn_decode(layer: Layer, q, K: Cache, V: Cache, N: int, Hkv: int, causal: i
     check(load().tq_attn_decode(ctypes.byref(layer.c), q.data_ptr(), _dtype_code(q), B, Hq, Hkv, Tq,
                                 N, causal, ctypes.byref(K.c), ctypes.byref(V.c), out.data_ptr(),
                                 _ptr(scores), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out, scores
+
+
+def attn_decode_static(layer: Layer, q, K: Cache, V: Cache, N: int, Hkv: int, causal: int = 0,
+                       want_scores: bool = False, out=None, scores=None, stream=None):
+    """tq_attn_decode_static: as attn_decode, with the library's fixed device
+    scratch instead of a workspace (out and scores are allocated here when not
+    given; the call itself allocates nothing)."""
+    import torch
+    assert q.is_contiguous() and q.dim() == 4 and q.shape[3] == layer.d
+    B, Hq, Tq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, Tq, d), dtype=torch.float32, device=q.device)
+    if want_scores and scores is None:
+        scores = torch.empty((B, Hq, Tq, N), dtype=torch.float32, device=q.device)
+    check(load().tq_attn_decode_static(ctypes.byref(layer.c), q.data_ptr(), _dtype_code(q), B, Hq, Hkv, Tq,
+                                       N, causal, ctypes.byref(K.c), ctypes.byref(V.c), out.data_ptr(),
+                                       _ptr(scores), _stream(stream)))
     return out, scores
 
 

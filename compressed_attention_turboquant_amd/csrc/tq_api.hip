@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -126,6 +127,113 @@ const void* blob_p(const tq_layer* L, size_t off) {
 tq_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return TQ_OK;
   return fail(TQ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Everything tq_attn_decode checks before it looks at the workspace; fills the
+// split plan.  Host only.
+tq_status check_decode(const tq_layer* layer, const void* q, int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                       int32_t Tq, int64_t N, int32_t causal, const tq_cache* K, const tq_cache* V,
+                       const float* out, const float* scores, Plan* plan) {
+  tq_status s = check_layer(layer);
+  if (s != TQ_OK) return s;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARG, "q_dtype must be TQ_F32 or TQ_F16");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1) return fail(TQ_ERR_INVALID_ARG, "B, Hq, Hkv and Tq must be >= 1");
+  if (Hq % Hkv) return fail(TQ_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  if (N < 1) return fail(TQ_ERR_INVALID_ARG, "N must be >= 1");
+  if (causal != 0 && causal != 1) return fail(TQ_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (causal && Tq > N) return fail(TQ_ERR_INVALID_ARG, "causal decode needs Tq <= N");
+  if ((s = check_cache(layer, TQ_KEYS, K, "K")) != TQ_OK) return s;
+  if ((s = check_cache(layer, TQ_VALUES, V, "V")) != TQ_OK) return s;
+  if (K->seqs != (int64_t)B * Hkv || V->seqs != (int64_t)B * Hkv)
+    return fail(TQ_ERR_INVALID_ARG, "K and V must hold B*Hkv sequences");
+  if (K->cap != V->cap) return fail(TQ_ERR_INVALID_ARG, "K and V must have the same capacity");
+  if (N > K->cap) return fail(TQ_ERR_INVALID_ARG, "N exceeds the cache capacity");
+  if (!q || !out) return fail(TQ_ERR_INVALID_ARG, "q and out are required");
+  if (!aligned16(q) || !aligned16(out) || (scores && !aligned16(scores)))
+    return fail(TQ_ERR_ALIGNMENT, "q, out and scores must be 16-byte aligned");
+  const int rows = Hq / Hkv * Tq;
+  if (!mfma_decode_supports(layer->d, rows) && !ref_decode_supports(layer->d, rows))
+    return fail(TQ_ERR_UNSUPPORTED, "(Hq/Hkv)*Tq too large for this head dimension");
+  if ((int64_t)B * Hkv > 0x7FFFFFFF) return fail(TQ_ERR_UNSUPPORTED, "too many sequences");
+  *plan = decode_plan(layer->d, layer->k_qjl, B, Hq, Hkv, Tq, N);
+  if (plan->nsplit > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many key splits");
+  return TQ_OK;
+}
+
+// Enqueues a checked decode call with its workspace at `workspace`.
+tq_status launch_decode(const tq_layer* layer, const void* q, int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                        int32_t Tq, int64_t N, int32_t causal, const tq_cache* K, const tq_cache* V, float* out,
+                        float* scores, const Plan& P, void* workspace, void* stream) {
+  const BlobLayout BL = blob_layout(layer->d);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Tq = Tq;
+  a.N = N;
+  a.cap = K->cap;
+  a.causal = causal;
+  a.d = layer->d;
+  a.kb = layer->k_bits;
+  a.vb = layer->v_bits;
+  a.qjl = layer->k_qjl;
+  a.R = blob_f(layer, BL.rot);
+  a.S = blob_f(layer, BL.proj);
+  a.cb = blob_f(layer, BL.codebook);
+  a.kidx = K->idx;
+  a.ksign = K->sign;
+  a.knorm = K->norm;
+  a.krnorm = K->rnorm;
+  a.vidx = V->idx;
+  a.vnorm = V->norm;
+  a.out = out;
+  a.scores = scores;
+  a.q_rot = reinterpret_cast<float*>(ws + P.off_qrot);
+  a.q_proj = reinterpret_cast<float*>(ws + P.off_qproj);
+  a.part = reinterpret_cast<float*>(ws + P.off_part);
+  a.nsplit = P.nsplit;
+  a.waves = P.waves;
+  a.keys_per_split = P.keys_per_split;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (P.mfma) {
+    DecodeMfmaExtra x{};
+    x.Rt = blob_f(layer, BL.rot_t);
+    x.St = blob_f(layer, BL.proj_t);
+    x.scales = blob_f(layer, BL.scales);
+    return hip_status(launch_decode_mfma(a, x, st), "decode launch");
+  }
+  return hip_status(launch_decode_ref(a, st), "decode launch");
+}
+// Decode scratch of tq_attn_decode_static: a fixed device array, so that the
+// call allocates nothing.  Host code must not use its name as an address (in
+// host code it names a host-side stand-in): the device address is looked up
+// once per device, with that device current, and kept in scratch_ptr.
+constexpr size_t kScratchBytes = TQ_DECODE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device.
+tq_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TQ_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress of the decode scratch");
+    if (!p) return fail(TQ_ERR_HIP, "hipGetSymbolAddress returned no address for the decode scratch");
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return TQ_OK;
 }
 }  // namespace
 
@@ -287,75 +395,29 @@ tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, 
                          int32_t Hq, int32_t Hkv, int32_t Tq, int64_t N, int32_t causal,
                          const tq_cache* K, const tq_cache* V, float* out, float* scores,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  tq_status s = check_layer(layer);
+  Plan P{};
+  tq_status s = check_decode(layer, q, q_dtype, B, Hq, Hkv, Tq, N, causal, K, V, out, scores, &P);
   if (s != TQ_OK) return s;
-  if (q_dtype != TQ_F32 && q_dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARG, "q_dtype must be TQ_F32 or TQ_F16");
-  if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1) return fail(TQ_ERR_INVALID_ARG, "B, Hq, Hkv and Tq must be >= 1");
-  if (Hq % Hkv) return fail(TQ_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
-  if (N < 1) return fail(TQ_ERR_INVALID_ARG, "N must be >= 1");
-  if (causal != 0 && causal != 1) return fail(TQ_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (causal && Tq > N) return fail(TQ_ERR_INVALID_ARG, "causal decode needs Tq <= N");
-  if ((s = check_cache(layer, TQ_KEYS, K, "K")) != TQ_OK) return s;
-  if ((s = check_cache(layer, TQ_VALUES, V, "V")) != TQ_OK) return s;
-  if (K->seqs != (int64_t)B * Hkv || V->seqs != (int64_t)B * Hkv)
-    return fail(TQ_ERR_INVALID_ARG, "K and V must hold B*Hkv sequences");
-  if (K->cap != V->cap) return fail(TQ_ERR_INVALID_ARG, "K and V must have the same capacity");
-  if (N > K->cap) return fail(TQ_ERR_INVALID_ARG, "N exceeds the cache capacity");
-  if (!q || !out) return fail(TQ_ERR_INVALID_ARG, "q and out are required");
-  if (!aligned16(q) || !aligned16(out) || (scores && !aligned16(scores)))
-    return fail(TQ_ERR_ALIGNMENT, "q, out and scores must be 16-byte aligned");
-  const int rows = Hq / Hkv * Tq;
-  if (!mfma_decode_supports(layer->d, rows) && !ref_decode_supports(layer->d, rows))
-    return fail(TQ_ERR_UNSUPPORTED, "(Hq/Hkv)*Tq too large for this head dimension");
-  if ((int64_t)B * Hkv > 0x7FFFFFFF) return fail(TQ_ERR_UNSUPPORTED, "too many sequences");
-  const Plan P = decode_plan(layer->d, layer->k_qjl, B, Hq, Hkv, Tq, N);
-  if (P.nsplit > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many key splits");
   if (!workspace) return fail(TQ_ERR_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)workspace & 255u) != 0) return fail(TQ_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
   if (workspace_bytes < P.total) return fail(TQ_ERR_WORKSPACE, "workspace smaller than tq_decode_workspace_bytes");
+  return launch_decode(layer, q, q_dtype, B, Hq, Hkv, Tq, N, causal, K, V, out, scores, P, workspace, stream);
+}
 
-  const BlobLayout BL = blob_layout(layer->d);
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  DecodeArgs a{};
-  a.q = q;
-  a.q_dtype = q_dtype;
-  a.B = B;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.Tq = Tq;
-  a.N = N;
-  a.cap = K->cap;
-  a.causal = causal;
-  a.d = layer->d;
-  a.kb = layer->k_bits;
-  a.vb = layer->v_bits;
-  a.qjl = layer->k_qjl;
-  a.R = blob_f(layer, BL.rot);
-  a.S = blob_f(layer, BL.proj);
-  a.cb = blob_f(layer, BL.codebook);
-  a.kidx = K->idx;
-  a.ksign = K->sign;
-  a.knorm = K->norm;
-  a.krnorm = K->rnorm;
-  a.vidx = V->idx;
-  a.vnorm = V->norm;
-  a.out = out;
-  a.scores = scores;
-  a.q_rot = reinterpret_cast<float*>(ws + P.off_qrot);
-  a.q_proj = reinterpret_cast<float*>(ws + P.off_qproj);
-  a.part = reinterpret_cast<float*>(ws + P.off_part);
-  a.nsplit = P.nsplit;
-  a.waves = P.waves;
-  a.keys_per_split = P.keys_per_split;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (P.mfma) {
-    DecodeMfmaExtra x{};
-    x.Rt = blob_f(layer, BL.rot_t);
-    x.St = blob_f(layer, BL.proj_t);
-    x.scales = blob_f(layer, BL.scales);
-    return hip_status(launch_decode_mfma(a, x, st), "decode launch");
-  }
-  return hip_status(launch_decode_ref(a, st), "decode launch");
+tq_status tq_attn_decode_static(const tq_layer* layer, const void* q, int32_t q_dtype, int32_t B,
+                                int32_t Hq, int32_t Hkv, int32_t Tq, int64_t N, int32_t causal,
+                                const tq_cache* K, const tq_cache* V, float* out, float* scores,
+                                void* stream) {
+  Plan P{};
+  tq_status s = check_decode(layer, q, q_dtype, B, Hq, Hkv, Tq, N, causal, K, V, out, scores, &P);
+  if (s != TQ_OK) return s;
+  if (P.total > kScratchBytes)
+    return fail(TQ_ERR_WORKSPACE, "this shape needs " + std::to_string(P.total) +
+                                      " bytes of decode scratch; tq_attn_decode_static holds " +
+                                      std::to_string(kScratchBytes) + " (call tq_attn_decode with a workspace)");
+  void* ws = nullptr;
+  if ((s = scratch_for_current_device(&ws)) != TQ_OK) return s;
+  return launch_decode(layer, q, q_dtype, B, Hq, Hkv, Tq, N, causal, K, V, out, scores, P, ws, stream);
 }
 
 tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,

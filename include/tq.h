@@ -174,6 +174,27 @@ tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, 
                          const tq_cache* K, const tq_cache* V, float* out, float* scores,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Maximum decode scratch of tq_attn_decode_static (bytes). */
+#define TQ_DECODE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* tq_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * tq_attn_decode; the split partials go to a fixed 16 MiB device array of the
+ * library instead (TQ_DECODE_STATIC_SCRATCH_BYTES; each GPU the library runs
+ * on holds its own copy until the process ends).  A shape whose
+ * tq_decode_workspace_bytes exceeds that returns TQ_ERR_WORKSPACE with nothing
+ * enqueued.  The first call on a device looks up that device's copy (a host
+ * call, no allocation); no call allocates or frees memory.  Nothing in the
+ * array needs to start at zero: every split writes its partial row before the
+ * merge reads it.  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents, so calls that overlap on one GPU (concurrent
+ * streams, threads) race: the caller must order them. */
+tq_status tq_attn_decode_static(const tq_layer* layer, const void* q, int32_t q_dtype, int32_t B,
+                                int32_t Hq, int32_t Hkv, int32_t Tq, int64_t N, int32_t causal,
+                                const tq_cache* K, const tq_cache* V, float* out, float* scores,
+                                void* stream);
+
 /* Reconstruct tokens 0..n-1 of every sequence: x_hat = n * R^T c[idx]
  * ([cuTile] listing, decompression function).  out is
  * [seqs][n][d] of out_dtype (TQ_F32 or TQ_F16). */

@@ -203,3 +203,21 @@ def test_cache_size_limit_is_rejected_before_any_gpu_call(lib):
     limit = ((1 << 31) - (1 << 20)) // 48
     assert lib.tq_cache_bytes(ctypes.byref(L3), B.TQ_KEYS, 1, limit // 8 * 8, out) == B.TQ_OK
     assert lib.tq_cache_bytes(ctypes.byref(L3), B.TQ_KEYS, 1, limit // 8 * 8 + 8, out) == B.TQ_ERR_UNSUPPORTED
+
+
+def test_static_scratch_decode_rejects_shapes_beyond_its_scratch(lib):
+    """tq_attn_decode_static checks the shape's scratch need against its fixed
+    16 MiB before any GPU call: 32768 query rows of d = 128 need 17.3 MB."""
+    L = _layer(d=128, kb=2, qjl=1, vb=2)
+    Bn, Hq, Hkv, N = 1024, 32, 8, 32
+    need = lib.tq_decode_workspace_bytes(ctypes.byref(L), Bn, Hq, Hkv, 1, N)
+    assert need > B.DECODE_STATIC_SCRATCH_BYTES
+    K = _cache(seqs=Bn * Hkv, cap=32, qjl=True)
+    V = _cache(seqs=Bn * Hkv, cap=32, qjl=False)
+    st = lib.tq_attn_decode_static(ctypes.byref(L), 4096, 1, Bn, Hq, Hkv, 1, N, 0, ctypes.byref(K),
+                                   ctypes.byref(V), 8192, None, None)
+    assert st == B.TQ_ERR_WORKSPACE
+    assert str(need) in _err(lib) and "tq_attn_decode with a workspace" in _err(lib)
+    # argument errors come first, as for tq_attn_decode
+    assert lib.tq_attn_decode_static(ctypes.byref(L), 4096, 1, Bn, 3, Hkv, 1, N, 0, ctypes.byref(K),
+                                     ctypes.byref(V), 8192, None, None) == B.TQ_ERR_INVALID_ARG
