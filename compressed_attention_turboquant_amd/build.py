@@ -14,6 +14,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
+# The streaming-read probe bench.py measures the part's read rate with (not
+# part of the TurboQuant library).
+PROBE_SRC = os.path.join(PKG, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(PKG, "libtqprobe.so")
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -68,8 +72,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, "-x", "hip", "-shared", PROBE_SRC, "-o", tmp] + HIP_FLAGS
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print("built", LIB, file=sys.stderr)
+        print("built", LIB, "and", PROBE_LIB, file=sys.stderr)
     return LIB
 
 

@@ -1,0 +1,76 @@
+// Streaming-read probe: the HBM read rate a plain kernel reaches on this part,
+// the yardstick the decode's packed-KV rate is compared with.  Not part of the
+// TurboQuant path; built into its own library (libtqprobe.so) for bench.py.
+//
+// Every thread reads 16-byte words in a grid-stride loop, four loads in flight,
+// folds them with XOR and stores one word at the end, so that no load can be
+// dropped.  The grid fills every CU with 8 workgroups of 256 threads.  With
+// plain loads the same kernel also serves bench.py as a cache flush: reading
+// 2 GiB of unrelated data leaves none of a workload's cache and no dirty lines
+// in the 256 MB last-level cache.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// NT: non-temporal loads (no allocation in the last-level cache) or plain
+// loads (which evict what the cache held, writing back dirty lines first).
+template <bool NT>
+__device__ __forceinline__ u4 ld(const u4* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+template <bool NT>
+__global__ void __launch_bounds__(256) stream_read_kernel(const u4* __restrict__ src, int64_t words,
+                                                          u4* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < words; i += 4 * stride) {
+    const u4 a = ld<NT>(src + i);
+    const u4 b = ld<NT>(src + i + stride);
+    const u4 c = ld<NT>(src + i + 2 * stride);
+    const u4 d = ld<NT>(src + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < words; i += stride) acc ^= src[i];
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Threads the probe launches (the sink must hold this many 16-byte words).
+int64_t tq_probe_stream_threads(void) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  return (int64_t)cus * 8 * 256;
+}
+
+// Reads `bytes` (a multiple of 16) at device pointer src once, with
+// non-temporal loads if nontemporal != 0, else with plain loads; sink: device
+// memory of tq_probe_stream_threads() * 16 bytes.  Returns a hipError_t.
+int tq_probe_stream_read(const void* src, int64_t bytes, void* sink, int nontemporal, void* stream) {
+  const int64_t threads = tq_probe_stream_threads();
+  const dim3 grid((unsigned)(threads / 256));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const u4* s = static_cast<const u4*>(src);
+  u4* k = static_cast<u4*>(sink);
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_read_kernel<true>, grid, dim3(256), 0, st, s, bytes / 16, k);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, grid, dim3(256), 0, st, s, bytes / 16, k);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"
