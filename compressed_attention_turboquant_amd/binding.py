@@ -17,18 +17,21 @@ TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_ALIGNMENT, TQ_ERR_WORKSPAC
 TQ_ROT_HAAR, TQ_ROT_HADAMARD = 0, 1
 TQ_F32, TQ_F16 = 0, 1
 TQ_KEYS, TQ_VALUES = 0, 1
+TQ_LAW_GAUSSIAN, TQ_LAW_BETA = 0, 1
+TQ_LAYER_BETA_CODEBOOK = 1
 
 EXPORTS = ["tq_abi_version", "tq_status_string", "tq_last_error", "tq_layer_blob_bytes",
-           "tq_cache_bytes", "tq_make_rotation", "tq_host_tables", "tq_get_codebook",
+           "tq_cache_bytes", "tq_make_rotation", "tq_make_layer", "tq_host_tables", "tq_get_codebook",
+           "tq_get_codebook_law",
            "tq_quantize_kv", "tq_decode_workspace_bytes", "tq_attn_decode", "tq_attn_decode_static",
-           "tq_dequantize"]
+           "tq_dequantize", "tq_dequantize_prod"]
 DECODE_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class tq_layer(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("rot", ctypes.c_int32), ("k_bits", ctypes.c_int32),
                 ("k_qjl", ctypes.c_int32), ("v_bits", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("flags", ctypes.c_int32), ("seed", ctypes.c_uint64),
                 ("blob", ctypes.c_void_p), ("blob_bytes", ctypes.c_size_t)]
 
 
@@ -64,13 +67,16 @@ def load(path: Optional[str] = None):
         "tq_layer_blob_bytes": (sz, [i32]),
         "tq_cache_bytes": (i32, [L, i32, i64, i64, ctypes.POINTER(sz)]),
         "tq_make_rotation": (i32, [L, i32, i32, u64, i32, i32, i32, vp, sz, vp]),
+        "tq_make_layer": (i32, [L, i32, i32, u64, i32, i32, i32, i32, vp, sz, vp]),
         "tq_host_tables": (i32, [i32, i32, u64, vp, vp]),
         "tq_get_codebook": (i32, [i32, i32, vp, vp]),
+        "tq_get_codebook_law": (i32, [i32, i32, i32, vp, vp]),
         "tq_quantize_kv": (i32, [L, i32, vp, i32, i64, i64, i64, C, vp]),
         "tq_decode_workspace_bytes": (sz, [L, i32, i32, i32, i32, i64]),
         "tq_attn_decode": (i32, [L, vp, i32, i32, i32, i32, i32, i64, i32, C, C, vp, vp, vp, sz, vp]),
         "tq_attn_decode_static": (i32, [L, vp, i32, i32, i32, i32, i32, i64, i32, C, C, vp, vp, vp]),
         "tq_dequantize": (i32, [L, i32, C, i64, vp, i32, vp]),
+        "tq_dequantize_prod": (i32, [L, i32, C, i64, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -107,11 +113,11 @@ def _dtype_code(t) -> int:
 
 # ---------------------------------------------------------------- host-only --
 
-def get_codebook(d: int, bits: int):
+def get_codebook(d: int, bits: int, law: int = TQ_LAW_GAUSSIAN):
     import numpy as np
     c = np.zeros(1 << bits, np.float32)
     b = np.zeros((1 << bits) - 1, np.float32)
-    check(load().tq_get_codebook(d, bits, c.ctypes.data, b.ctypes.data))
+    check(load().tq_get_codebook_law(d, bits, law, c.ctypes.data, b.ctypes.data))
     return c, b
 
 
@@ -128,21 +134,22 @@ def host_tables(d: int, rot: int, seed: int):
 class Layer:
     """A layer's codec tables on the device (owns the blob tensor)."""
 
-    def __init__(self, d, rot, seed, k_bits, k_qjl, v_bits, device="cuda", stream=None):
+    def __init__(self, d, rot, seed, k_bits, k_qjl, v_bits, device="cuda", stream=None, flags=0):
         import torch
         lib = load()
         self.blob = torch.empty(lib.tq_layer_blob_bytes(d), dtype=torch.uint8, device=device)
         self.c = tq_layer()
-        check(lib.tq_make_rotation(ctypes.byref(self.c), d, rot, seed, k_bits, k_qjl, v_bits,
-                                   self.blob.data_ptr(), self.blob.numel(), _stream(stream)))
+        check(lib.tq_make_layer(ctypes.byref(self.c), d, rot, seed, k_bits, k_qjl, v_bits, flags,
+                                self.blob.data_ptr(), self.blob.numel(), _stream(stream)))
 
     @property
     def d(self):
         return self.c.d
 
 
-def make_rotation(d, rot, seed, k_bits, k_qjl, v_bits, device="cuda", stream=None) -> Layer:
-    return Layer(d, rot, seed, k_bits, k_qjl, v_bits, device, stream)
+def make_rotation(d, rot, seed, k_bits, k_qjl, v_bits, device="cuda", stream=None, flags=0) -> Layer:
+    """tq_make_layer (tq_make_rotation when flags == 0)."""
+    return Layer(d, rot, seed, k_bits, k_qjl, v_bits, device, stream, flags)
 
 
 class Cache:
@@ -216,14 +223,16 @@ def attn_decode_static(layer: Layer, q, K: Cache, V: Cache, N: int, Hkv: int, ca
     return out, scores
 
 
-def dequantize(layer: Layer, which: int, cache: Cache, n: int, out_dtype=None, stream=None, out=None):
-    """tq_dequantize into out ([seqs][n][d], float32 or float16; allocated when
-    not given, of out_dtype, default float32)."""
+def dequantize(layer: Layer, which: int, cache: Cache, n: int, out_dtype=None, stream=None, out=None,
+               prod: bool = False):
+    """tq_dequantize (tq_dequantize_prod with prod=True) into out ([seqs][n][d],
+    float32 or float16; allocated when not given, of out_dtype, default float32)."""
     import torch
     if out is None:
         out = torch.empty((cache.c.seqs, n, layer.d), dtype=out_dtype or torch.float32, device=cache["idx"].device)
     elif tuple(out.shape) != (cache.c.seqs, n, layer.d) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [seqs][n][d] tensor")
-    check(load().tq_dequantize(ctypes.byref(layer.c), which, ctypes.byref(cache.c), n,
-                               out.data_ptr(), _dtype_code(out), _stream(stream)))
+    fn = load().tq_dequantize_prod if prod else load().tq_dequantize
+    check(fn(ctypes.byref(layer.c), which, ctypes.byref(cache.c), n, out.data_ptr(), _dtype_code(out),
+             _stream(stream)))
     return out

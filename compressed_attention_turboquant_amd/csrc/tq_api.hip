@@ -15,6 +15,8 @@ thread_local std::string g_last_error;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+constexpr int32_t kKnownLayerFlags = TQ_LAYER_BETA_CODEBOOK;
+
 // The kernels address one sequence of a cache array through 32-bit byte
 // offsets (buffer descriptors, with a few hundred keys of read-ahead past the
 // last block), so each array of a sequence must stay below 2^31 bytes with
@@ -96,6 +98,7 @@ tq_status check_layer(const tq_layer* L) {
   if (L->k_bits < 1 || L->k_bits > 4 || L->v_bits < 1 || L->v_bits > 4)
     return fail(TQ_ERR_INVALID_ARG, "bit widths must be 1..4");
   if (L->k_qjl != 0 && L->k_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "k_qjl must be 0 or 1");
+  if (L->flags & ~kKnownLayerFlags) return fail(TQ_ERR_INVALID_ARG, "unknown layer flags");
   if (!L->blob) return fail(TQ_ERR_INVALID_ARG, "layer blob is NULL");
   if (L->blob_bytes < blob_layout(L->d).total) return fail(TQ_ERR_INVALID_ARG, "layer blob too small");
   return TQ_OK;
@@ -127,6 +130,55 @@ const void* blob_p(const tq_layer* L, size_t off) {
 tq_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return TQ_OK;
   return fail(TQ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Checks of tq_dequantize (prod: also the QJL fields of tq_dequantize_prod).
+tq_status check_dequantize(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n, const void* out,
+                           int32_t out_dtype, bool prod) {
+  tq_status s = check_layer(layer);
+  if (s != TQ_OK) return s;
+  if (which != TQ_KEYS && which != TQ_VALUES) return fail(TQ_ERR_INVALID_ARG, "which must be TQ_KEYS or TQ_VALUES");
+  if (out_dtype != TQ_F32 && out_dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARG, "out_dtype must be TQ_F32 or TQ_F16");
+  if (!cache || !cache->idx || !cache->norm) return fail(TQ_ERR_INVALID_ARG, "cache idx and norm are required");
+  if (cache->seqs < 0 || cache->cap <= 0 || cache->cap % 8)
+    return fail(TQ_ERR_INVALID_ARG, "cache needs seqs >= 0 and cap a positive multiple of 8");
+  if (!aligned16(cache->idx) || !aligned16(cache->norm)) return fail(TQ_ERR_ALIGNMENT, "cache pointers must be 16-byte aligned");
+  if (prod) {
+    if (which != TQ_KEYS || !layer->k_qjl)
+      return fail(TQ_ERR_INVALID_ARG, "the two-stage reconstruction needs keys of a layer with QJL (k_qjl = 1)");
+    if (!cache->sign || !cache->rnorm) return fail(TQ_ERR_INVALID_ARG, "keys with QJL need sign and rnorm");
+    if (!aligned16(cache->sign) || !aligned16(cache->rnorm))
+      return fail(TQ_ERR_ALIGNMENT, "cache pointers must be 16-byte aligned");
+  }
+  if (n < 0 || n > cache->cap) return fail(TQ_ERR_INVALID_ARG, "n must be in [0, cap]");
+  if (cache->seqs > 65535) return fail(TQ_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+  if (!seq_bytes_ok(layer->d, which == TQ_KEYS ? layer->k_bits : layer->v_bits, cache->cap))
+    return fail(TQ_ERR_UNSUPPORTED, "cap * d * bits / 8 must stay below 2^31 - 2^20 bytes per sequence");
+  if (n > 0 && cache->seqs > 0) {
+    if (!out) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
+    if (!aligned16(out)) return fail(TQ_ERR_ALIGNMENT, "out must be 16-byte aligned");
+  }
+  return TQ_OK;
+}
+
+DequantArgs dequant_args(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n, void* out,
+                         int32_t out_dtype) {
+  const BlobLayout BL = blob_layout(layer->d);
+  DequantArgs a{};
+  a.idx = cache->idx;
+  a.norm = cache->norm;
+  a.seqs = cache->seqs;
+  a.n = n;
+  a.cap = cache->cap;
+  a.d = layer->d;
+  a.bits = which == TQ_KEYS ? layer->k_bits : layer->v_bits;
+  a.value_layout = which == TQ_VALUES;
+  a.R = blob_f(layer, BL.rot);
+  a.Rt = blob_f(layer, BL.rot_t);
+  a.cent = blob_f(layer, BL.codebook) + (which == TQ_KEYS ? 0 : 2 * kMaxLevels);
+  a.out = out;
+  a.out_dtype = out_dtype;
+  return a;
 }
 
 // Everything tq_attn_decode checks before it looks at the workspace; fills the
@@ -294,29 +346,37 @@ tq_status tq_host_tables(int32_t d, int32_t rot, uint64_t seed, double* rotation
   return TQ_OK;
 }
 
-tq_status tq_get_codebook(int32_t d, int32_t bits, float* centroids, float* boundaries) {
+tq_status tq_get_codebook_law(int32_t d, int32_t bits, int32_t law, float* centroids, float* boundaries) {
   if (!supported_d(d)) return fail(TQ_ERR_UNSUPPORTED, "d must be 64, 128 or 256");
   if (bits < 1 || bits > 4) return fail(TQ_ERR_INVALID_ARG, "bits must be 1..4");
+  if (law != TQ_LAW_GAUSSIAN && law != TQ_LAW_BETA) return fail(TQ_ERR_INVALID_ARG, "law must be TQ_LAW_GAUSSIAN or TQ_LAW_BETA");
   if (!centroids || !boundaries) return fail(TQ_ERR_INVALID_ARG, "outputs are required");
-  lloyd_max_codebook(bits, d, centroids, boundaries);
+  if (law == TQ_LAW_BETA)
+    lloyd_max_codebook_beta(bits, d, centroids, boundaries);
+  else
+    lloyd_max_codebook(bits, d, centroids, boundaries);
   return TQ_OK;
 }
 
-tq_status tq_make_rotation(tq_layer* layer, int32_t d, int32_t rot, uint64_t seed, int32_t k_bits,
-                           int32_t k_qjl, int32_t v_bits, void* dev_blob, size_t blob_bytes,
-                           void* stream) {
+tq_status tq_get_codebook(int32_t d, int32_t bits, float* centroids, float* boundaries) {
+  return tq_get_codebook_law(d, bits, TQ_LAW_GAUSSIAN, centroids, boundaries);
+}
+
+tq_status tq_make_layer(tq_layer* layer, int32_t d, int32_t rot, uint64_t seed, int32_t k_bits, int32_t k_qjl,
+                        int32_t v_bits, int32_t flags, void* dev_blob, size_t blob_bytes, void* stream) {
   if (!layer) return fail(TQ_ERR_INVALID_ARG, "layer is NULL");
   if (!supported_d(d)) return fail(TQ_ERR_UNSUPPORTED, "d must be 64, 128 or 256");
   if (rot != TQ_ROT_HAAR && rot != TQ_ROT_HADAMARD) return fail(TQ_ERR_INVALID_ARG, "bad rot");
   if (k_bits < 1 || k_bits > 4 || v_bits < 1 || v_bits > 4)
     return fail(TQ_ERR_INVALID_ARG, "bit widths must be 1..4");
   if (k_qjl != 0 && k_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "k_qjl must be 0 or 1");
+  if (flags & ~kKnownLayerFlags) return fail(TQ_ERR_INVALID_ARG, "unknown layer flags");
   if (!dev_blob) return fail(TQ_ERR_INVALID_ARG, "dev_blob is NULL");
   if (!aligned16(dev_blob)) return fail(TQ_ERR_ALIGNMENT, "dev_blob must be 16-byte aligned");
   const BlobLayout BL = blob_layout(d);
   if (blob_bytes < BL.total) return fail(TQ_ERR_INVALID_ARG, "blob_bytes < tq_layer_blob_bytes(d)");
   std::vector<unsigned char> image(BL.total);
-  build_blob_image(d, rot, seed, k_bits, v_bits, image.data());
+  build_blob_image(d, rot, seed, k_bits, v_bits, flags, image.data());
   hipStream_t st = static_cast<hipStream_t>(stream);
   tq_status s = hip_status(hipMemcpyAsync(dev_blob, image.data(), BL.total, hipMemcpyHostToDevice, st),
                            "copy layer tables");
@@ -328,11 +388,17 @@ tq_status tq_make_rotation(tq_layer* layer, int32_t d, int32_t rot, uint64_t see
   layer->k_bits = k_bits;
   layer->k_qjl = k_qjl;
   layer->v_bits = v_bits;
-  layer->reserved = 0;
+  layer->flags = flags;
   layer->seed = seed;
   layer->blob = dev_blob;
   layer->blob_bytes = blob_bytes;
   return TQ_OK;
+}
+
+tq_status tq_make_rotation(tq_layer* layer, int32_t d, int32_t rot, uint64_t seed, int32_t k_bits,
+                           int32_t k_qjl, int32_t v_bits, void* dev_blob, size_t blob_bytes,
+                           void* stream) {
+  return tq_make_layer(layer, d, rot, seed, k_bits, k_qjl, v_bits, 0, dev_blob, blob_bytes, stream);
 }
 
 tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, int32_t dtype,
@@ -422,38 +488,33 @@ tq_status tq_attn_decode_static(const tq_layer* layer, const void* q, int32_t q_
 
 tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,
                         void* out, int32_t out_dtype, void* stream) {
-  tq_status s = check_layer(layer);
+  tq_status s = check_dequantize(layer, which, cache, n, out, out_dtype, false);
   if (s != TQ_OK) return s;
-  if (which != TQ_KEYS && which != TQ_VALUES) return fail(TQ_ERR_INVALID_ARG, "which must be TQ_KEYS or TQ_VALUES");
-  if (out_dtype != TQ_F32 && out_dtype != TQ_F16) return fail(TQ_ERR_INVALID_ARG, "out_dtype must be TQ_F32 or TQ_F16");
-  if (!cache || !cache->idx || !cache->norm) return fail(TQ_ERR_INVALID_ARG, "cache idx and norm are required");
-  if (cache->seqs < 0 || cache->cap <= 0 || cache->cap % 8)
-    return fail(TQ_ERR_INVALID_ARG, "cache needs seqs >= 0 and cap a positive multiple of 8");
-  if (!aligned16(cache->idx) || !aligned16(cache->norm)) return fail(TQ_ERR_ALIGNMENT, "cache pointers must be 16-byte aligned");
-  if (n < 0 || n > cache->cap) return fail(TQ_ERR_INVALID_ARG, "n must be in [0, cap]");
-  if (cache->seqs > 65535) return fail(TQ_ERR_UNSUPPORTED, "at most 65535 sequences per call");
-  if (!seq_bytes_ok(layer->d, which == TQ_KEYS ? layer->k_bits : layer->v_bits, cache->cap))
-    return fail(TQ_ERR_UNSUPPORTED, "cap * d * bits / 8 must stay below 2^31 - 2^20 bytes per sequence");
-  if (n > 0 && cache->seqs > 0) {
-    if (!out) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
-    if (!aligned16(out)) return fail(TQ_ERR_ALIGNMENT, "out must be 16-byte aligned");
-  }
+  return hip_status(launch_dequant_mfma(dequant_args(layer, which, cache, n, out, out_dtype),
+                                        static_cast<hipStream_t>(stream)),
+                    "dequantize launch");
+}
+
+tq_status tq_dequantize_prod(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,
+                             void* out, int32_t out_dtype, void* stream) {
+  tq_status s = check_dequantize(layer, which, cache, n, out, out_dtype, true);
+  if (s != TQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s = hip_status(launch_dequant_mfma(dequant_args(layer, which, cache, n, out, out_dtype), st), "dequantize launch");
+  if (s != TQ_OK) return s;
   const BlobLayout BL = blob_layout(layer->d);
-  DequantArgs a{};
-  a.idx = cache->idx;
-  a.norm = cache->norm;
-  a.seqs = cache->seqs;
-  a.n = n;
-  a.cap = cache->cap;
-  a.d = layer->d;
-  a.bits = which == TQ_KEYS ? layer->k_bits : layer->v_bits;
-  a.value_layout = which == TQ_VALUES;
-  a.R = blob_f(layer, BL.rot);
-  a.Rt = blob_f(layer, BL.rot_t);
-  a.cent = blob_f(layer, BL.codebook) + (which == TQ_KEYS ? 0 : 2 * kMaxLevels);
-  a.out = out;
-  a.out_dtype = out_dtype;
-  return hip_status(launch_dequant_mfma(a, static_cast<hipStream_t>(stream)), "dequantize launch");
+  DequantQjlArgs q{};
+  q.sign = cache->sign;
+  q.norm = cache->norm;
+  q.rnorm = cache->rnorm;
+  q.seqs = cache->seqs;
+  q.n = n;
+  q.cap = cache->cap;
+  q.d = layer->d;
+  q.St = blob_f(layer, BL.proj_t);
+  q.out = out;
+  q.out_dtype = out_dtype;
+  return hip_status(launch_dequant_qjl(q, st), "dequantize QJL launch");
 }
 
 }  // extern "C"

@@ -243,7 +243,153 @@ hipError_t dispatch_bits(const DequantArgs& a, hipStream_t st) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// QJL term of the two-stage reconstruction ([Mobilint] "Two-Stage Approach",
+// stage 2 and the final reconstruction):
+//   x_hat += n * sqrt(pi/2)/d * gamma * S^T sigma,
+// added to rows that dequant_mfma_kernel has written (the MSE part).
+//
+// Y^T[j][t] = sum_k S^T[j][k] sigma_t[k] runs on v_mfma_f32_16x16x32_f16 with
+// output coordinates as rows and tokens as columns.  The B operand comes
+// straight from the packed sign bits: a half whose only set bit is exponent
+// bit p is 2^(2^(p-10) - 15), so rotating a token's 32 sign bits and masking
+// bits 10+w and 26+w (w = 0..3) gives four dwords of such powers (or 0), one
+// AND each.  The A operand carries S^T times the inverse powers (and 1/8, so
+// that it stays inside the fp16 range), split hi + lo; the product is
+// M = sum over sigma = +1 of S^T / 8, and S^T sigma = 16 M - sum_k S^T[j][k].
+// Lane (row block, k-group g4) of k-block kb covers coordinate
+// 32 kb + ((10 + w + 16 h + 4 g4) mod 32) with its element e = 2 w + h; the
+// four k-groups together cover the block's 32 coordinates.
+constexpr float kSignScale = 0.125f;
+
+__device__ __forceinline__ float sign_power_inverse(int w) {  // 2^(15 - 2^w)
+  return w == 0 ? 16384.f : w == 1 ? 8192.f : w == 2 ? 2048.f : 128.f;
+}
+
+template <int D, int OUT16>
+__global__ void __launch_bounds__(2 * D) dequant_qjl_kernel(DequantQjlArgs a) {
+  constexpr int NKB = D / 32;      // k-blocks, = sign dwords per token
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  const int l16 = lane % 16, g4 = lane / 16;
+
+  // Stationary A operand: rows j = 32 wave + 16 jb + l16 of S^T, and the row
+  // sums the lane's accumulator rows (32 wave + 16 jb + 4 g4 + r) need.
+  h8 shi[2][NKB], slo[2][NKB];
+  float rs[2][4];
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb) {
+    const int row = 32 * wave + 16 * jb + l16;
+    float part = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      h8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e / 2, h = e % 2;
+        const int coord = 32 * kb + ((10 + w + 16 * h + 4 * g4) & 31);
+        const float v = a.St[(size_t)row * D + coord];
+        part += v;
+        const float x = v * kSignScale * sign_power_inverse(w);
+        hi[e] = (_Float16)x;
+        lo[e] = (_Float16)(x - (float)hi[e]);
+      }
+      shi[jb][kb] = hi;
+      slo[jb][kb] = lo;
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rs[jb][r] = __shfl(part, 4 * g4 + r);
+  }
+
+  const float kappa = sqrtf(0.5f * (float)M_PI) / (float)D;
+  const int64_t n = a.n, cap = a.cap;
+  const int64_t tiles = (n + kTile - 1) / kTile;
+  const int64_t items = a.seqs * tiles;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t seq = item / tiles;
+    const int64_t t0 = (item % tiles) * kTile;
+#pragma unroll
+    for (int s = 0; s < kTile / 16; ++s) {
+      if (t0 + 16 * s >= n) break;  // uniform
+      const int64_t tok = t0 + 16 * s + l16;
+      const bool live = tok < n;
+      uint32_t sw[NKB];
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(a.sign + (seq * cap + tok) * (D / 8));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sw[kb] = live ? src[kb] : 0u;
+      const float f = live ? a.norm[seq * cap + tok] * kappa * a.rnorm[seq * cap + tok] : 0.f;
+      f4 acc[2];
+      acc[0] = acc[1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint32_t rot = __builtin_amdgcn_alignbit(sw[kb], sw[kb], 4 * g4);
+        u4 b;
+        sfor<0, 4>([&](auto w) {
+          constexpr int W = decltype(w)::value;
+          b[W] = rot & ((1u << (10 + W)) | (1u << (26 + W)));
+        });
+        const h8 bh = __builtin_bit_cast(h8, b);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi[jb][kb], bh, acc[jb], 0, 0, 0);
+          acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(slo[jb][kb], bh, acc[jb], 0, 0, 0);
+        }
+      }
+      if (live) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          const int64_t o = (seq * n + tok) * D + 32 * wave + 16 * jb + 4 * g4;
+          f4 y;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = f * (acc[jb][r] * (2.f / kSignScale) - rs[jb][r]);
+          if constexpr (OUT16) {
+            u2* dst = reinterpret_cast<u2*>(static_cast<__half*>(a.out) + o);
+            const u2 old = *dst;
+            const uint32_t v0 = old[0], v1 = old[1];
+            const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(v0 & 0xFFFFu)) + y[0];
+            const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(v0 >> 16)) + y[1];
+            const float x2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(v1 & 0xFFFFu)) + y[2];
+            const float x3 = (float)__builtin_bit_cast(_Float16, (uint16_t)(v1 >> 16)) + y[3];
+            *dst = u2{hbits((_Float16)x0) | (hbits((_Float16)x1) << 16), hbits((_Float16)x2) | (hbits((_Float16)x3) << 16)};
+          } else {
+            f4* dst = reinterpret_cast<f4*>(static_cast<float*>(a.out) + o);
+            *dst = *dst + y;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int D, int OUT16>
+hipError_t launch_qjl(const DequantQjlArgs& a, hipStream_t st) {
+  auto kern = dequant_qjl_kernel<D, OUT16>;
+  int dev = 0, cus = 256, per_cu = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 2 * D, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  const int64_t items = a.seqs * ((a.n + kTile - 1) / kTile);
+  const int64_t slots = (int64_t)cus * per_cu;
+  const int64_t grid = items < slots ? items : slots;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(2 * D), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_dequant_qjl(const DequantQjlArgs& a, hipStream_t st) {
+  if (a.n == 0 || a.seqs == 0) return hipSuccess;
+  const bool h = a.out_dtype == TQ_F16;
+  switch (a.d) {
+    case 64: return h ? launch_qjl<64, 1>(a, st) : launch_qjl<64, 0>(a, st);
+    case 128: return h ? launch_qjl<128, 1>(a, st) : launch_qjl<128, 0>(a, st);
+    default: return h ? launch_qjl<256, 1>(a, st) : launch_qjl<256, 0>(a, st);
+  }
+}
 
 hipError_t launch_dequant_mfma(const DequantArgs& a, hipStream_t st) {
   if (a.n == 0 || a.seqs == 0) return hipSuccess;

@@ -160,6 +160,90 @@ void lloyd_max_codebook(int bits, int d, float* centroids, float* boundaries) {
 }
 
 namespace {
+// Nodes x and weights w of the n-point Gauss-Legendre rule on [-1, 1]: the
+// roots of the Legendre polynomial P_n by Newton's method from the usual
+// cosine start, with w_i = 2 / ((1 - x_i^2) P_n'(x_i)^2).
+void gauss_legendre(int n, double* x, double* w) {
+  for (int i = 0; i < n; ++i) {
+    double z = std::cos(M_PI * (i + 0.75) / (n + 0.5));
+    double dp = 1.0;
+    for (int it = 0; it < 100; ++it) {
+      double p0 = 1.0, p1 = z;  // P_0, P_1; recurrence (k+1) P_{k+1} = (2k+1) z P_k - k P_{k-1}
+      for (int k = 1; k < n; ++k) {
+        const double p2 = ((2.0 * k + 1.0) * z * p1 - k * p0) / (k + 1.0);
+        p0 = p1;
+        p1 = p2;
+      }
+      dp = n * (z * p1 - p0) / (z * z - 1.0);  // P_n'(z)
+      const double dz = p1 / dp;
+      z -= dz;
+      if (std::fabs(dz) < 1e-16) break;
+    }
+    x[i] = z;
+    w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+  }
+}
+
+// Integral of (1 - t^2)^a over [lo, hi] (inside [-1, 1]) by composite 16-point
+// Gauss-Legendre (nodes gx, weights gw) on panels no wider than spread / 4; the part beyond `cut`
+// from the origin (where the integrand is below e^-72 of its peak) is left out.
+double beta_kernel_integral(double a, double lo, double hi, double spread, double cut, const double* gx,
+                            const double* gw) {
+  lo = std::fmax(lo, -cut);
+  hi = std::fmin(hi, cut);
+  if (hi <= lo) return 0.0;
+  const int panels = (int)std::ceil((hi - lo) / (spread / 4.0));
+  const double h = (hi - lo) / panels;
+  double total = 0.0;
+  for (int pnl = 0; pnl < panels; ++pnl) {
+    const double mid = lo + (pnl + 0.5) * h;
+    double part = 0.0;
+    for (int i = 0; i < 16; ++i) {
+      const double t = mid + 0.5 * h * gx[i];
+      part += gw[i] * std::pow(1.0 - t * t, a);
+    }
+    total += 0.5 * h * part;
+  }
+  return total;
+}
+}  // namespace
+
+void lloyd_max_codebook_beta(int bits, int d, float* centroids, float* boundaries) {
+  // Exact law of a coordinate of a rotated unit vector: density proportional
+  // to (1 - t^2)^a on [-1, 1], a = (d - 3) / 2.  Lloyd-Max as for the Gaussian:
+  // boundaries at midpoints, centroids the conditional means, here
+  //   E[X | lo < X < hi] = ((1 - lo^2)^(a+1) - (1 - hi^2)^(a+1)) / (2 (a+1) M),
+  //   M = integral of (1 - t^2)^a over [lo, hi] (quadrature).
+  const int L = 1 << bits;
+  const double a = (d - 3) / 2.0;
+  const double spread = 1.0 / std::sqrt((double)d);
+  const double cut = std::fmin(1.0, 12.0 * spread);
+  const double top = std::fmin(2.0 * spread, 1.0 - 1.0 / L);
+  double gx[16], gw[16];
+  gauss_legendre(16, gx, gw);
+  std::vector<double> c(L), nc(L), edge(L + 1);
+  for (int i = 0; i < L; ++i) c[i] = -top + 2.0 * top * i / (L - 1);
+  for (int it = 0; it < 200000; ++it) {
+    edge[0] = -1.0;
+    edge[L] = 1.0;
+    for (int i = 1; i < L; ++i) edge[i] = (c[i - 1] + c[i]) / 2.0;
+    double moved = 0.0;
+    for (int i = 0; i < L; ++i) {
+      const double lo = edge[i], hi = edge[i + 1];
+      const double m1 = (std::pow(1.0 - lo * lo, a + 1.0) - std::pow(1.0 - hi * hi, a + 1.0)) / (2.0 * (a + 1.0));
+      nc[i] = m1 / beta_kernel_integral(a, lo, hi, spread, cut, gx, gw);
+      moved = std::fmax(moved, std::fabs(nc[i] - c[i]));
+    }
+    c.swap(nc);
+    if (moved <= 1e-15) break;
+  }
+  std::vector<double> sym(L);
+  for (int i = 0; i < L; ++i) sym[i] = -(c[L - 1 - i] - c[i]) / 2.0;
+  for (int i = 0; i < L; ++i) centroids[i] = (float)sym[i];
+  for (int i = 0; i + 1 < L; ++i) boundaries[i] = (float)((sym[i] + sym[i + 1]) / 2.0);
+}
+
+namespace {
 // float -> IEEE half, round to nearest even (normal, subnormal and overflow cases).
 uint16_t to_half(float f) {
   uint32_t x;
@@ -247,7 +331,7 @@ float centroid_half_scale(const float* centroids, int levels, float* max_rel_err
   return sf;
 }
 
-void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, unsigned char* image) {
+void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, int flags, unsigned char* image) {
   const BlobLayout L = blob_layout(d);
   std::memset(image, 0, L.total);
   const size_t dd = (size_t)d * d;
@@ -279,8 +363,13 @@ void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, uns
       proj_t[(size_t)j * d + i] = (float)S[(size_t)i * d + j];
     }
   float* cb = reinterpret_cast<float*>(image + L.codebook);
-  lloyd_max_codebook(k_bits, d, cb, cb + kMaxLevels);
-  lloyd_max_codebook(v_bits, d, cb + 2 * kMaxLevels, cb + 3 * kMaxLevels);
+  if (flags & TQ_LAYER_BETA_CODEBOOK) {
+    lloyd_max_codebook_beta(k_bits, d, cb, cb + kMaxLevels);
+    lloyd_max_codebook_beta(v_bits, d, cb + 2 * kMaxLevels, cb + 3 * kMaxLevels);
+  } else {
+    lloyd_max_codebook(k_bits, d, cb, cb + kMaxLevels);
+    lloyd_max_codebook(v_bits, d, cb + 2 * kMaxLevels, cb + 3 * kMaxLevels);
+  }
   float* sc = reinterpret_cast<float*>(image + L.scales);
   sc[0] = centroid_half_scale(cb, 1 << k_bits, &sc[2]);
   sc[1] = centroid_half_scale(cb + 2 * kMaxLevels, 1 << v_bits, &sc[3]);

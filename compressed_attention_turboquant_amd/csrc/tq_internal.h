@@ -64,11 +64,13 @@ void stream_signs(uint64_t seed, uint64_t tag, size_t count, double* out);
 void make_rotation_f64(int d, int rot, uint64_t seed, double* R);
 void make_projection_f64(int d, uint64_t seed, double* S);
 void lloyd_max_codebook(int bits, int d, float* centroids, float* boundaries);
+// The same for the exact coordinate law (1 - t^2)^((d-3)/2) of a rotated unit vector.
+void lloyd_max_codebook_beta(int bits, int d, float* centroids, float* boundaries);
 // Common factor s for a codebook such that every s*c_i rounds to fp16 with the
 // smallest worst-case relative error; returns s and writes that error.
 float centroid_half_scale(const float* centroids, int levels, float* max_rel_err);
 // Fills a host image of the whole blob (layout.total bytes).
-void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, unsigned char* image);
+void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, int flags, unsigned char* image);
 
 // ---- error reporting (tq_api.hip) ----
 tq_status fail(tq_status s, const std::string& msg);

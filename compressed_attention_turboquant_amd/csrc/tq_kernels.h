@@ -46,6 +46,18 @@ struct DequantArgs {
   int out_dtype;
 };
 
+// Arguments of the kernel that adds the QJL term n sqrt(pi/2)/d gamma S^T sigma
+// to dequantized key rows (tq_dequantize_mfma.hip).
+struct DequantQjlArgs {
+  const uint8_t* sign;
+  const float *norm, *rnorm;
+  int64_t seqs, n, cap;
+  int d;
+  const float* St;  // S^T row-major
+  void* out;
+  int out_dtype;
+};
+
 // Arguments of the matrix-core decode split kernel (tq_decode_mfma.hip).
 struct DecodeMfmaParams {
   const void* q;                    // query rows [B][Hq][Tq][d]
@@ -105,6 +117,7 @@ constexpr int decode_simd_waves(int d, int qjl, int rows_per_group) {
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st);
 hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_dequant_mfma(const DequantArgs& a, hipStream_t st);
+hipError_t launch_dequant_qjl(const DequantQjlArgs& a, hipStream_t st);
 bool ref_decode_supports(int d, int rows);
 
 }  // namespace tq

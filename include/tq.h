@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -77,6 +77,11 @@ typedef enum tq_status {
 } tq_status;
 
 enum { TQ_ROT_HAAR = 0, TQ_ROT_HADAMARD = 1 };
+/* Codebook laws: Lloyd-Max for N(0, 1/d), or for the exact law of a rotated
+ * unit vector's coordinate, density proportional to (1 - t^2)^((d-3)/2). */
+enum { TQ_LAW_GAUSSIAN = 0, TQ_LAW_BETA = 1 };
+/* tq_layer.flags */
+enum { TQ_LAYER_BETA_CODEBOOK = 1 };
 enum { TQ_F32 = 0, TQ_F16 = 1 };
 enum { TQ_KEYS = 0, TQ_VALUES = 1 };
 
@@ -87,7 +92,7 @@ typedef struct tq_layer {
   int32_t k_bits;  /* MSE bits per key coordinate, 1..4 */
   int32_t k_qjl;   /* 1: keys also store QJL sign bits and the residual norm */
   int32_t v_bits;  /* MSE bits per value coordinate, 1..4 */
-  int32_t reserved;
+  int32_t flags;   /* TQ_LAYER_* bits; 0 for tq_make_rotation */
   uint64_t seed;   /* seed of the rotation, projection and sign streams */
   void* blob;      /* device: rotation, projection, signs and codebooks */
   size_t blob_bytes;
@@ -131,6 +136,18 @@ tq_status tq_make_rotation(tq_layer* layer, int32_t d, int32_t rot, uint64_t see
                            int32_t k_bits, int32_t k_qjl, int32_t v_bits,
                            void* dev_blob, size_t blob_bytes, void* stream);
 
+/* tq_make_rotation with layer options: `flags` is a combination of
+ *   TQ_LAYER_BETA_CODEBOOK  key and value codebooks are the Lloyd-Max
+ *                           quantizers of the exact coordinate law
+ *                           f(t) ~ (1 - t^2)^((d-3)/2) on [-1, 1] ([Mobilint]
+ *                           "Coordinates Become Predictable After Rotation" and
+ *                           "Designing the Optimal Codebook Without Data": the
+ *                           integrals done numerically) instead of N(0, 1/d).
+ * Unknown flag bits give TQ_ERR_INVALID_ARG. */
+tq_status tq_make_layer(tq_layer* layer, int32_t d, int32_t rot, uint64_t seed, int32_t k_bits,
+                        int32_t k_qjl, int32_t v_bits, int32_t flags, void* dev_blob, size_t blob_bytes,
+                        void* stream);
+
 /* Host-only: the float64 rotation matrix R (Pi or H*D, row-major, y = R u) and
  * projection S (row-major) the layer with this (d, rot, seed) uses.  Either
  * output may be NULL.  No GPU needed. */
@@ -140,6 +157,9 @@ tq_status tq_host_tables(int32_t d, int32_t rot, uint64_t seed, double* rotation
 /* Host-only: the float32 codebook for `bits` at head dimension d: 2^bits sorted
  * centroids and 2^bits-1 sorted boundaries ([cuTile] codebook function). */
 tq_status tq_get_codebook(int32_t d, int32_t bits, float* centroids, float* boundaries);
+
+/* Host-only: tq_get_codebook for a codebook law (TQ_LAW_GAUSSIAN or TQ_LAW_BETA). */
+tq_status tq_get_codebook_law(int32_t d, int32_t bits, int32_t law, float* centroids, float* boundaries);
 
 /* Compress tokens t0..t0+n-1 of every sequence into `cache` ([cuTile] listing,
  * key and value compression functions, values without QJL; [Mobilint]
@@ -200,6 +220,17 @@ tq_status tq_attn_decode_static(const tq_layer* layer, const void* q, int32_t q_
  * [seqs][n][d] of out_dtype (TQ_F32 or TQ_F16). */
 tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,
                         void* out, int32_t out_dtype, void* stream);
+
+/* Two-stage reconstruction of keys with QJL ([Mobilint] "Two-Stage Approach",
+ * final reconstruction): tokens 0..n-1 of every sequence become
+ *   x_hat = n * (R^T c[idx] + sqrt(pi/2)/d * gamma * S^T sigma),
+ * the MSE reconstruction of tq_dequantize plus the QJL back-projection of the
+ * residual's sign bits.  Same arguments as tq_dequantize; `which` must be
+ * TQ_KEYS of a layer with k_qjl = 1 and the cache must hold sign and rnorm
+ * (else TQ_ERR_INVALID_ARG).  Two launches on `stream`: the MSE rows, then
+ * the QJL term added to them in place. */
+tq_status tq_dequantize_prod(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,
+                             void* out, int32_t out_dtype, void* stream);
 
 #ifdef __cplusplus
 }

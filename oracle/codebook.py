@@ -22,6 +22,7 @@ Readings taken here:
 Assigning y to #{i : boundary_i < y} is the nearest-centroid rule the page
 states for the boundary update (ties go to the lower index).
 """
+import functools
 import math
 
 import numpy as np
@@ -58,9 +59,85 @@ def lloyd_max_normal(bits: int, tol: float = 1e-15, max_iter: int = 200000):
     return np.array([-half[i] for i in range(levels)], dtype=np.float64)
 
 
-def codebook(bits: int, d: int):
-    """(centroids float32 [2^b], boundaries float32 [2^b - 1]) for N(0, 1/d)."""
-    c = lloyd_max_normal(bits) / math.sqrt(d)
+@functools.lru_cache(maxsize=None)
+def lloyd_max_beta(bits: int, d: int, tol: float = 1e-15, max_iter: int = 200000):
+    """Centroids (ascending, fp64) of the b-bit Lloyd-Max quantizer of the exact
+    coordinate law of a rotated unit vector ([Mobilint], "Coordinates Become
+    Predictable After Rotation"): f(t) proportional to (1 - t^2)^((d-3)/2) on
+    [-1, 1], i.e. (X + 1) / 2 ~ Beta((d-1)/2, (d-1)/2).
+
+    Same iteration as for the Gaussian ("Designing the Optimal Codebook Without
+    Data": midpoint boundaries, conditional-mean centroids, integrals done
+    numerically): with a = (d-3)/2,
+      P(lo < X < hi)   = I_{(1+hi)/2}(a+1, a+1) - I_{(1+lo)/2}(a+1, a+1)
+                         (regularized incomplete beta, scipy.special.betainc),
+      E[X; lo < X < hi] = ((1-lo^2)^(a+1) - (1-hi^2)^(a+1)) / (2 (a+1) Z),
+      Z = B(1/2, a+1) = the integral of (1 - t^2)^a over [-1, 1].
+    Starts from the Gaussian start scaled to the coordinate spread 1/sqrt(d);
+    stops when no centroid moves by more than tol; then made exactly symmetric.
+    d >= 3."""
+    from scipy import special
+    if d < 3:
+        raise ValueError("the coordinate law needs d >= 3")
+    levels = 1 << bits
+    a = (d - 3) / 2.0
+    Z = special.beta(0.5, a + 1.0)
+    # Evenly spaced start over [-2, 2] standard deviations (1/sqrt(d)), kept
+    # inside the support so that every cell starts with positive mass.
+    top = min(2.0 / math.sqrt(d), 1.0 - 1.0 / levels)
+    c = [-top + 2.0 * top * i / (levels - 1) for i in range(levels)]
+
+    def mass(lo, hi):
+        return float(special.betainc(a + 1.0, a + 1.0, (1.0 + hi) / 2.0)
+                     - special.betainc(a + 1.0, a + 1.0, (1.0 + lo) / 2.0))
+
+    def first_moment(lo, hi):
+        return ((1.0 - lo * lo) ** (a + 1.0) - (1.0 - hi * hi) ** (a + 1.0)) / (2.0 * (a + 1.0) * Z)
+
+    for _ in range(max_iter):
+        edges = [-1.0] + [(c[i] + c[i + 1]) / 2.0 for i in range(levels - 1)] + [1.0]
+        new = [first_moment(edges[i], edges[i + 1]) / mass(edges[i], edges[i + 1]) for i in range(levels)]
+        moved = max(abs(x - y) for x, y in zip(c, new))
+        c = new
+        if moved <= tol:
+            break
+    half = [(c[levels - 1 - i] - c[i]) / 2.0 for i in range(levels)]
+    out = np.array([-half[i] for i in range(levels)], dtype=np.float64)
+    out.setflags(write=False)
+    return out
+
+
+def beta_mse(centroids, d: int) -> float:
+    """Expected squared error of a codebook (in the coordinate's own units) on
+    the exact coordinate law of dimension d: the sum over the nearest-centroid
+    cells of E[X^2; cell] - 2 c_i E[X; cell] + c_i^2 P(cell), each moment by
+    numerical quadrature of (1 - t^2)^((d-3)/2) / Z."""
+    from scipy import integrate, special
+    a = (d - 3) / 2.0
+    Z = special.beta(0.5, a + 1.0)
+    f = lambda t: (1.0 - t * t) ** a / Z
+    c = [float(v) for v in centroids]
+    edges = [-1.0] + [(c[i] + c[i + 1]) / 2.0 for i in range(len(c) - 1)] + [1.0]
+    total = 0.0
+    for i, ci in enumerate(c):
+        lo, hi = edges[i], edges[i + 1]
+        m0 = integrate.quad(f, lo, hi, epsabs=1e-15, epsrel=1e-13, limit=200)[0]
+        m1 = integrate.quad(lambda t: t * f(t), lo, hi, epsabs=1e-15, epsrel=1e-13, limit=200)[0]
+        m2 = integrate.quad(lambda t: t * t * f(t), lo, hi, epsabs=1e-15, epsrel=1e-13, limit=200)[0]
+        total += m2 - 2.0 * ci * m1 + ci * ci * m0
+    return total
+
+
+def codebook(bits: int, d: int, law: str = "gaussian"):
+    """(centroids float32 [2^b], boundaries float32 [2^b - 1]) for the
+    coordinate law: "gaussian" (N(0, 1/d), the default) or "beta" (the exact
+    law of lloyd_max_beta)."""
+    if law == "gaussian":
+        c = lloyd_max_normal(bits) / math.sqrt(d)
+    elif law == "beta":
+        c = lloyd_max_beta(bits, d)
+    else:
+        raise ValueError(law)
     mids = (c[:-1] + c[1:]) / 2.0
     return c.astype(np.float32), mids.astype(np.float32)
 

@@ -35,13 +35,14 @@ class OracleLayer:
     def __init__(self, cfg):
         self.R = transforms.rotation(cfg.d, cfg.rot, cfg.layer_seed)
         self.S = transforms.gaussian_projection(cfg.d, cfg.layer_seed)
-        self.ck, self.bk = codebook.codebook(cfg.k_bits, cfg.d)
-        self.cv, self.bv = codebook.codebook(cfg.v_bits, cfg.d)
+        self.ck, self.bk = codebook.codebook(cfg.k_bits, cfg.d, cfg.codebook)
+        self.cv, self.bv = codebook.codebook(cfg.v_bits, cfg.d, cfg.codebook)
 
 
 def gpu_layer(cfg):
     rot = B.TQ_ROT_HAAR if cfg.rot == "haar" else B.TQ_ROT_HADAMARD
-    return B.make_rotation(cfg.d, rot, cfg.layer_seed, cfg.k_bits, cfg.k_qjl, cfg.v_bits)
+    flags = B.TQ_LAYER_BETA_CODEBOOK if cfg.codebook == "beta" else 0
+    return B.make_rotation(cfg.d, rot, cfg.layer_seed, cfg.k_bits, cfg.k_qjl, cfg.v_bits, flags=flags)
 
 
 def torch_dtype(cfg):

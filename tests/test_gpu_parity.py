@@ -228,6 +228,28 @@ def test_key_widths_d128(kb, qjl):
     _end_to_end(cfg, f"d128 K{kb}{'+QJL' if qjl else ''} V{5 - kb}", seed=8)
 
 
+# Layers whose codebooks are the Lloyd-Max quantizers of the exact coordinate
+# law (1 - t^2)^((d-3)/2) ([Mobilint], "Coordinates Become Predictable After
+# Rotation"): every kernel family reads its codebook from the layer tables.
+BETA_CASES = {
+    "haar d128 fp16 K3+QJL V2 (matrix-core quantize and decode)":
+        workloads.CONFIGS["C2"].with_(Hq=8, Hkv=2, N=301, k_bits=3, v_bits=2, codebook="beta"),
+    "hadamard d256 fp16 K4 V4 (transform quantize)":
+        workloads.CONFIGS["C5"].with_(B=1, Hq=8, Hkv=2, N=301, codebook="beta"),
+    "haar d64 fp32 K2+QJL V3 (scalar kernels)":
+        workloads.CONFIGS["C1"].with_(d=64, Hq=4, Hkv=2, N=301, k_bits=2, v_bits=3, codebook="beta"),
+}
+
+
+@pytest.mark.parametrize("name", list(BETA_CASES))
+def test_beta_codebook_end_to_end(name):
+    cfg = BETA_CASES[name]
+    H.log(f"[exact-law codebook] {name}")
+    _end_to_end(cfg, name, seed=15)
+    # dequantize reconstructs with the same codebook
+    _check_dequantize(cfg, B.TQ_VALUES)
+
+
 @pytest.mark.parametrize("qjl", [0, 1])
 @pytest.mark.parametrize("d", [128, 256])
 def test_decode_all_width_pairs(d, qjl):
@@ -409,6 +431,42 @@ def test_dequantize_shapes(name, which):
     H.log(f"[dequantize] {name} which={which}")
     err = _check_dequantize(cfg, which, n_out)
     H.log(f"  max error / norm {err:.2e}")
+
+
+# Two-stage reconstruction of keys with QJL ([Mobilint] "Two-Stage Approach",
+# final reconstruction): every head dimension and both output dtypes, a prefix
+# of the stored tokens, ragged lengths.
+PROD_CASES = {
+    "haar d128 fp16 K2+QJL": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=203, k_bits=2), None),
+    "haar d128 fp16 K3+QJL, first 100 of 130": (workloads.CONFIGS["C3"].with_(B=1, N=130), 100),
+    "hadamard d256 fp16 K3+QJL": (workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=77, k_qjl=1, k_bits=3), None),
+    "haar d64 fp32 K1+QJL": (workloads.CONFIGS["C1"].with_(d=64, Hq=2, Hkv=2, N=70, k_bits=1), None),
+}
+
+
+@pytest.mark.parametrize("name", list(PROD_CASES))
+def test_dequantize_prod(name):
+    cfg, n_out = PROD_CASES[name]
+    H.log(f"[dequantize prod] {name}")
+    x = _kv(cfg, "K", seed=17)
+    S, n, d = x.shape
+    n_out = n if n_out is None else n_out
+    layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, B.TQ_KEYS)
+    rows = _rows(S, cap, n)
+    kf, st = H.check_keys(H.gpu_codes_key(cache, S, cap, d, cfg.k_bits, rows), cache["norm"].cpu().numpy()[rows],
+                          enc, ol, name, H.gpu_signs(cache, S, cap, d, rows), cache["rnorm"].cpu().numpy()[rows])
+    keep = np.array([s * n + t for s in range(S) for t in range(n_out)], dtype=np.int64)
+    ref = codec.reconstruct_prod(kf["idx"][keep], kf["norm"][keep], kf["sign"][keep], kf["rnorm"][keep],
+                                 ol.R, ol.ck, ol.S)
+    got = B.dequantize(layer, B.TQ_KEYS, cache, n_out, prod=True).cpu().numpy().reshape(-1, d)
+    err = np.abs(got - ref) / np.maximum(kf["norm"][keep][:, None], 1e-30)
+    assert err.max() < 2e-6, f"{name}: error {err.max():.2e} of the norm"
+    # the QJL term is really there: the MSE-only rows differ from these
+    mse = B.dequantize(layer, B.TQ_KEYS, cache, n_out).cpu().numpy().reshape(-1, d)
+    assert (np.abs(mse - got) / kf["norm"][keep][:, None]).max() > 1e-2
+    half = B.dequantize(layer, B.TQ_KEYS, cache, n_out, out_dtype=torch.float16, prod=True).cpu().numpy()
+    np.testing.assert_allclose(half.reshape(-1, d), got, rtol=2e-3, atol=2e-3)
+    H.log(f"  max error / norm {err.max():.2e} (band rows: codes {st['code_rows']}, signs {st['sign_rows']})")
 
 
 APPEND_CASES = {

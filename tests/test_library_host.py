@@ -30,15 +30,16 @@ def test_library_loads_and_exports_every_declared_symbol(lib):
     for name in declared:
         assert hasattr(lib, name), name
     assert set(B.EXPORTS) <= set(declared)
-    assert lib.tq_abi_version() == 1
+    assert lib.tq_abi_version() == 2
 
 
+@pytest.mark.parametrize("law", ["gaussian", "beta"])
 @pytest.mark.parametrize("d", [64, 128, 256])
-def test_codebooks_bit_equal_to_oracle(d):
+def test_codebooks_bit_equal_to_oracle(d, law):
     for bits in (1, 2, 3, 4):
-        c, b = B.get_codebook(d, bits)
-        oc, ob = codebook.codebook(bits, d)
-        assert np.array_equal(c, oc) and np.array_equal(b, ob)
+        c, b = B.get_codebook(d, bits, B.TQ_LAW_BETA if law == "beta" else B.TQ_LAW_GAUSSIAN)
+        oc, ob = codebook.codebook(bits, d, law)
+        assert np.array_equal(c, oc) and np.array_equal(b, ob), (d, bits, law)
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
@@ -81,6 +82,20 @@ def test_make_rotation_rejects_bad_arguments(lib):
     assert "blob_bytes" in _err(lib)
     assert lib.tq_make_rotation(None, 128, 0, 0, 2, 1, 2, 4096, nb, None) == B.TQ_ERR_INVALID_ARG
     assert L.d == 0  # nothing was written on failure
+
+
+def test_layer_flags_and_codebook_law_are_checked(lib):
+    L = B.tq_layer()
+    nb = lib.tq_layer_blob_bytes(128)
+    assert lib.tq_make_layer(ctypes.byref(L), 128, 0, 0, 2, 1, 2, 4, 4096, nb, None) == B.TQ_ERR_INVALID_ARG
+    assert "flags" in _err(lib)
+    c = (ctypes.c_float * 4)()
+    b = (ctypes.c_float * 3)()
+    assert lib.tq_get_codebook_law(128, 2, 2, c, b) == B.TQ_ERR_INVALID_ARG
+    Lf = _layer()
+    Lf.flags = 2
+    K = _cache()
+    assert lib.tq_quantize_kv(ctypes.byref(Lf), 0, 4096, 1, 2, 8, 0, ctypes.byref(K), None) == B.TQ_ERR_INVALID_ARG
 
 
 def test_cache_bytes(lib):
@@ -153,6 +168,19 @@ def test_dequantize_rejects_bad_arguments(lib):
     assert call(out=0) == B.TQ_ERR_INVALID_ARG
     assert call(out=4098) == B.TQ_ERR_ALIGNMENT
     assert call(which=3) == B.TQ_ERR_INVALID_ARG
+
+
+def test_dequantize_prod_needs_keys_with_qjl(lib):
+    """The two-stage reconstruction is defined for keys that carry QJL signs:
+    values, and keys of a layer without QJL, are rejected before any GPU call."""
+    K = _cache()
+    call = lambda L, which, cache: lib.tq_dequantize_prod(ctypes.byref(L), which, ctypes.byref(cache), 8, 4096, 0, None)
+    assert call(_layer(qjl=1), B.TQ_VALUES, _cache(qjl=False)) == B.TQ_ERR_INVALID_ARG
+    assert call(_layer(qjl=0), B.TQ_KEYS, _cache(qjl=False)) == B.TQ_ERR_INVALID_ARG
+    assert "k_qjl" in _err(lib)
+    assert call(_layer(qjl=1), B.TQ_KEYS, _cache(qjl=False)) == B.TQ_ERR_INVALID_ARG
+    assert call(_layer(qjl=1), B.TQ_KEYS, B.tq_cache(1 << 20, (2 << 20) + 4, 3 << 20, 4 << 20, 2, 16)) == \
+        B.TQ_ERR_ALIGNMENT
 
 
 def test_status_strings(lib):

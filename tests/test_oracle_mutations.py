@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as attention
+import oracle.codebook as codebook
 import oracle.codec as codec
 import oracle.transforms as transforms
 from tests import test_oracle_pins as pins
@@ -59,7 +60,13 @@ def _hadamard_signs_after(d, seed):
     return transforms.rademacher_signs(d, seed)[:, None] * transforms.sylvester_hadamard(d)
 
 
-MODULES = {"codec": codec, "transforms": transforms}
+def _beta_wrong_exponent(bits, d, tol=1e-15, max_iter=200000):
+    """The exact-law solver with the exponent (d-1)/2 instead of (d-3)/2."""
+    return _orig_beta.__wrapped__(bits, d + 2, tol, max_iter)
+
+
+_orig_beta = codebook.lloyd_max_beta
+MODULES = {"codec": codec, "transforms": transforms, "codebook": codebook}
 
 
 def _decode_variant(mutation):
@@ -99,6 +106,9 @@ def _decode_variant(mutation):
      [pins.test_slopes_mse_only_biased_qjl_unbiased, pins.test_unbiased_and_variance_bound]),
     ("Hadamard signs applied after the transform", ("transforms", "hadamard_rotation", _hadamard_signs_after),
      [lambda: pins.test_hadamard_applies_signs_before_transform(64)]),
+    ("exact-law exponent (d-1)/2", ("codebook", "lloyd_max_beta", _beta_wrong_exponent),
+     [lambda: pins.test_beta_codebook_one_bit_closed_form(64), lambda: pins.test_beta_codebook_d3_is_the_uniform_quantizer(2),
+      pins.test_beta_codebook_mse_on_rotated_unit_vectors]),
 ])
 def test_planted_codec_mistake_is_caught(monkeypatch, mutation, patch, checks):
     mod, name, fn = patch

@@ -14,6 +14,10 @@ Parity status per oracle function:
   codebook.*            printed 1-/2-bit codebooks and MSEs, Max (1960) table,
                         conditional-mean fixed point by quadrature,
                         Panter-Dite bound, monotone in b.
+  codebook.lloyd_max_beta  d = 3 uniform quantizer, b = 1 closed form,
+                        fixed point by quadrature, optimal against the
+                        Gaussian codebook on its law, tends to the Gaussian
+                        codebook as 1/d, MSE on Haar-rotated unit vectors.
   codec.encode_rows     nearest-centroid brute force, centroid round trip,
                         2/pi bias at b=1, slope 1-D_mse (MSE only) and 1 (QJL),
                         unbiasedness, variance bound.
@@ -226,6 +230,84 @@ def test_mse_bound_and_monotone():
         assert mse.mean() <= PANTER_DITE * 4.0 ** -b
         assert mse.mean() == pytest.approx(exact[b - 1], rel=0.05)
     assert all(means[i + 1] < means[i] for i in range(3))
+
+
+# ------------------------------------------------- exact-law codebook --
+# [Mobilint], "Coordinates Become Predictable After Rotation": a coordinate of
+# a rotated unit vector has density proportional to (1 - t^2)^((d-3)/2); the
+# codebook "Designing the Optimal Codebook Without Data" solves for is the
+# Lloyd-Max quantizer of that law.
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_beta_codebook_d3_is_the_uniform_quantizer(bits):
+    # d = 3: the law is uniform on [-1, 1] (Archimedes), whose Lloyd-Max
+    # quantizer is the uniform one: centroids -1 + (2i + 1) / L.
+    L = 1 << bits
+    c = codebook.lloyd_max_beta(bits, 3)
+    assert np.allclose(c, -1 + (2 * np.arange(L) + 1) / L, atol=1e-13)
+
+
+@pytest.mark.parametrize("d", [16, 64, 128, 256])
+def test_beta_codebook_one_bit_closed_form(d):
+    # E[X | X > 0] = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2)) for the density
+    # Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2)) (1 - t^2)^((d-3)/2) printed there.
+    from scipy import special
+    want = math.exp(special.gammaln(d / 2) - special.gammaln((d + 1) / 2)) / math.sqrt(math.pi)
+    c = codebook.lloyd_max_beta(1, d)
+    assert c[1] == pytest.approx(want, rel=1e-12) and c[0] == -c[1]
+
+
+@pytest.mark.parametrize("d", [16, 128])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_beta_codebook_fixed_point_by_quadrature(d, bits):
+    # Each centroid is the conditional mean of its cell under the printed
+    # density, by numerical integration (not the incomplete beta function the
+    # solver uses).
+    from scipy import special
+    a = (d - 3) / 2
+    norm = math.gamma(d / 2) / (math.sqrt(math.pi) * math.gamma((d - 1) / 2)) if d < 300 else None
+    f = lambda t: norm * (1 - t * t) ** a
+    assert integrate.quad(f, -1, 1)[0] == pytest.approx(1.0, abs=1e-12)
+    c = codebook.lloyd_max_beta(bits, d)
+    edges = [-1.0] + list((c[:-1] + c[1:]) / 2) + [1.0]
+    for i, ci in enumerate(c):
+        m0 = integrate.quad(f, edges[i], edges[i + 1], epsabs=1e-15, epsrel=1e-13, limit=200)[0]
+        m1 = integrate.quad(lambda t: t * f(t), edges[i], edges[i + 1], epsabs=1e-15, epsrel=1e-13, limit=200)[0]
+        assert m1 / m0 == pytest.approx(ci, rel=1e-9, abs=1e-12)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_beta_codebook_beats_gaussian_codebook_on_its_law(bits):
+    # The density is log-concave, so its Lloyd-Max quantizer is the unique
+    # MSE-optimal one: under the exact law it does strictly better than the
+    # N(0, 1/d) codebook, by a small margin at d = 64.
+    d = 64
+    mb = codebook.beta_mse(codebook.lloyd_max_beta(bits, d), d)
+    mg = codebook.beta_mse(codebook.lloyd_max_normal(bits) / math.sqrt(d), d)
+    assert mb < mg < mb * 1.01
+
+
+def test_beta_codebook_tends_to_the_gaussian_one():
+    # "In high dimensions this Beta distribution converges to a Gaussian
+    # N(0,1/d)": sqrt(d) c_beta -> c_gauss, the gap shrinking like 1/d.
+    g = codebook.lloyd_max_normal(3)
+    gap = [np.abs(codebook.lloyd_max_beta(3, d) * math.sqrt(d) - g).max() for d in (64, 256, 1024)]
+    assert gap[0] > gap[1] > gap[2]
+    assert 3.0 < gap[0] / gap[1] < 5.0 and 3.0 < gap[1] / gap[2] < 5.0
+
+
+def test_beta_codebook_mse_on_rotated_unit_vectors():
+    # Monte Carlo on actual Haar rotations of unit vectors at d = 16 (where the
+    # exact law and the Gaussian differ most): the per-coordinate squared error
+    # of the exact-law codebook matches beta_mse within the sampling error.
+    rs = np.random.default_rng(16)
+    d, n = 16, 4000
+    c = codebook.lloyd_max_beta(2, d)
+    beta = (c[:-1] + c[1:]) / 2
+    y = np.concatenate([(_random_rotation(rs, d) @ _unit_rows(rs, 1, d)[0])[None] for _ in range(n)])
+    err = (y - c[codebook.quantize_scalar(y, beta)]) ** 2
+    want = codebook.beta_mse(c, d)
+    assert err.mean() == pytest.approx(want, abs=4 * err.std() / math.sqrt(err.size / 2))
 
 
 # ---------------------------------------------------------------- codec --

@@ -47,6 +47,7 @@ class LayerConfig:
     causal: int
     dist: str           # "normal", "lognormal_channels", "outlier_channels", "student_t5"
     layer_seed: int = 0
+    codebook: str = "gaussian"   # codebook law: "gaussian" (N(0, 1/d)) or "beta" (exact coordinate law)
 
     @property
     def G(self) -> int:
