@@ -34,6 +34,7 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "i
 MULTI = {
     "tq_decode_mfma_inst.hip": [(f"d{d}_q{q}", [f"-DTQ_INST_D={d}", f"-DTQ_INST_QJL={q}"])
                                 for d in (128, 256) for q in (0, 1)],
+    "tq_decode_wide.hip": [(f"q{q}", [f"-DTQ_INST_QJL={q}"]) for q in (0, 1)],
 }
 
 

@@ -27,6 +27,7 @@ bool seq_bytes_ok(int d, int bits, int64_t cap) { return cap <= kSeqBytesMax / (
 
 struct Plan {  // split-K plan of one decode call
   bool mfma;     // matrix-core kernel (else the reference kernels)
+  bool wide;     // the many-rows matrix-core kernel
   int nsplit;
   int waves;     // per workgroup (matrix-core kernel)
   int64_t keys_per_split;
@@ -46,6 +47,22 @@ Plan decode_plan(int d, int qjl, int B, int Hq, int Hkv, int Tq, int64_t N) {
     // each wave at least 4 blocks.  The plan depends on the shape only, so the
     // workspace size does too.
     const int64_t blocks = (N + 31) / 32;
+    if (decode_is_wide(d, Hq / Hkv * Tq)) {
+      // One 4-wave workgroup per CU (each wave holds 32 query rows' operands
+      // and accumulators, one wave per SIMD); split the keys so that the
+      // workgroups fill the 256 CUs once, each split at least 8 blocks.
+      const int64_t groups = seqs * ((Hq / Hkv * Tq + kWideRowsPerGroup - 1) / kWideRowsPerGroup);
+      int64_t want = (256 * kWideGroupsPerCU + groups - 1) / groups;
+      const int64_t max_split = (blocks + 7) / 8;
+      if (want > max_split) want = max_split;
+      if (want > 1024) want = 1024;
+      if (want < 1) want = 1;
+      const int64_t bps = (blocks + want - 1) / want;
+      p.wide = true;
+      p.waves = 4;
+      p.keys_per_split = bps * 32;
+      p.nsplit = (int)((blocks + bps - 1) / bps);
+    } else {
     const int rw = decode_rows_per_group(Hq / Hkv * Tq);
     const int64_t groups = seqs * ((Hq / Hkv * Tq + rw - 1) / rw);
     const int simd_waves = decode_simd_waves(d, qjl, rw);
@@ -69,6 +86,7 @@ Plan decode_plan(int d, int qjl, int B, int Hq, int Hkv, int Tq, int64_t N) {
     split_keys(4);
     if (simd_waves == 2 && rw == 4 && groups <= 256 && groups * p.nsplit >= 512 && p.keys_per_split < 4 * 16 * 32)
       split_keys(8);
+    }
   } else {
     int64_t want = (2048 + seqs - 1) / seqs;
     const int64_t max_split = (N + 63) / 64;
@@ -248,6 +266,7 @@ tq_status launch_decode(const tq_layer* layer, const void* q, int32_t q_dtype, i
   a.part = reinterpret_cast<float*>(ws + P.off_part);
   a.nsplit = P.nsplit;
   a.waves = P.waves;
+  a.wide = P.wide;
   a.keys_per_split = P.keys_per_split;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (P.mfma) {
@@ -255,6 +274,10 @@ tq_status launch_decode(const tq_layer* layer, const void* q, int32_t q_dtype, i
     x.Rt = blob_f(layer, BL.rot_t);
     x.St = blob_f(layer, BL.proj_t);
     x.scales = blob_f(layer, BL.scales);
+    x.rot_hi = blob_p(layer, BL.rot_hi);
+    x.rot_lo = blob_p(layer, BL.rot_lo);
+    x.proj_hi = blob_p(layer, BL.proj_hi);
+    x.proj_lo = blob_p(layer, BL.proj_lo);
     return hip_status(launch_decode_mfma(a, x, st), "decode launch");
   }
   return hip_status(launch_decode_ref(a, st), "decode launch");

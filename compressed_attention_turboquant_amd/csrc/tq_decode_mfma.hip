@@ -255,6 +255,24 @@ constexpr int kFirstShare = 1331;
 
 bool mfma_decode_supports(int d, int rows) { return (d == 128 || d == 256) && rows >= 1; }
 
+namespace {
+// The merge of the splits' partials and the un-rotation.  Many query rows: 4
+// per block (R read a quarter as often; C4's 16384 rows, -1.5%).  Fewer than
+// 2048: one per block, which keeps more blocks in flight for the latency-bound
+// small calls.
+hipError_t launch_combine(const DecodeArgs& a, int64_t qrows, dim3 rgrid, hipStream_t st) {
+  constexpr int kRB = 4;
+  if (a.d == 128 && qrows >= 512 * kRB)
+    hipLaunchKernelGGL(combine_rows128_kernel<kRB>, dim3((unsigned)((qrows + kRB - 1) / kRB)), dim3(256), 0, st,
+                       a.part, a.nsplit, qrows, a.R, a.out);
+  else if (a.d == 128)
+    hipLaunchKernelGGL(combine_kernel<128>, rgrid, dim3(256), 0, st, a.part, a.nsplit, qrows, a.R, a.out);
+  else
+    hipLaunchKernelGGL(combine_kernel<256>, rgrid, dim3(256), 0, st, a.part, a.nsplit, qrows, a.R, a.out);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st) {
   const int64_t qrows = (int64_t)a.B * a.Hq * a.Tq;
   const dim3 rgrid((unsigned)qrows);
@@ -282,6 +300,19 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   p.keys_per_split = a.keys_per_split;
   p.part = a.part;
   p.scores = a.scores;
+  p.rot_hi = x.rot_hi;
+  p.rot_lo = x.rot_lo;
+  p.proj_hi = x.proj_hi;
+  p.proj_lo = x.proj_lo;
+  hipError_t e;
+  if (a.wide) {
+    p.rgroups = (a.Hq / a.Hkv * a.Tq + kWideRowsPerGroup - 1) / kWideRowsPerGroup;
+    p.first_wgs = 0;
+    const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * p.rgroups), (unsigned)a.nsplit);
+    e = a.qjl ? launch_decode_wide<1>(p, a.kb, a.vb, grid, st) : launch_decode_wide<0>(p, a.kb, a.vb, grid, st);
+    if (e != hipSuccess) return e;
+    return launch_combine(a, qrows, rgrid, st);
+  }
   const int rw = decode_rows_per_group(a.Hq / a.Hkv * a.Tq);
   p.rgroups = (a.Hq / a.Hkv * a.Tq + rw - 1) / rw;
   const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * p.rgroups), (unsigned)a.nsplit);
@@ -293,7 +324,6 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
                           (int64_t)grid.x * grid.y == 2 * (int64_t)cus;
   p.first_wgs = two_per_cu ? cus : 0;
   p.first_share = kFirstShare;
-  hipError_t e;
   const int w = a.waves;
   if (a.d == 128)
     e = a.qjl ? launch_decode_split<128, 1>(p, a.kb, a.vb, w, grid, st)
@@ -302,18 +332,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
     e = a.qjl ? launch_decode_split<256, 1>(p, a.kb, a.vb, w, grid, st)
               : launch_decode_split<256, 0>(p, a.kb, a.vb, w, grid, st);
   if (e != hipSuccess) return e;
-  // Many query rows: 4 per block (R read a quarter as often; C4's 16384 rows,
-  // -1.5%).  Fewer than 2048: one per block, which keeps more blocks in flight
-  // for the latency-bound small calls.
-  constexpr int kRB = 4;
-  if (a.d == 128 && qrows >= 512 * kRB)
-    hipLaunchKernelGGL(combine_rows128_kernel<kRB>, dim3((unsigned)((qrows + kRB - 1) / kRB)), dim3(256), 0, st,
-                       a.part, a.nsplit, qrows, a.R, a.out);
-  else if (a.d == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, rgrid, dim3(256), 0, st, a.part, a.nsplit, qrows, a.R, a.out);
-  else
-    hipLaunchKernelGGL(combine_kernel<256>, rgrid, dim3(256), 0, st, a.part, a.nsplit, qrows, a.R, a.out);
-  return hipGetLastError();
+  return launch_combine(a, qrows, rgrid, st);
 }
 
 }  // namespace tq

@@ -377,6 +377,8 @@ void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, int
              reinterpret_cast<uint16_t*>(image + L.rot_lo));
   split_half(SR.data(), dd, 1.0, reinterpret_cast<uint16_t*>(image + L.projr_hi),
              reinterpret_cast<uint16_t*>(image + L.projr_lo));
+  split_half(S.data(), dd, 1.0, reinterpret_cast<uint16_t*>(image + L.proj_hi),
+             reinterpret_cast<uint16_t*>(image + L.proj_lo));
 }
 
 }  // namespace tq

@@ -30,6 +30,8 @@ struct BlobLayout {
   size_t rot_lo;
   size_t projr_hi;  // half [d][d]: S R^T split as hi + lo
   size_t projr_lo;
+  size_t proj_hi;   // half [d][d]: S split as hi + lo (query projection on the matrix cores)
+  size_t proj_lo;
   size_t total;
 };
 
@@ -54,6 +56,8 @@ inline BlobLayout blob_layout(int d) {
   L.rot_lo = o;    o = align_up(o + hmat, 256);
   L.projr_hi = o;  o = align_up(o + hmat, 256);
   L.projr_lo = o;  o = align_up(o + hmat, 256);
+  L.proj_hi = o;   o = align_up(o + hmat, 256);
+  L.proj_lo = o;   o = align_up(o + hmat, 256);
   L.total = o;
   return L;
 }

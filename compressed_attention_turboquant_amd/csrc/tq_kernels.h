@@ -33,6 +33,7 @@ struct DecodeArgs {
   float *q_rot, *q_proj, *part;
   int nsplit;
   int waves;  // waves per decode workgroup (matrix-core kernel)
+  bool wide;  // the many-rows kernel (tq_decode_wide.hip)
   int64_t keys_per_split;
 };
 
@@ -67,6 +68,8 @@ struct DecodeMfmaParams {
   const float *knorm, *krnorm, *vnorm, *cb;
   const float* scales;              // blob: fp16 table factors for key and value centroids
   const float* R;                   // rotation (row-major) for the final un-rotation
+  const void *rot_hi, *rot_lo;      // sqrt(d) R split fp16 hi + lo (query rotation on the matrix cores)
+  const void *proj_hi, *proj_lo;    // S split fp16 hi + lo
   float* out;
   int Hq, Hkv, Tq, causal;
   int rgroups;                      // groups of up to 4 query rows per KV head
@@ -81,6 +84,7 @@ struct DecodeMfmaParams {
 // Blob and workspace pieces the matrix-core decode needs besides DecodeArgs.
 struct DecodeMfmaExtra {
   const float *Rt, *St, *scales;
+  const void *rot_hi, *rot_lo, *proj_hi, *proj_lo;
 };
 
 // Arguments of the matrix-core quantize kernel (tq_quantize_mfma.hip, d = 128, fp16 input).
@@ -107,6 +111,22 @@ hipError_t launch_decode_split(const DecodeMfmaParams& p, int kb, int vb, int wa
 // Query rows one decode workgroup serves (4, or 8 when a KV head has more than
 // 4 query rows: the matrix-core rows then carry 8 query rows x {hi, lo}).
 inline int decode_rows_per_group(int rows_per_head) { return rows_per_head > 4 ? 8 : 4; }
+
+// KV heads with at least this many query rows (at d = 128) use the wide
+// kernel (tq_decode_wide.hip): 4 waves x 16 rows per workgroup (two
+// workgroups per CU), each decoded code serving 16 rows.  (32 rows per wave
+// halve the decoding but need one wave per SIMD: 1037 vs 910 us at C4.)
+constexpr int kWideMinRows = 64;
+#ifndef TQ_WIDE_CT
+#define TQ_WIDE_CT 1
+#endif
+constexpr int kWideCT = TQ_WIDE_CT;             // 16-row column tiles per wave
+constexpr int kWideRowsPerGroup = 64 * kWideCT;  // 4 waves x 16 CT rows
+// Workgroups of the wide kernel one CU holds at once.
+constexpr int kWideGroupsPerCU = 3 - kWideCT;
+inline bool decode_is_wide(int d, int rows_per_head) { return d == 128 && rows_per_head >= kWideMinRows; }
+template <int QJL>
+hipError_t launch_decode_wide(const DecodeMfmaParams& p, int kb, int vb, dim3 grid, hipStream_t st);
 
 // Decode waves one SIMD runs at once: 2, except at d = 256 with QJL keys or row
 // groups of 8, whose register use allows one.

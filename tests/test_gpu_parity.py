@@ -118,6 +118,13 @@ ROW_GROUP_CASES = {
     # 2048 query rows in all: the combine merges 4 rows per block.
     "16 rows x 128 heads (G=4, Tq=4, causal)": workloads.CONFIGS["C3"].with_(B=16, Tq=4, N=203, causal=1,
                                                                              dist="normal"),
+    # 64 and more rows per KV head at d = 128 take the wide kernel (4 waves x 32
+    # rows per workgroup): half a row group, two groups with a partial second
+    # one and MSE-only keys, fp32 queries.
+    "64 rows (G=8, Tq=8, causal): wide kernel, half a group": workloads.CONFIGS["C4"].with_(B=1, Tq=8, N=300),
+    "200 rows (G=8, Tq=25, causal, K3 V4 MSE-only): wide kernel, 2 groups":
+        workloads.CONFIGS["C4"].with_(B=1, Hq=8, Hkv=1, Tq=25, N=333, k_bits=3, v_bits=4, k_qjl=0),
+    "128 rows fp32 (G=16, Tq=8): wide kernel": workloads.CONFIGS["C1"].with_(Hq=16, Hkv=1, Tq=8, N=300),
 }
 
 
@@ -251,23 +258,26 @@ def test_beta_codebook_end_to_end(name):
 
 
 @pytest.mark.parametrize("qjl", [0, 1])
-@pytest.mark.parametrize("d", [128, 256])
-def test_decode_all_width_pairs(d, qjl):
+@pytest.mark.parametrize("d,rows", [(128, 4), (256, 4), (128, 64)])
+def test_decode_all_width_pairs(d, rows, qjl):
     """Decode alone on seeded random caches for all 16 (key bits, value bits)
-    pairs of the matrix-core kernel, with and without QJL keys."""
+    pairs of the matrix-core kernels, with and without QJL keys; 64 query rows
+    per KV head (8 heads x 8 causal tokens) take the wide kernel."""
     worst = 0.0
     for kb in (1, 2, 3, 4):
         for vb in (1, 2, 3, 4):
             cfg = workloads.CONFIGS["C2"].with_(d=d, Hq=8, Hkv=2, N=211, k_bits=kb, v_bits=vb, k_qjl=qjl)
+            if rows == 64:
+                cfg = cfg.with_(Hq=16, Tq=8, causal=1)
             cap = (cfg.N + 7) // 8 * 8
             packed = workloads.random_packed_numpy(cfg, cfg.B * cfg.Hkv, cap, seed=20 + kb * 4 + vb)
             q = workloads.q_numpy(cfg, seed=20 + kb * 4 + vb)
             out, scores, ref_out, ref_scores, cache, ol = _decode_both(cfg, packed, q, cfg.N)
             scale = H.score_scale(q, ol.R, ol.S, ol.ck, cache, cfg.N, cfg.G, cfg.k_qjl)
-            what = f"d={d} qjl={qjl} K{kb} V{vb}"
+            what = f"d={d} rows={rows} qjl={qjl} K{kb} V{vb}"
             worst = max(worst, H.compare_scores(scores, ref_scores, scale, what))
             H.compare_out(out, ref_out, what)
-    H.log(f"[decode width pairs] d={d} qjl={qjl}: worst score rel {worst:.2e}")
+    H.log(f"[decode width pairs] d={d} rows={rows} qjl={qjl}: worst score rel {worst:.2e}")
 
 
 # Rows with norms far above the fp16 range of the P.V operand: fp32 inputs
