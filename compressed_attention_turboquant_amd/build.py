@@ -32,8 +32,8 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "i
 # Sources compiled more than once, each time with its own defines: the decode
 # split kernel's instantiations, one object per (head dimension, key kind).
 MULTI = {
-    "tq_decode_mfma_inst.hip": [(f"d{d}_q{q}", [f"-DTQ_INST_D={d}", f"-DTQ_INST_QJL={q}"])
-                                for d in (128, 256) for q in (0, 1)],
+    "tq_decode_mfma_inst.hip": [(f"d{d}_k{k}", [f"-DTQ_INST_D={d}", f"-DTQ_INST_KIND={k}"])
+                                for d in (128, 256) for k in (0, 1, 2)],
     "tq_decode_wide.hip": [(f"q{q}", [f"-DTQ_INST_QJL={q}"]) for q in (0, 1)],
 }
 

@@ -15,7 +15,12 @@ thread_local std::string g_last_error;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-constexpr int32_t kKnownLayerFlags = TQ_LAYER_BETA_CODEBOOK;
+constexpr int32_t kKnownLayerFlags = TQ_LAYER_BETA_CODEBOOK | TQ_LAYER_DITHER;
+// The dithered variant is defined for the randomized Hadamard rotation and
+// keys without QJL.
+bool dither_ok(int32_t flags, int32_t rot, int32_t k_qjl) {
+  return !(flags & TQ_LAYER_DITHER) || (rot == TQ_ROT_HADAMARD && k_qjl == 0);
+}
 
 // The kernels address one sequence of a cache array through 32-bit byte
 // offsets (buffer descriptors, with a few hundred keys of read-ahead past the
@@ -35,7 +40,8 @@ struct Plan {  // split-K plan of one decode call
   size_t off_qrot, off_qproj, off_part, total;
 };
 
-Plan decode_plan(int d, int qjl, int B, int Hq, int Hkv, int Tq, int64_t N) {
+// dither: the dithered variant, which the many-rows kernel does not implement.
+Plan decode_plan(int d, int qjl, int dither, int B, int Hq, int Hkv, int Tq, int64_t N) {
   Plan p{};
   const int64_t seqs = (int64_t)B * Hkv;
   p.mfma = mfma_decode_supports(d, Hq / Hkv * Tq);
@@ -47,7 +53,7 @@ Plan decode_plan(int d, int qjl, int B, int Hq, int Hkv, int Tq, int64_t N) {
     // each wave at least 4 blocks.  The plan depends on the shape only, so the
     // workspace size does too.
     const int64_t blocks = (N + 31) / 32;
-    if (decode_is_wide(d, Hq / Hkv * Tq)) {
+    if (!dither && decode_is_wide(d, Hq / Hkv * Tq)) {
       // One 4-wave workgroup per CU (each wave holds 32 query rows' operands
       // and accumulators, one wave per SIMD); split the keys so that the
       // workgroups fill the 256 CUs once, each split at least 8 blocks.
@@ -117,6 +123,8 @@ tq_status check_layer(const tq_layer* L) {
     return fail(TQ_ERR_INVALID_ARG, "bit widths must be 1..4");
   if (L->k_qjl != 0 && L->k_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "k_qjl must be 0 or 1");
   if (L->flags & ~kKnownLayerFlags) return fail(TQ_ERR_INVALID_ARG, "unknown layer flags");
+  if (!dither_ok(L->flags, L->rot, L->k_qjl))
+    return fail(TQ_ERR_INVALID_ARG, "TQ_LAYER_DITHER needs the Hadamard rotation and keys without QJL");
   if (!L->blob) return fail(TQ_ERR_INVALID_ARG, "layer blob is NULL");
   if (L->blob_bytes < blob_layout(L->d).total) return fail(TQ_ERR_INVALID_ARG, "layer blob too small");
   return TQ_OK;
@@ -196,6 +204,9 @@ DequantArgs dequant_args(const tq_layer* layer, int32_t which, const tq_cache* c
   a.cent = blob_f(layer, BL.codebook) + (which == TQ_KEYS ? 0 : 2 * kMaxLevels);
   a.out = out;
   a.out_dtype = out_dtype;
+  a.dither = (layer->flags & TQ_LAYER_DITHER) != 0;
+  a.dither_s0 = dither_stream_start(layer->seed, which == TQ_KEYS ? kDitherTagKeys : kDitherTagValues);
+  a.dither_w = blob_f(layer, BL.scales) + (which == TQ_KEYS ? 4 : 5);
   return a;
 }
 
@@ -225,7 +236,7 @@ tq_status check_decode(const tq_layer* layer, const void* q, int32_t q_dtype, in
   if (!mfma_decode_supports(layer->d, rows) && !ref_decode_supports(layer->d, rows))
     return fail(TQ_ERR_UNSUPPORTED, "(Hq/Hkv)*Tq too large for this head dimension");
   if ((int64_t)B * Hkv > 0x7FFFFFFF) return fail(TQ_ERR_UNSUPPORTED, "too many sequences");
-  *plan = decode_plan(layer->d, layer->k_qjl, B, Hq, Hkv, Tq, N);
+  *plan = decode_plan(layer->d, layer->k_qjl, layer->flags & TQ_LAYER_DITHER, B, Hq, Hkv, Tq, N);
   if (plan->nsplit > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many key splits");
   return TQ_OK;
 }
@@ -268,6 +279,10 @@ tq_status launch_decode(const tq_layer* layer, const void* q, int32_t q_dtype, i
   a.waves = P.waves;
   a.wide = P.wide;
   a.keys_per_split = P.keys_per_split;
+  a.dither = (layer->flags & TQ_LAYER_DITHER) != 0;
+  a.kd0 = dither_stream_start(layer->seed, kDitherTagKeys);
+  a.vd0 = dither_stream_start(layer->seed, kDitherTagValues);
+  a.scales = blob_f(layer, BL.scales);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (P.mfma) {
     DecodeMfmaExtra x{};
@@ -394,6 +409,8 @@ tq_status tq_make_layer(tq_layer* layer, int32_t d, int32_t rot, uint64_t seed, 
     return fail(TQ_ERR_INVALID_ARG, "bit widths must be 1..4");
   if (k_qjl != 0 && k_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "k_qjl must be 0 or 1");
   if (flags & ~kKnownLayerFlags) return fail(TQ_ERR_INVALID_ARG, "unknown layer flags");
+  if (!dither_ok(flags, rot, k_qjl))
+    return fail(TQ_ERR_INVALID_ARG, "TQ_LAYER_DITHER needs the Hadamard rotation and keys without QJL");
   if (!dev_blob) return fail(TQ_ERR_INVALID_ARG, "dev_blob is NULL");
   if (!aligned16(dev_blob)) return fail(TQ_ERR_ALIGNMENT, "dev_blob must be 16-byte aligned");
   const BlobLayout BL = blob_layout(d);
@@ -468,7 +485,12 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
   a.sign = cache->sign;
   a.norm = cache->norm;
   a.rnorm = cache->rnorm;
+  a.dither = (layer->flags & TQ_LAYER_DITHER) != 0;
+  a.dither_s0 = dither_stream_start(layer->seed, which == TQ_KEYS ? kDitherTagKeys : kDitherTagValues);
+  a.dither_w = blob_f(layer, BL.scales) + (which == TQ_KEYS ? 4 : 5);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.dither && !fwht_quantize_supports(a.d, a.rot, a.qjl))
+    return fail(TQ_ERR_UNSUPPORTED, "the dithered variant needs the transform quantizer");
   if (fwht_quantize_supports(a.d, a.rot, a.qjl)) return hip_status(launch_quantize_fwht(a, st), "quantize launch");
   if (mfma_quantize_supports(a.d, a.dtype)) return hip_status(launch_quantize_mfma(a, st), "quantize launch");
   return hip_status(launch_quantize_ref(a, st), "quantize launch");
@@ -477,7 +499,7 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
 size_t tq_decode_workspace_bytes(const tq_layer* layer, int32_t B, int32_t Hq, int32_t Hkv,
                                  int32_t Tq, int64_t N) {
   if (!layer || !supported_d(layer->d) || B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || N < 1) return 0;
-  return decode_plan(layer->d, layer->k_qjl, B, Hq, Hkv, Tq, N).total;
+  return decode_plan(layer->d, layer->k_qjl, layer->flags & TQ_LAYER_DITHER, B, Hq, Hkv, Tq, N).total;
 }
 
 tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, int32_t B,

@@ -304,6 +304,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   p.rot_lo = x.rot_lo;
   p.proj_hi = x.proj_hi;
   p.proj_lo = x.proj_lo;
+  p.kd0 = a.kd0;
+  p.vd0 = a.vd0;
   hipError_t e;
   if (a.wide) {
     p.rgroups = (a.Hq / a.Hkv * a.Tq + kWideRowsPerGroup - 1) / kWideRowsPerGroup;
@@ -326,11 +328,13 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hip
   p.first_share = kFirstShare;
   const int w = a.waves;
   if (a.d == 128)
-    e = a.qjl ? launch_decode_split<128, 1>(p, a.kb, a.vb, w, grid, st)
-              : launch_decode_split<128, 0>(p, a.kb, a.vb, w, grid, st);
+    e = a.qjl      ? launch_decode_split<128, kKeysQjl>(p, a.kb, a.vb, w, grid, st)
+        : a.dither ? launch_decode_split<128, kKeysDither>(p, a.kb, a.vb, w, grid, st)
+                   : launch_decode_split<128, kKeysMse>(p, a.kb, a.vb, w, grid, st);
   else
-    e = a.qjl ? launch_decode_split<256, 1>(p, a.kb, a.vb, w, grid, st)
-              : launch_decode_split<256, 0>(p, a.kb, a.vb, w, grid, st);
+    e = a.qjl      ? launch_decode_split<256, kKeysQjl>(p, a.kb, a.vb, w, grid, st)
+        : a.dither ? launch_decode_split<256, kKeysDither>(p, a.kb, a.vb, w, grid, st)
+                   : launch_decode_split<256, kKeysMse>(p, a.kb, a.vb, w, grid, st);
   if (e != hipSuccess) return e;
   return launch_combine(a, qrows, rgrid, st);
 }

@@ -303,9 +303,15 @@ struct WaveState {
   int limit[NR];
   int64_t srow[NR];
   const uint32_t *ktab, *vtab;  // code -> fp16 tables in LDS
+  // Dithered variant: cd = sum_j (R q)_j log2(e) / sqrt(d) per row (the score
+  // term of the key offset is n delta cd); dacc = sum over this lane's keys of
+  // p n_v delta_v (the value offset's share, the same for every coordinate).
+  float cd[NR], dacc[NR];
+  float dkw, dvw;  // offset widths
+  int64_t seq;
 };
 
-template <int D, int KB, int QJL, int VB, int SCORES, int NR>
+template <int D, int KB, int QJL, int VB, int SCORES, int NR, int DITHER>
 __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws, const Block<D, KB, QJL, VB>& cur,
                                               int k0, const DecodeMfmaParams& p, _Float16 (*pb)[4 * NR][32],
                                               int l16, int g4, int rows) {
@@ -363,6 +369,16 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
   u4 bv[kCBp];
   sfor<0, kCBp>([&](auto cb) { bv[cb] = decode8<VB, 8 * VB * cb>(cur.vw, ws.vtab); });
   __builtin_amdgcn_sched_barrier(0);
+  // Dithered variant: the offsets of this lane's two keys (key and value streams).
+  float dk[2] = {0.f, 0.f}, dv[2] = {0.f, 0.f};
+  if constexpr (DITHER) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int key = k0 + 16 * t + l16;
+      dk[t] = cur.kn[t] * dither_offset(p.kd0, ws.seq, key, ws.dkw);
+      dv[t] = cur.vn[t] * dither_offset(p.vd0, ws.seq, key, ws.dvw);
+    }
+  }
   // Phase 4: scores of lane (query rows NR g4 + j, key l16), online softmax.
   float st[NR][2];
 #pragma unroll
@@ -371,6 +387,7 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
     for (int t = 0; t < 2; ++t) {
       const float cent = NR == 1 ? sk[t][0] + sk[t][1] : sk[t][2 * j] + sk[t][2 * j + 1];
       float s = (cur.kn[t] * ws.ca[j]) * cent;
+      if constexpr (DITHER) s = fmaf(dk[t], ws.cd[j], s);
       if constexpr (QJL) {
         const float sgn = NR == 1 ? ss[t][2] + ss[t][3] : ss[t][2 * j] + ss[t][2 * j + 1];
         s = fmaf(cur.kn[t] * cur.kg[t], fmaf(ws.c2[j], sgn, ws.c0[j]), s);
@@ -395,6 +412,7 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
       const float mnew = fmaxf(ws.m[j], rmax);
       const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(ws.m[j] - mnew);
       ws.lsum[j] *= alpha;
+      if constexpr (DITHER) ws.dacc[j] *= alpha;
 #pragma unroll
       for (int i = 0; i < S::CB; ++i) {
         if constexpr (NR == 1) {
@@ -435,6 +453,7 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
     const float p0 = __builtin_amdgcn_exp2f(st[j][0] - ws.msafe[j]);
     const float p1 = __builtin_amdgcn_exp2f(st[j][1] - ws.msafe[j]);
     ws.lsum[j] += p0 + p1;
+    if constexpr (DITHER) ws.dacc[j] = fmaf(p0, dv[0], fmaf(p1, dv[1], ws.dacc[j]));
     const float q0 = p0 * cur.vn[0] * ws.vsc, q1 = p1 * cur.vn[1] * ws.vsc;
     const _Float16 h0 = (_Float16)q0, h1 = (_Float16)q1;
     const int qr = NR * g4 + j;
@@ -554,7 +573,8 @@ __device__ __forceinline__ void split_blocks(const DecodeMfmaParams& p, int spli
 // W waves per workgroup; the SIMDs hold two waves each where
 // decode_simd_waves allows (the bound keeps a code change from silently
 // halving occupancy).
-template <int D, int KB, int QJL, int VB, int SCORES, int NR, int W>
+// DITHER: the dithered variant (keys without QJL): reconstructions c[idx] + delta.
+template <int D, int KB, int QJL, int VB, int SCORES, int NR, int W, int DITHER>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(decode_simd_waves(D, QJL, 4 * NR))))
 decode_mfma_kernel(DecodeMfmaParams p) {
   using S = Shape<D, KB, QJL, VB>;
@@ -568,7 +588,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   __shared__ float mrg_m[W][RW], mrg_l[W][RW];
   __shared__ float qsh[RW][D];     // the workgroup's query rows
   __shared__ float qrs[2][RW][D];  // R q / s_k and S q of those rows
-  __shared__ float qcon[RW][4];    // per row: c1, c2, -sum(S q)
+  __shared__ float qcon[RW][4];    // per row: c1, c2, -sum(S q), sum(R q) (dithered variant)
   // The rotation's k-slice partial sums (set-up) and the waves' accumulators
   // (merge, after the key loop) share one buffer.
   constexpr int kRpart = (T / (D / 4)) * 4 * (D / 4) * 16, kMrg = W * RW * D * 4;
@@ -644,10 +664,11 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   __syncthreads();
 #pragma unroll
   for (int r = wave; r < RW; r += W) {  // wave w normalises rows w, w + W, ...
-    float ma = 0.f, mb = 0.f, sbv = 0.f;
+    float ma = 0.f, mb = 0.f, sbv = 0.f, sav = 0.f;
 #pragma unroll
     for (int j = lane; j < D; j += 64) {
       ma = fmaxf(ma, fabsf(qrs[0][r][j]));
+      if constexpr (DITHER) sav += qrs[0][r][j];
       if constexpr (QJL) {
         mb = fmaxf(mb, fabsf(qrs[1][r][j]));
         sbv += qrs[1][r][j];
@@ -658,6 +679,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
       ma = fmaxf(ma, __shfl_xor(ma, o));
       mb = fmaxf(mb, __shfl_xor(mb, o));
       sbv += __shfl_xor(sbv, o);
+      if constexpr (DITHER) sav += __shfl_xor(sav, o);
     }
     if (lane == 0) {
       int e1 = 0, e2 = 0;
@@ -666,6 +688,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
       qcon[r][0] = ma > 0.f ? ldexpf(1.f, e1 - 1) : 1.f;
       qcon[r][1] = mb > 0.f ? ldexpf(1.f, e2) : 2.f;
       qcon[r][2] = QJL ? -sbv : 0.f;
+      qcon[r][3] = sav * scale_k;  // qrs[0] holds R q / s_k
     }
   }
   __syncthreads();
@@ -712,7 +735,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
     const int q = NR * g4 + j;
-    ws.ca[j] = ws.c2[j] = ws.c0[j] = 0.f;
+    ws.ca[j] = ws.c2[j] = ws.c0[j] = ws.cd[j] = ws.dacc[j] = 0.f;
     ws.limit[j] = -1;
     ws.srow[j] = 0;
     if (q < rows) {
@@ -723,6 +746,7 @@ decode_mfma_kernel(DecodeMfmaParams p) {
       ws.ca[j] = rc[0] * inv_sqrt_d * kLog2e;
       ws.c2[j] = rc[1] * cq;
       ws.c0[j] = rc[2] * cq;
+      ws.cd[j] = rc[3] * inv_sqrt_d * kLog2e;
       ws.limit[j] = (int)(p.causal ? p.N - p.Tq + ((r0 + q) % p.Tq) + 1 : p.N);
     }
     ws.m[j] = -INFINITY;
@@ -733,6 +757,9 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   for (int i = 0; i < S::CB; ++i) ws.acc[i] = f4{0.f, 0.f, 0.f, 0.f};
   ws.vsc = kInvSlack;
   ws.vlim = ldexpf(1.f, kVExp) / kInvSlack;
+  ws.seq = seq;
+  ws.dkw = DITHER ? p.scales[4] : 0.f;
+  ws.dvw = DITHER ? p.scales[5] : 0.f;
 
   // Three register sets rotate so two blocks are in flight while one is used
   // (d = 256: two sets, one block in flight).  The prefetches are
@@ -742,21 +769,21 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   if constexpr (D == 128) {
     for (; blk < blk1; blk += 3 * W) {
       load_block(b2, sb, (blk + 2 * W) * 32, l16, g4);
-      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
+      process_block<D, KB, QJL, VB, SCORES, NR, DITHER>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
       if (blk + W >= blk1) break;
       load_block(b0, sb, (blk + 3 * W) * 32, l16, g4);
-      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b1, (blk + W) * 32, p, pbuf[wave], l16, g4, rows);
+      process_block<D, KB, QJL, VB, SCORES, NR, DITHER>(ws, b1, (blk + W) * 32, p, pbuf[wave], l16, g4, rows);
       if (blk + 2 * W >= blk1) break;
       load_block(b1, sb, (blk + 4 * W) * 32, l16, g4);
-      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b2, (blk + 2 * W) * 32, p, pbuf[wave], l16, g4, rows);
+      process_block<D, KB, QJL, VB, SCORES, NR, DITHER>(ws, b2, (blk + 2 * W) * 32, p, pbuf[wave], l16, g4, rows);
     }
   } else {
     for (; blk < blk1; blk += 2 * W) {
       load_block(b1, sb, (blk + W) * 32, l16, g4);
-      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
+      process_block<D, KB, QJL, VB, SCORES, NR, DITHER>(ws, b0, blk * 32, p, pbuf[wave], l16, g4, rows);
       if (blk + W >= blk1) break;
       load_block(b0, sb, (blk + 2 * W) * 32, l16, g4);
-      process_block<D, KB, QJL, VB, SCORES, NR>(ws, b1, (blk + W) * 32, p, pbuf[wave], l16, g4, rows);
+      process_block<D, KB, QJL, VB, SCORES, NR, DITHER>(ws, b1, (blk + W) * 32, p, pbuf[wave], l16, g4, rows);
     }
   }
 
@@ -772,9 +799,15 @@ decode_mfma_kernel(DecodeMfmaParams p) {
       mrg_m[wave][NR * g4 + j] = ws.m[j];
       mrg_l[wave][NR * g4 + j] = lsum;
     }
+    float dsum = 0.f;  // the value offsets' share of every coordinate
+    if constexpr (DITHER) {
+      dsum = ws.dacc[j];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) dsum += __shfl_xor(dsum, o);
+    }
 #pragma unroll
     for (int cb = 0; cb < S::CB; ++cb)
-      mrg_acc[wave][NR * g4 + j][l16 * S::CB + cb] = (ws.acc[cb][2 * j] + ws.acc[cb][2 * j + 1]) * inv_sv;
+      mrg_acc[wave][NR * g4 + j][l16 * S::CB + cb] = fmaf(ws.acc[cb][2 * j] + ws.acc[cb][2 * j + 1], inv_sv, dsum);
   }
   __syncthreads();
   const int64_t rows_total = (int64_t)(gridDim.x / p.rgroups) / p.Hkv * p.Hq * p.Tq;

@@ -54,7 +54,9 @@ __device__ __forceinline__ void sfor(F&& f) {
   }
 }
 
-template <int D, int BITS, int VALUES, int OUT16>
+// DITHER: the dithered variant, x_hat = n * R^T (c[idx] + delta): the offset
+// term n * delta * (R^T 1)_j is added with the row sums of R^T.
+template <int D, int BITS, int VALUES, int OUT16, int DITHER>
 __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   constexpr int W = D / 32;           // waves: each owns 32 output coordinates
   constexpr int T = 64 * W;           // threads: 2 D, one per 32 codes of a tile
@@ -65,6 +67,7 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   __shared__ __align__(8) u2 tpair[kPairs];
   __shared__ __align__(16) _Float16 bhi[kTile][PITCH], blo[kTile][PITCH];
   __shared__ float nsh[kTile];
+  __shared__ float dsh[DITHER ? kTile : 1];  // dithered variant: the tile's offsets, times kFactor^2
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -79,6 +82,7 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
 
   // This wave's rows of 16 R^T: row j = 32 wave + 16 jb + l16, k = 32 kb + 8 g4 + e.
   h8 ahi[2][NKB], alo[2][NKB];
+  float rpart[2] = {0.f, 0.f};  // dithered variant: partial row sums of R^T
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
@@ -91,11 +95,27 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
         const float v = (e < 4 ? x0[e] : x1[e - 4]) * kFactor;
         hi[e] = (_Float16)v;
         lo[e] = (_Float16)(v - (float)hi[e]);
+        if constexpr (DITHER) rpart[jb] += e < 4 ? x0[e] : x1[e - 4];
       }
       ahi[jb][kb] = hi;
       alo[jb][kb] = lo;
     }
   }
+  // Row sums for the accumulator's rows 32 wave + 16 jb + 4 g4 + r: lane l16
+  // of every k-group holds row 16 jb + l16 once the k-groups are summed.
+  f4 rsum[2];
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb) {
+    rsum[jb] = f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (DITHER) {
+      float r = rpart[jb];
+      r += __shfl_xor(r, 16);
+      r += __shfl_xor(r, 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rsum[jb][i] = __shfl(r, 4 * g4 + i);
+    }
+  }
+  const float dwidth = DITHER ? *a.dither_w : 0.f;
 
   const int64_t n = a.n, cap = a.cap;
   const int64_t tiles = (n + kTile - 1) / kTile;
@@ -104,7 +124,7 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   // are loaded one tile ahead, so that the loads are in flight while the
   // matrix cores work on the previous tile.
   uint32_t w[BITS];
-  float nrm = 0.f;
+  float nrm = 0.f, dlt = 0.f;
   auto load_codes = [&](int64_t item) {
     const int64_t seq = item / tiles, t0 = (item % tiles) * kTile;
     bool live;
@@ -123,6 +143,9 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
 #pragma unroll
     for (int i = 0; i < BITS; ++i) w[i] = live ? src[i] : 0u;
     if (tid < kTile) nrm = t0 + tid < n ? a.norm[seq * cap + t0 + tid] * (1.f / (kFactor * kFactor)) : 0.f;
+    if constexpr (DITHER) {
+      if (tid < kTile) dlt = dither_offset(a.dither_s0, seq, t0 + tid, dwidth) * (kFactor * kFactor);
+    }
   };
   if (blockIdx.x < items) load_codes(blockIdx.x);
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
@@ -158,6 +181,9 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
         }
       }
       if (tid < kTile) nsh[tid] = nrm;
+      if constexpr (DITHER) {
+        if (tid < kTile) dsh[tid] = dlt;
+      }
     }
     __syncthreads();
     if (item + gridDim.x < items) load_codes(item + gridDim.x);
@@ -174,6 +200,7 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
       }
       const int tok = 16 * s + l16;
       const float nt = nsh[tok];
+      const float dl = DITHER ? dsh[tok] : 0.f;
       // Four independent accumulation chains (per row block: hi*hi, and the two
       // correction products) so that no product waits on the one before it.
       f4 acc[2], cor[2];
@@ -194,7 +221,9 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
       for (int jb = 0; jb < 2; ++jb) {
         if (tok < left) {
           const int64_t o = (seq * n + t0 + tok) * D + 32 * wave + 16 * jb + 4 * g4;
-          const f4 v = (acc[jb] + cor[jb]) * nt;
+          f4 v = acc[jb] + cor[jb];
+          if constexpr (DITHER) v += dl * rsum[jb];
+          v *= nt;
           if constexpr (OUT16) {
             const u2 hv = {hbits((_Float16)v[0]) | (hbits((_Float16)v[1]) << 16),
                            hbits((_Float16)v[2]) | (hbits((_Float16)v[3]) << 16)};
@@ -210,9 +239,9 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
 
 // Persistent grid: as many workgroups as the CUs hold at once, or one per
 // tile if there are fewer.
-template <int D, int BITS, int VALUES, int OUT16>
+template <int D, int BITS, int VALUES, int OUT16, int DITHER>
 hipError_t launch(const DequantArgs& a, hipStream_t st) {
-  auto kern = dequant_mfma_kernel<D, BITS, VALUES, OUT16>;
+  auto kern = dequant_mfma_kernel<D, BITS, VALUES, OUT16, DITHER>;
   int dev = 0, cus = 256, per_cu = 0;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
@@ -226,11 +255,16 @@ hipError_t launch(const DequantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D, int BITS, int DITHER>
+hipError_t dispatch_out(const DequantArgs& a, hipStream_t st) {
+  const bool h = a.out_dtype == TQ_F16;
+  if (a.value_layout) return h ? launch<D, BITS, 1, 1, DITHER>(a, st) : launch<D, BITS, 1, 0, DITHER>(a, st);
+  return h ? launch<D, BITS, 0, 1, DITHER>(a, st) : launch<D, BITS, 0, 0, DITHER>(a, st);
+}
+
 template <int D, int BITS>
 hipError_t dispatch_layout(const DequantArgs& a, hipStream_t st) {
-  const bool h = a.out_dtype == TQ_F16;
-  if (a.value_layout) return h ? launch<D, BITS, 1, 1>(a, st) : launch<D, BITS, 1, 0>(a, st);
-  return h ? launch<D, BITS, 0, 1>(a, st) : launch<D, BITS, 0, 0>(a, st);
+  return a.dither ? dispatch_out<D, BITS, 1>(a, st) : dispatch_out<D, BITS, 0>(a, st);
 }
 
 template <int D>

@@ -373,6 +373,8 @@ void build_blob_image(int d, int rot, uint64_t seed, int k_bits, int v_bits, int
   float* sc = reinterpret_cast<float*>(image + L.scales);
   sc[0] = centroid_half_scale(cb, 1 << k_bits, &sc[2]);
   sc[1] = centroid_half_scale(cb + 2 * kMaxLevels, 1 << v_bits, &sc[3]);
+  sc[4] = cb[(1 << k_bits) / 2] - cb[(1 << k_bits) / 2 - 1];
+  sc[5] = cb[2 * kMaxLevels + (1 << v_bits) / 2] - cb[2 * kMaxLevels + (1 << v_bits) / 2 - 1];
   split_half(R.data(), dd, std::sqrt((double)d), reinterpret_cast<uint16_t*>(image + L.rot_hi),
              reinterpret_cast<uint16_t*>(image + L.rot_lo));
   split_half(SR.data(), dd, 1.0, reinterpret_cast<uint16_t*>(image + L.projr_hi),

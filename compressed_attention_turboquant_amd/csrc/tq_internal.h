@@ -24,8 +24,9 @@ struct BlobLayout {
   size_t rot_t;     // [d][d] R^T row-major (coalesced reads of R by output index)
   size_t proj_t;    // [d][d] S^T row-major
   size_t codebook;  // [4][16]: key centroids, key boundaries, value centroids, value boundaries
-  size_t scales;    // [4]: fp16 table scale for key and value centroids, and their worst relative
-                    // fp16 rounding error (see centroid_half_scale)
+  size_t scales;    // [8]: fp16 table scale for key and value centroids, their worst relative fp16
+                    // rounding error (see centroid_half_scale), then the dither widths
+                    // c[L/2] - c[L/2-1] of the key and value codebooks
   size_t rot_hi;    // half [d][d]: sqrt(d)*R split as hi + lo (MFMA operands)
   size_t rot_lo;
   size_t projr_hi;  // half [d][d]: S R^T split as hi + lo
@@ -51,7 +52,7 @@ inline BlobLayout blob_layout(int d) {
   L.rot_t = o;     o = align_up(o + mat, 256);
   L.proj_t = o;    o = align_up(o + mat, 256);
   L.codebook = o;  o = align_up(o + 4 * kMaxLevels * sizeof(float), 256);
-  L.scales = o;    o = align_up(o + 4 * sizeof(float), 256);
+  L.scales = o;    o = align_up(o + 8 * sizeof(float), 256);
   L.rot_hi = o;    o = align_up(o + hmat, 256);
   L.rot_lo = o;    o = align_up(o + hmat, 256);
   L.projr_hi = o;  o = align_up(o + hmat, 256);

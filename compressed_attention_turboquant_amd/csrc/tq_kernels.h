@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "tq_dither.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -17,6 +18,11 @@ struct QuantizeArgs {
   const void *rot_hi, *rot_lo, *projr_hi, *projr_lo;  // half splits for MFMA
   uint8_t *idx, *sign;
   float *norm, *rnorm;
+  // Dithered variant: offsets from the stream starting at dither_s0, width at
+  // *dither_w (device, in the layer blob).
+  int dither;
+  uint64_t dither_s0;
+  const float* dither_w;
 };
 
 struct DecodeArgs {
@@ -35,6 +41,10 @@ struct DecodeArgs {
   int waves;  // waves per decode workgroup (matrix-core kernel)
   bool wide;  // the many-rows kernel (tq_decode_wide.hip)
   int64_t keys_per_split;
+  // Dithered variant: key / value offset streams; widths in the blob's scales[4], [5].
+  int dither;
+  uint64_t kd0, vd0;
+  const float* scales;
 };
 
 struct DequantArgs {
@@ -45,6 +55,9 @@ struct DequantArgs {
   const float *R, *Rt, *cent;  // R and R^T row-major
   void* out;
   int out_dtype;
+  int dither;  // dithered variant: offsets from the stream at dither_s0, width *dither_w
+  uint64_t dither_s0;
+  const float* dither_w;
 };
 
 // Arguments of the kernel that adds the QJL term n sqrt(pi/2)/d gamma S^T sigma
@@ -79,6 +92,7 @@ struct DecodeMfmaParams {
   // splits of a row group have keys_per_split keys.
   int first_wgs, first_share;
   float *part, *scores;
+  uint64_t kd0, vd0;  // dithered variant: key / value offset streams (widths in scales[4], [5])
 };
 
 // Blob and workspace pieces the matrix-core decode needs besides DecodeArgs.
@@ -104,9 +118,12 @@ bool fwht_quantize_supports(int d, int rot, int qjl);
 hipError_t launch_quantize_fwht(const QuantizeArgs& a, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 bool mfma_decode_supports(int d, int rows);
-// The split kernel for one head dimension and key kind; each (D, QJL) pair is
+// Key kinds of the split kernel: MSE codes only, with QJL signs, or MSE codes of
+// the dithered variant.
+constexpr int kKeysMse = 0, kKeysQjl = 1, kKeysDither = 2;
+// The split kernel for one head dimension and key kind; each (D, KIND) pair is
 // instantiated by its own compilation of tq_decode_mfma_inst.hip.
-template <int D, int QJL>
+template <int D, int KIND>
 hipError_t launch_decode_split(const DecodeMfmaParams& p, int kb, int vb, int waves, dim3 grid, hipStream_t st);
 // Query rows one decode workgroup serves (4, or 8 when a KV head has more than
 // 4 query rows: the matrix-core rows then carry 8 query rows x {hi, lo}).

@@ -191,7 +191,8 @@ __global__ void __launch_bounds__(kThreads) decode_split_ref(
     int64_t keys_per_split, const uint8_t* __restrict__ kidx, const uint8_t* __restrict__ ksign,
     const float* __restrict__ knorm, const float* __restrict__ krnorm,
     const uint8_t* __restrict__ vidx, const float* __restrict__ vnorm,
-    const float* __restrict__ cb, float* __restrict__ part, float* __restrict__ scores) {
+    const float* __restrict__ cb, float* __restrict__ part, float* __restrict__ scores,
+    int dither, uint64_t kd0, uint64_t vd0, const float* __restrict__ dwidth) {
   extern __shared__ float smem[];
   const int G = Hq / Hkv;
   const int rows = G * Tq;
@@ -214,6 +215,8 @@ __global__ void __launch_bounds__(kThreads) decode_split_ref(
   const int64_t k_end = min(N, k_begin + keys_per_split);
   const float* ck = cb;
   const float* cv = cb + 2 * kMaxLevels;
+  // dithered variant: offset widths of keys and values
+  const float kw = dither ? dwidth[0] : 0.f, vw = dither ? dwidth[1] : 0.f;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
   const float kappa = sqrtf(0.5f * (float)M_PI) / (float)d;
   const int64_t rows_total = (int64_t)gridDim.x / Hkv * Hq * Tq;
@@ -240,6 +243,10 @@ __global__ void __launch_bounds__(kThreads) decode_split_ref(
         if (qjl) ks[e] = stream_code(ksign + (seq * cap + t) * (d / 8), j, 1) ? 1.f : -1.f;
         const uint8_t* tile = vidx + (seq * (cap / 8) + t / 8) * vtb;
         vv[e] = vnorm[seq * cap + t] * cv[stream_code(tile, 8 * j + (t & 7), vb)];
+        if (dither) {  // reconstruction c[idx] + delta
+          kc[e] += dither_offset(kd0, seq, t, kw);
+          vv[e] = fmaf(vnorm[seq * cap + t], dither_offset(vd0, seq, t, vw), vv[e]);
+        }
       }
     }
     for (int kk = tid; kk < kcount; kk += kThreads) {
@@ -425,7 +432,7 @@ hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st) {
                      dim3(kThreads), ref_decode_smem(a.d, rows), st, a.q_rot, a.q_proj, a.Hq,
                      a.Hkv, a.Tq, a.N, a.cap, a.causal, a.d, a.kb, a.vb, a.qjl, KC,
                      a.keys_per_split, a.kidx, a.ksign, a.knorm, a.krnorm, a.vidx, a.vnorm,
-                     a.cb, a.part, a.scores);
+                     a.cb, a.part, a.scores, a.dither, a.kd0, a.vd0, a.scales ? a.scales + 4 : nullptr);
   return launch_decode_combine(a, st);
 }
 

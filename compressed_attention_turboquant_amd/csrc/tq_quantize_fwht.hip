@@ -78,9 +78,12 @@ struct FwhtParams {
   const float *dsign, *bnd;
   uint8_t* idx;
   float* norm;
+  uint64_t ds0;       // dithered variant: offset stream and width
+  const float* dw;
 };
 
-template <int D, int BITS, int VALUES, typename Tin>
+// DITHER: the dithered variant, codes of y - delta for the token's offset delta.
+template <int D, int BITS, int VALUES, typename Tin, int DITHER>
 __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
   constexpr int NC = D / 64, V = 8 * NC, ROW = lds_row<D>();
   constexpr int K = BITS > 1 ? (1 << (BITS - 1)) - 1 : 1;  // positive boundaries (array size)
@@ -112,6 +115,7 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
 #pragma unroll
   for (int i = 0; i < K; ++i) beta[i] = BITS > 1 ? p.bnd[(1 << (BITS - 1)) + i] : 0.f;
   const float sqrt_d = sqrtf((float)D);
+  const float dwidth = DITHER ? *p.dw : 0.f;
 
   const int64_t items = p.seqs * p.tiles;
   const int64_t wstride = (int64_t)gridDim.x * kWaves;
@@ -170,10 +174,12 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
     ss += dpp<kDppXor2>(ss);
     ss += dpp<kDppXor8>(ss);
     const float nn = sqrtf(ss);
-    // thresholds in the unnormalised transform's units: beta * n * sqrt(d)
+    // thresholds in the unnormalised transform's units: beta * n * sqrt(d).  A
+    // dithered zero row (y = 0) is compared at unit scale, so -delta decides.
+    const float unit = DITHER && nn == 0.f ? 1.f : nn * sqrt_d;
     float th[K];
 #pragma unroll
-    for (int i = 0; i < K; ++i) th[i] = beta[i] * (nn * sqrt_d);
+    for (int i = 0; i < K; ++i) th[i] = beta[i] * unit;
 
     // unnormalised Walsh-Hadamard transform: register bits, then lane bits
 #pragma unroll
@@ -192,6 +198,12 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
     for (int v = 0; v < V; ++v) x[v] = fmaf(s2, x[v], dpp<kDppXor2>(x[v]));
 #pragma unroll
     for (int v = 0; v < V; ++v) x[v] = fmaf(s8, x[v], dpp<kDppXor8>(x[v]));
+    if constexpr (DITHER) {
+      // y - delta in the unnormalised transform's units
+      const float shift = dither_offset(p.ds0, s, tile * 8 + tl, dwidth) * unit;
+#pragma unroll
+      for (int v = 0; v < V; ++v) x[v] -= shift;
+    }
 
     // codes into LDS, [token][coordinate]: code = #{i : beta_i < y}
 #pragma unroll
@@ -291,22 +303,27 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
   }
 }
 
-template <int D, int VALUES, typename Tin>
+template <int D, int VALUES, typename Tin, int DITHER>
 hipError_t launch_bits(const FwhtParams& p, int bits, unsigned grid, hipStream_t st) {
   switch (bits) {
-    case 1: hipLaunchKernelGGL((quantize_fwht_kernel<D, 1, VALUES, Tin>), dim3(grid), dim3(kThreads), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((quantize_fwht_kernel<D, 2, VALUES, Tin>), dim3(grid), dim3(kThreads), 0, st, p); break;
-    case 3: hipLaunchKernelGGL((quantize_fwht_kernel<D, 3, VALUES, Tin>), dim3(grid), dim3(kThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((quantize_fwht_kernel<D, 4, VALUES, Tin>), dim3(grid), dim3(kThreads), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((quantize_fwht_kernel<D, 1, VALUES, Tin, DITHER>), dim3(grid), dim3(kThreads), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((quantize_fwht_kernel<D, 2, VALUES, Tin, DITHER>), dim3(grid), dim3(kThreads), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((quantize_fwht_kernel<D, 3, VALUES, Tin, DITHER>), dim3(grid), dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((quantize_fwht_kernel<D, 4, VALUES, Tin, DITHER>), dim3(grid), dim3(kThreads), 0, st, p); break;
   }
   return hipGetLastError();
 }
 
+template <int D, typename Tin>
+hipError_t launch_in(const FwhtParams& p, const QuantizeArgs& a, unsigned grid, hipStream_t st) {
+  if (a.dither)
+    return a.value_layout ? launch_bits<D, 1, Tin, 1>(p, a.bits, grid, st) : launch_bits<D, 0, Tin, 1>(p, a.bits, grid, st);
+  return a.value_layout ? launch_bits<D, 1, Tin, 0>(p, a.bits, grid, st) : launch_bits<D, 0, Tin, 0>(p, a.bits, grid, st);
+}
+
 template <int D>
 hipError_t launch_d(const FwhtParams& p, const QuantizeArgs& a, unsigned grid, hipStream_t st) {
-  if (a.dtype == TQ_F16)
-    return a.value_layout ? launch_bits<D, 1, _Float16>(p, a.bits, grid, st) : launch_bits<D, 0, _Float16>(p, a.bits, grid, st);
-  return a.value_layout ? launch_bits<D, 1, float>(p, a.bits, grid, st) : launch_bits<D, 0, float>(p, a.bits, grid, st);
+  return a.dtype == TQ_F16 ? launch_in<D, _Float16>(p, a, grid, st) : launch_in<D, float>(p, a, grid, st);
 }
 
 }  // namespace
@@ -329,6 +346,8 @@ hipError_t launch_quantize_fwht(const QuantizeArgs& a, hipStream_t st) {
   p.bnd = a.bnd;
   p.idx = a.idx;
   p.norm = a.norm;
+  p.ds0 = a.dither_s0;
+  p.dw = a.dither_w;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;

@@ -81,7 +81,7 @@ enum { TQ_ROT_HAAR = 0, TQ_ROT_HADAMARD = 1 };
  * unit vector's coordinate, density proportional to (1 - t^2)^((d-3)/2). */
 enum { TQ_LAW_GAUSSIAN = 0, TQ_LAW_BETA = 1 };
 /* tq_layer.flags */
-enum { TQ_LAYER_BETA_CODEBOOK = 1 };
+enum { TQ_LAYER_BETA_CODEBOOK = 1, TQ_LAYER_DITHER = 2 };
 enum { TQ_F32 = 0, TQ_F16 = 1 };
 enum { TQ_KEYS = 0, TQ_VALUES = 1 };
 
@@ -143,7 +143,19 @@ tq_status tq_make_rotation(tq_layer* layer, int32_t d, int32_t rot, uint64_t see
  *                           "Coordinates Become Predictable After Rotation" and
  *                           "Designing the Optimal Codebook Without Data": the
  *                           integrals done numerically) instead of N(0, 1/d).
- * Unknown flag bits give TQ_ERR_INVALID_ARG. */
+ *   TQ_LAYER_DITHER         dithered randomized-Hadamard variant
+ *                           (thelatestinai.com paper page 2606.10458, third
+ *                           abstract: HD, then a random scalar offset
+ *                           subtracted before quantizing): each token's
+ *                           rotated coordinates are coded as
+ *                           #{i : beta_i < y_j - delta} and reconstructed as
+ *                           c[idx] + delta, delta = w (u - 1/2) with w the
+ *                           spacing of the codebook's two central centroids
+ *                           and u the uniform of output seq * 2^32 + t + 1 of
+ *                           the layer's SplitMix64 stream with tag 3 (keys) or
+ *                           4 (values), regenerated wherever it is needed.
+ *                           Needs rot = TQ_ROT_HADAMARD and k_qjl = 0.
+ * Unknown flag bits, or TQ_LAYER_DITHER without those, give TQ_ERR_INVALID_ARG. */
 tq_status tq_make_layer(tq_layer* layer, int32_t d, int32_t rot, uint64_t seed, int32_t k_bits,
                         int32_t k_qjl, int32_t v_bits, int32_t flags, void* dev_blob, size_t blob_bytes,
                         void* stream);

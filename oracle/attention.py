@@ -12,6 +12,9 @@ factor sqrt(pi/2)/d.  Per key t and query q:
 where the value reconstruction n_v R^T c_v[idx] is summed in the rotated
 domain and un-rotated once.
 
+In the dithered randomized-Hadamard variant the cache also holds each
+token's offset ("k_dither", "v_dither"): the reconstruction is c[idx] + delta.
+
 Readings (pages silent; parity unpinned by the pages):
   * grouped-query heads: query head h reads KV head h // (Hq / Hkv);
   * with Tq query tokens and `causal`, query i (0-based) sees keys
@@ -68,6 +71,8 @@ def decode(q, R, S, ck, cv, cache: dict, N: int, causal: bool,
     for b, h in todo:
         g = h // G
         kc = ck[cache["k_idx"][b, g, :N]]             # [N, d] centroid values
+        if "k_dither" in cache:                       # dithered variant: c[idx] + delta
+            kc = kc + cache["k_dither"][b, g, :N][:, None]
         t1 = q_rot[b, h] @ kc.T                       # [Tq, N]
         s = t1
         if qjl:
@@ -81,7 +86,10 @@ def decode(q, R, S, ck, cv, cache: dict, N: int, causal: bool,
         m = s.max(axis=1, keepdims=True)
         p = np.exp(s - m)
         p = p / p.sum(axis=1, keepdims=True)
-        v_rot = cache["v_norm"][b, g, :N][:, None] * cv[cache["v_idx"][b, g, :N]]
+        vc = cv[cache["v_idx"][b, g, :N]]
+        if "v_dither" in cache:
+            vc = vc + cache["v_dither"][b, g, :N][:, None]
+        v_rot = cache["v_norm"][b, g, :N][:, None] * vc
         acc = p @ v_rot                               # [Tq, d], rotated domain
         out[b, h] = acc @ R                           # row form of R^T acc
         scores[b, h] = s

@@ -31,18 +31,39 @@ import math
 
 import numpy as np
 
+from . import rng
+
 KAPPA_NUM = math.sqrt(math.pi / 2.0)      # QJL correction sqrt(pi/2); divided by d
 
 
 # ---------------------------------------------------------------- encoding --
 
-def encode_rows(x, R, centroids, boundaries, S=None) -> dict:
+def dither_offsets(seed: int, which: str, seq, t, centroids):
+    """Per-token offsets of the dithered randomized-Hadamard variant
+    (thelatestinai.com paper page 2606.10458, third abstract: HD, then a random
+    scalar offset subtracted before quantizing).  Readings (the abstract fixes
+    neither): one offset per token, the same for all its coordinates, uniform
+    over the spacing of the two central centroids,
+        delta = (c[L/2] - c[L/2 - 1]) * (u - 1/2),
+    u the uniform of output seq * 2^32 + t + 1 of the layer's stream with tag
+    3 (keys) or 4 (values), so the decoder regenerates it (nothing is stored).
+    seq, t: integer arrays of equal shape."""
+    c = np.asarray(centroids, dtype=np.float64)
+    L = c.size
+    width = c[L // 2] - c[L // 2 - 1]
+    tag = rng.TAG_DITHER_K if which == "K" else rng.TAG_DITHER_V
+    k = np.asarray(seq, dtype=np.int64) * (1 << 32) + np.asarray(t, dtype=np.int64) + 1
+    return width * (rng.uniform_at(seed, tag, k) - 0.5)
+
+
+def encode_rows(x, R, centroids, boundaries, S=None, dither=None) -> dict:
     """Encode rows of x [rows, d].  Returns unpacked fields plus diagnostics.
 
     idx [rows, d] int64; norm [rows] fp64; u [rows, d] the unit rows; y
-    [rows, d] the rotated unit vectors (to locate coordinates near a
-    boundary); with S: sign [rows, d] bool (True means +1), rnorm [rows] fp64
-    and proj [rows, d] = S r (see qjl_stage).
+    [rows, d] the values compared with the boundaries: the rotated unit
+    vectors, minus the per-row offsets `dither` when given (dithered
+    variant, keys without QJL and values); with S: sign [rows, d] bool (True
+    means +1), rnorm [rows] fp64 and proj [rows, d] = S r (see qjl_stage).
     """
     x = np.asarray(x, dtype=np.float64)
     R = np.asarray(R, dtype=np.float64)
@@ -53,6 +74,8 @@ def encode_rows(x, R, centroids, boundaries, S=None) -> dict:
     safe = np.where(norm > 0.0, norm, 1.0)
     u = np.where(norm[:, None] > 0.0, x / safe[:, None], 0.0)
     y = u @ R.T                                   # row form of y = R u
+    if dither is not None:                        # dithered variant: quantize y - delta
+        y = y - np.asarray(dither, dtype=np.float64)[:, None]
     idx = (y[..., None] > beta).sum(axis=-1)      # #{i : beta_i < y_j}
     out = {"idx": idx, "norm": norm, "y": y, "u": u}
     if S is not None:
@@ -75,11 +98,15 @@ def qjl_stage(u, idx, R, centroids, S) -> dict:
     return {"sign": proj >= 0.0, "rnorm": np.sqrt(np.sum(r * r, axis=1)), "proj": proj}
 
 
-def reconstruct_mse(idx, norm, R, centroids) -> np.ndarray:
+def reconstruct_mse(idx, norm, R, centroids, dither=None) -> np.ndarray:
     """x_hat = n * R^T c[idx] ([cuTile] listing, decompression function:
-    centroid lookup, inverse rotation, norm rescale)."""
+    centroid lookup, inverse rotation, norm rescale); with per-row `dither`,
+    x_hat = n * R^T (c[idx] + delta) (the offset added back)."""
     c = np.asarray(centroids, dtype=np.float64)
-    return np.asarray(norm, dtype=np.float64)[:, None] * (c[idx] @ np.asarray(R, np.float64))
+    yhat = c[idx]
+    if dither is not None:
+        yhat = yhat + np.asarray(dither, dtype=np.float64)[:, None]
+    return np.asarray(norm, dtype=np.float64)[:, None] * (yhat @ np.asarray(R, np.float64))
 
 
 def reconstruct_prod(idx, norm, sign, rnorm, R, centroids, S) -> np.ndarray:

@@ -19,7 +19,9 @@ number generators", OOPSLA 2014, with the published 64-bit finaliser):
           rho = sqrt(-2 ln u1);  z0 = rho cos(2 pi u2);  z1 = rho sin(2 pi u2)
   matrices are filled row-major, element 2p from z0 and 2p+1 from z1 of pair p.
   signs:  D_j = +1 when the top bit of output j+1 is 0, else -1.
-Tags: 0 = Gaussian matrix for the Haar rotation, 1 = projection S, 2 = signs D.
+Tags: 0 = Gaussian matrix for the Haar rotation, 1 = projection S, 2 = signs D,
+3 / 4 = per-token dither offsets of keys / values (output number
+seq * 2^32 + t + 1 for token t of sequence seq).
 """
 import math
 
@@ -28,6 +30,7 @@ GAMMA = 0x9E3779B97F4A7C15
 TAG_MUL = 0xD1B54A32D192ED03
 
 TAG_HAAR, TAG_PROJ, TAG_SIGNS = 0, 1, 2
+TAG_DITHER_K, TAG_DITHER_V = 3, 4
 
 
 def _mix(z: int) -> int:
@@ -61,3 +64,13 @@ def normals(seed: int, tag: int, count: int):
 
 def signs(seed: int, tag: int, count: int):
     return [1 if (z >> 63) == 0 else -1 for z in stream(seed, tag, count)]
+
+
+def uniform_at(seed: int, tag: int, k):
+    """Uniform (0, 1) of output number k (k >= 1, scalar or integer array) of
+    stream (seed, tag): counter-based access to the same stream."""
+    import numpy as np
+    s0 = (seed ^ ((tag * TAG_MUL) & MASK64)) & MASK64
+    ks = np.asarray(k, dtype=object)
+    z = np.vectorize(lambda kk: _mix((s0 + int(kk) * GAMMA) & MASK64), otypes=[object])(ks)
+    return np.vectorize(lambda zz: ((zz >> 11) + 0.5) * 2.0 ** -53, otypes=[float])(z).astype(np.float64)

@@ -37,11 +37,24 @@ class OracleLayer:
         self.S = transforms.gaussian_projection(cfg.d, cfg.layer_seed)
         self.ck, self.bk = codebook.codebook(cfg.k_bits, cfg.d, cfg.codebook)
         self.cv, self.bv = codebook.codebook(cfg.v_bits, cfg.d, cfg.codebook)
+        self.seed = cfg.layer_seed
+        self.dither = cfg.dither
+
+    def offsets(self, which, S, n, t0=0):
+        """Dithered variant: offsets of tokens t0..t0+n-1 of sequences 0..S-1,
+        one per row in [S, n] order (None for other layers)."""
+        if not self.dither:
+            return None
+        seq, t = np.meshgrid(np.arange(S), np.arange(t0, t0 + n), indexing="ij")
+        c = self.ck if which == B.TQ_KEYS else self.cv
+        return codec.dither_offsets(self.seed, "K" if which == B.TQ_KEYS else "V", seq.ravel(), t.ravel(), c)
 
 
 def gpu_layer(cfg):
     rot = B.TQ_ROT_HAAR if cfg.rot == "haar" else B.TQ_ROT_HADAMARD
     flags = B.TQ_LAYER_BETA_CODEBOOK if cfg.codebook == "beta" else 0
+    if cfg.dither:
+        flags |= B.TQ_LAYER_DITHER
     return B.make_rotation(cfg.d, rot, cfg.layer_seed, cfg.k_bits, cfg.k_qjl, cfg.v_bits, flags=flags)
 
 
@@ -86,6 +99,8 @@ def check_keys(gpu_idx, gpu_norm, enc, ol, what, gpu_sign=None, gpu_rnorm=None):
     flipped = compare_codes(gpu_idx, enc, ol.bk, what + " codes")
     np.testing.assert_allclose(gpu_norm, enc["norm"], rtol=2e-6, atol=0, err_msg=what + ": norms")
     fields = {"idx": gpu_idx, "norm": enc["norm"]}
+    if "dither" in enc:
+        fields["dither"] = enc["dither"]
     stats = {"code_rows": int(flipped.sum()), "sign_rows": 0}
     if gpu_sign is not None:
         sign, rnorm, proj = enc["sign"].copy(), enc["rnorm"].copy(), enc["proj"].copy()
@@ -109,7 +124,10 @@ def check_values(gpu_idx, gpu_norm, enc, ol, what):
     a band code difference."""
     flipped = compare_codes(gpu_idx, enc, ol.bv, what + " codes")
     np.testing.assert_allclose(gpu_norm, enc["norm"], rtol=2e-6, atol=0, err_msg=what + ": norms")
-    return {"idx": gpu_idx, "norm": enc["norm"]}, int(flipped.sum())
+    fields = {"idx": gpu_idx, "norm": enc["norm"]}
+    if "dither" in enc:
+        fields["dither"] = enc["dither"]
+    return fields, int(flipped.sum())
 
 
 def oracle_cache(kf, vf, B, Hkv, N, d):
@@ -119,6 +137,10 @@ def oracle_cache(kf, vf, B, Hkv, N, d):
     if "sign" in kf:
         cache["k_sign"] = kf["sign"].reshape(B, Hkv, N, d)
         cache["k_rnorm"] = kf["rnorm"].reshape(B, Hkv, N)
+    if "dither" in kf:
+        cache["k_dither"] = kf["dither"].reshape(B, Hkv, N)
+    if "dither" in vf:
+        cache["v_dither"] = vf["dither"].reshape(B, Hkv, N)
     return cache
 
 
@@ -127,7 +149,10 @@ def score_scale(q, R, S, ck, cache, N, G, qjl):
     Bn, Hq, Tq, d = q.shape
     qn = np.linalg.norm(q.astype(np.float64), axis=-1)                    # [B,Hq,Tq]
     q1 = np.abs(q.astype(np.float64) @ S.T).sum(axis=-1) if qjl else 0.0  # ||S q||_1
-    cn = np.linalg.norm(ck[cache["k_idx"][:, :, :N]], axis=-1)            # [B,Hkv,N]
+    kc = ck[cache["k_idx"][:, :, :N]]
+    if "k_dither" in cache:                                               # dithered variant
+        kc = kc + cache["k_dither"][:, :, :N, None]
+    cn = np.linalg.norm(kc, axis=-1)                                      # [B,Hkv,N]
     kap = math.sqrt(math.pi / 2) / d
     out = np.empty((Bn, Hq, Tq, N))
     for h in range(Hq):
@@ -200,7 +225,10 @@ def run_quantize_both(cfg, x_np, which, layer=None, olayer=None):
     torch.cuda.synchronize()
     c, bnd = (olayer.ck, olayer.bk) if which == B.TQ_KEYS else (olayer.cv, olayer.bv)
     Sm = olayer.S if (which == B.TQ_KEYS and cfg.k_qjl) else None
-    enc = codec.encode_rows(x_np.reshape(-1, d), olayer.R, c, bnd, Sm)
+    dith = olayer.offsets(which, S, n)
+    enc = codec.encode_rows(x_np.reshape(-1, d), olayer.R, c, bnd, Sm, dither=dith)
+    if dith is not None:
+        enc["dither"] = dith
     return layer, olayer, cache, enc, cap
 
 

@@ -257,6 +257,40 @@ def test_beta_codebook_end_to_end(name):
     _check_dequantize(cfg, B.TQ_VALUES)
 
 
+# The dithered randomized Hadamard variant (thelatestinai.com paper page
+# 2606.10458, third abstract): one seeded offset per token is subtracted from
+# its rotated coordinates before quantizing and added back in every
+# reconstruction.  d = 64 decodes on the scalar kernels, d = 128 and 256 on the
+# matrix-core split kernel with 4- and 8-row groups; 128 query rows per KV head
+# would take the many-rows kernel for other layers.  Zero key rows, causal
+# chunks and ragged lengths included.
+DITHER_CASES = {
+    "d128 fp16 K3 V2, 4 rows per KV head": workloads.CONFIGS["C2"].with_(
+        Hq=8, Hkv=2, N=301, k_bits=3, k_qjl=0, v_bits=2, rot="hadamard", dither=1),
+    "d128 fp16 K2 V3, 8 heads x 4 causal tokens": workloads.CONFIGS["C4"].with_(
+        B=1, N=203, Tq=4, k_qjl=0, v_bits=3, rot="hadamard", dither=1),
+    "d128 fp16 K1 V4, 128 rows per KV head": workloads.CONFIGS["C4"].with_(
+        B=1, N=150, k_bits=1, k_qjl=0, v_bits=4, rot="hadamard", dither=1),
+    "d256 fp16 K4 V4": workloads.CONFIGS["C5"].with_(B=1, Hq=8, Hkv=2, N=301, dither=1),
+    "d256 fp16 K2 V1, exact-law codebook": workloads.CONFIGS["C5"].with_(
+        B=1, Hq=8, Hkv=2, N=97, k_bits=2, v_bits=1, codebook="beta", dither=1),
+    "d64 fp32 K1 V4": workloads.CONFIGS["C1"].with_(
+        d=64, Hq=4, Hkv=2, N=133, k_bits=1, k_qjl=0, v_bits=4, rot="hadamard", dither=1),
+}
+
+
+@pytest.mark.parametrize("name", list(DITHER_CASES))
+def test_dithered_hadamard_end_to_end(name):
+    cfg = DITHER_CASES[name]
+    H.log(f"[dithered hadamard] {name}")
+    xk, xv = _kv(cfg, "K", seed=19), _kv(cfg, "V", seed=19)
+    xk[:, 5] = 0  # zero key rows: codes of -delta
+    _decode_check(cfg, xk, xv, workloads.q_numpy(cfg, seed=19), name)
+    for which in (B.TQ_KEYS, B.TQ_VALUES):
+        err = _check_dequantize(cfg, which)
+        H.log(f"  dequantize which={which}: max error / norm {err:.2e}")
+
+
 @pytest.mark.parametrize("qjl", [0, 1])
 @pytest.mark.parametrize("d,rows", [(128, 4), (256, 4), (128, 64)])
 def test_decode_all_width_pairs(d, rows, qjl):
@@ -400,7 +434,8 @@ def _check_dequantize(cfg, which, n_out=None):
     got = B.dequantize(layer, which, cache, n_out).cpu().numpy().reshape(-1, d)
     c, bnd = (ol.ck, ol.bk) if which == B.TQ_KEYS else (ol.cv, ol.bv)
     keep = np.array([s * n + t for s in range(S) for t in range(n_out)], dtype=np.int64)
-    ref = codec.reconstruct_mse(enc["idx"][keep], enc["norm"][keep], ol.R, c)
+    dith = enc["dither"][keep] if "dither" in enc else None
+    ref = codec.reconstruct_mse(enc["idx"][keep], enc["norm"][keep], ol.R, c, dither=dith)
     rows = np.array([s * cap + t for s in range(S) for t in range(n)])
     bits = cfg.k_bits if which == B.TQ_KEYS else cfg.v_bits
     gidx = (H.gpu_codes_key(cache, S, cap, d, bits, rows) if which == B.TQ_KEYS
@@ -481,6 +516,8 @@ def test_dequantize_prod(name):
 
 APPEND_CASES = {
     "haar-d128-f16": workloads.CONFIGS["C2"].with_(N=40),
+    "dithered-hadamard-d128-f16": workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=40, d=128, k_bits=2,
+                                                                 v_bits=3, dither=1),
     "hadamard-d256-f16": workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=40),
     "hadamard-d64-f32": workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=40, d=64, dtype="f32",
                                                        k_bits=2, v_bits=3),
@@ -515,7 +552,14 @@ def test_append_in_pieces_matches_one_call(case):
             g1 = codec.unpack_value_codes(parts["idx"].cpu().numpy(), cfg.v_bits, S, 48, d)
             changed = (g0 != g1).any(axis=2)
             assert not changed[:, :21].any() and not changed[:, 22:40].any()
-            assert (g1[:, 21] == (1 << (cfg.v_bits - 1)) - 1).all()  # zero row: lower-middle code
+            if cfg.dither:
+                # zero row of the dithered variant: the codes of -delta (token 21's offset)
+                ol = H.OracleLayer(cfg)
+                dl = ol.offsets(B.TQ_VALUES, S, 1, t0=21)
+                exp = codec.encode_rows(np.zeros((S, d)), ol.R, ol.cv, ol.bv, dither=dl)["idx"]
+                assert (g1[:, 21] == exp).all()
+            else:
+                assert (g1[:, 21] == (1 << (cfg.v_bits - 1)) - 1).all()  # zero row: lower-middle code
         assert torch.equal(parts["norm"].view(S, 48)[:, 21], torch.zeros(S, device="cuda"))
 
 

@@ -93,9 +93,32 @@ def test_layer_flags_and_codebook_law_are_checked(lib):
     b = (ctypes.c_float * 3)()
     assert lib.tq_get_codebook_law(128, 2, 2, c, b) == B.TQ_ERR_INVALID_ARG
     Lf = _layer()
-    Lf.flags = 2
+    Lf.flags = 4
     K = _cache()
     assert lib.tq_quantize_kv(ctypes.byref(Lf), 0, 4096, 1, 2, 8, 0, ctypes.byref(K), None) == B.TQ_ERR_INVALID_ARG
+    assert "flags" in _err(lib)
+
+
+def test_dither_needs_hadamard_without_qjl(lib):
+    """The dithered variant is defined on the randomized Hadamard rotation, for
+    MSE-only keys; other layers asking for it are refused before any GPU call."""
+    L = B.tq_layer()
+    nb = lib.tq_layer_blob_bytes(128)
+    D = B.TQ_LAYER_DITHER
+    # Haar rotation
+    assert lib.tq_make_layer(ctypes.byref(L), 128, B.TQ_ROT_HAAR, 0, 2, 0, 2, D, 4096, nb, None) == B.TQ_ERR_INVALID_ARG
+    assert "Hadamard" in _err(lib)
+    # keys with QJL
+    assert lib.tq_make_layer(ctypes.byref(L), 128, B.TQ_ROT_HADAMARD, 0, 2, 1, 2, D, 4096, nb, None) == \
+        B.TQ_ERR_INVALID_ARG
+    assert L.d == 0
+    for rot, qjl in ((0, 0), (1, 1)):
+        Lf = _layer(qjl=qjl)
+        Lf.rot, Lf.flags = rot, D
+        K = _cache(qjl=bool(qjl))
+        assert lib.tq_quantize_kv(ctypes.byref(Lf), 0, 4096, 1, 2, 8, 0, ctypes.byref(K), None) == \
+            B.TQ_ERR_INVALID_ARG
+        assert "DITHER" in _err(lib)
 
 
 def test_cache_bytes(lib):

@@ -55,6 +55,11 @@ def _reconstruct_prod_wrong_kappa(idx, norm, sign, rnorm, R, centroids, S):
 _orig_encode = codec.encode_rows
 
 
+def _encode_dither_added(x, R, centroids, boundaries, S=None, dither=None):
+    """The offset added before quantizing instead of subtracted."""
+    return _orig_encode(x, R, centroids, boundaries, S, None if dither is None else -np.asarray(dither))
+
+
 def _hadamard_signs_after(d, seed):
     """D H instead of H D: the signs scale the rows of the transform."""
     return transforms.rademacher_signs(d, seed)[:, None] * transforms.sylvester_hadamard(d)
@@ -106,6 +111,8 @@ def _decode_variant(mutation):
      [pins.test_slopes_mse_only_biased_qjl_unbiased, pins.test_unbiased_and_variance_bound]),
     ("Hadamard signs applied after the transform", ("transforms", "hadamard_rotation", _hadamard_signs_after),
      [lambda: pins.test_hadamard_applies_signs_before_transform(64)]),
+    ("dither added instead of subtracted", ("codec", "encode_rows", _encode_dither_added),
+     [pins.test_dithered_hadamard_mse_within_the_bound, lambda: pins.test_decode_equals_dense_bruteforce("dither")]),
     ("exact-law exponent (d-1)/2", ("codebook", "lloyd_max_beta", _beta_wrong_exponent),
      [lambda: pins.test_beta_codebook_one_bit_closed_form(64), lambda: pins.test_beta_codebook_d3_is_the_uniform_quantizer(2),
       pins.test_beta_codebook_mse_on_rotated_unit_vectors]),

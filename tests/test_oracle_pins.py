@@ -23,8 +23,13 @@ Parity status per oracle function:
                         unbiasedness, variance bound.
   codec.pack_*          hand-worked bytes in tests/golden/bit_layouts.txt.
   attention.decode      estimator identity s = <q, x_hat>/sqrt(d), dense
-                        softmax brute force, N=1, identical keys, retrieval,
-                        causal alignment, score error falls with bits.
+                        softmax brute force (also dithered), N=1, identical
+                        keys, retrieval, causal alignment, score error falls
+                        with bits.
+  codec.dither_offsets  uniform over the central centroid spacing, K / V and
+                        sequences independent; dithered HD MSE within the
+                        pi sqrt(3)/2 4^-b bound and decreasing in b; the offset
+                        moves the reconstruction only along D e_0.
 """
 import math
 import os
@@ -310,6 +315,61 @@ def test_beta_codebook_mse_on_rotated_unit_vectors():
     assert err.mean() == pytest.approx(want, abs=4 * err.std() / math.sqrt(err.size / 2))
 
 
+# -------------------------------------------- dithered Hadamard variant --
+# thelatestinai.com paper page 2606.10458, third abstract: randomized Hadamard
+# HD, then a random scalar offset subtracted before quantizing; the dithered
+# TurboQuant's MSE is (pi sqrt(3)/2 + o(1)) 4^-b.
+
+def test_dither_offsets_uniform_and_independent():
+    c, _ = codebook.codebook(3, 128)
+    w = float(c[4]) - float(c[3])
+    t = np.arange(20000)
+    zero = np.zeros_like(t)
+    dk = codec.dither_offsets(11, "K", zero, t, c)
+    assert (np.abs(dk) < w / 2).all()
+    assert stats.kstest(dk / w + 0.5, "uniform").pvalue > 1e-3
+    dv = codec.dither_offsets(11, "V", zero, t, c)
+    d1 = codec.dither_offsets(11, "K", zero + 1, t, c)
+    assert abs(np.corrcoef(dk, dv)[0, 1]) < 0.05 and abs(np.corrcoef(dk, d1)[0, 1]) < 0.05
+
+
+def _dithered_mse(bits, d, n, seed):
+    rs = np.random.default_rng(seed)
+    HD = transforms.hadamard_rotation(d, seed)
+    u = _unit_rows(rs, n, d)
+    c, beta = codebook.codebook(bits, d)
+    dl = codec.dither_offsets(seed, "K", np.zeros(n, np.int64), np.arange(n), c)
+    enc = codec.encode_rows(u, HD, c, beta, dither=dl)
+    xh = codec.reconstruct_mse(enc["idx"], enc["norm"], HD, c, dither=dl)
+    return ((xh - u) ** 2).sum(axis=1).mean()
+
+
+def test_dithered_hadamard_mse_within_the_bound():
+    mses = [_dithered_mse(b, 256, 3000, 21) for b in (1, 2, 3, 4)]
+    for b, m in zip((1, 2, 3, 4), mses):
+        assert m <= PANTER_DITE * 4.0 ** -b
+    assert all(mses[i + 1] < mses[i] for i in range(3))
+
+
+def test_dithered_reconstruction_moves_only_along_d_e0():
+    # The offset is added to every rotated coordinate: (H D)^T (delta 1) =
+    # delta D H 1 = delta sqrt(d) D_0 e_0 (H 1 = sqrt(d) e_0 for the Sylvester
+    # H), so the dithered reconstruction differs from the plain one only in
+    # coordinate 0, by n delta sqrt(d) D_0.
+    d, seed = 64, 5
+    HD = transforms.hadamard_rotation(d, seed)
+    D0 = float(rng.signs(seed, rng.TAG_SIGNS, 1)[0])
+    rs = np.random.default_rng(5)
+    x = rs.standard_normal((40, d)) * 3.0
+    c, beta = codebook.codebook(2, d)
+    dl = codec.dither_offsets(seed, "V", np.zeros(40, np.int64), np.arange(40), c)
+    enc = codec.encode_rows(x, HD, c, beta, dither=dl)
+    diff = (codec.reconstruct_mse(enc["idx"], enc["norm"], HD, c, dither=dl)
+            - codec.reconstruct_mse(enc["idx"], enc["norm"], HD, c))
+    assert np.abs(diff[:, 1:]).max() < 1e-12
+    assert np.allclose(diff[:, 0], enc["norm"] * dl * math.sqrt(d) * D0, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------- codec --
 
 def test_encode_matches_nearest_centroid_bruteforce():
@@ -478,23 +538,39 @@ def _encode_tiny(rs, B, Hkv, N, d, kb, vb, qjl, P, S, ck, bk, cv, bv, kscale=1.0
     return K, V, ek, ev, cache
 
 
-@pytest.mark.parametrize("qjl", [0, 1])
+@pytest.mark.parametrize("qjl", [0, 1, "dither"])
 def test_decode_equals_dense_bruteforce(qjl):
     # Estimator identity: s = <q, x_hat_k>/sqrt(d) with the explicit two-stage
     # (or MSE) reconstruction, and out = softmax(s) @ x_hat_v.  Pins the
     # pre-rotation trick, the QJL factor, the 1/sqrt(d) scaling, the GQA map
     # and the un-rotation against a plain dense computation.
-    rs = np.random.default_rng(10 + qjl)
+    dither = qjl == "dither"
+    qjl = 1 if qjl == 1 else 0
+    rs = np.random.default_rng(10 + qjl + 2 * dither)
     B, Hq, Hkv, Tq, N, d = 2, 4, 2, 3, 9, 16
     P, S, ck, bk, cv, bv = _tiny_layer(rs, d, 2, 3, qjl)
-    K, V, ek, ev, cache = _encode_tiny(rs, B, Hkv, N, d, 2, 3, qjl, P, S, ck, bk, cv, bv)
+    if dither:
+        P = transforms.hadamard_rotation(d, 4)
+        seq = np.repeat(np.arange(B * Hkv), N)
+        tok = np.tile(np.arange(N), B * Hkv)
+        dk = codec.dither_offsets(4, "K", seq, tok, ck)
+        dv = codec.dither_offsets(4, "V", seq, tok, cv)
+        K = rs.standard_normal((B * Hkv * N, d))
+        V = rs.standard_normal((B * Hkv * N, d))
+        ek = codec.encode_rows(K, P, ck, bk, dither=dk)
+        ev = codec.encode_rows(V, P, cv, bv, dither=dv)
+        cache = {"k_idx": ek["idx"].reshape(B, Hkv, N, d), "k_norm": ek["norm"].reshape(B, Hkv, N),
+                 "k_dither": dk.reshape(B, Hkv, N), "v_dither": dv.reshape(B, Hkv, N),
+                 "v_idx": ev["idx"].reshape(B, Hkv, N, d), "v_norm": ev["norm"].reshape(B, Hkv, N)}
+    else:
+        K, V, ek, ev, cache = _encode_tiny(rs, B, Hkv, N, d, 2, 3, qjl, P, S, ck, bk, cv, bv)
     q = rs.standard_normal((B, Hq, Tq, d))
     out, scores = attention.decode(q, P, S, ck, cv, cache, N, causal=False)
     if qjl:
         kh = codec.reconstruct_prod(ek["idx"], ek["norm"], ek["sign"], ek["rnorm"], P, ck, S)
     else:
-        kh = codec.reconstruct_mse(ek["idx"], ek["norm"], P, ck)
-    vh = codec.reconstruct_mse(ev["idx"], ev["norm"], P, cv)
+        kh = codec.reconstruct_mse(ek["idx"], ek["norm"], P, ck, dither=dk if dither else None)
+    vh = codec.reconstruct_mse(ev["idx"], ev["norm"], P, cv, dither=dv if dither else None)
     kh = kh.reshape(B, Hkv, N, d)
     vh = vh.reshape(B, Hkv, N, d)
     for b in range(B):

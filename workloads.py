@@ -48,6 +48,7 @@ class LayerConfig:
     dist: str           # "normal", "lognormal_channels", "outlier_channels", "student_t5"
     layer_seed: int = 0
     codebook: str = "gaussian"   # codebook law: "gaussian" (N(0, 1/d)) or "beta" (exact coordinate law)
+    dither: int = 0              # 1: dithered randomized Hadamard (per-token offset before quantizing)
 
     @property
     def G(self) -> int:
