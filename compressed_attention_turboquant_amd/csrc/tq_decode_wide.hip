@@ -129,18 +129,24 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
   __builtin_amdgcn_sched_barrier(0);
 
   // Value norms of the lane's keys; keys at or past N carry weight 0 and their
-  // norm words may hold anything, so they count as 0.
+  // norm words may hold anything, so they count as 0.  Key indices are taken
+  // relative to the lane's first key: keys below nrel exist, keys below lrel
+  // are visible to the row (one subtraction per block, not an addition per key).
+  const int kbase = k0 + 8 * g4;
+  const int nrel = N - kbase;
   float vnv[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) vnv[e] = k0 + 8 * g4 + e < N ? cur.vn[e / 4][e % 4] : 0.f;
+  for (int e = 0; e < 8; ++e) vnv[e] = e < nrel ? cur.vn[e / 4][e % 4] : 0.f;
   // Value-norm scale (as in the split kernel): the block's largest norm over
-  // the lane's 8 keys and the four lane groups.
+  // the lane's 8 keys and the four lane groups.  The norms are >= 0, so their
+  // bit patterns order like the values (integer maxima, no NaN handling).
   {
-    float vl = fmaxf(fmaxf(fmaxf(vnv[0], vnv[1]), fmaxf(vnv[2], vnv[3])),
-                     fmaxf(fmaxf(vnv[4], vnv[5]), fmaxf(vnv[6], vnv[7])));
+    uint32_t vb = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vb = max(vb, __float_as_uint(vnv[e]));
+    float vl = __uint_as_float(vb);
     if (__any(vl > ws.vlim)) {
-      vl = fmaxf(vl, __shfl_xor(vl, 16));
-      vl = fmaxf(vl, __shfl_xor(vl, 32));
+      vl = max_over_row_groups(vl);
       int e = 0;
       frexpf(vl, &e);
       const float nsc = fminf(ws.vsc, ldexpf(1.f, kVExp - e));
@@ -157,23 +163,22 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
   h8 ph[CT], pl[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
+    const int lrel = ws.limit[ct] - kbase;
     float s[8];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 8 * g4 + 4 * t + i;
         float v = (cur.kn[t][i] * ws.ca[ct]) * sc[t][ct][i];
         if constexpr (QJL) v = fmaf(cur.kn[t][i] * cur.kg[t][i], fmaf(ws.c2[ct], ss[t][ct][i], ws.c0[ct]), v);
-        v = key < ws.limit[ct] ? v : -INFINITY;
+        v = 4 * t + i < lrel ? v : -INFINITY;
         if constexpr (SCORES) {
-          if (ws.limit[ct] >= 0 && key < N) p.scores[srow[ct] * p.N + key] = v * kLn2;
+          if (ws.limit[ct] >= 0 && 4 * t + i < nrel) p.scores[srow[ct] * p.N + kbase + 4 * t + i] = v * kLn2;
         }
         s[4 * t + i] = v;
       }
     float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_over_row_groups(mx);
     if (__any(mx > ws.m[ct] + kSlack)) {
       const float mnew = fmaxf(ws.m[ct], mx);
       const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(ws.m[ct] - mnew);
@@ -441,9 +446,7 @@ decode_wide_kernel(DecodeMfmaParams p) {
   const float inv_sv = 1.f / (ws.vsc * scale_v);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    float L = ws.lsum[ct];
-    L += __shfl_xor(L, 16);
-    L += __shfl_xor(L, 32);
+    const float L = sum_over_row_groups(ws.lsum[ct]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = row0 + 16 * ct + 4 * g4 + r;
