@@ -242,13 +242,29 @@ decode_wide_kernel(DecodeMfmaParams p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int l16 = lane % 16, g4 = lane / 16;
-  const int64_t seq = blockIdx.x / p.rgroups;
+  // Workgroup -> (sequence, row group).  Workgroups are dealt to the eight
+  // XCDs in turn by their linear index, and each XCD has its own L2: the row
+  // groups of one sequence read the same keys, so they are given indices eight
+  // apart (same XCD, running at about the same time), and the second finds
+  // the keys in L2.  This needs the sequence count to be a multiple of 8 (the
+  // row of workgroups of one split then starts on XCD 0); else the plain order.
+  const int nseq = (int)gridDim.x / p.rgroups;
+  int64_t seq;
+  int rg;
+  if (p.rgroups > 1 && nseq % 8 == 0) {
+    const int x = (int)blockIdx.x, slot = x / 8;
+    rg = slot % p.rgroups;
+    seq = (int64_t)(slot / p.rgroups) * 8 + x % 8;
+  } else {
+    seq = blockIdx.x / p.rgroups;
+    rg = (int)(blockIdx.x % p.rgroups);
+  }
   const int split = blockIdx.y;
   const int64_t b_ = seq / p.Hkv;
   const int hkv = (int)(seq % p.Hkv);
   const int G = p.Hq / p.Hkv;
   const int RH = G * p.Tq;  // query rows of the KV head
-  const int row0 = (int)(blockIdx.x % p.rgroups) * (kWW * kRowsWave) + kRowsWave * wave;
+  const int row0 = rg * (kWW * kRowsWave) + kRowsWave * wave;
   static_assert(kWW * kRowsWave == kWideRowsPerGroup, "row group size");
   auto qrow_of = [&](int c) -> int64_t { return (b_ * p.Hq + (int64_t)hkv * G + c / p.Tq) * p.Tq + c % p.Tq; };
 

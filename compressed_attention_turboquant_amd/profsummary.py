@@ -15,7 +15,9 @@ library kernel) calibrates both counters: its known byte count divided by what
 the counter reports gives the factor that turns a counter reading into bytes.
 
 Writes `kernels_<workload>.md` (per-kernel durations), `traffic_<workload>.md`
-(per-dispatch HBM bytes next to the algorithmic bytes) and, for bench.py,
+(per-dispatch HBM bytes next to the algorithmic bytes), with --sq
+`counters_<workload>.md` (instruction mix per wave, matrix-core and vector-ALU
+busy, LDS bank conflicts from SQ counter runs) and, for bench.py,
 `traffic_decode_<workload>.json` and `traffic_quantize_<workload>.json`, each
 stamped with the digest of the kernel sources they were measured on.
 """
@@ -31,7 +33,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
 
 # (tag, substring of the kernel name) for the launches one library call makes
-DECODE_KERNELS = ("prerotate_ref", "decode_mfma_kernel", "decode_split_ref", "decode_combine_ref",
+DECODE_KERNELS = ("prerotate_ref", "decode_mfma_kernel", "decode_wide_kernel", "decode_split_ref", "decode_combine_ref",
                   "combine_kernel", "combine_rows128_kernel")
 QUANT_KERNELS = ("quantize_mfma_kernel", "quantize_tile_ref", "quantize_fwht")
 DEQUANT_KERNELS = ("dequant_mfma_kernel",)
@@ -118,6 +120,46 @@ def counters(directory, counter):
     return per, COPY_BYTES / (copy * 1024.0)
 
 
+def sq_counters(directories):
+    """Per-kernel mean of every counter in the given --pmc runs' CSVs (library
+    kernels only): {kernel name: {counter: mean per dispatch}}."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in directories:
+        for r in csv.DictReader(open(_one(d, "counter_collection.csv"))):
+            if _is_lib(r["Kernel_Name"]):
+                per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+
+
+# (counter, what it says) for the summary table; per-wave figures divide by SQ_WAVES.
+SQ_PER_WAVE = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD")
+
+
+def counters_table(cfg, sq, digest, cmds):
+    lines = [f"# Shader counters per dispatch, workload {cfg.name}", "",
+             f"Kernel sources digest: `{digest}`", "",
+             "Commands (from the repository root, TMPDIR=/tmp), one counter set per run:", "", "```"]
+    lines += list(cmds) + ["```", "",
+                           "Summary written by `python -m compressed_attention_turboquant_amd.profsummary`.", "",
+                           "Per wave: instructions issued by one wave (SQ_INSTS_* / SQ_WAVES).  MfmaUtil: "
+                           "matrix-core busy cycles over GPU-busy cycles x SIMDs (%).  VALUBusy: vector-ALU "
+                           "busy (%).  LDS conflict: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE, the share "
+                           "of LDS-active cycles lost to bank conflicts.", "",
+                           "| kernel | waves | VALU / wave | MFMA / wave | LDS / wave | SALU / wave | "
+                           "VMEM rd / wave | MfmaUtil % | VALUBusy % | LDS conflict |",
+                           "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for name in sorted(sq):
+        c = sq[name]
+        w = c.get("SQ_WAVES", 0.0)
+        per_wave = [f"{c[k] / w:.0f}" if w and k in c else "-" for k in SQ_PER_WAVE]
+        util = f"{c['MfmaUtil']:.1f}" if "MfmaUtil" in c else "-"
+        busy = f"{c['VALUBusy']:.1f}" if "VALUBusy" in c else "-"
+        conf = (f"{c['SQ_LDS_BANK_CONFLICT'] / c['SQ_LDS_IDX_ACTIVE']:.3f}"
+                if c.get("SQ_LDS_IDX_ACTIVE") else "-")
+        lines.append(f"| `{_short(name)}` | {w:.0f} | " + " | ".join(per_wave) + f" | {util} | {busy} | {conf} |")
+    return lines
+
+
 def packed_bytes(cfg):
     k = cfg.d * cfg.k_bits // 8 + 4 + (cfg.d // 8 + 4 if cfg.k_qjl else 0)
     v = cfg.d * cfg.v_bits // 8 + 4
@@ -133,6 +175,8 @@ def main():
     ap.add_argument("--trace-cmd", required=True)
     ap.add_argument("--fetch-cmd", required=True)
     ap.add_argument("--write-cmd", required=True)
+    ap.add_argument("--sq", nargs="*", default=[], help="directories of --pmc runs with SQ counters")
+    ap.add_argument("--sq-cmd", nargs="*", default=[], help="the commands of those runs")
     ap.add_argument("--out", default="profiles")
     a = ap.parse_args()
 
@@ -213,6 +257,11 @@ def main():
             json.dump({"workload": cfg.name, "sources_digest": digest, "bytes_per_launch": round(val),
                        "algorithmic_bytes_per_launch": alg, "fetch_factor": round(ff, 4),
                        "write_factor": round(fw, 4), "commands": [a.fetch_cmd, a.write_cmd]}, f, indent=1)
+    if a.sq:
+        c = counters_table(cfg, sq_counters(a.sq), digest, a.sq_cmd)
+        with open(os.path.join(a.out, f"counters_{cfg.name}.md"), "w") as f:
+            f.write("\n".join(c) + "\n")
+        t += [""] + c
     print("\n".join(lines + [""] + t))
 
 
