@@ -192,6 +192,52 @@ __device__ __forceinline__ void fill_lut(uint32_t* tab, const float* c, float s,
   }
 }
 
+// Column tables for 4-bit codes: 32 copies of the 256-entry pair table (two
+// fp16 centroids per 4-byte entry), entry e of copy c at dword e * 32 + c.
+// Lane l reads copy l % 32, so every lane of a 32-lane half reads its own bank
+// whatever the codes (random entries of one shared 1 KB table collide in most
+// reads).  32 KB.
+constexpr int kColDwords4 = 256 * 32;
+
+template <int T>
+__device__ __forceinline__ void fill_lut_cols4(uint32_t* tab, const float* c, float s, int tid) {
+  for (int i = tid; i < 256 * 32; i += T) {
+    const int e = i / 32;
+    tab[i] = half_bits(s * c[e & 15]) | (half_bits(s * c[e >> 4]) << 16);
+  }
+}
+
+// decode8 for 4-bit codes from a column table; colp = the lane's copy (tab +
+// l % 32).
+template <int O, int NW>
+__device__ __forceinline__ u4 decode8_cols4(const uint32_t (&w)[NW], const uint32_t* colp) {
+  u4 r;
+  sfor<0, 4>([&](auto i) {
+    r[decltype(i)::value] = colp[32 * field<O + 8 * decltype(i)::value, 8, 0>(w)];
+  });
+  return r;
+}
+
+// Code -> fp16 operand lookup from the kernel's table for BITS-bit codes: the
+// column table (COL, 4-bit codes) or the shared table.
+template <int BITS, bool COL, int O, int NW>
+__device__ __forceinline__ u4 lookup8(const uint32_t (&w)[NW], const uint32_t* tab, const uint32_t* colp) {
+  if constexpr (COL)
+    return decode8_cols4<O>(w, colp);
+  else
+    return decode8<BITS, O>(w, tab);
+}
+
+// Which tables of a (KB, VB) kernel are column tables: 4-bit ones, unless the
+// other width is 3 (its 32 KB table next to a 32 KB column table would leave
+// room for only one workgroup per CU).
+template <int KB, int VB>
+struct Tables {
+  static constexpr bool kColK = KB == 4 && VB != 3, kColV = VB == 4 && KB != 3;
+  static constexpr int kK = kColK ? kColDwords4 : Lut<KB>::kDwords;
+  static constexpr int kV = KB == VB ? 0 : (kColV ? kColDwords4 : Lut<VB>::kDwords);
+};
+
 // Sign-term B operand: k-block kb, dword w selects exponent bit p = 10 + w of the
 // sign word rotated left by 4*(kb % 4), in both halves.
 template <int W>
@@ -320,6 +366,7 @@ struct WaveState {
   int limit[NR];
   int64_t srow[NR];
   const uint32_t *ktab, *vtab;  // code -> fp16 tables in LDS
+  const uint32_t *kcol, *vcol;  // this lane's copy in a column table
   // Dithered variant: cd = sum_j (R q)_j log2(e) / sqrt(d) per row (the score
   // term of the key offset is n delta cd); dacc = sum over this lane's keys of
   // p n_v delta_v (the value offset's share, the same for every coordinate).
@@ -367,7 +414,9 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
     u4 bk[2][S::KBLK];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      sfor<0, S::KBLK>([&](auto kb) { bk[t][kb] = decode8<KB, 8 * KB * kb>(cur.kw[t], ws.ktab); });
+      sfor<0, S::KBLK>([&](auto kb) {
+        bk[t][kb] = lookup8<KB, Tables<KB, VB>::kColK, 8 * KB * kb>(cur.kw[t], ws.ktab, ws.kcol);
+      });
     __builtin_amdgcn_sched_barrier(0);
     // Phase 2: score MFMAs.
     score_tile(0, bk[0]);
@@ -376,7 +425,9 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       u4 bk[S::KBLK];
-      sfor<0, S::KBLK>([&](auto kb) { bk[kb] = decode8<KB, 8 * KB * kb>(cur.kw[t], ws.ktab); });
+      sfor<0, S::KBLK>([&](auto kb) {
+        bk[kb] = lookup8<KB, Tables<KB, VB>::kColK, 8 * KB * kb>(cur.kw[t], ws.ktab, ws.kcol);
+      });
       __builtin_amdgcn_sched_barrier(0);
       score_tile(t, bk);
     }
@@ -384,7 +435,9 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
   // Phase 3: value-code lookups (the first part at d = 256), in flight while the
   // softmax arithmetic runs.
   u4 bv[kCBp];
-  sfor<0, kCBp>([&](auto cb) { bv[cb] = decode8<VB, 8 * VB * cb>(cur.vw, ws.vtab); });
+  sfor<0, kCBp>([&](auto cb) {
+    bv[cb] = lookup8<VB, Tables<KB, VB>::kColV, 8 * VB * cb>(cur.vw, ws.vtab, ws.vcol);
+  });
   __builtin_amdgcn_sched_barrier(0);
   // Dithered variant: the offsets of this lane's two keys (key and value streams).
   float dk[2] = {0.f, 0.f}, dv[2] = {0.f, 0.f};
@@ -495,7 +548,9 @@ __device__ __forceinline__ void process_block(WaveState<D, KB, QJL, VB, NR>& ws,
     ws.acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(h8, bv[cb]), ws.acc[cb], 0, 0, 0);
   });
   if constexpr (kLean) {
-    sfor<0, kCBp>([&](auto cb) { bv[cb] = decode8<VB, 8 * VB * (cb + kCBp)>(cur.vw, ws.vtab); });
+    sfor<0, kCBp>([&](auto cb) {
+      bv[cb] = lookup8<VB, Tables<KB, VB>::kColV, 8 * VB * (cb + kCBp)>(cur.vw, ws.vtab, ws.vcol);
+    });
     sfor<0, kCBp>([&](auto cb) {
       ws.acc[cb + kCBp] =
           __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, __builtin_bit_cast(h8, bv[cb]), ws.acc[cb + kCBp], 0, 0, 0);
@@ -599,8 +654,8 @@ decode_mfma_kernel(DecodeMfmaParams p) {
   constexpr int RW = 4 * NR;  // query rows per workgroup
   // One table serves keys and values when their widths match (the codebook and
   // its fp16 factor depend only on the width and the head dimension).
-  constexpr int kKtab = Lut<KB>::kDwords, kVtab = KB == VB ? 0 : Lut<VB>::kDwords;
-  __shared__ __align__(16) uint32_t lut[kKtab + kVtab];
+  using TB = Tables<KB, VB>;
+  __shared__ __align__(16) uint32_t lut[TB::kK + TB::kV];
   __shared__ __align__(16) _Float16 pbuf[W][2][RW][32];
   __shared__ float mrg_m[W][RW], mrg_l[W][RW];
   __shared__ float qsh[RW][D];     // the workgroup's query rows
@@ -652,10 +707,20 @@ decode_mfma_kernel(DecodeMfmaParams p) {
 
   WaveState<D, KB, QJL, VB, NR> ws;
   const float scale_k = p.scales[0], scale_v = KB == VB ? scale_k : p.scales[1];
-  fill_lut<KB, T>(lut, p.cb, scale_k, tid);
-  if constexpr (KB != VB) fill_lut<VB, T>(lut + kKtab, p.cb + 2 * kMaxLevels, scale_v, tid);
+  if constexpr (TB::kColK)
+    fill_lut_cols4<T>(lut, p.cb, scale_k, tid);
+  else
+    fill_lut<KB, T>(lut, p.cb, scale_k, tid);
+  if constexpr (KB != VB) {
+    if constexpr (TB::kColV)
+      fill_lut_cols4<T>(lut + TB::kK, p.cb + 2 * kMaxLevels, scale_v, tid);
+    else
+      fill_lut<VB, T>(lut + TB::kK, p.cb + 2 * kMaxLevels, scale_v, tid);
+  }
   ws.ktab = lut;
-  ws.vtab = KB == VB ? lut : lut + kKtab;
+  ws.vtab = KB == VB ? lut : lut + TB::kK;
+  ws.kcol = ws.ktab + lane % 32;
+  ws.vcol = ws.vtab + lane % 32;
 
   // Rotate the query rows once (R q, S q) and normalise them for the fp16
   // operand split: qa = (R q) / (s_k c1), qb = 2 (S q) / c2 with c1, c2 powers of
