@@ -202,6 +202,8 @@ DequantArgs dequant_args(const tq_layer* layer, int32_t which, const tq_cache* c
   a.R = blob_f(layer, BL.rot);
   a.Rt = blob_f(layer, BL.rot_t);
   a.cent = blob_f(layer, BL.codebook) + (which == TQ_KEYS ? 0 : 2 * kMaxLevels);
+  a.rot = layer->rot;
+  a.dsign = blob_f(layer, BL.signs);
   a.out = out;
   a.out_dtype = out_dtype;
   a.dither = (layer->flags & TQ_LAYER_DITHER) != 0;
@@ -535,7 +537,7 @@ tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* ca
                         void* out, int32_t out_dtype, void* stream) {
   tq_status s = check_dequantize(layer, which, cache, n, out, out_dtype, false);
   if (s != TQ_OK) return s;
-  return hip_status(launch_dequant_mfma(dequant_args(layer, which, cache, n, out, out_dtype),
+  return hip_status(launch_dequant(dequant_args(layer, which, cache, n, out, out_dtype),
                                         static_cast<hipStream_t>(stream)),
                     "dequantize launch");
 }
@@ -545,7 +547,7 @@ tq_status tq_dequantize_prod(const tq_layer* layer, int32_t which, const tq_cach
   tq_status s = check_dequantize(layer, which, cache, n, out, out_dtype, true);
   if (s != TQ_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  s = hip_status(launch_dequant_mfma(dequant_args(layer, which, cache, n, out, out_dtype), st), "dequantize launch");
+  s = hip_status(launch_dequant(dequant_args(layer, which, cache, n, out, out_dtype), st), "dequantize launch");
   if (s != TQ_OK) return s;
   const BlobLayout BL = blob_layout(layer->d);
   DequantQjlArgs q{};

@@ -53,6 +53,8 @@ struct DequantArgs {
   int64_t seqs, n, cap;
   int d, bits, value_layout;
   const float *R, *Rt, *cent;  // R and R^T row-major
+  int rot;                      // TQ_ROT_*: the Hadamard rotation has its own kernel
+  const float* dsign;           // [d] +-1 signs D of the Hadamard rotation
   void* out;
   int out_dtype;
   int dither;  // dithered variant: offsets from the stream at dither_s0, width *dither_w
@@ -154,6 +156,9 @@ constexpr int decode_simd_waves(int d, int qjl, int rows_per_group) {
 hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodeMfmaExtra& x, hipStream_t st);
 hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_dequant_mfma(const DequantArgs& a, hipStream_t st);
+hipError_t launch_dequant_fwht(const DequantArgs& a, hipStream_t st);
+// launch_dequant_fwht for the Hadamard rotation, launch_dequant_mfma otherwise.
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t st);
 hipError_t launch_dequant_qjl(const DequantQjlArgs& a, hipStream_t st);
 bool ref_decode_supports(int d, int rows);
 
