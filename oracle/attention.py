@@ -15,6 +15,11 @@ domain and un-rotated once.
 In the dithered randomized-Hadamard variant the cache also holds each
 token's offset ("k_dither", "v_dither"): the reconstruction is c[idx] + delta.
 
+Values with QJL (TurboQuant_prod on V; [Mobilint] "Two-Stage Approach",
+final reconstruction) carry "v_sign" and "v_rnorm": each value is the
+two-stage reconstruction n (R^T c[idx] + sqrt(pi/2)/d gamma S^T sigma) and
+the output is the softmax-weighted sum of those rows.
+
 Readings (pages silent; parity unpinned by the pages):
   * grouped-query heads: query head h reads KV head h // (Hq / Hkv);
   * with Tq query tokens and `causal`, query i (0-based) sees keys
@@ -86,11 +91,17 @@ def decode(q, R, S, ck, cv, cache: dict, N: int, causal: bool,
         m = s.max(axis=1, keepdims=True)
         p = np.exp(s - m)
         p = p / p.sum(axis=1, keepdims=True)
-        vc = cv[cache["v_idx"][b, g, :N]]
-        if "v_dither" in cache:
-            vc = vc + cache["v_dither"][b, g, :N][:, None]
-        v_rot = cache["v_norm"][b, g, :N][:, None] * vc
-        acc = p @ v_rot                               # [Tq, d], rotated domain
-        out[b, h] = acc @ R                           # row form of R^T acc
+        if "v_sign" in cache:                         # values with QJL: two-stage rows
+            v_hat = codec.reconstruct_prod(cache["v_idx"][b, g, :N], cache["v_norm"][b, g, :N],
+                                           cache["v_sign"][b, g, :N], cache["v_rnorm"][b, g, :N],
+                                           R, cv, S)
+            out[b, h] = p @ v_hat
+        else:
+            vc = cv[cache["v_idx"][b, g, :N]]
+            if "v_dither" in cache:
+                vc = vc + cache["v_dither"][b, g, :N][:, None]
+            v_rot = cache["v_norm"][b, g, :N][:, None] * vc
+            acc = p @ v_rot                           # [Tq, d], rotated domain
+            out[b, h] = acc @ R                       # row form of R^T acc
         scores[b, h] = s
     return out, scores

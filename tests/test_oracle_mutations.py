@@ -44,6 +44,11 @@ def _encode_ge_tie(x, R, centroids, boundaries, S=None):
     return {"idx": idx, "norm": n, "y": y}
 
 
+def _reconstruct_prod_without_qjl(idx, norm, sign, rnorm, R, centroids, S):
+    """The two-stage reconstruction without its QJL term."""
+    return codec.reconstruct_mse(idx, norm, R, centroids)
+
+
 def _reconstruct_prod_wrong_kappa(idx, norm, sign, rnorm, R, centroids, S):
     d = np.asarray(R).shape[0]
     c = np.asarray(centroids, np.float64)
@@ -108,7 +113,10 @@ def _decode_variant(mutation):
     ("ties to the upper index", ("codec", "encode_rows", _encode_ge_tie),
      [pins.test_zero_row_is_lower_middle_index]),
     ("QJL factor pi/2 instead of sqrt(pi/2)", ("codec", "reconstruct_prod", _reconstruct_prod_wrong_kappa),
-     [pins.test_slopes_mse_only_biased_qjl_unbiased, pins.test_unbiased_and_variance_bound]),
+     [pins.test_slopes_mse_only_biased_qjl_unbiased, pins.test_unbiased_and_variance_bound,
+      pins.test_value_qjl_output_unbiased_over_projections]),
+    ("QJL term of the two-stage reconstruction dropped", ("codec", "reconstruct_prod", _reconstruct_prod_without_qjl),
+     [pins.test_value_qjl_output_unbiased_over_projections]),
     ("Hadamard signs applied after the transform", ("transforms", "hadamard_rotation", _hadamard_signs_after),
      [lambda: pins.test_hadamard_applies_signs_before_transform(64)]),
     ("dither added instead of subtracted", ("codec", "encode_rows", _encode_dither_added),

@@ -538,15 +538,16 @@ def _encode_tiny(rs, B, Hkv, N, d, kb, vb, qjl, P, S, ck, bk, cv, bv, kscale=1.0
     return K, V, ek, ev, cache
 
 
-@pytest.mark.parametrize("qjl", [0, 1, "dither"])
+@pytest.mark.parametrize("qjl", [0, 1, "dither", "values"])
 def test_decode_equals_dense_bruteforce(qjl):
     # Estimator identity: s = <q, x_hat_k>/sqrt(d) with the explicit two-stage
     # (or MSE) reconstruction, and out = softmax(s) @ x_hat_v.  Pins the
     # pre-rotation trick, the QJL factor, the 1/sqrt(d) scaling, the GQA map
     # and the un-rotation against a plain dense computation.
     dither = qjl == "dither"
-    qjl = 1 if qjl == 1 else 0
-    rs = np.random.default_rng(10 + qjl + 2 * dither)
+    vqjl = qjl == "values"        # QJL on keys and values
+    qjl = 1 if qjl in (1, "values") else 0
+    rs = np.random.default_rng(10 + qjl + 2 * dither + 4 * vqjl)
     B, Hq, Hkv, Tq, N, d = 2, 4, 2, 3, 9, 16
     P, S, ck, bk, cv, bv = _tiny_layer(rs, d, 2, 3, qjl)
     if dither:
@@ -564,13 +565,20 @@ def test_decode_equals_dense_bruteforce(qjl):
                  "v_idx": ev["idx"].reshape(B, Hkv, N, d), "v_norm": ev["norm"].reshape(B, Hkv, N)}
     else:
         K, V, ek, ev, cache = _encode_tiny(rs, B, Hkv, N, d, 2, 3, qjl, P, S, ck, bk, cv, bv)
+    if vqjl:
+        ev = codec.encode_rows(V, P, cv, bv, S)
+        cache.update({"v_idx": ev["idx"].reshape(B, Hkv, N, d), "v_norm": ev["norm"].reshape(B, Hkv, N),
+                      "v_sign": ev["sign"].reshape(B, Hkv, N, d), "v_rnorm": ev["rnorm"].reshape(B, Hkv, N)})
     q = rs.standard_normal((B, Hq, Tq, d))
     out, scores = attention.decode(q, P, S, ck, cv, cache, N, causal=False)
     if qjl:
         kh = codec.reconstruct_prod(ek["idx"], ek["norm"], ek["sign"], ek["rnorm"], P, ck, S)
     else:
         kh = codec.reconstruct_mse(ek["idx"], ek["norm"], P, ck, dither=dk if dither else None)
-    vh = codec.reconstruct_mse(ev["idx"], ev["norm"], P, cv, dither=dv if dither else None)
+    if vqjl:
+        vh = codec.reconstruct_prod(ev["idx"], ev["norm"], ev["sign"], ev["rnorm"], P, cv, S)
+    else:
+        vh = codec.reconstruct_mse(ev["idx"], ev["norm"], P, cv, dither=dv if dither else None)
     kh = kh.reshape(B, Hkv, N, d)
     vh = vh.reshape(B, Hkv, N, d)
     for b in range(B):
@@ -581,6 +589,44 @@ def test_decode_equals_dense_bruteforce(qjl):
             p = np.exp(s - s.max(axis=1, keepdims=True))
             p /= p.sum(axis=1, keepdims=True)
             assert np.allclose(out[b, h], p @ vh[b, g], rtol=1e-11, atol=1e-12)
+
+
+def test_value_qjl_output_unbiased_over_projections():
+    # With QJL on values every value row is reconstructed without bias over the
+    # projection S (E[sqrt(pi/2)/d ||r|| S^T sign(S r)] = r, [Mobilint]
+    # "Two-Stage Approach"), and the keys (MSE-only) do not depend on S, so
+    # the decode output averaged over many independent S is the
+    # softmax-weighted sum of the exact values.
+    rs = np.random.default_rng(21)
+    d, N = 16, 5
+    P = _random_rotation(rs, d)
+    ck, bk = codebook.codebook(2, d)
+    cv, bv = codebook.codebook(1, d)
+    K = rs.standard_normal((N, d))
+    V = rs.standard_normal((N, d))
+    ek = codec.encode_rows(K, P, ck, bk)
+    q = rs.standard_normal((1, 1, 1, d))
+    runs = 4000
+    acc = np.zeros(d)
+    for _ in range(runs):
+        S = rs.standard_normal((d, d))
+        ev = codec.encode_rows(V, P, cv, bv, S)
+        cache = {"k_idx": ek["idx"].reshape(1, 1, N, d), "k_norm": ek["norm"].reshape(1, 1, N),
+                 "v_idx": ev["idx"].reshape(1, 1, N, d), "v_norm": ev["norm"].reshape(1, 1, N),
+                 "v_sign": ev["sign"].reshape(1, 1, N, d), "v_rnorm": ev["rnorm"].reshape(1, 1, N)}
+        out, scores = attention.decode(q, P, S, ck, cv, cache, N, causal=False)
+        acc += out[0, 0, 0]
+    s = scores[0, 0, 0]
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    want = p @ V
+    # per coordinate, the QJL noise of one run is of order ||V|| / sqrt(d) per row
+    err = np.abs(acc / runs - want).max()
+    assert err < 0.1, err
+    # and the MSE-only value reconstruction is biased for 1-bit codes (pins
+    # that the QJL term is there): its error is several times larger
+    mse = p @ codec.reconstruct_mse(ev["idx"], ev["norm"], P, cv)
+    assert np.abs(mse - want).max() > 3 * err
 
 
 def test_decode_single_key_and_identical_keys():
