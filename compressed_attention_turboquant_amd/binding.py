@@ -20,6 +20,7 @@ TQ_KEYS, TQ_VALUES = 0, 1
 TQ_LAW_GAUSSIAN, TQ_LAW_BETA = 0, 1
 TQ_LAYER_BETA_CODEBOOK = 1
 TQ_LAYER_DITHER = 2
+TQ_LAYER_VALUE_QJL = 4
 
 EXPORTS = ["tq_abi_version", "tq_status_string", "tq_last_error", "tq_layer_blob_bytes",
            "tq_cache_bytes", "tq_make_rotation", "tq_make_layer", "tq_host_tables", "tq_get_codebook",

@@ -15,11 +15,17 @@ thread_local std::string g_last_error;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-constexpr int32_t kKnownLayerFlags = TQ_LAYER_BETA_CODEBOOK | TQ_LAYER_DITHER;
+constexpr int32_t kKnownLayerFlags = TQ_LAYER_BETA_CODEBOOK | TQ_LAYER_DITHER | TQ_LAYER_VALUE_QJL;
 // The dithered variant is defined for the randomized Hadamard rotation and
 // keys without QJL.
 bool dither_ok(int32_t flags, int32_t rot, int32_t k_qjl) {
-  return !(flags & TQ_LAYER_DITHER) || (rot == TQ_ROT_HADAMARD && k_qjl == 0);
+  return !(flags & TQ_LAYER_DITHER) ||
+         (rot == TQ_ROT_HADAMARD && k_qjl == 0 && !(flags & TQ_LAYER_VALUE_QJL));
+}
+
+// Whether rows of tensor `which` carry QJL sign bits and residual norms.
+bool rows_qjl(const tq_layer* L, int which) {
+  return which == TQ_KEYS ? L->k_qjl != 0 : (L->flags & TQ_LAYER_VALUE_QJL) != 0;
 }
 
 // The kernels address one sequence of a cache array through 32-bit byte
@@ -40,11 +46,13 @@ struct Plan {  // split-K plan of one decode call
   size_t off_qrot, off_qproj, off_part, total;
 };
 
-// dither: the dithered variant, which the many-rows kernel does not implement.
-Plan decode_plan(int d, int qjl, int dither, int B, int Hq, int Hkv, int Tq, int64_t N) {
+// dither: the dithered variant, which the many-rows kernel does not implement;
+// vqjl: values with QJL, which only the reference kernels implement (their
+// partial rows also carry the sum of the values' QJL terms).
+Plan decode_plan(int d, int qjl, int dither, int vqjl, int B, int Hq, int Hkv, int Tq, int64_t N) {
   Plan p{};
   const int64_t seqs = (int64_t)B * Hkv;
-  p.mfma = mfma_decode_supports(d, Hq / Hkv * Tq);
+  p.mfma = !vqjl && mfma_decode_supports(d, Hq / Hkv * Tq);
   if (p.mfma) {
     // Work in blocks of 32 keys.  A workgroup serves up to 4 (or 8) query rows
     // of one KV head; split the keys so that the workgroups fill the chip's 256
@@ -54,9 +62,9 @@ Plan decode_plan(int d, int qjl, int dither, int B, int Hq, int Hkv, int Tq, int
     // workspace size does too.
     const int64_t blocks = (N + 31) / 32;
     if (!dither && decode_is_wide(d, Hq / Hkv * Tq)) {
-      // One 4-wave workgroup per CU (each wave holds 32 query rows' operands
-      // and accumulators, one wave per SIMD); split the keys so that the
-      // workgroups fill the 256 CUs once, each split at least 8 blocks.
+      // 4-wave workgroups of 64 query rows (16 per wave), kWideGroupsPerCU
+      // per CU; split the keys so that the workgroups fill the 256 CUs once,
+      // each split at least 8 blocks.
       const int64_t groups = seqs * ((Hq / Hkv * Tq + kWideRowsPerGroup - 1) / kWideRowsPerGroup);
       int64_t want = (256 * kWideGroupsPerCU + groups - 1) / groups;
       const int64_t max_split = (blocks + 7) / 8;
@@ -109,7 +117,7 @@ Plan decode_plan(int d, int qjl, int dither, int B, int Hq, int Hkv, int Tq, int
   const size_t qbytes = p.mfma ? 0 : (size_t)p.rows_total * d * sizeof(float);
   p.off_qrot = o;  o = align_up(o + qbytes, 256);
   p.off_qproj = o; o = align_up(o + qbytes, 256);
-  p.off_part = o;  o = align_up(o + (size_t)p.nsplit * p.rows_total * (d + kPartPad) * sizeof(float), 256);
+  p.off_part = o;  o = align_up(o + (size_t)p.nsplit * p.rows_total * ((vqjl ? 2 * d : d) + kPartPad) * sizeof(float), 256);
   p.total = o;
   return p;
 }
@@ -124,7 +132,7 @@ tq_status check_layer(const tq_layer* L) {
   if (L->k_qjl != 0 && L->k_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "k_qjl must be 0 or 1");
   if (L->flags & ~kKnownLayerFlags) return fail(TQ_ERR_INVALID_ARG, "unknown layer flags");
   if (!dither_ok(L->flags, L->rot, L->k_qjl))
-    return fail(TQ_ERR_INVALID_ARG, "TQ_LAYER_DITHER needs the Hadamard rotation and keys without QJL");
+    return fail(TQ_ERR_INVALID_ARG, "TQ_LAYER_DITHER needs the Hadamard rotation and keys and values without QJL");
   if (!L->blob) return fail(TQ_ERR_INVALID_ARG, "layer blob is NULL");
   if (L->blob_bytes < blob_layout(L->d).total) return fail(TQ_ERR_INVALID_ARG, "layer blob too small");
   return TQ_OK;
@@ -135,10 +143,10 @@ tq_status check_cache(const tq_layer* L, int which, const tq_cache* c, const cha
   if (!c) return fail(TQ_ERR_INVALID_ARG, n + " cache is NULL");
   if (c->seqs < 0) return fail(TQ_ERR_INVALID_ARG, n + ": seqs must be >= 0");
   if (c->cap <= 0 || c->cap % 8) return fail(TQ_ERR_INVALID_ARG, n + ": cap must be a positive multiple of 8");
-  const bool qjl = which == TQ_KEYS && L->k_qjl;
+  const bool qjl = rows_qjl(L, which);
   if (!c->idx || !c->norm) return fail(TQ_ERR_INVALID_ARG, n + ": idx and norm are required");
   if (qjl && (!c->sign || !c->rnorm))
-    return fail(TQ_ERR_INVALID_ARG, n + ": keys with QJL need sign and rnorm");
+    return fail(TQ_ERR_INVALID_ARG, n + ": rows with QJL need sign and rnorm");
   if (!aligned16(c->idx) || !aligned16(c->norm) || (qjl && (!aligned16(c->sign) || !aligned16(c->rnorm))))
     return fail(TQ_ERR_ALIGNMENT, n + ": cache pointers must be 16-byte aligned");
   if (!seq_bytes_ok(L->d, which == TQ_KEYS ? L->k_bits : L->v_bits, c->cap))
@@ -170,9 +178,11 @@ tq_status check_dequantize(const tq_layer* layer, int32_t which, const tq_cache*
     return fail(TQ_ERR_INVALID_ARG, "cache needs seqs >= 0 and cap a positive multiple of 8");
   if (!aligned16(cache->idx) || !aligned16(cache->norm)) return fail(TQ_ERR_ALIGNMENT, "cache pointers must be 16-byte aligned");
   if (prod) {
-    if (which != TQ_KEYS || !layer->k_qjl)
-      return fail(TQ_ERR_INVALID_ARG, "the two-stage reconstruction needs keys of a layer with QJL (k_qjl = 1)");
-    if (!cache->sign || !cache->rnorm) return fail(TQ_ERR_INVALID_ARG, "keys with QJL need sign and rnorm");
+    if (!rows_qjl(layer, which))
+      return fail(TQ_ERR_INVALID_ARG,
+                  "the two-stage reconstruction needs rows with QJL (keys with k_qjl = 1, values with "
+                  "TQ_LAYER_VALUE_QJL)");
+    if (!cache->sign || !cache->rnorm) return fail(TQ_ERR_INVALID_ARG, "rows with QJL need sign and rnorm");
     if (!aligned16(cache->sign) || !aligned16(cache->rnorm))
       return fail(TQ_ERR_ALIGNMENT, "cache pointers must be 16-byte aligned");
   }
@@ -235,10 +245,13 @@ tq_status check_decode(const tq_layer* layer, const void* q, int32_t q_dtype, in
   if (!aligned16(q) || !aligned16(out) || (scores && !aligned16(scores)))
     return fail(TQ_ERR_ALIGNMENT, "q, out and scores must be 16-byte aligned");
   const int rows = Hq / Hkv * Tq;
-  if (!mfma_decode_supports(layer->d, rows) && !ref_decode_supports(layer->d, rows))
+  const bool vqjl = (layer->flags & TQ_LAYER_VALUE_QJL) != 0;
+  if (vqjl ? !ref_decode_supports(layer->d, rows, true)
+           : !mfma_decode_supports(layer->d, rows) && !ref_decode_supports(layer->d, rows, false))
     return fail(TQ_ERR_UNSUPPORTED, "(Hq/Hkv)*Tq too large for this head dimension");
   if ((int64_t)B * Hkv > 0x7FFFFFFF) return fail(TQ_ERR_UNSUPPORTED, "too many sequences");
-  *plan = decode_plan(layer->d, layer->k_qjl, layer->flags & TQ_LAYER_DITHER, B, Hq, Hkv, Tq, N);
+  *plan = decode_plan(layer->d, layer->k_qjl, layer->flags & TQ_LAYER_DITHER, layer->flags & TQ_LAYER_VALUE_QJL, B,
+                      Hq, Hkv, Tq, N);
   if (plan->nsplit > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many key splits");
   return TQ_OK;
 }
@@ -282,6 +295,9 @@ tq_status launch_decode(const tq_layer* layer, const void* q, int32_t q_dtype, i
   a.wide = P.wide;
   a.keys_per_split = P.keys_per_split;
   a.dither = (layer->flags & TQ_LAYER_DITHER) != 0;
+  a.vqjl = (layer->flags & TQ_LAYER_VALUE_QJL) != 0;
+  a.vsign = V->sign;
+  a.vrnorm = V->rnorm;
   a.kd0 = dither_stream_start(layer->seed, kDitherTagKeys);
   a.vd0 = dither_stream_start(layer->seed, kDitherTagValues);
   a.scales = blob_f(layer, BL.scales);
@@ -368,7 +384,7 @@ tq_status tq_cache_bytes(const tq_layer* layer, int32_t which, int64_t seqs, int
   if (bits < 1 || bits > 4) return fail(TQ_ERR_INVALID_ARG, "bit widths must be 1..4");
   if (!seq_bytes_ok(layer->d, bits, cap))
     return fail(TQ_ERR_UNSUPPORTED, "cap * d * bits / 8 must stay below 2^31 - 2^20 bytes per sequence");
-  const bool qjl = which == TQ_KEYS && layer->k_qjl;
+  const bool qjl = rows_qjl(layer, which);
   const size_t tokens = (size_t)seqs * (size_t)cap;
   out[0] = tokens * layer->d * bits / 8;
   out[1] = qjl ? tokens * layer->d / 8 : 0;
@@ -412,7 +428,7 @@ tq_status tq_make_layer(tq_layer* layer, int32_t d, int32_t rot, uint64_t seed, 
   if (k_qjl != 0 && k_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "k_qjl must be 0 or 1");
   if (flags & ~kKnownLayerFlags) return fail(TQ_ERR_INVALID_ARG, "unknown layer flags");
   if (!dither_ok(flags, rot, k_qjl))
-    return fail(TQ_ERR_INVALID_ARG, "TQ_LAYER_DITHER needs the Hadamard rotation and keys without QJL");
+    return fail(TQ_ERR_INVALID_ARG, "TQ_LAYER_DITHER needs the Hadamard rotation and keys and values without QJL");
   if (!dev_blob) return fail(TQ_ERR_INVALID_ARG, "dev_blob is NULL");
   if (!aligned16(dev_blob)) return fail(TQ_ERR_ALIGNMENT, "dev_blob must be 16-byte aligned");
   const BlobLayout BL = blob_layout(d);
@@ -471,7 +487,7 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
   a.cap = cache->cap;
   a.d = layer->d;
   a.bits = which == TQ_KEYS ? layer->k_bits : layer->v_bits;
-  a.qjl = which == TQ_KEYS ? layer->k_qjl : 0;
+  a.qjl = rows_qjl(layer, which) ? 1 : 0;
   a.value_layout = which == TQ_VALUES;
   a.rot = layer->rot;
   a.dsign = blob_f(layer, BL.signs);
@@ -493,6 +509,8 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.dither && !fwht_quantize_supports(a.d, a.rot, a.qjl))
     return fail(TQ_ERR_UNSUPPORTED, "the dithered variant needs the transform quantizer");
+  // Values with QJL: only the reference kernel writes sign rows for the value layout.
+  if (a.value_layout && a.qjl) return hip_status(launch_quantize_ref(a, st), "quantize launch");
   if (fwht_quantize_supports(a.d, a.rot, a.qjl)) return hip_status(launch_quantize_fwht(a, st), "quantize launch");
   if (mfma_quantize_supports(a.d, a.dtype)) return hip_status(launch_quantize_mfma(a, st), "quantize launch");
   return hip_status(launch_quantize_ref(a, st), "quantize launch");
@@ -501,7 +519,8 @@ tq_status tq_quantize_kv(const tq_layer* layer, int32_t which, const void* x, in
 size_t tq_decode_workspace_bytes(const tq_layer* layer, int32_t B, int32_t Hq, int32_t Hkv,
                                  int32_t Tq, int64_t N) {
   if (!layer || !supported_d(layer->d) || B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || N < 1) return 0;
-  return decode_plan(layer->d, layer->k_qjl, layer->flags & TQ_LAYER_DITHER, B, Hq, Hkv, Tq, N).total;
+  return decode_plan(layer->d, layer->k_qjl, layer->flags & TQ_LAYER_DITHER, layer->flags & TQ_LAYER_VALUE_QJL, B,
+                     Hq, Hkv, Tq, N).total;
 }
 
 tq_status tq_attn_decode(const tq_layer* layer, const void* q, int32_t q_dtype, int32_t B,

@@ -41,6 +41,10 @@ struct DecodeArgs {
   int waves;  // waves per decode workgroup (matrix-core kernel)
   bool wide;  // the many-rows kernel (tq_decode_wide.hip)
   int64_t keys_per_split;
+  // Values with QJL (reference kernels): their sign rows and residual norms.
+  int vqjl;
+  const uint8_t* vsign;
+  const float* vrnorm;
   // Dithered variant: key / value offset streams; widths in the blob's scales[4], [5].
   int dither;
   uint64_t kd0, vd0;
@@ -160,6 +164,7 @@ hipError_t launch_dequant_fwht(const DequantArgs& a, hipStream_t st);
 // launch_dequant_fwht for the Hadamard rotation, launch_dequant_mfma otherwise.
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t st);
 hipError_t launch_dequant_qjl(const DequantQjlArgs& a, hipStream_t st);
-bool ref_decode_supports(int d, int rows);
+// vqjl: values with QJL (a second accumulator per query row and coordinate).
+bool ref_decode_supports(int d, int rows, bool vqjl);
 
 }  // namespace tq

@@ -133,17 +133,6 @@ __global__ void __launch_bounds__(kThreads) quantize_tile_ref(
       }
       idx[(s * cap + t) * rb + k] = (uint8_t)byte;
     }
-    if (qjl) {
-      const int sb = d / 8;
-      for (int e = tid; e < 8 * sb; e += kThreads) {
-        const int i = e / sb, k = e % sb;
-        const int64_t t = tile * 8 + i;
-        if (!valid(t)) continue;
-        uint32_t byte = 0;
-        for (int bit = 0; bit < 8; ++bit) byte |= (uint32_t)sg[i * d + k * 8 + bit] << bit;
-        sign[(s * cap + t) * sb + k] = (uint8_t)byte;
-      }
-    }
   } else {
     const int tb = d * bits;  // bytes per 8-token tile
     for (int k = tid; k < tb; k += kThreads) {
@@ -160,6 +149,17 @@ __global__ void __launch_bounds__(kThreads) quantize_tile_ref(
       uint8_t* dst = idx + (s * (cap / 8) + tile) * tb + k;
       if (keep) byte |= *dst & keep;
       *dst = (uint8_t)byte;
+    }
+  }
+  if (qjl) {  // sign rows, one d/8-byte stream per token in both layouts
+    const int sb = d / 8;
+    for (int e = tid; e < 8 * sb; e += kThreads) {
+      const int i = e / sb, k = e % sb;
+      const int64_t t = tile * 8 + i;
+      if (!valid(t)) continue;
+      uint32_t byte = 0;
+      for (int bit = 0; bit < 8; ++bit) byte |= (uint32_t)sg[i * d + k * 8 + bit] << bit;
+      sign[(s * cap + t) * sb + k] = (uint8_t)byte;
     }
   }
 }
@@ -192,14 +192,18 @@ __global__ void __launch_bounds__(kThreads) decode_split_ref(
     const float* __restrict__ knorm, const float* __restrict__ krnorm,
     const uint8_t* __restrict__ vidx, const float* __restrict__ vnorm,
     const float* __restrict__ cb, float* __restrict__ part, float* __restrict__ scores,
-    int dither, uint64_t kd0, uint64_t vd0, const float* __restrict__ dwidth) {
+    int dither, uint64_t kd0, uint64_t vd0, const float* __restrict__ dwidth,
+    int vqjl, const uint8_t* __restrict__ vsign, const float* __restrict__ vrnorm) {
   extern __shared__ float smem[];
   const int G = Hq / Hkv;
   const int rows = G * Tq;
   float* kc = smem;                 // [KC][d]
   float* ks = kc + KC * d;          // [KC][d]
   float* vv = ks + KC * d;          // [KC][d]
-  float* sc = vv + KC * d;          // [rows][KC]
+  // values with QJL: n_v gamma_v sigma_v, the value's QJL term before the
+  // factor sqrt(pi/2)/d and S^T (applied once, in the combine)
+  float* vs = vv + KC * d;          // [KC][d] (vqjl only)
+  float* sc = vs + (vqjl ? KC * d : 0);  // [rows][KC]
   float* mrow = sc + rows * KC;     // [rows]
   float* lrow = mrow + rows;
   float* alpha = lrow + rows;
@@ -226,7 +230,9 @@ __global__ void __launch_bounds__(kThreads) decode_split_ref(
     mrow[r] = -INFINITY;
     lrow[r] = 0.f;
   }
-  const int nacc = (rows * d + kThreads - 1) / kThreads;
+  // accumulator a of this thread: element tid + a kThreads of [rows][d] (the
+  // values' MSE part), then, with vqjl, of [rows][d] again (their QJL part)
+  const int nacc = (rows * d * (vqjl ? 2 : 1) + kThreads - 1) / kThreads;
   float acc[kMaxAcc];
 #pragma unroll
   for (int a = 0; a < kMaxAcc; ++a) acc[a] = 0.f;
@@ -246,6 +252,10 @@ __global__ void __launch_bounds__(kThreads) decode_split_ref(
         if (dither) {  // reconstruction c[idx] + delta
           kc[e] += dither_offset(kd0, seq, t, kw);
           vv[e] = fmaf(vnorm[seq * cap + t], dither_offset(vd0, seq, t, vw), vv[e]);
+        }
+        if (vqjl) {
+          const float g = vnorm[seq * cap + t] * vrnorm[seq * cap + t];
+          vs[e] = stream_code(vsign + (seq * cap + t) * (d / 8), j, 1) ? g : -g;
         }
       }
     }
@@ -299,49 +309,60 @@ __global__ void __launch_bounds__(kThreads) decode_split_ref(
 #pragma unroll
     for (int a = 0; a < kMaxAcc; ++a) {
       if (a < nacc) {
-        const int p = tid + a * kThreads;
-        if (p < rows * d) {
+        const int p0 = tid + a * kThreads;
+        if (p0 < rows * d * (vqjl ? 2 : 1)) {
+          const bool second = p0 >= rows * d;
+          const int p = second ? p0 - rows * d : p0;
           const int r = p / d, j = p % d;
+          const float* src = second ? vs : vv;
           float v = acc[a] * alpha[r];
-          for (int kk = 0; kk < kcount; ++kk) v = fmaf(sc[r * KC + kk], vv[kk * d + j], v);
+          for (int kk = 0; kk < kcount; ++kk) v = fmaf(sc[r * KC + kk], src[kk * d + j], v);
           acc[a] = v;
         }
       }
     }
     __syncthreads();
   }
+  // partial rows: [acc (d) | acc of the QJL terms (d, vqjl only) | max | sum | padding]
+  const int dd = vqjl ? 2 * d : d;
 #pragma unroll
   for (int a = 0; a < kMaxAcc; ++a) {
     if (a < nacc) {
-      const int p = tid + a * kThreads;
-      if (p < rows * d) {
+      const int p0 = tid + a * kThreads;
+      if (p0 < rows * d * (vqjl ? 2 : 1)) {
+        const bool second = p0 >= rows * d;
+        const int p = second ? p0 - rows * d : p0;
         const int r = p / d, j = p % d;
-        part[((int64_t)split * rows_total + qrow_of(r)) * (d + kPartPad) + j] = acc[a];
+        part[((int64_t)split * rows_total + qrow_of(r)) * (dd + kPartPad) + (second ? d : 0) + j] = acc[a];
       }
     }
   }
   for (int r = tid; r < rows; r += kThreads) {
-    float* dst = part + ((int64_t)split * rows_total + qrow_of(r)) * (d + kPartPad) + d;
+    float* dst = part + ((int64_t)split * rows_total + qrow_of(r)) * (dd + kPartPad) + dd;
     dst[0] = mrow[r];
     dst[1] = lrow[r];
   }
 }
 
 // Merge the per-split partial softmax sums and un-rotate once per query row.
-// Partial rows are [acc (d) | max (natural log) | sum | padding], d + kPartPad floats.
+// Partial rows are [acc (d) | max (natural log) | sum | padding], d + kPartPad
+// floats; with values carrying QJL, [acc (d) | acc2 (d) | max | sum | padding]
+// and the output adds sqrt(pi/2)/d S^T acc2 (S row-major).
 __global__ void __launch_bounds__(kThreads) decode_combine_ref(const float* __restrict__ part,
                                                                int nsplit, int64_t rows_total,
                                                                int d, const float* __restrict__ R,
+                                                               int vqjl, const float* __restrict__ S,
                                                                float* __restrict__ out) {
-  __shared__ float o[256];
+  __shared__ float o[2][256];
   __shared__ float wts[2][1024];  // per-split weight, and its contribution to the sum
   __shared__ float invL;
+  const int dd = vqjl ? 2 * d : d, stride = dd + kPartPad;
   const int64_t row = blockIdx.x;
   const int j = threadIdx.x;
   // max over splits, then weights: one thread per split (looping if more splits than threads)
   __shared__ float red[kThreads];
   float M = -INFINITY;
-  for (int s = j; s < nsplit; s += kThreads) M = fmaxf(M, part[((int64_t)s * rows_total + row) * (d + kPartPad) + d]);
+  for (int s = j; s < nsplit; s += kThreads) M = fmaxf(M, part[((int64_t)s * rows_total + row) * stride + dd]);
   red[j] = M;
   __syncthreads();
   for (int off = kThreads / 2; off > 0; off >>= 1) {
@@ -352,10 +373,10 @@ __global__ void __launch_bounds__(kThreads) decode_combine_ref(const float* __re
   __syncthreads();
   float lsum = 0.f;
   for (int s = j; s < nsplit; s += kThreads) {
-    const float* p = part + ((int64_t)s * rows_total + row) * (d + kPartPad);
-    const float w = p[d] == -INFINITY ? 0.f : expf(p[d] - M);
+    const float* p = part + ((int64_t)s * rows_total + row) * stride;
+    const float w = p[dd] == -INFINITY ? 0.f : expf(p[dd] - M);
     if (s < 1024) wts[0][s] = w;
-    lsum = fmaf(w, p[d + 1], lsum);
+    lsum = fmaf(w, p[dd + 1], lsum);
   }
   red[j] = lsum;
   __syncthreads();
@@ -365,27 +386,41 @@ __global__ void __launch_bounds__(kThreads) decode_combine_ref(const float* __re
   }
   if (j == 0) invL = 1.0f / red[0];
   __syncthreads();
-  if (j < d) {
-    float a0 = 0.f, a1 = 0.f;
-    int s = 0;
-    for (; s + 1 < nsplit; s += 2) {
-      const float w0 = s < 1024 ? wts[0][s] : 0.f, w1 = s + 1 < 1024 ? wts[0][s + 1] : 0.f;
-      a0 = fmaf(w0, part[((int64_t)s * rows_total + row) * (d + kPartPad) + j], a0);
-      a1 = fmaf(w1, part[((int64_t)(s + 1) * rows_total + row) * (d + kPartPad) + j], a1);
+  for (int h = 0; h < (vqjl ? 2 : 1); ++h) {
+    if (j < d) {
+      const int c = h * d + j;
+      float a0 = 0.f, a1 = 0.f;
+      int s = 0;
+      for (; s + 1 < nsplit; s += 2) {
+        const float w0 = s < 1024 ? wts[0][s] : 0.f, w1 = s + 1 < 1024 ? wts[0][s + 1] : 0.f;
+        a0 = fmaf(w0, part[((int64_t)s * rows_total + row) * stride + c], a0);
+        a1 = fmaf(w1, part[((int64_t)(s + 1) * rows_total + row) * stride + c], a1);
+      }
+      for (; s < nsplit; ++s) a0 = fmaf(s < 1024 ? wts[0][s] : 0.f, part[((int64_t)s * rows_total + row) * stride + c], a0);
+      o[h][j] = (a0 + a1) * invL;
     }
-    for (; s < nsplit; ++s) a0 = fmaf(s < 1024 ? wts[0][s] : 0.f, part[((int64_t)s * rows_total + row) * (d + kPartPad) + j], a0);
-    o[j] = (a0 + a1) * invL;
   }
   __syncthreads();
   if (j >= d) return;
   float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
   for (int k = 0; k < d; k += 4) {  // (R^T o)_j
-    v0 = fmaf(R[(size_t)k * d + j], o[k], v0);
-    v1 = fmaf(R[(size_t)(k + 1) * d + j], o[k + 1], v1);
-    v2 = fmaf(R[(size_t)(k + 2) * d + j], o[k + 2], v2);
-    v3 = fmaf(R[(size_t)(k + 3) * d + j], o[k + 3], v3);
+    v0 = fmaf(R[(size_t)k * d + j], o[0][k], v0);
+    v1 = fmaf(R[(size_t)(k + 1) * d + j], o[0][k + 1], v1);
+    v2 = fmaf(R[(size_t)(k + 2) * d + j], o[0][k + 2], v2);
+    v3 = fmaf(R[(size_t)(k + 3) * d + j], o[0][k + 3], v3);
   }
-  out[row * d + j] = (v0 + v1) + (v2 + v3);
+  float y = (v0 + v1) + (v2 + v3);
+  if (vqjl) {  // + sqrt(pi/2)/d (S^T o2)_j
+    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+    for (int k = 0; k < d; k += 4) {
+      w0 = fmaf(S[(size_t)k * d + j], o[1][k], w0);
+      w1 = fmaf(S[(size_t)(k + 1) * d + j], o[1][k + 1], w1);
+      w2 = fmaf(S[(size_t)(k + 2) * d + j], o[1][k + 2], w2);
+      w3 = fmaf(S[(size_t)(k + 3) * d + j], o[1][k + 3], w3);
+    }
+    y = fmaf(sqrtf(0.5f * (float)M_PI) / (float)d, (w0 + w1) + (w2 + w3), y);
+  }
+  out[row * d + j] = y;
 }
 
 }  // namespace
@@ -412,14 +447,14 @@ hipError_t launch_quantize_ref(const QuantizeArgs& a, hipStream_t st) {
 
 int ref_decode_kc(int d) { return d >= 256 ? 8 : 16; }
 
-size_t ref_decode_smem(int d, int rows) {
+size_t ref_decode_smem(int d, int rows, bool vqjl) {
   const int KC = ref_decode_kc(d);
-  return sizeof(float) * ((size_t)3 * KC * d + (size_t)rows * KC + 3 * rows + 2 * KC);
+  return sizeof(float) * ((size_t)(vqjl ? 4 : 3) * KC * d + (size_t)rows * KC + 3 * rows + 2 * KC);
 }
 
-bool ref_decode_supports(int d, int rows) {
-  return rows <= kThreads && (int64_t)rows * d <= (int64_t)kMaxAcc * kThreads &&
-         ref_decode_smem(d, rows) <= 64 * 1024;
+bool ref_decode_supports(int d, int rows, bool vqjl) {
+  return rows <= kThreads && (int64_t)rows * d * (vqjl ? 2 : 1) <= (int64_t)kMaxAcc * kThreads &&
+         ref_decode_smem(d, rows, vqjl) <= 64 * 1024;
 }
 
 hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st) {
@@ -429,17 +464,18 @@ hipError_t launch_decode_ref(const DecodeArgs& a, hipStream_t st) {
                      a.d, a.R, a.S, a.qjl, a.q_rot, a.q_proj);
   const int KC = ref_decode_kc(a.d);
   hipLaunchKernelGGL(decode_split_ref, dim3((unsigned)(a.B * a.Hkv), (unsigned)a.nsplit),
-                     dim3(kThreads), ref_decode_smem(a.d, rows), st, a.q_rot, a.q_proj, a.Hq,
+                     dim3(kThreads), ref_decode_smem(a.d, rows, a.vqjl), st, a.q_rot, a.q_proj, a.Hq,
                      a.Hkv, a.Tq, a.N, a.cap, a.causal, a.d, a.kb, a.vb, a.qjl, KC,
                      a.keys_per_split, a.kidx, a.ksign, a.knorm, a.krnorm, a.vidx, a.vnorm,
-                     a.cb, a.part, a.scores, a.dither, a.kd0, a.vd0, a.scales ? a.scales + 4 : nullptr);
+                     a.cb, a.part, a.scores, a.dither, a.kd0, a.vd0, a.scales ? a.scales + 4 : nullptr,
+                     a.vqjl, a.vsign, a.vrnorm);
   return launch_decode_combine(a, st);
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
   const int64_t qrows = (int64_t)a.B * a.Hq * a.Tq;
   hipLaunchKernelGGL(decode_combine_ref, dim3((unsigned)qrows), dim3(kThreads), 0, st, a.part,
-                     a.nsplit, qrows, a.d, a.R, a.out);
+                     a.nsplit, qrows, a.d, a.R, a.vqjl, a.S, a.out);
   return hipGetLastError();
 }
 

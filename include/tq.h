@@ -81,7 +81,7 @@ enum { TQ_ROT_HAAR = 0, TQ_ROT_HADAMARD = 1 };
  * unit vector's coordinate, density proportional to (1 - t^2)^((d-3)/2). */
 enum { TQ_LAW_GAUSSIAN = 0, TQ_LAW_BETA = 1 };
 /* tq_layer.flags */
-enum { TQ_LAYER_BETA_CODEBOOK = 1, TQ_LAYER_DITHER = 2 };
+enum { TQ_LAYER_BETA_CODEBOOK = 1, TQ_LAYER_DITHER = 2, TQ_LAYER_VALUE_QJL = 4 };
 enum { TQ_F32 = 0, TQ_F16 = 1 };
 enum { TQ_KEYS = 0, TQ_VALUES = 1 };
 
@@ -90,7 +90,8 @@ typedef struct tq_layer {
   int32_t d;       /* head dimension: 64, 128 or 256 */
   int32_t rot;     /* TQ_ROT_HAAR or TQ_ROT_HADAMARD */
   int32_t k_bits;  /* MSE bits per key coordinate, 1..4 */
-  int32_t k_qjl;   /* 1: keys also store QJL sign bits and the residual norm */
+  int32_t k_qjl;   /* 1: keys also store QJL sign bits and the residual norm
+                      (values do with the layer flag TQ_LAYER_VALUE_QJL) */
   int32_t v_bits;  /* MSE bits per value coordinate, 1..4 */
   int32_t flags;   /* TQ_LAYER_* bits; 0 for tq_make_rotation */
   uint64_t seed;   /* seed of the rotation, projection and sign streams */
@@ -102,9 +103,10 @@ typedef struct tq_layer {
  * All pointers are device pointers owned by the caller. */
 typedef struct tq_cache {
   uint8_t* idx;   /* codes, seqs*cap*d*bits/8 bytes */
-  uint8_t* sign;  /* keys with QJL: seqs*cap*d/8 bytes; otherwise NULL */
+  uint8_t* sign;  /* rows with QJL (keys with k_qjl, values with TQ_LAYER_VALUE_QJL):
+                     seqs*cap*d/8 bytes; otherwise NULL */
   float* norm;    /* seqs*cap floats */
-  float* rnorm;   /* keys with QJL: seqs*cap floats; otherwise NULL */
+  float* rnorm;   /* rows with QJL: seqs*cap floats; otherwise NULL */
   int64_t seqs;
   int64_t cap;    /* tokens per sequence, a positive multiple of 8 */
 } tq_cache;
@@ -155,7 +157,17 @@ tq_status tq_make_rotation(tq_layer* layer, int32_t d, int32_t rot, uint64_t see
  *                           the layer's SplitMix64 stream with tag 3 (keys) or
  *                           4 (values), regenerated wherever it is needed.
  *                           Needs rot = TQ_ROT_HADAMARD and k_qjl = 0.
- * Unknown flag bits, or TQ_LAYER_DITHER without those, give TQ_ERR_INVALID_ARG. */
+ *   TQ_LAYER_VALUE_QJL      values carry QJL too (TurboQuant_prod on V:
+ *                           [Mobilint] "Two-Stage Approach", applied to the
+ *                           value rows): value caches then hold sign
+ *                           (d/8 bytes per token, one stream per token as for
+ *                           keys) and rnorm, and every value enters decode as
+ *                           its two-stage reconstruction
+ *                           n (R^T c[idx] + sqrt(pi/2)/d gamma S^T sigma).
+ *                           Such layers run the reference (scalar) quantize
+ *                           and decode kernels.  Not with TQ_LAYER_DITHER.
+ * Unknown flag bits, TQ_LAYER_DITHER without those, or both DITHER and
+ * VALUE_QJL, give TQ_ERR_INVALID_ARG. */
 tq_status tq_make_layer(tq_layer* layer, int32_t d, int32_t rot, uint64_t seed, int32_t k_bits,
                         int32_t k_qjl, int32_t v_bits, int32_t flags, void* dev_blob, size_t blob_bytes,
                         void* stream);
@@ -233,13 +245,14 @@ tq_status tq_attn_decode_static(const tq_layer* layer, const void* q, int32_t q_
 tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,
                         void* out, int32_t out_dtype, void* stream);
 
-/* Two-stage reconstruction of keys with QJL ([Mobilint] "Two-Stage Approach",
+/* Two-stage reconstruction of rows with QJL ([Mobilint] "Two-Stage Approach",
  * final reconstruction): tokens 0..n-1 of every sequence become
  *   x_hat = n * (R^T c[idx] + sqrt(pi/2)/d * gamma * S^T sigma),
  * the MSE reconstruction of tq_dequantize plus the QJL back-projection of the
  * residual's sign bits.  Same arguments as tq_dequantize; `which` must be
- * TQ_KEYS of a layer with k_qjl = 1 and the cache must hold sign and rnorm
- * (else TQ_ERR_INVALID_ARG).  Two launches on `stream`: the MSE rows, then
+ * TQ_KEYS of a layer with k_qjl = 1, or TQ_VALUES of a layer with
+ * TQ_LAYER_VALUE_QJL, and the cache must hold sign and rnorm (else
+ * TQ_ERR_INVALID_ARG).  Two launches on `stream`: the MSE rows, then
  * the QJL term added to them in place. */
 tq_status tq_dequantize_prod(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,
                              void* out, int32_t out_dtype, void* stream);

@@ -34,7 +34,7 @@ from . import codec
 
 
 def unpack_cache(packed: dict, B: int, Hkv: int, cap: int, d: int,
-                 k_bits: int, v_bits: int, k_qjl: int) -> dict:
+                 k_bits: int, v_bits: int, k_qjl: int, v_qjl: int = 0) -> dict:
     """Packed arrays in the library layout -> unpacked [B, Hkv, cap, ...] fields."""
     S = B * Hkv
     out = {
@@ -46,6 +46,9 @@ def unpack_cache(packed: dict, B: int, Hkv: int, cap: int, d: int,
     if k_qjl:
         out["k_sign"] = codec.unpack_key_codes(packed["k_sign"], 1, d).reshape(B, Hkv, cap, d) == 1
         out["k_rnorm"] = np.asarray(packed["k_rnorm"], np.float64).reshape(B, Hkv, cap)
+    if v_qjl:  # sign rows have the same per-token layout for values as for keys
+        out["v_sign"] = codec.unpack_key_codes(packed["v_sign"], 1, d).reshape(B, Hkv, cap, d) == 1
+        out["v_rnorm"] = np.asarray(packed["v_rnorm"], np.float64).reshape(B, Hkv, cap)
     return out
 
 

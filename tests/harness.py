@@ -55,6 +55,8 @@ def gpu_layer(cfg):
     flags = B.TQ_LAYER_BETA_CODEBOOK if cfg.codebook == "beta" else 0
     if cfg.dither:
         flags |= B.TQ_LAYER_DITHER
+    if cfg.v_qjl:
+        flags |= B.TQ_LAYER_VALUE_QJL
     return B.make_rotation(cfg.d, rot, cfg.layer_seed, cfg.k_bits, cfg.k_qjl, cfg.v_bits, flags=flags)
 
 
@@ -81,9 +83,10 @@ def compare_codes(gpu_idx, enc, boundaries, what):
     return diff.any(axis=1)
 
 
-def check_keys(gpu_idx, gpu_norm, enc, ol, what, gpu_sign=None, gpu_rnorm=None):
-    """Validate the GPU's key fields against the oracle's encoding `enc` of the
-    same rows and return the oracle's view of those keys as decode inputs.
+def check_keys(gpu_idx, gpu_norm, enc, ol, what, gpu_sign=None, gpu_rnorm=None, values=False):
+    """Validate the GPU's key fields (values' with `values`, which carry QJL
+    when the layer gives them QJL) against the oracle's encoding `enc` of the
+    same rows and return the oracle's view of those rows as decode inputs.
 
     Codes: exact outside the band (compare_codes).  Norms: within 2e-6.  With
     QJL, expected signs and gamma come from the oracle's own codes for rows
@@ -96,7 +99,8 @@ def check_keys(gpu_idx, gpu_norm, enc, ol, what, gpu_sign=None, gpu_rnorm=None):
     oracle's is a legal band choice) and the oracle's fp64 norms and gammas;
     stats counts rows with a band code difference and with a band sign
     difference."""
-    flipped = compare_codes(gpu_idx, enc, ol.bk, what + " codes")
+    c, bnd = (ol.cv, ol.bv) if values else (ol.ck, ol.bk)
+    flipped = compare_codes(gpu_idx, enc, bnd, what + " codes")
     np.testing.assert_allclose(gpu_norm, enc["norm"], rtol=2e-6, atol=0, err_msg=what + ": norms")
     fields = {"idx": gpu_idx, "norm": enc["norm"]}
     if "dither" in enc:
@@ -105,7 +109,7 @@ def check_keys(gpu_idx, gpu_norm, enc, ol, what, gpu_sign=None, gpu_rnorm=None):
     if gpu_sign is not None:
         sign, rnorm, proj = enc["sign"].copy(), enc["rnorm"].copy(), enc["proj"].copy()
         if flipped.any():
-            redo = codec.qjl_stage(enc["u"][flipped], gpu_idx[flipped], ol.R, ol.ck, ol.S)
+            redo = codec.qjl_stage(enc["u"][flipped], gpu_idx[flipped], ol.R, c, ol.S)
             sign[flipped], rnorm[flipped], proj[flipped] = redo["sign"], redo["rnorm"], redo["proj"]
         sdiff = gpu_sign != sign
         bad = sdiff & ~(np.abs(proj) < BAND)
@@ -137,6 +141,9 @@ def oracle_cache(kf, vf, B, Hkv, N, d):
     if "sign" in kf:
         cache["k_sign"] = kf["sign"].reshape(B, Hkv, N, d)
         cache["k_rnorm"] = kf["rnorm"].reshape(B, Hkv, N)
+    if "sign" in vf:
+        cache["v_sign"] = vf["sign"].reshape(B, Hkv, N, d)
+        cache["v_rnorm"] = vf["rnorm"].reshape(B, Hkv, N)
     if "dither" in kf:
         cache["k_dither"] = kf["dither"].reshape(B, Hkv, N)
     if "dither" in vf:
@@ -190,7 +197,10 @@ def upload_packed(layer, cfg, packed, S, cap, device="cuda"):
         "idx": t(packed["k_idx"]), "norm": t(packed["k_norm"]),
         "sign": t(packed["k_sign"]) if cfg.k_qjl else None,
         "rnorm": t(packed["k_rnorm"]) if cfg.k_qjl else None})
-    V = B.Cache(layer, B.TQ_VALUES, S, cap, arrays={"idx": t(packed["v_idx"]), "norm": t(packed["v_norm"])})
+    V = B.Cache(layer, B.TQ_VALUES, S, cap, arrays={
+        "idx": t(packed["v_idx"]), "norm": t(packed["v_norm"]),
+        "sign": t(packed["v_sign"]) if cfg.v_qjl else None,
+        "rnorm": t(packed["v_rnorm"]) if cfg.v_qjl else None})
     return K, V
 
 
@@ -224,7 +234,7 @@ def run_quantize_both(cfg, x_np, which, layer=None, olayer=None):
     B.quantize_kv(layer, which, x, cache)
     torch.cuda.synchronize()
     c, bnd = (olayer.ck, olayer.bk) if which == B.TQ_KEYS else (olayer.cv, olayer.bv)
-    Sm = olayer.S if (which == B.TQ_KEYS and cfg.k_qjl) else None
+    Sm = olayer.S if (cfg.k_qjl if which == B.TQ_KEYS else cfg.v_qjl) else None
     dith = olayer.offsets(which, S, n)
     enc = codec.encode_rows(x_np.reshape(-1, d), olayer.R, c, bnd, Sm, dither=dith)
     if dith is not None:
@@ -249,6 +259,12 @@ def quantize_and_check(cfg, xk, xv, layer=None, ol=None, what=""):
                             gpu_signs(K, S, cap, d, rows), K["rnorm"].cpu().numpy()[rows])
     else:
         kf, st = check_keys(gpu_codes_key(K, S, cap, d, cfg.k_bits, rows), kn, ek, ol, what + " K")
-    vf, st["value_rows"] = check_values(gpu_codes_value(V, S, cap, d, cfg.v_bits)[rows],
-                                        V["norm"].cpu().numpy()[rows], ev, ol, what + " V")
+    vidx = gpu_codes_value(V, S, cap, d, cfg.v_bits)[rows]
+    vn = V["norm"].cpu().numpy()[rows]
+    if cfg.v_qjl:
+        vf, vst = check_keys(vidx, vn, ev, ol, what + " V", gpu_signs(V, S, cap, d, rows),
+                             V["rnorm"].cpu().numpy()[rows], values=True)
+        st["value_rows"], st["value_sign_rows"] = vst["code_rows"], vst["sign_rows"]
+    else:
+        vf, st["value_rows"] = check_values(vidx, vn, ev, ol, what + " V")
     return layer, ol, K, V, oracle_cache(kf, vf, cfg.B, cfg.Hkv, N, d), st

@@ -82,7 +82,8 @@ def _decode_both(cfg, packed, q_np, N, want_scores=True):
     q = torch.from_numpy(q_np).cuda()
     out, scores = B.attn_decode(layer, q, K, V, N, cfg.Hkv, cfg.causal, want_scores=want_scores)
     torch.cuda.synchronize()
-    cache = attention.unpack_cache(packed, cfg.B, cfg.Hkv, cap, cfg.d, cfg.k_bits, cfg.v_bits, cfg.k_qjl)
+    cache = attention.unpack_cache(packed, cfg.B, cfg.Hkv, cap, cfg.d, cfg.k_bits, cfg.v_bits, cfg.k_qjl,
+                                   cfg.v_qjl)
     ref_out, ref_scores = attention.decode(q_np, ol.R, ol.S, ol.ck, ol.cv, cache, N, cfg.causal)
     return out.cpu().numpy(), (scores.cpu().numpy() if scores is not None else None), \
         ref_out, ref_scores, cache, ol
@@ -291,6 +292,52 @@ def test_dithered_hadamard_end_to_end(name):
         H.log(f"  dequantize which={which}: max error / norm {err:.2e}")
 
 
+# Values with QJL (TurboQuant_prod on V; [Mobilint] "Two-Stage Approach",
+# final reconstruction): each value row is n (R^T c[idx] + sqrt(pi/2)/d gamma
+# S^T sigma).  Decode keeps the sum of the softmax-weighted QJL terms beside
+# the MSE sum and back-projects it once per query row.  Haar and Hadamard,
+# d = 64, 128 and 256, keys with and without QJL, causal chunks, up to 64
+# query rows per KV head; a zero value row; ragged lengths.
+VALUE_QJL_CASES = {
+    "haar d128 fp16 K2+QJL V2+QJL, 4 rows per KV head": workloads.CONFIGS["C2"].with_(
+        Hq=8, Hkv=2, N=301, k_bits=2, v_bits=2, v_qjl=1),
+    "haar d128 fp16 K3 V3+QJL, 8 heads x 4 causal tokens": workloads.CONFIGS["C4"].with_(
+        B=1, N=203, Tq=4, k_bits=3, k_qjl=0, v_bits=3, rot="haar", v_qjl=1),
+    "haar d128 fp16 K2+QJL V1+QJL, 64 rows per KV head": workloads.CONFIGS["C2"].with_(
+        Hq=16, Hkv=1, Tq=4, causal=1, N=150, v_bits=1, v_qjl=1),
+    "hadamard d256 fp16 K4 V4+QJL": workloads.CONFIGS["C5"].with_(B=1, Hq=8, Hkv=2, N=155, v_qjl=1),
+    "haar d64 fp32 K1+QJL V4+QJL": workloads.CONFIGS["C1"].with_(
+        d=64, Hq=4, Hkv=2, N=133, k_bits=1, v_bits=4, v_qjl=1),
+}
+
+
+@pytest.mark.parametrize("name", list(VALUE_QJL_CASES))
+def test_values_with_qjl_end_to_end(name):
+    cfg = VALUE_QJL_CASES[name]
+    H.log(f"[values with QJL] {name}")
+    xk, xv = _kv(cfg, "K", seed=23), _kv(cfg, "V", seed=23)
+    xv[:, 3] = 0  # a zero value row: zero norm, no QJL term
+    _decode_check(cfg, xk, xv, workloads.q_numpy(cfg, seed=23), name)
+
+
+@pytest.mark.parametrize("name", list(VALUE_QJL_CASES)[:2])
+def test_values_with_qjl_on_random_cache(name):
+    """Decode alone: seeded random codes, value signs and residual norms."""
+    cfg = VALUE_QJL_CASES[name]
+    cap = (cfg.N + 7) // 8 * 8
+    packed = workloads.random_packed_numpy(cfg, cfg.B * cfg.Hkv, cap, seed=29)
+    q = workloads.q_numpy(cfg, seed=29)
+    out, scores, ref_out, ref_scores, cache, ol = _decode_both(cfg, packed, q, cfg.N)
+    scale = H.score_scale(q, ol.R, ol.S, ol.ck, cache, cfg.N, cfg.G, cfg.k_qjl)
+    H.compare_scores(scores, ref_scores, scale, name)
+    err = H.compare_out(out, ref_out, name)
+    # the values' QJL term is really there: the oracle without it differs
+    mse = {k: v for k, v in cache.items() if k not in ("v_sign", "v_rnorm")}
+    ref_mse, _ = attention.decode(q, ol.R, ol.S, ol.ck, ol.cv, mse, cfg.N, cfg.causal)
+    assert np.abs(ref_mse - ref_out).max() > 50 * max(err, 1e-6)
+    H.log(f"  out abs err {err:.2e}, QJL term up to {np.abs(ref_mse - ref_out).max():.2e}")
+
+
 @pytest.mark.parametrize("qjl", [0, 1])
 @pytest.mark.parametrize("d,rows", [(128, 4), (256, 4), (128, 64)])
 def test_decode_all_width_pairs(d, rows, qjl):
@@ -478,38 +525,50 @@ def test_dequantize_shapes(name, which):
     H.log(f"  max error / norm {err:.2e}")
 
 
-# Two-stage reconstruction of keys with QJL ([Mobilint] "Two-Stage Approach",
-# final reconstruction): every head dimension and both output dtypes, a prefix
-# of the stored tokens, ragged lengths.
+# Two-stage reconstruction of rows with QJL ([Mobilint] "Two-Stage Approach",
+# final reconstruction): keys with QJL and values of layers with QJL on
+# values, every head dimension and both output dtypes, a prefix of the stored
+# tokens, ragged lengths.
 PROD_CASES = {
-    "haar d128 fp16 K2+QJL": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=203, k_bits=2), None),
-    "haar d128 fp16 K3+QJL, first 100 of 130": (workloads.CONFIGS["C3"].with_(B=1, N=130), 100),
-    "hadamard d256 fp16 K3+QJL": (workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=77, k_qjl=1, k_bits=3), None),
-    "haar d64 fp32 K1+QJL": (workloads.CONFIGS["C1"].with_(d=64, Hq=2, Hkv=2, N=70, k_bits=1), None),
+    "haar d128 fp16 K2+QJL": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=203, k_bits=2), None, B.TQ_KEYS),
+    "haar d128 fp16 K3+QJL, first 100 of 130": (workloads.CONFIGS["C3"].with_(B=1, N=130), 100, B.TQ_KEYS),
+    "hadamard d256 fp16 K3+QJL": (workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=77, k_qjl=1, k_bits=3), None,
+                                  B.TQ_KEYS),
+    "haar d64 fp32 K1+QJL": (workloads.CONFIGS["C1"].with_(d=64, Hq=2, Hkv=2, N=70, k_bits=1), None, B.TQ_KEYS),
+    "haar d128 fp16 V3+QJL, first 90 of 203": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=203, v_qjl=1), 90,
+                                               B.TQ_VALUES),
+    "hadamard d256 fp16 V4+QJL": (workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=77, v_qjl=1), None,
+                                  B.TQ_VALUES),
+    "hadamard d64 fp32 V2+QJL": (workloads.CONFIGS["C5"].with_(B=1, Hq=2, Hkv=2, N=70, d=64, dtype="f32",
+                                                               v_bits=2, v_qjl=1), None, B.TQ_VALUES),
 }
 
 
 @pytest.mark.parametrize("name", list(PROD_CASES))
 def test_dequantize_prod(name):
-    cfg, n_out = PROD_CASES[name]
+    cfg, n_out, which = PROD_CASES[name]
     H.log(f"[dequantize prod] {name}")
-    x = _kv(cfg, "K", seed=17)
+    values = which == B.TQ_VALUES
+    x = _kv(cfg, "V" if values else "K", seed=17)
     S, n, d = x.shape
     n_out = n if n_out is None else n_out
-    layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, B.TQ_KEYS)
+    layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, which)
     rows = _rows(S, cap, n)
-    kf, st = H.check_keys(H.gpu_codes_key(cache, S, cap, d, cfg.k_bits, rows), cache["norm"].cpu().numpy()[rows],
-                          enc, ol, name, H.gpu_signs(cache, S, cap, d, rows), cache["rnorm"].cpu().numpy()[rows])
+    bits = cfg.v_bits if values else cfg.k_bits
+    gidx = (H.gpu_codes_value(cache, S, cap, d, bits)[rows] if values
+            else H.gpu_codes_key(cache, S, cap, d, bits, rows))
+    kf, st = H.check_keys(gidx, cache["norm"].cpu().numpy()[rows], enc, ol, name,
+                          H.gpu_signs(cache, S, cap, d, rows), cache["rnorm"].cpu().numpy()[rows], values=values)
     keep = np.array([s * n + t for s in range(S) for t in range(n_out)], dtype=np.int64)
     ref = codec.reconstruct_prod(kf["idx"][keep], kf["norm"][keep], kf["sign"][keep], kf["rnorm"][keep],
-                                 ol.R, ol.ck, ol.S)
-    got = B.dequantize(layer, B.TQ_KEYS, cache, n_out, prod=True).cpu().numpy().reshape(-1, d)
+                                 ol.R, ol.cv if values else ol.ck, ol.S)
+    got = B.dequantize(layer, which, cache, n_out, prod=True).cpu().numpy().reshape(-1, d)
     err = np.abs(got - ref) / np.maximum(kf["norm"][keep][:, None], 1e-30)
     assert err.max() < 2e-6, f"{name}: error {err.max():.2e} of the norm"
     # the QJL term is really there: the MSE-only rows differ from these
-    mse = B.dequantize(layer, B.TQ_KEYS, cache, n_out).cpu().numpy().reshape(-1, d)
+    mse = B.dequantize(layer, which, cache, n_out).cpu().numpy().reshape(-1, d)
     assert (np.abs(mse - got) / kf["norm"][keep][:, None]).max() > 1e-2
-    half = B.dequantize(layer, B.TQ_KEYS, cache, n_out, out_dtype=torch.float16, prod=True).cpu().numpy()
+    half = B.dequantize(layer, which, cache, n_out, out_dtype=torch.float16, prod=True).cpu().numpy()
     np.testing.assert_allclose(half.reshape(-1, d), got, rtol=2e-3, atol=2e-3)
     H.log(f"  max error / norm {err.max():.2e} (band rows: codes {st['code_rows']}, signs {st['sign_rows']})")
 

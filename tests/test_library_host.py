@@ -87,13 +87,13 @@ def test_make_rotation_rejects_bad_arguments(lib):
 def test_layer_flags_and_codebook_law_are_checked(lib):
     L = B.tq_layer()
     nb = lib.tq_layer_blob_bytes(128)
-    assert lib.tq_make_layer(ctypes.byref(L), 128, 0, 0, 2, 1, 2, 4, 4096, nb, None) == B.TQ_ERR_INVALID_ARG
+    assert lib.tq_make_layer(ctypes.byref(L), 128, 0, 0, 2, 1, 2, 8, 4096, nb, None) == B.TQ_ERR_INVALID_ARG
     assert "flags" in _err(lib)
     c = (ctypes.c_float * 4)()
     b = (ctypes.c_float * 3)()
     assert lib.tq_get_codebook_law(128, 2, 2, c, b) == B.TQ_ERR_INVALID_ARG
     Lf = _layer()
-    Lf.flags = 4
+    Lf.flags = 8
     K = _cache()
     assert lib.tq_quantize_kv(ctypes.byref(Lf), 0, 4096, 1, 2, 8, 0, ctypes.byref(K), None) == B.TQ_ERR_INVALID_ARG
     assert "flags" in _err(lib)
@@ -119,6 +119,46 @@ def test_dither_needs_hadamard_without_qjl(lib):
         assert lib.tq_quantize_kv(ctypes.byref(Lf), 0, 4096, 1, 2, 8, 0, ctypes.byref(K), None) == \
             B.TQ_ERR_INVALID_ARG
         assert "DITHER" in _err(lib)
+
+
+def test_dither_excludes_values_with_qjl(lib):
+    L = B.tq_layer()
+    nb = lib.tq_layer_blob_bytes(128)
+    flags = B.TQ_LAYER_DITHER | B.TQ_LAYER_VALUE_QJL
+    assert lib.tq_make_layer(ctypes.byref(L), 128, B.TQ_ROT_HADAMARD, 0, 2, 0, 2, flags, 4096, nb, None) == \
+        B.TQ_ERR_INVALID_ARG
+    assert L.d == 0
+
+
+def test_values_with_qjl_carry_signs_and_residual_norms(lib):
+    """TQ_LAYER_VALUE_QJL gives value rows the same sign and residual-norm
+    arrays as keys with QJL; quantize, decode and dequantize_prod check them."""
+    L = _layer(d=128, kb=3, qjl=0, vb=2)
+    L.flags = B.TQ_LAYER_VALUE_QJL
+    out = (ctypes.c_size_t * 4)()
+    assert lib.tq_cache_bytes(ctypes.byref(L), B.TQ_VALUES, 4, 64, out) == B.TQ_OK
+    assert list(out) == [4 * 64 * 32, 4 * 64 * 16, 4 * 64 * 4, 4 * 64 * 4]
+    assert lib.tq_cache_bytes(ctypes.byref(L), B.TQ_KEYS, 4, 64, out) == B.TQ_OK
+    assert list(out) == [4 * 64 * 48, 0, 4 * 64 * 4, 0]
+    # value caches without sign or rnorm are refused
+    assert lib.tq_quantize_kv(ctypes.byref(L), B.TQ_VALUES, 4096, 1, 2, 8, 0, ctypes.byref(_cache(qjl=False)),
+                              None) == B.TQ_ERR_INVALID_ARG
+    assert "rnorm" in _err(lib)
+    call = lambda which, cache: lib.tq_dequantize_prod(ctypes.byref(L), which, ctypes.byref(cache), 8, 4096, 0,
+                                                       None)
+    assert call(B.TQ_VALUES, _cache(qjl=False)) == B.TQ_ERR_INVALID_ARG
+    assert call(B.TQ_KEYS, _cache(qjl=False)) == B.TQ_ERR_INVALID_ARG      # these keys carry no QJL
+
+    def decode(Hq, Hkv, Tq, V):
+        ws = lib.tq_decode_workspace_bytes(ctypes.byref(L), 1, Hq, Hkv, Tq, 16)
+        return lib.tq_attn_decode(ctypes.byref(L), 4096, 1, 1, Hq, Hkv, Tq, 16, 0,
+                                  ctypes.byref(_cache(seqs=Hkv, qjl=False)), ctypes.byref(V), 8192, None,
+                                  1 << 16, max(ws, 1), None)
+    assert decode(4, 2, 1, _cache(seqs=2, qjl=False)) == B.TQ_ERR_INVALID_ARG
+    # the split kernel keeps both value sums of every query row of a KV head
+    # on chip: 128 rows of d = 128 are beyond it (64 are not)
+    assert decode(128, 1, 1, _cache(seqs=1)) == B.TQ_ERR_UNSUPPORTED
+    assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 1, 64, 1, 1, 16) > 0
 
 
 def test_cache_bytes(lib):
@@ -194,8 +234,9 @@ def test_dequantize_rejects_bad_arguments(lib):
 
 
 def test_dequantize_prod_needs_keys_with_qjl(lib):
-    """The two-stage reconstruction is defined for keys that carry QJL signs:
-    values, and keys of a layer without QJL, are rejected before any GPU call."""
+    """The two-stage reconstruction is defined for rows that carry QJL signs:
+    values of a layer without TQ_LAYER_VALUE_QJL, and keys of a layer without
+    QJL, are rejected before any GPU call."""
     K = _cache()
     call = lambda L, which, cache: lib.tq_dequantize_prod(ctypes.byref(L), which, ctypes.byref(cache), 8, 4096, 0, None)
     assert call(_layer(qjl=1), B.TQ_VALUES, _cache(qjl=False)) == B.TQ_ERR_INVALID_ARG

@@ -49,6 +49,7 @@ class LayerConfig:
     layer_seed: int = 0
     codebook: str = "gaussian"   # codebook law: "gaussian" (N(0, 1/d)) or "beta" (exact coordinate law)
     dither: int = 0              # 1: dithered randomized Hadamard (per-token offset before quantizing)
+    v_qjl: int = 0               # 1: values also carry QJL sign bits and the residual norm
 
     @property
     def G(self) -> int:
@@ -166,6 +167,9 @@ def random_packed_numpy(cfg: LayerConfig, S: int, cap: int, seed: int = 0) -> di
     if cfg.k_qjl:
         out["k_sign"] = r.integers(0, 256, size=S * cap * d // 8, dtype=np.uint8)
         out["k_rnorm"] = np.abs(0.3 * r.standard_normal(S * cap)).astype(np.float32)
+    if cfg.v_qjl:
+        out["v_sign"] = r.integers(0, 256, size=S * cap * d // 8, dtype=np.uint8)
+        out["v_rnorm"] = np.abs(0.3 * r.standard_normal(S * cap)).astype(np.float32)
     return out
 
 
