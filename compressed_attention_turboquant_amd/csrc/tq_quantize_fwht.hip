@@ -16,8 +16,16 @@
 //    coordinates j = 8k + 64c + e (e < 8, c < d/64) with k = (l & 3) | (l>>1 & 4):
 //    8 lanes share a token.  Index bits 0-2 and 6-7 of j live in registers,
 //    bits 3, 4 and 5 in lane bits 0, 1 and 3, so every cross-lane butterfly is
-//    one DPP move (quad_perm for lane xor 1 and 2, row_ror:8 for lane xor 8)
-//    plus one FMA with a +-1 factor.
+//    one FMA whose multiplicand is read through DPP (quad_perm for lane xor 1
+//    and 2, row_ror:8 for lane xor 8): own + s * partner with s = -1 on the
+//    upper lane, which yields the upper output negated.  The negation is the
+//    same for all of a lane's values, so it is carried as one sign per lane
+//    (the product of its three s) and applied where the codes are taken.
+//  * 3- and 4-bit codes come from a binned table in LDS instead of a search:
+//    the coordinate on the codebook's N(0, 1) scale is cut into bins narrower
+//    than any gap between boundaries, each bin holding the count of
+//    boundaries below it and its own boundary, if any, so a code is one
+//    lookup and one compare.
 //  * Each chunk of 8 coordinates is one 16-byte load of fp16 input (a token's
 //    8 lanes read 128 contiguous bytes per load).
 //  * Codes go through LDS as bytes ([token][coordinate]) and leave as whole
@@ -38,6 +46,17 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
+// Code table: kBins bins of width 1 / kBinScale on the codebook's N(0, 1) scale
+// z = y sqrt(d) (y a coordinate of the unit vector), centred on 0, so they
+// cover |z| < 4; the bins outside hold no boundary (the outermost boundary of
+// the 4-bit codebooks is below 2.5), so values beyond them clamp to the end
+// bins.  Every codebook's boundaries are more than one bin apart (the
+// narrowest gap is about 0.25), so a bin holds at most one.  32 copies, one
+// per lane of a half wave, keep the lookups free of bank conflicts.
+constexpr int kBins = 64;
+constexpr float kBinScale = 8.f;
+constexpr int kBinCopies = 32;
+
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -51,6 +70,31 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
+
+// One cross-lane butterfly stage on 8 values: a[i] += s * a[i] of the partner
+// lane, one v_fmac_f32 with its multiplicand read through DPP (the compiler
+// does not fold a DPP move into an FMAC).  A DPP read of a VGPR needs two wait
+// states after the VALU write of it, hence the s_nop; inside the block each
+// instruction reads a different register.
+#define TQ_BUTTERFLY8(NAME, MOD)                                                                    \
+  __device__ __forceinline__ void NAME(float* a, float s) {                                       \
+    asm volatile("s_nop 1\n\t"                                                                     \
+                 "v_fmac_f32_dpp %0, %0, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %1, %1, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %2, %2, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %3, %3, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %4, %4, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %5, %5, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %6, %6, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %7, %7, %8 " MOD " row_mask:0xf bank_mask:0xf"                    \
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),         \
+                   "+v"(a[6]), "+v"(a[7])                                                          \
+                 : "v"(s));                                                                        \
+  }
+TQ_BUTTERFLY8(butterfly8_xor1, "quad_perm:[1,0,3,2]")
+TQ_BUTTERFLY8(butterfly8_xor2, "quad_perm:[2,3,0,1]")
+TQ_BUTTERFLY8(butterfly8_xor8, "row_ror:8")
+#undef TQ_BUTTERFLY8
 
 // BITS consecutive dwords to a 4-byte aligned address (16-byte aligned when
 // BITS is 4), as one vector store.
@@ -90,7 +134,9 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
   constexpr bool kHalf = std::is_same<Tin, _Float16>::value;
   constexpr int RW = kHalf ? 4 : 8;  // dwords per chunk of 8 inputs
   typedef uint32_t Raw __attribute__((ext_vector_type(RW)));
+  constexpr bool kTable = BITS >= 3;
   __shared__ __align__(16) uint8_t codes[kWaves][8][ROW];
+  __shared__ __align__(16) uint2 ctab[kTable ? kBins * kBinCopies : 1];  // {boundary in bin units, count below}
 
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int k = (lane & 3) | ((lane >> 1) & 4);
@@ -109,12 +155,32 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
         dm[c][q] = p.dsign[8 * k + 64 * c + q] < 0.f ? 0x80000000u : 0u;
       }
     }
-  // +1 where this lane is the lower partner of a cross-lane butterfly.
+  // +1 where this lane is the lower partner of a cross-lane butterfly; the
+  // lane's transform outputs come out multiplied by sgn = s1 s2 s8.
   const float s1 = (lane & 1) ? -1.f : 1.f, s2 = (lane & 2) ? -1.f : 1.f, s8 = (lane & 8) ? -1.f : 1.f;
+  const float sgn = s1 * s2 * s8;
   float beta[K];
 #pragma unroll
   for (int i = 0; i < K; ++i) beta[i] = BITS > 1 ? p.bnd[(1 << (BITS - 1)) + i] : 0.f;
   const float sqrt_d = sqrtf((float)D);
+  // Boundary b in bin units: u = z kBinScale + kBins / 2 with z = b sqrt(d).
+  const float ubin = sqrt_d * kBinScale;
+  if constexpr (kTable) {
+    constexpr int L = 1 << BITS;
+    for (int e = threadIdx.x; e < kBins * kBinCopies; e += kThreads) {
+      const int bin = e / kBinCopies;
+      uint32_t below = 0;
+      float inner = INFINITY;
+      for (int i = 0; i + 1 < L; ++i) {
+        const float ub = fmaf(p.bnd[i], ubin, 0.5f * kBins);
+        if (ub < (float)bin) ++below;
+        else if (ub < (float)(bin + 1)) inner = ub;
+      }
+      ctab[e] = make_uint2(__float_as_uint(inner), below);
+    }
+    __syncthreads();
+  }
+  const uint2* ctab_lane = ctab + (kTable ? lane % kBinCopies : 0);
   const float dwidth = DITHER ? *p.dw : 0.f;
 
   const int64_t items = p.seqs * p.tiles;
@@ -180,6 +246,9 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
     float th[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) th[i] = beta[i] * unit;
+    // table search: bin units per transform unit, with the lane's sign (a zero
+    // row without dither stays at u = kBins / 2, the lower middle code)
+    const float su = unit > 0.f ? sgn * ubin / unit : 0.f;
 
     // unnormalised Walsh-Hadamard transform: register bits, then lane bits
 #pragma unroll
@@ -192,15 +261,17 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
         x[v + b] = u - z;
       }
     }
+    // cross-lane stages: own + s * partner (the upper lane's result negated)
 #pragma unroll
-    for (int v = 0; v < V; ++v) x[v] = fmaf(s1, x[v], dpp<kDppXor1>(x[v]));
+    for (int v = 0; v < V; v += 8) butterfly8_xor1(x + v, s1);
 #pragma unroll
-    for (int v = 0; v < V; ++v) x[v] = fmaf(s2, x[v], dpp<kDppXor2>(x[v]));
+    for (int v = 0; v < V; v += 8) butterfly8_xor2(x + v, s2);
 #pragma unroll
-    for (int v = 0; v < V; ++v) x[v] = fmaf(s8, x[v], dpp<kDppXor8>(x[v]));
+    for (int v = 0; v < V; v += 8) butterfly8_xor8(x + v, s8);
+    // x = sgn * y from here on
     if constexpr (DITHER) {
       // y - delta in the unnormalised transform's units
-      const float shift = dither_offset(p.ds0, s, tile * 8 + tl, dwidth) * unit;
+      const float shift = sgn * dither_offset(p.ds0, s, tile * 8 + tl, dwidth) * unit;
 #pragma unroll
       for (int v = 0; v < V; ++v) x[v] -= shift;
     }
@@ -209,9 +280,22 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       uint32_t wd[2] = {0u, 0u};
+      if constexpr (kTable) {
+        // all 8 lookups in flight before the first compare
+        float u[8];
+        uint2 ent[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        wd[e / 4] |= symmetric_code<BITS>(x[8 * c + e], th) << (8 * (e % 4));
+        for (int e = 0; e < 8; ++e) {
+          u[e] = fmaf(x[8 * c + e], su, 0.5f * kBins);
+          const int bin = (int)__builtin_amdgcn_fmed3f(u[e], 0.f, (float)(kBins - 1));
+          ent[e] = ctab_lane[bin * kBinCopies];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          wd[e / 4] |= (ent[e].y + (u[e] > __uint_as_float(ent[e].x) ? 1u : 0u)) << (8 * (e % 4));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wd[e / 4] |= symmetric_code<BITS>(sgn * x[8 * c + e], th) << (8 * (e % 4));
       }
       *reinterpret_cast<uint2*>(&codes[w][tl][8 * k + 64 * c]) = make_uint2(wd[0], wd[1]);
     }

@@ -42,6 +42,20 @@ def test_codebooks_bit_equal_to_oracle(d, law):
         assert np.array_equal(c, oc) and np.array_equal(b, ob), (d, bits, law)
 
 
+@pytest.mark.parametrize("law", ["gaussian", "beta"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_codebooks_fit_the_quantizer_bin_table(d, law):
+    """The Hadamard quantizer takes 3- and 4-bit codes from a table of 64 bins
+    of width 1/8 on the codebook's N(0, 1) scale (b * sqrt(d)), covering
+    [-4, 4): every boundary must lie inside that range and any two must be
+    more than a bin apart, so that a bin holds at most one."""
+    for bits in (3, 4):
+        _, b = B.get_codebook(d, bits, B.TQ_LAW_BETA if law == "beta" else B.TQ_LAW_GAUSSIAN)
+        z = b.astype(np.float64) * np.sqrt(d)
+        assert np.abs(z).max() < 4.0 - 0.125, (d, bits, law)
+        assert np.diff(z).min() > 0.125 * 1.5, (d, bits, law, np.diff(z).min())
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("rot", ["haar", "hadamard"])
 def test_rotation_and_projection_match_oracle(d, rot):
