@@ -45,6 +45,10 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+#ifndef TQ_FWHT_AHEAD
+#define TQ_FWHT_AHEAD 2
+#endif
+constexpr int kAhead = TQ_FWHT_AHEAD;  // tiles whose loads a wave keeps in flight
 
 // Code table: kBins bins of width 1 / kBinScale on the codebook's N(0, 1) scale
 // z = y sqrt(d) (y a coordinate of the unit vector), centred on 0, so they
@@ -96,17 +100,38 @@ TQ_BUTTERFLY8(butterfly8_xor2, "quad_perm:[2,3,0,1]")
 TQ_BUTTERFLY8(butterfly8_xor8, "row_ror:8")
 #undef TQ_BUTTERFLY8
 
-// BITS consecutive dwords to a 4-byte aligned address (16-byte aligned when
-// BITS is 4), as one vector store.
+// Sum and difference of the two fp16 halves of w, in fp32 (exact conversions,
+// one rounding each): v_fma_mix_f32 reads the halves directly, where the
+// compiler would convert both first.
+__device__ __forceinline__ void half_sum_diff(uint32_t w, float& sum, float& diff) {
+  asm("v_fma_mix_f32 %0, %2, 1.0, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mix_f32 %1, %2, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+      : "=&v"(sum), "=v"(diff)
+      : "v"(w));
+}
+
+// Memory goes through buffer instructions on per-tile records: an access
+// that must not happen gets an offset past the record (a load returns 0, a
+// store is dropped) instead of a branch, so every tile issues the same memory
+// instructions and the compiler can count them when it waits for the loads
+// issued two tiles earlier.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;  // past every record used here
+__device__ __forceinline__ Rsrc record(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);  // raw buffer
+}
+
+// BITS consecutive dwords at byte offset off of r (16-byte aligned when BITS is 4).
 template <int BITS>
-__device__ __forceinline__ void store_words(uint8_t* dst, const uint32_t (&w)[BITS]) {
+__device__ __forceinline__ void store_words(Rsrc r, uint32_t off, const uint32_t (&w)[BITS]) {
   if constexpr (BITS == 4) {
-    *reinterpret_cast<u4*>(dst) = u4{w[0], w[1], w[2], w[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(u4{w[0], w[1], w[2], w[3]}, r, off, 0, 0);
   } else if constexpr (BITS == 2) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u2v{w[0], w[1]}, r, off, 0, 0);
   } else {
 #pragma unroll
-    for (int q = 0; q < BITS; ++q) reinterpret_cast<uint32_t*>(dst)[q] = w[q];
+    for (int q = 0; q < BITS; ++q) __builtin_amdgcn_raw_buffer_store_b32(w[q], r, off + 4 * q, 0, 0);
   }
 }
 
@@ -138,7 +163,7 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
   __shared__ __align__(16) uint8_t codes[kWaves][8][ROW];
   __shared__ __align__(16) uint2 ctab[kTable ? kBins * kBinCopies : 1];  // {boundary in bin units, count below}
 
-  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int k = (lane & 3) | ((lane >> 1) & 4);
   const int tl = ((lane >> 2) & 1) | ((lane >> 3) & 6);
 
@@ -187,55 +212,94 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
   const int64_t wstride = (int64_t)gridDim.x * kWaves;
   const int64_t t0 = p.t0, tend = p.t0 + p.n;
   constexpr int kRowB = D * BITS / 8;  // key stream bytes per token
-  const bool small = items <= 0x7FFFFFFF;
-  auto split = [&](int64_t item, int64_t& s, int64_t& tile) {  // item -> (sequence, tile), uniform
-    if (small) {
-      const uint32_t q = (uint32_t)item / (uint32_t)p.tiles;
-      s = q;
-      tile = p.tile_first + ((uint32_t)item - q * (uint32_t)p.tiles);
-    } else {
-      s = item / p.tiles;
-      tile = p.tile_first + item % p.tiles;
+  // Keys with 1, 2 or 4 bits: a lane's 8 consecutive coordinates make whole
+  // bytes of the stream, packed in registers and stored directly.
+  constexpr bool kDirect = !VALUES && BITS != 3;
+  // The wave's items are item0 + i * wstride: (sequence, tile) advance by
+  // (wstride / tiles, wstride % tiles) with one carry, so no division per tile.
+  // Two cursors: the tile being quantized and the one whose loads are issued.
+  struct Cursor {
+    int64_t item, s, tile;  // tile relative to tile_first
+  };
+  const int64_t ds = wstride / p.tiles, dt = wstride % p.tiles;
+  auto advance = [&](Cursor& c) {
+    c.item += wstride;
+    c.s += ds;
+    c.tile += dt;
+    if (c.tile >= p.tiles) {
+      c.tile -= p.tiles;
+      c.s += 1;
     }
   };
-  const int lane_off = tl * D + 8 * k;  // this lane's first input, relative to the tile's first row
-  auto load = [&](int64_t item, Raw (&raw)[NC]) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) raw[c] = Raw{};
-    if (item >= items) return;
-    int64_t s, tile;
-    split(item, s, tile);
+  // Input of one tile: its rows in [t0, t0 + n) as one record (none past the
+  // last item); rows outside read as 0.
+  auto load = [&](const Cursor& cu, Raw (&raw)[NC]) {
+    const int64_t tile = p.tile_first + cu.tile;
+    const int64_t lo = max(tile * 8, t0), hi = min(tile * 8 + 8, tend);
+    const Rsrc r = record(static_cast<const Tin*>(p.x) + (cu.s * p.n + lo - t0) * D,
+                          cu.item < items ? (hi - lo) * D * (int64_t)sizeof(Tin) : 0);
     const int64_t t = tile * 8 + tl;
-    if (t < t0 || t >= tend) return;
-    const Tin* src = static_cast<const Tin*>(p.x) + (s * p.n + tile * 8 - t0) * D + lane_off;
+    const uint32_t off = t >= lo && t < hi ? (uint32_t)(((t - lo) * D + 8 * k) * sizeof(Tin)) : kOob;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) raw[c] = *reinterpret_cast<const Raw*>(src + 64 * c);
+    for (int c = 0; c < NC; ++c) {
+      const uint32_t o = off + 64 * c * sizeof(Tin);
+      if constexpr (kHalf) {
+        raw[c] = __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
+      } else {
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
+        const u4 b = __builtin_amdgcn_raw_buffer_load_b128(r, o + 16, 0, 0);
+        raw[c] = Raw{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      }
+    }
   };
 
   // Converts this tile's raw input, refills `raw` with the tile two steps
   // ahead (so its loads are in flight for two tiles of work), then quantizes.
-  auto process = [&](int64_t item, Raw (&raw)[NC]) {
-    int64_t s, tile;
-    split(item, s, tile);
+  auto process = [&](const Cursor& cu, const Cursor& ahead, Raw (&raw)[NC]) {
+    // (tiles stay in order: work of the next tile, in particular the wait for
+    // its input, is not moved up into this one)
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t s = cu.s, tile = p.tile_first + cu.tile;
+    // Values: the tile's record, and the old words a partial tile keeps (the
+    // codes of tokens outside [t0, t0 + n)), read first so that waiting for
+    // them does not wait for the next tiles' loads; a full tile reads them as
+    // 0 without a memory access.
+    const int ln = lane % (D / 4);
+    const bool st_ok = lane < D / 4;  // lanes that store packed words
+    const Rsrc vrec = record(p.idx + (s * (p.cap / 8) + tile) * (D * BITS), D * BITS);
+    const uint32_t voff = st_ok ? (uint32_t)(ln * 4 * BITS) : kOob;
+    const bool partial = tile * 8 < t0 || tile * 8 + 8 > tend;  // uniform
+    uint32_t old[VALUES ? BITS : 1];
+    if constexpr (VALUES) {
+#pragma unroll
+      for (int q = 0; q < BITS; ++q)
+        old[q] = __builtin_amdgcn_raw_buffer_load_b32(vrec, partial ? voff + 4 * q : kOob, 0, 0);
+    }
     float x[V];
+    float ss = 0.f;  // squared norm of the lane's part (D does not change it)
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const Raw r = raw[c] ^ dm[c];  // D applied to the input's sign bits
+      if constexpr (kHalf) {
+        // first butterfly stage (coordinate bit 0) fused with the conversion
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (kHalf) {
-          const uint32_t h = e % 2 ? r[e / 2] >> 16 : r[e / 2] & 0xFFFFu;
-          x[8 * c + e] = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-        } else {
+        for (int q = 0; q < 4; ++q) {
+          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+          // (through a scalar: a bit cast of a vector element reads element 0)
+          const uint32_t wq = r[q];
+          const h2 pr = __builtin_bit_cast(h2, wq);
+          ss = __builtin_amdgcn_fdot2(pr, pr, ss, false);
+          half_sum_diff(wq, x[8 * c + 2 * q], x[8 * c + 2 * q + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
           x[8 * c + e] = __uint_as_float(r[e]);
+          ss = fmaf(x[8 * c + e], x[8 * c + e], ss);
         }
       }
     }
-    load(item + 2 * wstride, raw);
-    // norm over the token's 8 lanes (D does not change it)
-    float ss = 0.f;
-#pragma unroll
-    for (int v = 0; v < V; ++v) ss = fmaf(x[v], x[v], ss);
+    load(ahead, raw);
     ss += dpp<kDppXor1>(ss);
     ss += dpp<kDppXor2>(ss);
     ss += dpp<kDppXor8>(ss);
@@ -251,8 +315,9 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
     const float su = unit > 0.f ? sgn * ubin / unit : 0.f;
 
     // unnormalised Walsh-Hadamard transform: register bits, then lane bits
+    // (bit 0 was done above for fp16 input)
 #pragma unroll
-    for (int b = 1; b < V; b <<= 1) {
+    for (int b = kHalf ? 2 : 1; b < V; b <<= 1) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         if (v & b) continue;
@@ -276,10 +341,14 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
       for (int v = 0; v < V; ++v) x[v] -= shift;
     }
 
-    // codes into LDS, [token][coordinate]: code = #{i : beta_i < y}
+    // code = #{i : beta_i < y}; keys of 1, 2 or 4 bits go straight to memory,
+    // the others through LDS as bytes, [token][coordinate]
+    const int64_t tok = tile * 8 + tl;
+    const bool tok_ok = tok >= t0 && tok < tend;
+    const Rsrc krec = record(p.idx + (s * p.cap + tile * 8) * kRowB, 8 * kRowB);  // the tile's key rows
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      uint32_t wd[2] = {0u, 0u};
+      uint32_t cd[8];
       if constexpr (kTable) {
         // all 8 lookups in flight before the first compare
         float u[8];
@@ -291,66 +360,96 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
           ent[e] = ctab_lane[bin * kBinCopies];
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          wd[e / 4] |= (ent[e].y + (u[e] > __uint_as_float(ent[e].x) ? 1u : 0u)) << (8 * (e % 4));
+        for (int e = 0; e < 8; ++e) cd[e] = ent[e].y + (u[e] > __uint_as_float(ent[e].x) ? 1u : 0u);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wd[e / 4] |= symmetric_code<BITS>(sgn * x[8 * c + e], th) << (8 * (e % 4));
+        for (int e = 0; e < 8; ++e) cd[e] = symmetric_code<BITS>(sgn * x[8 * c + e], th);
       }
-      *reinterpret_cast<uint2*>(&codes[w][tl][8 * k + 64 * c]) = make_uint2(wd[0], wd[1]);
+      if constexpr (kDirect) {
+        // coordinates 8 (k + 8 c) .. + 7: bytes BITS (k + 8 c) .. + BITS - 1 of the row
+        uint32_t wd = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wd |= cd[e] << (BITS * e);
+        const uint32_t off = tok_ok ? (uint32_t)(tl * kRowB + BITS * (k + 8 * c)) : kOob;
+        if constexpr (BITS == 4) __builtin_amdgcn_raw_buffer_store_b32(wd, krec, off, 0, 0);
+        else if constexpr (BITS == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)wd, krec, off, 0, 0);
+        else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)wd, krec, off, 0, 0);
+      } else {
+        uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wd[e / 4] |= cd[e] << (8 * (e % 4));
+        *reinterpret_cast<uint2*>(&codes[w][tl][8 * k + 64 * c]) = make_uint2(wd[0], wd[1]);
+      }
     }
-    const int64_t tok = tile * 8 + tl;
-    if (k == 0 && tok >= t0 && tok < tend) p.norm[s * p.cap + tok] = nn;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nn), record(p.norm + s * p.cap + tile * 8, 32),
+                                          k == 0 && tok_ok ? (uint32_t)(4 * tl) : kOob, 0, 0);
+    if constexpr (kDirect) return;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // pack 32 codes per lane into BITS dwords and store
-    if (lane < D / 4) {
-      uint32_t cw[8];  // 32 code bytes, in stream order
-      if constexpr (!VALUES) {
-        const int t = lane / (D / 32), jb = lane % (D / 32);
-        const u4 a = *reinterpret_cast<const u4*>(&codes[w][t][32 * jb]);
-        const u4 b = *reinterpret_cast<const u4*>(&codes[w][t][32 * jb + 16]);
-        cw[0] = a[0]; cw[1] = a[1]; cw[2] = a[2]; cw[3] = a[3];
-        cw[4] = b[0]; cw[5] = b[1]; cw[6] = b[2]; cw[7] = b[3];
-      } else {
-        // stream positions 8 j + t, j = 4 lane + i: byte i of r[t] is code (j, t)
+    // pack 32 codes per lane into BITS dwords and store (lanes past D / 4
+    // repeat lane % (D / 4) and store nothing)
+    {
+      uint32_t out[BITS];
+      if constexpr (VALUES && BITS == 4) {
+        // stream positions 8 j + t, j = 4 lane + i: dword i holds the codes of
+        // coordinate j for tokens t = 0..7 at bits 4 t.  Nibble pairs of tokens
+        // (2 m, 2 m + 1) first, then a 4 x 4 byte transpose with byte permutes.
         uint32_t r[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) r[t] = *reinterpret_cast<const uint32_t*>(&codes[w][t][4 * lane]);
+        for (int t = 0; t < 8; ++t) r[t] = *reinterpret_cast<const uint32_t*>(&codes[w][t][4 * ln]);
+        const uint32_t p0 = r[0] | (r[1] << 4), p1 = r[2] | (r[3] << 4);
+        const uint32_t p2 = r[4] | (r[5] << 4), p3 = r[6] | (r[7] << 4);
+        const uint32_t q0 = __builtin_amdgcn_perm(p1, p0, 0x05010400u);  // p0.b0 p1.b0 p0.b1 p1.b1
+        const uint32_t q1 = __builtin_amdgcn_perm(p1, p0, 0x07030602u);  // p0.b2 p1.b2 p0.b3 p1.b3
+        const uint32_t q2 = __builtin_amdgcn_perm(p3, p2, 0x05010400u);
+        const uint32_t q3 = __builtin_amdgcn_perm(p3, p2, 0x07030602u);
+        out[0] = __builtin_amdgcn_perm(q2, q0, 0x05040100u);  // byte i of p0 p1 p2 p3, i = 0
+        out[1] = __builtin_amdgcn_perm(q2, q0, 0x07060302u);  // i = 1
+        out[2] = __builtin_amdgcn_perm(q3, q1, 0x05040100u);  // i = 2
+        out[3] = __builtin_amdgcn_perm(q3, q1, 0x07060302u);  // i = 3
+      } else {
+        uint32_t cw[8];  // 32 code bytes, in stream order
+        if constexpr (!VALUES) {
+          const int t = ln / (D / 32), jb = ln % (D / 32);
+          const u4 a = *reinterpret_cast<const u4*>(&codes[w][t][32 * jb]);
+          const u4 b = *reinterpret_cast<const u4*>(&codes[w][t][32 * jb + 16]);
+          cw[0] = a[0]; cw[1] = a[1]; cw[2] = a[2]; cw[3] = a[3];
+          cw[4] = b[0]; cw[5] = b[1]; cw[6] = b[2]; cw[7] = b[3];
+        } else {
+          // stream positions 8 j + t, j = 4 lane + i: byte i of r[t] is code (j, t)
+          uint32_t r[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t lo = 0, hi = 0;
+          for (int t = 0; t < 8; ++t) r[t] = *reinterpret_cast<const uint32_t*>(&codes[w][t][4 * ln]);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) lo |= ((r[t] >> (8 * i)) & 0xFFu) << (8 * t);
+          for (int i = 0; i < 4; ++i) {
+            uint32_t lo = 0, hi = 0;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) hi |= ((r[4 + t] >> (8 * i)) & 0xFFu) << (8 * t);
-          cw[2 * i] = lo;
-          cw[2 * i + 1] = hi;
+            for (int t = 0; t < 4; ++t) lo |= ((r[t] >> (8 * i)) & 0xFFu) << (8 * t);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) hi |= ((r[4 + t] >> (8 * i)) & 0xFFu) << (8 * t);
+            cw[2 * i] = lo;
+            cw[2 * i + 1] = hi;
+          }
         }
-      }
-      uint32_t out[BITS];
 #pragma unroll
-      for (int q = 0; q < BITS; ++q) out[q] = 0u;
+        for (int q = 0; q < BITS; ++q) out[q] = 0u;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const uint32_t cd = (cw[i / 4] >> (8 * (i % 4))) & 0xFFu;
-        const int bit = BITS * i;
-        out[bit / 32] |= cd << (bit % 32);
-        if (bit % 32 + BITS > 32) out[bit / 32 + 1] |= cd >> (32 - bit % 32);
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t cd = (cw[i / 4] >> (8 * (i % 4))) & 0xFFu;
+          const int bit = BITS * i;
+          out[bit / 32] |= cd << (bit % 32);
+          if (bit % 32 + BITS > 32) out[bit / 32 + 1] |= cd >> (32 - bit % 32);
+        }
       }
       if constexpr (!VALUES) {
-        const int t = lane / (D / 32), jb = lane % (D / 32);
+        const int t = ln / (D / 32), jb = ln % (D / 32);
         const int64_t tk = tile * 8 + t;
-        if (tk >= t0 && tk < tend) {
-          store_words<BITS>(p.idx + (s * p.cap + tile * 8) * kRowB + t * kRowB + jb * 4 * BITS, out);
-        }
+        store_words<BITS>(krec, st_ok && tk >= t0 && tk < tend ? (uint32_t)(t * kRowB + jb * 4 * BITS) : kOob, out);
       } else {
-        uint32_t* dst = reinterpret_cast<uint32_t*>(p.idx + (s * (p.cap / 8) + tile) * (D * BITS) + lane * 4 * BITS);
         const int64_t first = tile * 8;
-        if (first < t0 || first + 8 > tend) {
-          // partial tile: keep the codes of tokens outside [t0, t0 + n)
+        {
           uint32_t keep[BITS];
 #pragma unroll
           for (int q = 0; q < BITS; ++q) keep[q] = 0u;
@@ -365,49 +464,87 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
             }
           }
 #pragma unroll
-          for (int q = 0; q < BITS; ++q) out[q] = (out[q] & ~keep[q]) | (dst[q] & keep[q]);
+          for (int q = 0; q < BITS; ++q) out[q] = (out[q] & ~keep[q]) | (old[q] & keep[q]);
         }
-        store_words<BITS>(reinterpret_cast<uint8_t*>(dst), out);
+        store_words<BITS>(vrec, voff, out);
       }
     }
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Two tiles of loads in flight per wave.
-  int64_t item = (int64_t)blockIdx.x * kWaves + w;
-  Raw ra[NC], rb[NC];
-  load(item, ra);
-  load(item + wstride, rb);
-  while (item < items) {
-    process(item, ra);
-    item += wstride;
-    if (item >= items) break;
-    process(item, rb);
-    item += wstride;
+  // kAhead tiles of loads in flight per wave.
+  const int64_t item0 = (int64_t)blockIdx.x * kWaves + w;
+  Cursor cur{item0, item0 / p.tiles, item0 % p.tiles};
+  Cursor ahead = cur;
+  Raw rbuf[kAhead][NC];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) {
+    load(ahead, rbuf[i]);
+    advance(ahead);
+  }
+  // The memory counter is in order and counts stores too: inside the loop a
+  // tile's loads are followed by the stores and loads of kAhead - 1 tiles
+  // before they are waited for.  Stores to an empty record (dropped, no
+  // memory access) give the path into the loop as many, so that the waits
+  // the compiler places, which must hold on both paths, leave the loads of
+  // the next tiles in flight.
+  const Rsrc none = record(p.norm, 0);
+#pragma unroll
+  for (int i = 0; i < 16 * (kAhead - 1); ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 64 * i, 0, 0);
+  // Whole rounds of kAhead tiles without an exit test inside (so the loop is
+  // entered only from above and from its own end, and each buffer's wait sees
+  // the same history), then the remaining tiles.
+  const int64_t mine = item0 < items ? (items - item0 + wstride - 1) / wstride : 0;  // this wave's tiles
+  for (int64_t r = mine / kAhead; r > 0; --r) {
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      process(cur, ahead, rbuf[i]);
+      advance(cur);
+      advance(ahead);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kAhead - 1; ++i) {
+    if (cur.item >= items) return;
+    process(cur, ahead, rbuf[i]);
+    advance(cur);
+    advance(ahead);
   }
 }
 
-template <int D, int VALUES, typename Tin, int DITHER>
-hipError_t launch_bits(const FwhtParams& p, int bits, unsigned grid, hipStream_t st) {
-  switch (bits) {
-    case 1: hipLaunchKernelGGL((quantize_fwht_kernel<D, 1, VALUES, Tin, DITHER>), dim3(grid), dim3(kThreads), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((quantize_fwht_kernel<D, 2, VALUES, Tin, DITHER>), dim3(grid), dim3(kThreads), 0, st, p); break;
-    case 3: hipLaunchKernelGGL((quantize_fwht_kernel<D, 3, VALUES, Tin, DITHER>), dim3(grid), dim3(kThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((quantize_fwht_kernel<D, 4, VALUES, Tin, DITHER>), dim3(grid), dim3(kThreads), 0, st, p); break;
-  }
+// Up to 8 workgroups per CU, each looping over its tiles: about twice what is
+// resident at once, which measured a little faster than one round of exactly
+// the resident workgroups (the second round fills in as the first finishes).
+template <int D, int BITS, int VALUES, typename Tin, int DITHER>
+hipError_t launch_k(const FwhtParams& p, int64_t groups, int cus, hipStream_t st) {
+  const int64_t grid = groups < (int64_t)cus * 8 ? groups : (int64_t)cus * 8;
+  hipLaunchKernelGGL((quantize_fwht_kernel<D, BITS, VALUES, Tin, DITHER>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     st, p);
   return hipGetLastError();
 }
 
+template <int D, int VALUES, typename Tin, int DITHER>
+hipError_t launch_bits(const FwhtParams& p, int bits, int64_t groups, int cus, hipStream_t st) {
+  switch (bits) {
+    case 1: return launch_k<D, 1, VALUES, Tin, DITHER>(p, groups, cus, st);
+    case 2: return launch_k<D, 2, VALUES, Tin, DITHER>(p, groups, cus, st);
+    case 3: return launch_k<D, 3, VALUES, Tin, DITHER>(p, groups, cus, st);
+    default: return launch_k<D, 4, VALUES, Tin, DITHER>(p, groups, cus, st);
+  }
+}
+
 template <int D, typename Tin>
-hipError_t launch_in(const FwhtParams& p, const QuantizeArgs& a, unsigned grid, hipStream_t st) {
+hipError_t launch_in(const FwhtParams& p, const QuantizeArgs& a, int64_t groups, int cus, hipStream_t st) {
   if (a.dither)
-    return a.value_layout ? launch_bits<D, 1, Tin, 1>(p, a.bits, grid, st) : launch_bits<D, 0, Tin, 1>(p, a.bits, grid, st);
-  return a.value_layout ? launch_bits<D, 1, Tin, 0>(p, a.bits, grid, st) : launch_bits<D, 0, Tin, 0>(p, a.bits, grid, st);
+    return a.value_layout ? launch_bits<D, 1, Tin, 1>(p, a.bits, groups, cus, st)
+                          : launch_bits<D, 0, Tin, 1>(p, a.bits, groups, cus, st);
+  return a.value_layout ? launch_bits<D, 1, Tin, 0>(p, a.bits, groups, cus, st)
+                        : launch_bits<D, 0, Tin, 0>(p, a.bits, groups, cus, st);
 }
 
 template <int D>
-hipError_t launch_d(const FwhtParams& p, const QuantizeArgs& a, unsigned grid, hipStream_t st) {
-  return a.dtype == TQ_F16 ? launch_in<D, _Float16>(p, a, grid, st) : launch_in<D, float>(p, a, grid, st);
+hipError_t launch_d(const FwhtParams& p, const QuantizeArgs& a, int64_t groups, int cus, hipStream_t st) {
+  return a.dtype == TQ_F16 ? launch_in<D, _Float16>(p, a, groups, cus, st) : launch_in<D, float>(p, a, groups, cus, st);
 }
 
 }  // namespace
@@ -437,13 +574,11 @@ hipError_t launch_quantize_fwht(const QuantizeArgs& a, hipStream_t st) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
-  const int64_t items = p.seqs * p.tiles;
-  int64_t grid = (items + kWaves - 1) / kWaves;
-  if (grid > (int64_t)cus * 8) grid = (int64_t)cus * 8;
+  const int64_t groups = (p.seqs * p.tiles + kWaves - 1) / kWaves;  // workgroups with a tile per wave
   switch (a.d) {
-    case 64: return launch_d<64>(p, a, (unsigned)grid, st);
-    case 128: return launch_d<128>(p, a, (unsigned)grid, st);
-    default: return launch_d<256>(p, a, (unsigned)grid, st);
+    case 64: return launch_d<64>(p, a, groups, cus, st);
+    case 128: return launch_d<128>(p, a, groups, cus, st);
+    default: return launch_d<256>(p, a, groups, cus, st);
   }
 }
 
