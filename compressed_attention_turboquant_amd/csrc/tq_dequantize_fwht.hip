@@ -13,14 +13,25 @@
 // holds the coordinates j = 8k + 64c + e (e < 8, c < d/64) with
 // k = (l & 3) | (l>>1 & 4); index bits 0-2 and 6-7 of j live in registers,
 // bits 3, 4 and 5 in lane bits 0, 1 and 3, so every cross-lane butterfly is one
-// DPP move plus one FMA with a +-1 factor.
+// v_fmac_f32 whose multiplicand is read through DPP (own + s * partner, the
+// upper lane's result negated; the lane's sign is folded into its output
+// scale).
 //  * The tile's packed codes (key rows or a coordinate-major value tile, d * bits
-//    bytes either way) come in with 16-byte loads into the wave's LDS slice; each
-//    lane then extracts the codes of its coordinates.
+//    bytes either way) come in with one 16-byte load per lane, a tile ahead,
+//    and go through the wave's LDS slice; each lane then reads the words that
+//    hold its coordinates' codes (one per 8 coordinates of a key row; 2 bits
+//    words per 8 coordinates of a value tile).
 //  * Centroids come from a 16-entry fp32 table in LDS (every lane reads one of
 //    16 words: no bank conflicts).
-//  * Each lane stores its 8-coordinate chunks of the output row as 16- or
-//    32-byte pieces.
+//  * The dithered variant's offset adds the same delta to every centroid; the
+//    transform takes a constant vector to d delta at coordinate 0, so it is one
+//    add on that coordinate.
+//  * D is a sign flip of each output (an xor of the sign bit), after the
+//    scale n / sqrt(d).
+//  * Memory goes through buffer instructions on per-tile records, with an
+//    out-of-range offset for what must not be accessed (a load returns 0, a
+//    store is dropped), so each tile issues the same memory instructions and the
+//    compiler's waits leave the next tile's loads in flight.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -38,16 +49,36 @@ constexpr int kThreads = 64 * kWaves;
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-
-// DPP controls (gfx9 encoding).
-constexpr int kDppXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kDppXor8 = 0x128; // row_ror:8 (within a row of 16 lanes: lane ^ 8)
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;  // past every record used here
+__device__ __forceinline__ Rsrc record(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);  // raw buffer
 }
+
+// One cross-lane butterfly stage on 8 values: a[i] += s * a[i] of the partner
+// lane, one v_fmac_f32 with its multiplicand read through DPP (the compiler
+// does not fold a DPP move into an FMAC).  A DPP read of a VGPR needs two wait
+// states after the VALU write of it, hence the s_nop; inside the block each
+// instruction reads a different register.
+#define TQ_BUTTERFLY8(NAME, MOD)                                                                    \
+  __device__ __forceinline__ void NAME(float* a, float s) {                                       \
+    asm volatile("s_nop 1\n\t"                                                                     \
+                 "v_fmac_f32_dpp %0, %0, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %1, %1, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %2, %2, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %3, %3, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %4, %4, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %5, %5, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %6, %6, %8 " MOD " row_mask:0xf bank_mask:0xf\n\t"              \
+                 "v_fmac_f32_dpp %7, %7, %8 " MOD " row_mask:0xf bank_mask:0xf"                    \
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),         \
+                   "+v"(a[6]), "+v"(a[7])                                                          \
+                 : "v"(s));                                                                        \
+  }
+TQ_BUTTERFLY8(butterfly8_xor1, "quad_perm:[1,0,3,2]")
+TQ_BUTTERFLY8(butterfly8_xor2, "quad_perm:[2,3,0,1]")
+TQ_BUTTERFLY8(butterfly8_xor8, "row_ror:8")
+#undef TQ_BUTTERFLY8
 
 struct FwhtDequantParams {
   const uint8_t* idx;
@@ -70,43 +101,78 @@ __global__ void __launch_bounds__(kThreads) dequant_fwht_kernel(FwhtDequantParam
   constexpr int NC = D / 64, V = 8 * NC;
   constexpr int kTileBytes = D * BITS;  // packed codes of 8 tokens, either layout
   constexpr uint32_t kMask = (1u << BITS) - 1u;
-  // The wave's tile bytes, with 8 bytes of slack for the two-word reads of bits_at.
+  constexpr int kOsz = OUT16 ? 2 : 4;   // output bytes per coordinate
+  // The wave's tile bytes, with 16 bytes of slack for the two-word reads of bits_at.
   __shared__ __align__(16) uint8_t raw[kWaves][kTileBytes + 16];
   __shared__ float ctab[16];
 
-  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int k = (lane & 3) | ((lane >> 1) & 4);
   const int tl = ((lane >> 2) & 1) | ((lane >> 3) & 6);
   if (threadIdx.x < 16) ctab[threadIdx.x] = threadIdx.x < (1 << BITS) ? p.cent[threadIdx.x] : 0.f;
   __syncthreads();
 
-  // Per lane coordinate factors D_j / sqrt(d).
-  float dsc[V];
-  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  // D as sign-bit masks on the lane's outputs (fp16 pairs or fp32 words).
+  constexpr int NM = OUT16 ? V / 2 : V;
+  uint32_t dmask[NM];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dsc[8 * c + e] = p.dsign[8 * k + 64 * c + e] * inv_sqrt_d;
+    for (int e = 0; e < 8; ++e) {
+      const bool neg = p.dsign[8 * k + 64 * c + e] < 0.f;
+      if constexpr (OUT16) {
+        if (e % 2 == 0) dmask[4 * c + e / 2] = 0u;
+        dmask[4 * c + e / 2] |= neg ? (e % 2 ? 0x80000000u : 0x8000u) : 0u;
+      } else {
+        dmask[8 * c + e] = neg ? 0x80000000u : 0u;
+      }
+    }
   const float s1 = (lane & 1) ? -1.f : 1.f, s2 = (lane & 2) ? -1.f : 1.f, s8 = (lane & 8) ? -1.f : 1.f;
+  const float osc = s1 * s2 * s8 / sqrtf((float)D);  // the lane's transform sign and 1/sqrt(d)
   const float dwidth = DITHER ? *p.dw : 0.f;
 
   const int64_t items = p.seqs * p.tiles;
   const int64_t wstride = (int64_t)gridDim.x * kWaves;
   const int64_t rowb = D * BITS / 8;
-  for (int64_t item = (int64_t)blockIdx.x * kWaves + w; item < items; item += wstride) {
-    const int64_t s = item / p.tiles, tile = item % p.tiles;
-    // ---- the tile's packed codes into LDS ----
-    const uint8_t* src = VALUES ? p.idx + (s * (p.cap / 8) + tile) * kTileBytes
-                                : p.idx + (s * p.cap + tile * 8) * rowb;
-#pragma unroll
-    for (int o = 16 * lane; o < kTileBytes; o += 1024)
-      *reinterpret_cast<u4*>(&raw[w][o]) = *reinterpret_cast<const u4*>(src + o);
+  struct Cursor {
+    int64_t item, s, tile;
+  };
+  const int64_t ds = wstride / p.tiles, dt = wstride % p.tiles;
+  auto advance = [&](Cursor& c) {
+    c.item += wstride;
+    c.s += ds;
+    c.tile += dt;
+    if (c.tile >= p.tiles) {
+      c.tile -= p.tiles;
+      c.s += 1;
+    }
+  };
+  struct In {
+    u4 codes;  // 16 bytes of the tile's packed codes (lane l: bytes 16 l ..)
+    float nn;  // the norm of the lane's token (0 past n)
+  };
+  const uint32_t coff = 16 * lane < kTileBytes ? 16u * lane : kOob;
+  auto load = [&](const Cursor& cu, In& in) {
+    const bool live = cu.item < items;  // uniform
+    const uint8_t* src = VALUES ? p.idx + (cu.s * (p.cap / 8) + cu.tile) * kTileBytes
+                                : p.idx + (cu.s * p.cap + cu.tile * 8) * rowb;
+    in.codes = __builtin_amdgcn_raw_buffer_load_b128(record(src, live ? kTileBytes : 0), coff, 0, 0);
+    const int64_t rows = min(p.n - cu.tile * 8, (int64_t)8);
+    in.nn = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        record(p.norm + cu.s * p.cap + cu.tile * 8, live ? 4 * rows : 0), 4 * tl, 0, 0));
+  };
+
+  auto process = [&](const Cursor& cu, const Cursor& ahead, In& in) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t s = cu.s, tile = cu.tile;
+    // ---- the tile's packed codes into LDS, then the next tile's loads ----
+    if (16 * lane < kTileBytes) *reinterpret_cast<u4*>(&raw[w][16 * lane]) = in.codes;
+    const float nn = in.nn;
+    load(ahead, in);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    const int64_t t = tile * 8 + tl;
-    const float delta = DITHER ? dither_offset(p.ds0, s, t, dwidth) : 0.f;
     // ---- centroids of the lane's coordinates ----
     float x[V];
 #pragma unroll
@@ -114,19 +180,30 @@ __global__ void __launch_bounds__(kThreads) dequant_fwht_kernel(FwhtDequantParam
       const int j0 = 8 * k + 64 * c;
       if constexpr (!VALUES) {
         // 8 consecutive codes of token tl's row, from bit BITS (tl D + j0)
-        const uint32_t b = bits_at(raw[w], BITS * (tl * D + j0));
+        uint32_t b;
+        if constexpr (BITS == 4) b = *reinterpret_cast<const uint32_t*>(&raw[w][(tl * D + j0) / 2]);
+        else b = bits_at(raw[w], BITS * (tl * D + j0));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[8 * c + e] = ctab[(b >> (BITS * e)) & kMask] + delta;
+        for (int e = 0; e < 8; ++e) x[8 * c + e] = ctab[(b >> (BITS * e)) & kMask];
+      } else if constexpr (BITS == 3) {
+        // code (j, tl) at bit 3 (8 j + tl) of the tile
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[8 * c + e] = ctab[bits_at(raw[w], 3 * (8 * (j0 + e) + tl)) & kMask];
       } else {
-        // code (j, tl) at bit BITS (8 j + tl) of the tile
+        // codes (j0 .. j0 + 7, t) are the 2 BITS words from byte BITS j0; code
+        // (j0 + e, tl) at bit BITS (8 e + tl) of them
+        uint32_t wd[2 * BITS];
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(&raw[w][BITS * j0]);
+#pragma unroll
+        for (int q = 0; q < 2 * BITS; ++q) wd[q] = src[q];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t b = bits_at(raw[w], BITS * (8 * (j0 + e) + tl));
-          x[8 * c + e] = ctab[b & kMask] + delta;
+          const int bit = BITS * 8 * e;  // + BITS tl, inside one word
+          x[8 * c + e] = ctab[(wd[bit / 32] >> ((bit % 32) + BITS * tl)) & kMask];
         }
       }
     }
-    __builtin_amdgcn_wave_barrier();  // raw[w] is rewritten by the next item
+    __builtin_amdgcn_wave_barrier();  // raw[w] is rewritten by the next tile
 
     // ---- unnormalised Walsh-Hadamard transform: register bits, then lane bits ----
 #pragma unroll
@@ -140,37 +217,71 @@ __global__ void __launch_bounds__(kThreads) dequant_fwht_kernel(FwhtDequantParam
       }
     }
 #pragma unroll
-    for (int v = 0; v < V; ++v) x[v] = fmaf(s1, x[v], dpp<kDppXor1>(x[v]));
+    for (int v = 0; v < V; v += 8) butterfly8_xor1(x + v, s1);
 #pragma unroll
-    for (int v = 0; v < V; ++v) x[v] = fmaf(s2, x[v], dpp<kDppXor2>(x[v]));
+    for (int v = 0; v < V; v += 8) butterfly8_xor2(x + v, s2);
 #pragma unroll
-    for (int v = 0; v < V; ++v) x[v] = fmaf(s8, x[v], dpp<kDppXor8>(x[v]));
+    for (int v = 0; v < V; v += 8) butterfly8_xor8(x + v, s8);
+    if constexpr (DITHER) {
+      // c[idx] + delta for every coordinate: H takes delta 1 to (d delta, 0, ...)
+      const float delta = dither_offset(p.ds0, s, tile * 8 + tl, dwidth);
+      if (k == 0) x[0] += (float)D * delta;  // lanes k = 0 hold coordinate 0 with sign +1
+    }
 
-    // ---- x_hat = n D H c / sqrt(d); the lane's 8-coordinate pieces of row t ----
-    if (t < p.n) {
-      const float nn = p.norm[s * p.cap + t];
-      const int64_t o = (s * p.n + t) * D + 8 * k;
+    // ---- x_hat = n D H c / sqrt(d): the lane's 8-coordinate pieces of row t ----
+    const int64_t rows = min(p.n - tile * 8, (int64_t)8);
+    const Rsrc orec = record(static_cast<uint8_t*>(p.out) + (s * p.n + tile * 8) * D * kOsz, rows * D * kOsz);
+    const uint32_t ooff = tl < rows ? (uint32_t)((tl * D + 8 * k) * kOsz) : kOob;
+    const float m = nn * osc;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        float y[8];
+    for (int c = 0; c < NC; ++c) {
+      if constexpr (OUT16) {
+        u4 h;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = x[8 * c + e] * (nn * dsc[8 * c + e]);
-        if constexpr (OUT16) {
-          u4 h;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const _Float16 a = (_Float16)y[2 * q], bh = (_Float16)y[2 * q + 1];
-            h[q] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, bh) << 16);
-          }
-          *reinterpret_cast<u4*>(static_cast<__half*>(p.out) + o + 64 * c) = h;
-        } else {
-          f4* dst = reinterpret_cast<f4*>(static_cast<float*>(p.out) + o + 64 * c);
-          dst[0] = f4{y[0], y[1], y[2], y[3]};
-          dst[1] = f4{y[4], y[5], y[6], y[7]};
+        for (int q = 0; q < 4; ++q) {
+          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+          const h2 pr = h2{(_Float16)(x[8 * c + 2 * q] * m), (_Float16)(x[8 * c + 2 * q + 1] * m)};
+          h[q] = __builtin_bit_cast(uint32_t, pr) ^ dmask[4 * c + q];
         }
+        __builtin_amdgcn_raw_buffer_store_b128(h, orec, ooff + 64 * c * kOsz, 0, 0);
+      } else {
+        u4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = __float_as_uint(x[8 * c + e] * m) ^ dmask[8 * c + e];
+          hi[e] = __float_as_uint(x[8 * c + 4 + e] * m) ^ dmask[8 * c + 4 + e];
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(lo, orec, ooff + 64 * c * kOsz, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(hi, orec, ooff + 64 * c * kOsz + 16, 0, 0);
       }
     }
+  };
+
+  // Two tiles in flight per wave: rounds of two without an exit test inside
+  // (so the loop is entered only from above and from its own end), then the
+  // last tile if the count is odd.  Dropped stores to an empty record give the
+  // path into the loop the same memory count as the loop's own end.
+  const int64_t item0 = (int64_t)blockIdx.x * kWaves + w;
+  Cursor cur{item0, item0 / p.tiles, item0 % p.tiles};
+  Cursor ahead = cur;
+  In in[2];
+  load(ahead, in[0]);
+  advance(ahead);
+  load(ahead, in[1]);
+  advance(ahead);
+  const Rsrc none = record(p.norm, 0);
+#pragma unroll
+  for (int i = 0; i < 2 * NC * (OUT16 ? 1 : 2) + 4; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 64 * i, 0, 0);
+  const int64_t mine = item0 < items ? (items - item0 + wstride - 1) / wstride : 0;
+  for (int64_t r = mine / 2; r > 0; --r) {
+    process(cur, ahead, in[0]);
+    advance(cur);
+    advance(ahead);
+    process(cur, ahead, in[1]);
+    advance(cur);
+    advance(ahead);
   }
+  if (mine % 2) process(cur, ahead, in[0]);
 }
 
 template <int D, int BITS, int VALUES, int OUT16>
