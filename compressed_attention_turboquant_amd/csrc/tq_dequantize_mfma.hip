@@ -21,6 +21,7 @@
 #include <type_traits>
 
 #include "tq_kernels.h"
+#include "tq_quant_common.h"
 
 namespace tq {
 namespace {
@@ -32,6 +33,12 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 64;        // tokens per workgroup step
 constexpr float kFactor = 16.f;  // scale of R^T and of the centroids
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;  // past every record used here
+__device__ __forceinline__ Rsrc record(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);  // raw buffer
+}
 
 __device__ __forceinline__ uint32_t hbits(_Float16 h) { return (uint32_t)__builtin_bit_cast(uint16_t, h); }
 
@@ -120,38 +127,67 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   const int64_t n = a.n, cap = a.cap;
   const int64_t tiles = (n + kTile - 1) / kTile;
   const int64_t items = a.seqs * tiles;
+  // Items item0 + i * gridDim.x: (sequence, tile) advance by a precomputed
+  // step with one carry, no division per tile.
+  const int64_t step_s = (int64_t)gridDim.x / tiles, step_t = (int64_t)gridDim.x % tiles;
+  int64_t item = blockIdx.x, seq = item / tiles, tile = item % tiles;
+  auto advance = [&](int64_t& it, int64_t& sq, int64_t& tl) {
+    it += gridDim.x;
+    sq += step_s;
+    tl += step_t;
+    if (tl >= tiles) {
+      tl -= tiles;
+      sq += 1;
+    }
+  };
   // The thread's 32 codes of a tile (and, for threads < 64, a token's norm)
   // are loaded one tile ahead, so that the loads are in flight while the
-  // matrix cores work on the previous tile.
+  // matrix cores work on the previous tile.  Loads and stores are buffer
+  // instructions on per-tile records with out-of-range offsets (a load returns
+  // 0, a store is dropped) instead of branches, so every tile issues the same
+  // memory instructions and the compiler's waits can count them.
   uint32_t w[BITS];
-  float nrm = 0.f, dlt = 0.f;
-  auto load_codes = [&](int64_t item) {
-    const int64_t seq = item / tiles, t0 = (item % tiles) * kTile;
-    bool live;
-    const uint32_t* src;
+  float nrm = 0.f;
+  auto load_codes = [&](int64_t it, int64_t sq, int64_t tl) {
+    const bool live = it < items;  // uniform
+    const int64_t t0 = tl * kTile;
+    const int64_t rows = live ? min(n - t0, (int64_t)kTile) : 0;  // tokens of the tile
+    uint32_t off;
+    const uint8_t* base;
+    int64_t bytes;
     if constexpr (VALUES) {
       // Value tiles of 8 tokens: code 8 k + i is coordinate k of token i, so
       // the thread's codes are coordinates 4q..4q+3 of the tile's 8 tokens.
       const int vt = tid / (D / 4), q = tid % (D / 4);
-      live = t0 + 8 * vt < n;
-      src = reinterpret_cast<const uint32_t*>(a.idx + (seq * (cap / 8) + t0 / 8 + vt) * (D * BITS) + q * 4 * BITS);
+      base = a.idx + (sq * (cap / 8) + t0 / 8) * (D * BITS);
+      bytes = (rows + 7) / 8 * (D * BITS);
+      off = 8 * vt < rows ? (uint32_t)(vt * (D * BITS) + q * 4 * BITS) : kOob;
     } else {
       const int tt = tid / NKB, q = tid % NKB;
-      live = t0 + tt < n;
-      src = reinterpret_cast<const uint32_t*>(a.idx + (seq * cap + t0 + tt) * (D * BITS / 8) + q * 4 * BITS);
+      base = a.idx + (sq * cap + t0) * (D * BITS / 8);
+      bytes = rows * (D * BITS / 8);
+      off = tt < rows ? (uint32_t)(tt * (D * BITS / 8) + q * 4 * BITS) : kOob;
     }
+    const Rsrc rc = record(base, bytes);
 #pragma unroll
-    for (int i = 0; i < BITS; ++i) w[i] = live ? src[i] : 0u;
-    if (tid < kTile) nrm = t0 + tid < n ? a.norm[seq * cap + t0 + tid] * (1.f / (kFactor * kFactor)) : 0.f;
-    if constexpr (DITHER) {
-      if (tid < kTile) dlt = dither_offset(a.dither_s0, seq, t0 + tid, dwidth) * (kFactor * kFactor);
-    }
+    for (int i = 0; i < BITS; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, off + 4 * i, 0, 0);
+    nrm = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(record(a.norm + sq * cap + t0, 4 * rows),
+                                                               tid < kTile ? 4u * tid : kOob, 0, 0));
   };
-  if (blockIdx.x < items) load_codes(blockIdx.x);
-  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-    const int64_t seq = item / tiles;
-    const int64_t t0 = (item % tiles) * kTile;
-    __syncthreads();  // the previous tile's operands have been read
+  load_codes(item, seq, tile);
+  {
+    // The loop's own path to its top has the tile's stores after these loads;
+    // as many dropped stores to an empty record give the path from here the
+    // same count, so the wait at the top leaves the stores in flight.
+    const Rsrc none = record(a.norm, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * (kTile / 16); ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 64 * i, 0, 0);
+  }
+  int64_t nitem = item, nseq = seq, ntile = tile;
+  advance(nitem, nseq, ntile);
+  for (; item < items; item = nitem, seq = nseq, tile = ntile, advance(nitem, nseq, ntile)) {
+    const int64_t t0 = tile * kTile;
+    lds_barrier();  // the previous tile's operands have been read
     // Decode: thread -> 32 consecutive codes of the packed stream.
     {
       uint32_t ph[16], pl[16];
@@ -180,18 +216,20 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
           *reinterpret_cast<u4*>(&blo[tt][32 * q + 8 * c]) = u4{pl[4 * c], pl[4 * c + 1], pl[4 * c + 2], pl[4 * c + 3]};
         }
       }
-      if (tid < kTile) nsh[tid] = nrm;
+      if (tid < kTile) nsh[tid] = nrm * (1.f / (kFactor * kFactor));
       if constexpr (DITHER) {
-        if (tid < kTile) dsh[tid] = dlt;
+        if (tid < kTile) dsh[tid] = dither_offset(a.dither_s0, seq, t0 + tid, dwidth) * (kFactor * kFactor);
       }
     }
-    __syncthreads();
-    if (item + gridDim.x < items) load_codes(item + gridDim.x);
-    // Sixteen tokens at a time: B operand lane (token l16, k-group g4).
-    const int64_t left = n - t0;
+    lds_barrier();
+    load_codes(nitem, nseq, ntile);
+    // Sixteen tokens at a time: B operand lane (token l16, k-group g4); the
+    // rows past n of the last tile are computed and not stored.
+    const int64_t rows = min(n - t0, (int64_t)kTile);
+    const Rsrc orec = record(static_cast<uint8_t*>(a.out) + (seq * n + t0) * D * (OUT16 ? 2 : 4),
+                             rows * D * (OUT16 ? 2 : 4));
 #pragma unroll
     for (int s = 0; s < kTile / 16; ++s) {
-      if (16 * s >= left) break;
       h8 bh[NKB], bl[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -219,18 +257,17 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
       }
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
-        if (tok < left) {
-          const int64_t o = (seq * n + t0 + tok) * D + 32 * wave + 16 * jb + 4 * g4;
-          f4 v = acc[jb] + cor[jb];
-          if constexpr (DITHER) v += dl * rsum[jb];
-          v *= nt;
-          if constexpr (OUT16) {
-            const u2 hv = {hbits((_Float16)v[0]) | (hbits((_Float16)v[1]) << 16),
-                           hbits((_Float16)v[2]) | (hbits((_Float16)v[3]) << 16)};
-            *reinterpret_cast<u2*>(static_cast<__half*>(a.out) + o) = hv;
-          } else {
-            *reinterpret_cast<f4*>(static_cast<float*>(a.out) + o) = v;
-          }
+        const int col = 32 * wave + 16 * jb + 4 * g4;
+        const uint32_t off = tok < rows ? (uint32_t)((tok * D + col) * (OUT16 ? 2 : 4)) : kOob;
+        f4 v = acc[jb] + cor[jb];
+        if constexpr (DITHER) v += dl * rsum[jb];
+        v *= nt;
+        if constexpr (OUT16) {
+          const u2 hv = {hbits((_Float16)v[0]) | (hbits((_Float16)v[1]) << 16),
+                         hbits((_Float16)v[2]) | (hbits((_Float16)v[3]) << 16)};
+          __builtin_amdgcn_raw_buffer_store_b64(hv, orec, off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), orec, off, 0, 0);
         }
       }
     }

@@ -43,4 +43,14 @@ __device__ __forceinline__ uint32_t symmetric_code(float y, const float (&t)[BIT
   return magnitude<BITS>(fabsf(y), t) ^ (y > 0.f ? K + 1u : K);
 }
 
+// Workgroup barrier that orders LDS only: global loads and stores stay in
+// flight across it (a plain __syncthreads also waits for every outstanding
+// global access, which drains prefetched loads and pending stores).  For
+// barriers whose only purpose is to hand LDS data between waves.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace tq
