@@ -17,6 +17,9 @@ Printed (one JSON line on stdout):
   roofline           decode kernels vs the 8 TB/s HBM peak
   roofline_quantize, roofline_dequantize   the other two calls vs the same peak
   stream_read_gbs    the best rate of a streaming-read kernel on this GPU
+  stream_rw_probe    the best rates of plain kernels that read 4 bytes per
+                     byte written and 1 per 4 written (the mixes of quantize and
+                     dequantize), with *_frac_of_stream_rw against them
   workloads          all five layer configurations: decode after the flush
                      and back to back, each against its own bound
                      (C1 launch latency, C4 matrix cores, the others HBM);
@@ -182,6 +185,9 @@ class Probe:
         self.lib.tq_probe_stream_read.restype = ctypes.c_int
         self.lib.tq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                                   ctypes.c_void_p]
+        self.lib.tq_probe_stream_rw.restype = ctypes.c_int
+        self.lib.tq_probe_stream_rw.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                                ctypes.c_void_p]
         self.sink = torch.empty(self.lib.tq_probe_stream_threads() * 16, dtype=torch.uint8, device=dev)
         self.flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
 
@@ -215,6 +221,32 @@ class Probe:
                     best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
             out["nontemporal" if nt else "plain"] = round(best, 1)
         del buf
+        return out
+
+    def peak_rw(self, dev, stream, small_bytes=2 << 30, reps=5):
+        """Best rate (bytes read + written per second, GB/s) of plain kernels
+        that read 4 bytes per byte written (a quantize call's mix) and read 1
+        byte per 4 written (a dequantize call's), 2 GiB on the small side."""
+        import torch
+        words = small_bytes // 16
+        small = torch.ones(small_bytes // 4, dtype=torch.int32, device=dev)
+        large = torch.ones(4 * small_bytes // 4, dtype=torch.int32, device=dev)
+        out = {}
+        for read4, tag in ((1, "read4_write1"), (0, "read1_write4")):
+            src, dst = (large, small) if read4 else (small, large)
+            best = 0.0
+            for i in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = self.lib.tq_probe_stream_rw(src.data_ptr(), dst.data_ptr(), words, read4, stream.cuda_stream)
+                e1.record(stream)
+                if rc != 0:
+                    raise RuntimeError(f"stream probe launch failed: {rc}")
+                torch.cuda.synchronize()
+                if i > 0:
+                    best = max(best, 5 * small_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+            out[tag] = round(best, 1)
+        del small, large
         return out
 
 
@@ -272,7 +304,7 @@ def timed(stream, fn, iters, before=None):
     return sum(e0.elapsed_time(e1) for e0, e1 in ev) / iters
 
 
-def measure_workload(L, stream, probe, iters, stream_gbs):
+def measure_workload(L, stream, probe, iters, stream_gbs, rw=None):
     """Decode (after a cache flush, and back to back), quantize and dequantize
     of one workload, each against its bound."""
     import torch
@@ -311,6 +343,10 @@ def measure_workload(L, stream, probe, iters, stream_gbs):
         "dequantize_gbs": round(cfg.rows * (cfg.d * (cfg.k_bits + cfg.v_bits) // 8 + 8 + 2 * cfg.d * in_b)
                                 / (deq * 1e-3) / 1e9, 1),
     }
+    if rw:
+        # against plain kernels with the same read/write mix (4:1 in, 1:4 out)
+        rec["quantize_frac_of_stream_rw"] = round(rec["quantize_gbs"] / rw["read4_write1"], 4)
+        rec["dequantize_frac_of_stream_rw"] = round(rec["dequantize_gbs"] / rw["read1_write4"], 4)
     if cfg.name == "C1":
         rec["roofline"] = {"bound": "latency", "achieved": round(cold * 1e3, 2), "unit": "us per call",
                            "peak": None, "frac": None,
@@ -488,6 +524,11 @@ def main():
         res["stream_read_probe"] = peaks
         res["decode_frac_of_stream"] = round(dec_gbs / sgbs, 4)
         log(f"streaming-read probe: {peaks} GB/s")
+        rw = probe.peak_rw(dev, stream)
+        res["stream_rw_probe"] = rw
+        res["quantize_frac_of_stream_rw"] = round(q_gbs / rw["read4_write1"], 4)
+        res["dequantize_frac_of_stream_rw"] = round(dq_gbs / rw["read1_write4"], 4)
+        log(f"read/write streaming probe: {rw} GB/s")
         wl = {}
         for name in ("C1", "C2", "C3", "C4", "C5"):
             c = workloads.CONFIGS[name]
@@ -496,7 +537,7 @@ def main():
             else:
                 log(f"workload {name}: generating and quantizing")
                 W = Layer(c, dev)
-            wl[name] = measure_workload(W, stream, probe, args.workload_iters, sgbs)
+            wl[name] = measure_workload(W, stream, probe, args.workload_iters, sgbs, rw)
             r = wl[name]
             log(f"  {name}: decode {r['decode_ms']:.4f} ms after a cache flush ({r['decode_gbs']:.0f} GB/s), "
                 f"{r['decode_ms_back_to_back']:.4f} ms back to back; quantize {r['quantize_k_ms']:.3f} + "

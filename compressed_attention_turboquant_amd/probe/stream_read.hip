@@ -1,5 +1,6 @@
-// Streaming-read probe: the HBM read rate a plain kernel reaches on this part,
-// the yardstick the decode's packed-KV rate is compared with.  Not part of the
+// Streaming probes: the HBM rates plain kernels reach on this part, the
+// yardsticks the library's rates are compared with (reads alone for decode;
+// 4:1 and 1:4 read/write mixes for quantize and dequantize).  Not part of the
 // TurboQuant path; built into its own library (libtqprobe.so) for bench.py.
 //
 // Every thread reads 16-byte words in a grid-stride loop, four loads in flight,
@@ -43,6 +44,27 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u4* __restrict__
   sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// Mixed streams of plain 16-byte loads and stores: each thread, per step,
+// either reads four words and writes their XOR (READ4 = true: 4 bytes read per
+// byte written, the shape of a quantize call, fp16 rows in and codes out) or
+// reads one word and writes it to four places (1 byte read per 4 written, a
+// dequantize call's shape).  `words` counts the smaller side.
+template <bool READ4>
+__global__ void __launch_bounds__(256) stream_rw_kernel(const u4* __restrict__ src, u4* __restrict__ dst,
+                                                        int64_t words) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride) {
+    const int64_t base = (i / stride) * 4 * stride + i % stride;  // four words stride apart
+    if constexpr (READ4) {
+      dst[i] = src[base] ^ src[base + stride] ^ src[base + 2 * stride] ^ src[base + 3 * stride];
+    } else {
+      const u4 v = src[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[base + k * stride] = v + (uint32_t)k;
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -70,6 +92,23 @@ int tq_probe_stream_read(const void* src, int64_t bytes, void* sink, int nontemp
     hipLaunchKernelGGL(stream_read_kernel<true>, grid, dim3(256), 0, st, s, bytes / 16, k);
   else
     hipLaunchKernelGGL(stream_read_kernel<false>, grid, dim3(256), 0, st, s, bytes / 16, k);
+  return (int)hipGetLastError();
+}
+
+// Mixed read/write stream: read4 != 0 reads 4 * words 16-byte words at src and
+// writes words at dst; read4 == 0 reads words at src and writes 4 * words at
+// dst (words a multiple of tq_probe_stream_threads()).  Returns a hipError_t.
+int tq_probe_stream_rw(const void* src, void* dst, int64_t words, int read4, void* stream) {
+  const int64_t threads = tq_probe_stream_threads();
+  const dim3 grid((unsigned)(threads / 256));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (words % threads) return (int)hipErrorInvalidValue;
+  if (read4)
+    hipLaunchKernelGGL(stream_rw_kernel<true>, grid, dim3(256), 0, st, static_cast<const u4*>(src),
+                       static_cast<u4*>(dst), words);
+  else
+    hipLaunchKernelGGL(stream_rw_kernel<false>, grid, dim3(256), 0, st, static_cast<const u4*>(src),
+                       static_cast<u4*>(dst), words);
   return (int)hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
@@ -36,7 +37,7 @@ COPY_BYTES = 1 << 30
 DECODE_KERNELS = ("prerotate_ref", "decode_mfma_kernel", "decode_wide_kernel", "decode_split_ref", "decode_combine_ref",
                   "combine_kernel", "combine_rows128_kernel")
 QUANT_KERNELS = ("quantize_mfma_kernel", "quantize_tile_ref", "quantize_fwht")
-DEQUANT_KERNELS = ("dequant_mfma_kernel",)
+DEQUANT_KERNELS = ("dequant_mfma_kernel", "dequant_fwht_kernel", "dequant_qjl_kernel")
 
 
 def strip_comments(src):
@@ -85,8 +86,38 @@ def _one(directory, suffix):
     return hits[0]
 
 
+def _unmangle(name):
+    """name<args> for a mangled library kernel whose template arguments are
+    integers, float or _Float16 (the profiler leaves names with _Float16
+    arguments mangled); the name unchanged if it is not of that form."""
+    m = re.match(r"_ZN2tq12_GLOBAL__N_1(\d+)", name)
+    if not m:
+        return name
+    i = m.end()
+    base = name[i:i + int(m.group(1))]
+    i += int(m.group(1))
+    if not name.startswith("I", i):
+        return base
+    i += 1
+    args = []
+    while i < len(name) and name[i] != "E":
+        if name.startswith("Li", i):
+            j = name.index("E", i)
+            args.append(name[i + 2:j])
+            i = j + 1
+        elif name.startswith("DF16_", i):
+            args.append("_Float16")
+            i += 5
+        elif name[i] in "fi":
+            args.append({"f": "float", "i": "int"}[name[i]])
+            i += 1
+        else:
+            return name
+    return f"{base}<{', '.join(args)}>"
+
+
 def _short(name):
-    name = name.replace("tq::(anonymous namespace)::", "").replace("void ", "")
+    name = _unmangle(name).replace("tq::(anonymous namespace)::", "").replace("void ", "")
     return name.split("(")[0] if "(" in name and "<" not in name.split("(")[0][-2:] else name[:80]
 
 
