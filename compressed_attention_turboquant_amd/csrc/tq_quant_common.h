@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 
 namespace tq {
@@ -41,6 +42,47 @@ template <int BITS>
 __device__ __forceinline__ uint32_t symmetric_code(float y, const float (&t)[BITS > 1 ? (1 << (BITS - 1)) - 1 : 1]) {
   constexpr uint32_t K = (1u << (BITS - 1)) - 1u;
   return magnitude<BITS>(fabsf(y), t) ^ (y > 0.f ? K + 1u : K);
+}
+
+// Binned code table for 3- and 4-bit codes.  The coordinate on the codebook's
+// N(0, 1) scale, z = y sqrt(d) (y a coordinate of the unit vector), is cut into
+// kBins bins of width 1 / kBinScale centred on 0, so they cover |z| < 4; the
+// bins outside hold no boundary (the outermost boundary of the 4-bit codebooks
+// is below 2.5), so values beyond them clamp to the end bins.  Every codebook's
+// boundaries are more than one bin apart (the narrowest gap is about 0.25), so
+// a bin holds at most one: its entry is {that boundary in bin units u = z
+// kBinScale + kBins / 2, or +inf; the count of boundaries below the bin}, and a
+// code is one lookup and one compare.  kBinCopies copies, one per lane of a
+// half wave, keep the lookups free of bank conflicts.
+constexpr int kBins = 64;
+constexpr float kBinScale = 8.f;
+constexpr int kBinCopies = 32;
+constexpr int kCodeTableEntries = kBins * kBinCopies;
+
+// Fills the table (kCodeTableEntries entries) from the 2^BITS - 1 sorted
+// boundaries bnd; ubin = sqrt(d) * kBinScale.  Threads tid of nthreads share the work.
+template <int BITS>
+__device__ __forceinline__ void fill_code_table(uint2* tab, const float* bnd, float ubin, int tid, int nthreads) {
+  constexpr int L = 1 << BITS;
+  for (int e = tid; e < kCodeTableEntries; e += nthreads) {
+    const int bin = e / kBinCopies;
+    uint32_t below = 0;
+    float inner = INFINITY;
+    for (int i = 0; i + 1 < L; ++i) {
+      const float ub = fmaf(bnd[i], ubin, 0.5f * kBins);
+      if (ub < (float)bin) ++below;
+      else if (ub < (float)(bin + 1)) inner = ub;
+    }
+    tab[e] = make_uint2(__float_as_uint(inner), below);
+  }
+}
+
+// Code of a value at u = z kBinScale + kBins / 2 (bin units) from the lane's
+// copy of the table (tab + lane % kBinCopies).
+__device__ __forceinline__ uint32_t table_code(const uint2* lane_tab, float u) {
+  const int bin = (int)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kBins - 1));
+  const uint2 ent = lane_tab[bin * kBinCopies];
+  return ent.y + (u > __uint_as_float(ent.x) ? 1u : 0u);
 }
 
 // Workgroup barrier that orders LDS only: global loads and stores stay in

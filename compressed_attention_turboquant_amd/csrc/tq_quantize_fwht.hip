@@ -50,16 +50,6 @@ constexpr int kThreads = 64 * kWaves;
 #endif
 constexpr int kAhead = TQ_FWHT_AHEAD;  // tiles whose loads a wave keeps in flight
 
-// Code table: kBins bins of width 1 / kBinScale on the codebook's N(0, 1) scale
-// z = y sqrt(d) (y a coordinate of the unit vector), centred on 0, so they
-// cover |z| < 4; the bins outside hold no boundary (the outermost boundary of
-// the 4-bit codebooks is below 2.5), so values beyond them clamp to the end
-// bins.  Every codebook's boundaries are more than one bin apart (the
-// narrowest gap is about 0.25), so a bin holds at most one.  32 copies, one
-// per lane of a half wave, keep the lookups free of bank conflicts.
-constexpr int kBins = 64;
-constexpr float kBinScale = 8.f;
-constexpr int kBinCopies = 32;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f8 __attribute__((ext_vector_type(8)));
@@ -161,7 +151,7 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
   typedef uint32_t Raw __attribute__((ext_vector_type(RW)));
   constexpr bool kTable = BITS >= 3;
   __shared__ __align__(16) uint8_t codes[kWaves][8][ROW];
-  __shared__ __align__(16) uint2 ctab[kTable ? kBins * kBinCopies : 1];  // {boundary in bin units, count below}
+  __shared__ __align__(16) uint2 ctab[kTable ? kCodeTableEntries : 1];  // binned code table
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int k = (lane & 3) | ((lane >> 1) & 4);
@@ -191,18 +181,7 @@ __global__ void __launch_bounds__(kThreads) quantize_fwht_kernel(FwhtParams p) {
   // Boundary b in bin units: u = z kBinScale + kBins / 2 with z = b sqrt(d).
   const float ubin = sqrt_d * kBinScale;
   if constexpr (kTable) {
-    constexpr int L = 1 << BITS;
-    for (int e = threadIdx.x; e < kBins * kBinCopies; e += kThreads) {
-      const int bin = e / kBinCopies;
-      uint32_t below = 0;
-      float inner = INFINITY;
-      for (int i = 0; i + 1 < L; ++i) {
-        const float ub = fmaf(p.bnd[i], ubin, 0.5f * kBins);
-        if (ub < (float)bin) ++below;
-        else if (ub < (float)(bin + 1)) inner = ub;
-      }
-      ctab[e] = make_uint2(__float_as_uint(inner), below);
-    }
+    fill_code_table<BITS>(ctab, p.bnd, ubin, threadIdx.x, kThreads);
     __syncthreads();
   }
   const uint2* ctab_lane = ctab + (kTable ? lane % kBinCopies : 0);

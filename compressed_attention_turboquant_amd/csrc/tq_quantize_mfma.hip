@@ -20,8 +20,10 @@
 //    what it stores: keys (row-major streams) use D = W * X^T, a lane holding 8
 //    consecutive coordinates of a token; values (8-token coordinate-major
 //    tiles) use D = X * W^T, a lane holding one coordinate of 8 tokens.
-//  * The scalar quantizer compares |y| with the positive half of the symmetric
-//    boundaries and picks the centroid magnitude in the same pass.
+//  * The scalar quantizer takes 3- and 4-bit codes from the binned table of
+//    tq_quant_common.h (one LDS lookup and one compare per value) and 1- and
+//    2-bit codes from a branchless search of |y| over the positive half of the
+//    symmetric boundaries.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -61,6 +63,8 @@ quantize_mfma_kernel(QuantMfmaParams p) {
   __shared__ __align__(16) _Float16 rs[2][kSlots][D + 8];    // residual hi / lo
   __shared__ float nrm[kSlots];
   __shared__ float rsq[kSlots][16];
+  constexpr bool kTable = BITS >= 3;  // 3- and 4-bit codes from the binned table
+  __shared__ __align__(16) uint2 ctabl[kTable ? kCodeTableEntries : 1];
 
   const int tid = threadIdx.x;
   const int w = tid / 64, lane = tid % 64;
@@ -90,6 +94,12 @@ quantize_mfma_kernel(QuantMfmaParams p) {
   for (int i = 0; i < KP; ++i) beta[i] = BITS > 1 ? p.bnd[(1 << (BITS - 1)) + i] : 0.f;
   const int ctab = __float_as_int(p.cent[lane % 16]);
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  const float ubin = sqrtf((float)D) * kBinScale;  // unit-vector coordinate -> bin units
+  if constexpr (kTable) {
+    fill_code_table<BITS>(ctabl, p.bnd, ubin, tid, kThreads);
+    __syncthreads();
+  }
+  const uint2* ctab_lane = ctabl + (kTable ? lane % kBinCopies : 0);
 
   // Work unit: 4 consecutive value tiles (32 token slots) of one sequence.
   const int tiles = (int)(p.tile_last - p.tile_first + 1);  // tiles per sequence touched
@@ -203,7 +213,9 @@ quantize_mfma_kernel(QuantMfmaParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float y = acc[ct][tt][q] * inv;
-            const uint32_t code = symmetric_code<BITS>(y, beta);
+            uint32_t code;
+            if constexpr (kTable) code = table_code(ctab_lane, fmaf(acc[ct][tt][q], inv * ubin, 0.5f * kBins));
+            else code = symmetric_code<BITS>(y, beta);
             const float c = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(code << 2), ctab));
             packed |= code << (BITS * (4 * ct + q));
             r[4 * ct + q] = y - c;
@@ -315,7 +327,10 @@ quantize_mfma_kernel(QuantMfmaParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int k = 4 * tt + q;
-            packed |= symmetric_code<BITS>(acc[ct][tt][q] * inv[k], beta) << (BITS * k);
+            if constexpr (kTable)
+              packed |= table_code(ctab_lane, fmaf(acc[ct][tt][q], inv[k] * ubin, 0.5f * kBins)) << (BITS * k);
+            else
+              packed |= symmetric_code<BITS>(acc[ct][tt][q] * inv[k], beta) << (BITS * k);
           }
         if (tile_ok) {
           uint8_t* dst = tile_base + out_coord(w, ct, l16) * BITS;
