@@ -78,7 +78,10 @@ struct WideState {
   h8 bqh[CT][4], bql[CT][4];                         // centroid term, hi and lo
   h8 bsh[QJL ? CT : 1][4], bsl[QJL ? CT : 1][4];     // sign term, hi and lo
   f4 acc[CT][8];                                     // P.V, rotated domain
-  float m[CT], msafe[CT], lsum[CT], ca[CT], c2[CT], c0[CT];
+  // Scores are kept in units of 1/ca (ca: the row's factor to log2 units), the
+  // factor applied in the exponent's FMA: s = kn (sc + kg r2 ss), with the
+  // sign product ss started at r0 (the offset of the masked-exponent operand).
+  float m[CT], cm[CT], sl[CT], lsum[CT], ca[CT], r2[CT], r0[CT];  // cm = -ca * max, sl = kSlack / ca
   int limit[CT];
   float vsc, vlim;
   const uint32_t *ktab, *vtab;
@@ -93,7 +96,10 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) sc[t][ct] = ss[t][ct] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct) {
+      sc[t][ct] = f4{0.f, 0.f, 0.f, 0.f};
+      ss[t][ct] = f4{ws.r0[ct], ws.r0[ct], ws.r0[ct], ws.r0[ct]};
+    }
   // Scores: decoded keys (A) times the query rows' hi and lo parts (B).
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -169,19 +175,21 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = (cur.kn[t][i] * ws.ca[ct]) * sc[t][ct][i];
-        if constexpr (QJL) v = fmaf(cur.kn[t][i] * cur.kg[t][i], fmaf(ws.c2[ct], ss[t][ct][i], ws.c0[ct]), v);
+        float v;
+        if constexpr (QJL) v = cur.kn[t][i] * fmaf(cur.kg[t][i] * ws.r2[ct], ss[t][ct][i], sc[t][ct][i]);
+        else v = cur.kn[t][i] * sc[t][ct][i];
         v = 4 * t + i < lrel ? v : -INFINITY;
         if constexpr (SCORES) {
-          if (ws.limit[ct] >= 0 && 4 * t + i < nrel) p.scores[srow[ct] * p.N + kbase + 4 * t + i] = v * kLn2;
+          if (ws.limit[ct] >= 0 && 4 * t + i < nrel)
+            p.scores[srow[ct] * p.N + kbase + 4 * t + i] = v * (ws.ca[ct] * kLn2);
         }
         s[4 * t + i] = v;
       }
     float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     mx = max_over_row_groups(mx);
-    if (__any(mx > ws.m[ct] + kSlack)) {
+    if (__any(mx > ws.m[ct] + ws.sl[ct])) {
       const float mnew = fmaxf(ws.m[ct], mx);
-      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(ws.m[ct] - mnew);
+      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(ws.ca[ct] * (ws.m[ct] - mnew));
       ws.lsum[ct] *= alpha;
       float ar[4];  // factors of the accumulator rows 4 g4 + r (held by lanes l16 = 4 g4 + r)
 #pragma unroll
@@ -191,7 +199,7 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
 #pragma unroll
         for (int r = 0; r < 4; ++r) ws.acc[ct][cb][r] *= ar[r];
       ws.m[ct] = mnew;
-      ws.msafe[ct] = mnew == -INFINITY ? 0.f : mnew;
+      ws.cm[ct] = mnew == -INFINITY ? 0.f : -ws.ca[ct] * mnew;
     }
     float ls = 0.f;
 #pragma unroll
@@ -199,7 +207,7 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * t + i;
-        const float pr = __builtin_amdgcn_exp2f(s[e] - ws.msafe[ct]);
+        const float pr = __builtin_amdgcn_exp2f(fmaf(ws.ca[ct], s[e], ws.cm[ct]));
         ls += pr;
         const float q = pr * vnv[e] * ws.vsc;
         const _Float16 h = (_Float16)q;
@@ -428,12 +436,15 @@ decode_wide_kernel(DecodeMfmaParams p) {
       // v = sqrt(d) R q, so the centroid product carries sqrt(d) / c1 on top
       // of R q: c1 / sqrt(d) undoes it, and 1 / sqrt(d) is the score's factor.
       ws.ca[ct] = c1 * inv_sqrt_d * inv_sqrt_d * kLog2e;
-      ws.c2[ct] = c2v * cq;
-      ws.c0[ct] = -sum * cq;
+      // sign term c2v cq (ss + r0) with ss the product of the normalised
+      // operand; offset r0 = -sum / c2v; in units of 1/ca
+      ws.r2[ct] = c2v * cq / ws.ca[ct];
+      ws.r0[ct] = -sum / c2v;
+      ws.sl[ct] = kSlack / ws.ca[ct];
       const int c = row0 + 16 * ct + l16;
       ws.limit[ct] = c < RH ? (int)(p.causal ? p.N - p.Tq + (c % p.Tq) + 1 : p.N) : -1;
       ws.m[ct] = -INFINITY;
-      ws.msafe[ct] = 0.f;
+      ws.cm[ct] = 0.f;
       ws.lsum[ct] = 0.f;
     }
   }
@@ -477,7 +488,7 @@ decode_wide_kernel(DecodeMfmaParams p) {
     const int c = row0 + 16 * ct + l16;
     if (g4 == 0 && c < RH) {
       float* dst = p.part + ((int64_t)split * rows_total + qrow_of(c)) * (kWD + kPartPad);
-      dst[kWD] = ws.m[ct] * kLn2;  // natural-log units, as the combine kernel expects
+      dst[kWD] = ws.m[ct] * (ws.ca[ct] * kLn2);  // natural-log units, as the combine kernel expects
       dst[kWD + 1] = L;
     }
   }
