@@ -283,21 +283,27 @@ struct SeqBuffers {
 };
 
 constexpr int kBufCfg = 0x00020000;  // raw (untyped) buffer on gfx9
+// Cache policy of the packed-cache loads (the aux operand of the buffer
+// loads): kLoadNT marks them non-temporal (streamed past the caches).  That
+// measured faster for the split kernel at d = 128, whose loads are whole
+// lines (C3 360 -> 357 us), and much slower at d = 256 (C5 786 -> 995 us) and
+// for the many-rows kernel, whose row groups meet each key block in L2.
+constexpr int kLoadNT = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufCfg);
 }
 
-template <int N>
+template <int N, int kLoadAux = 0>
 __device__ __forceinline__ void buf_load(uint32_t (&dst)[N], __amdgpu_buffer_rsrc_t r, int off) {
   if constexpr (N == 1) {
-    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadAux);
   } else if constexpr (N == 2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadAux);
     dst[0] = v[0];
     dst[1] = v[1];
   } else if constexpr (N == 3) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, kLoadAux);
     dst[0] = v[0];
     dst[1] = v[1];
     dst[2] = v[2];
@@ -306,7 +312,7 @@ __device__ __forceinline__ void buf_load(uint32_t (&dst)[N], __amdgpu_buffer_rsr
     if constexpr (N % 4 == 0) {
 #pragma unroll
       for (int i = 0; i < N; i += 4) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, kLoadAux);
         dst[i] = v[0];
         dst[i + 1] = v[1];
         dst[i + 2] = v[2];
@@ -315,8 +321,8 @@ __device__ __forceinline__ void buf_load(uint32_t (&dst)[N], __amdgpu_buffer_rsr
     } else {  // 6 or 12 dwords: b128 + b64 pieces
 #pragma unroll
       for (int i = 0; i < N; i += 6) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0);
-        const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * i + 16, 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, kLoadAux);
+        const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * i + 16, 0, kLoadAux);
         dst[i] = v[0];
         dst[i + 1] = v[1];
         dst[i + 2] = v[2];
@@ -328,27 +334,29 @@ __device__ __forceinline__ void buf_load(uint32_t (&dst)[N], __amdgpu_buffer_rsr
   }
 }
 
+template <int kLoadAux = 0>
 __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadAux));
 }
 
 template <int D, int KB, int QJL, int VB>
 __device__ __forceinline__ void load_block(Block<D, KB, QJL, VB>& b, const SeqBuffers& sb, int k0,
                                            int l16, int g4) {
   using S = Shape<D, KB, QJL, VB>;
+  constexpr int A = D == 128 ? kLoadNT : 0;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int key = k0 + 16 * t + l16;
-    buf_load(b.kw[t], sb.kidx, key * S::KROW + g4 * (S::KROW / 4));
-    if constexpr (QJL) buf_load(b.sw[t], sb.ksign, key * (D / 8) + g4 * (D / 32));
-    b.kn[t] = buf_f32(sb.knorm, key * 4);
-    if constexpr (QJL) b.kg[t] = buf_f32(sb.krnorm, key * 4);
-    b.vn[t] = buf_f32(sb.vnorm, key * 4);
+    buf_load<S::NWK, A>(b.kw[t], sb.kidx, key * S::KROW + g4 * (S::KROW / 4));
+    if constexpr (QJL) buf_load<S::NSW, A>(b.sw[t], sb.ksign, key * (D / 8) + g4 * (D / 32));
+    b.kn[t] = buf_f32<A>(sb.knorm, key * 4);
+    if constexpr (QJL) b.kg[t] = buf_f32<A>(sb.krnorm, key * 4);
+    b.vn[t] = buf_f32<A>(sb.vnorm, key * 4);
   }
   // The tile index is below 2^24 (buffer offsets are 32-bit), so a 24-bit
   // multiply is exact; a 32-bit one compiles to a 64-bit multiply-add whose
   // unused high operand can make the loop wait for every load in flight.
-  buf_load(b.vw, sb.vidx, (int)__umul24((unsigned)(k0 / 8 + g4), (unsigned)S::VTILE) + l16 * (S::VTILE / 16));
+  buf_load<S::NWV, A>(b.vw, sb.vidx, (int)__umul24((unsigned)(k0 / 8 + g4), (unsigned)S::VTILE) + l16 * (S::VTILE / 16));
 }
 
 // Per-wave state of the running softmax and the query operands.  A lane holds
