@@ -284,10 +284,12 @@ struct SeqBuffers {
 
 constexpr int kBufCfg = 0x00020000;  // raw (untyped) buffer on gfx9
 // Cache policy of the packed-cache loads (the aux operand of the buffer
-// loads): kLoadNT marks them non-temporal (streamed past the caches).  That
-// measured faster for the split kernel at d = 128, whose loads are whole
-// lines (C3 360 -> 357 us), and much slower at d = 256 (C5 786 -> 995 us) and
-// for the many-rows kernel, whose row groups meet each key block in L2.
+// loads): kLoadNT marks them non-temporal (streamed past the caches).  In the
+// split kernel the key codes, signs and norms load that way (measured in one
+// run: C3 357 -> 340 us, C5 786 -> 771 us); the value tiles do not: their
+// lanes read 48- or 64-byte pieces in several 16-byte loads, which then fetch
+// their lines again (C5 786 -> 953 us with them non-temporal).  The
+// many-rows kernel keeps the default: its row groups meet each key block in L2.
 constexpr int kLoadNT = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -343,7 +345,7 @@ template <int D, int KB, int QJL, int VB>
 __device__ __forceinline__ void load_block(Block<D, KB, QJL, VB>& b, const SeqBuffers& sb, int k0,
                                            int l16, int g4) {
   using S = Shape<D, KB, QJL, VB>;
-  constexpr int A = D == 128 ? kLoadNT : 0;
+  constexpr int A = kLoadNT, AV = 0;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int key = k0 + 16 * t + l16;
@@ -356,7 +358,7 @@ __device__ __forceinline__ void load_block(Block<D, KB, QJL, VB>& b, const SeqBu
   // The tile index is below 2^24 (buffer offsets are 32-bit), so a 24-bit
   // multiply is exact; a 32-bit one compiles to a 64-bit multiply-add whose
   // unused high operand can make the loop wait for every load in flight.
-  buf_load<S::NWV, A>(b.vw, sb.vidx, (int)__umul24((unsigned)(k0 / 8 + g4), (unsigned)S::VTILE) + l16 * (S::VTILE / 16));
+  buf_load<S::NWV, AV>(b.vw, sb.vidx, (int)__umul24((unsigned)(k0 / 8 + g4), (unsigned)S::VTILE) + l16 * (S::VTILE / 16));
 }
 
 // Per-wave state of the running softmax and the query operands.  A lane holds
