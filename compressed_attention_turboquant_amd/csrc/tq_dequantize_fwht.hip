@@ -51,6 +51,9 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr uint32_t kOob = 0x80000000u;  // past every record used here
+// Non-temporal cache policy (streamed past the caches) for the codes read and
+// the rows written, each touched once (C5 K + V 4.41 -> 4.27 ms).
+constexpr int kNT = 2;
 __device__ __forceinline__ Rsrc record(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);  // raw buffer
 }
@@ -156,7 +159,7 @@ __global__ void __launch_bounds__(kThreads) dequant_fwht_kernel(FwhtDequantParam
     const bool live = cu.item < items;  // uniform
     const uint8_t* src = VALUES ? p.idx + (cu.s * (p.cap / 8) + cu.tile) * kTileBytes
                                 : p.idx + (cu.s * p.cap + cu.tile * 8) * rowb;
-    in.codes = __builtin_amdgcn_raw_buffer_load_b128(record(src, live ? kTileBytes : 0), coff, 0, 0);
+    in.codes = __builtin_amdgcn_raw_buffer_load_b128(record(src, live ? kTileBytes : 0), coff, 0, kNT);
     const int64_t rows = min(p.n - cu.tile * 8, (int64_t)8);
     in.nn = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
         record(p.norm + cu.s * p.cap + cu.tile * 8, live ? 4 * rows : 0), 4 * tl, 0, 0));
@@ -243,7 +246,7 @@ __global__ void __launch_bounds__(kThreads) dequant_fwht_kernel(FwhtDequantParam
           const h2 pr = h2{(_Float16)(x[8 * c + 2 * q] * m), (_Float16)(x[8 * c + 2 * q + 1] * m)};
           h[q] = __builtin_bit_cast(uint32_t, pr) ^ dmask[4 * c + q];
         }
-        __builtin_amdgcn_raw_buffer_store_b128(h, orec, ooff + 64 * c * kOsz, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(h, orec, ooff + 64 * c * kOsz, 0, kNT);
       } else {
         u4 lo, hi;
 #pragma unroll
@@ -251,8 +254,8 @@ __global__ void __launch_bounds__(kThreads) dequant_fwht_kernel(FwhtDequantParam
           lo[e] = __float_as_uint(x[8 * c + e] * m) ^ dmask[8 * c + e];
           hi[e] = __float_as_uint(x[8 * c + 4 + e] * m) ^ dmask[8 * c + 4 + e];
         }
-        __builtin_amdgcn_raw_buffer_store_b128(lo, orec, ooff + 64 * c * kOsz, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(hi, orec, ooff + 64 * c * kOsz + 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(lo, orec, ooff + 64 * c * kOsz, 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b128(hi, orec, ooff + 64 * c * kOsz + 16, 0, kNT);
       }
     }
   };
