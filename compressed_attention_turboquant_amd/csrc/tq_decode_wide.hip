@@ -87,7 +87,9 @@ struct WideState {
   const uint32_t *ktab, *vtab;
 };
 
-template <int KB, int QJL, int VB, int SCORES, int CT>
+// MASK: the block may hold keys at or past N or past a row's causal limit
+// (the tail of a split); other blocks skip those selects.
+template <int KB, int QJL, int VB, int SCORES, int CT, bool MASK>
 __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideBlock<KB, QJL, VB>& cur, int k0,
                                              const DecodeMfmaParams& p, const int64_t (&srow)[CT], int l16,
                                              int g4) {
@@ -142,7 +144,7 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
   const int nrel = N - kbase;
   float vnv[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) vnv[e] = e < nrel ? cur.vn[e / 4][e % 4] : 0.f;
+  for (int e = 0; e < 8; ++e) vnv[e] = !MASK || e < nrel ? cur.vn[e / 4][e % 4] : 0.f;
   // Value-norm scale (as in the split kernel): the block's largest norm over
   // the lane's 8 keys and the four lane groups.  The norms are >= 0, so their
   // bit patterns order like the values (integer maxima, no NaN handling).
@@ -178,7 +180,7 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
         float v;
         if constexpr (QJL) v = cur.kn[t][i] * fmaf(cur.kg[t][i] * ws.r2[ct], ss[t][ct][i], sc[t][ct][i]);
         else v = cur.kn[t][i] * sc[t][ct][i];
-        v = 4 * t + i < lrel ? v : -INFINITY;
+        if constexpr (MASK) v = 4 * t + i < lrel ? v : -INFINITY;
         if constexpr (SCORES) {
           if (ws.limit[ct] >= 0 && 4 * t + i < nrel)
             p.scores[srow[ct] * p.N + kbase + 4 * t + i] = v * (ws.ca[ct] * kLn2);
@@ -459,12 +461,23 @@ decode_wide_kernel(DecodeMfmaParams p) {
   // Two rotating register sets, one block in flight while the other is used
   // (a block's matrix-core work covers the load latency).  Prefetches past the
   // split stay inside the sequence (or return 0 past its capacity).
+  // Blocks wholly below N and below every row's causal limit (at least
+  // N - Tq + 1) need no masks: pairs of them first, then the rest masked.
+  const int64_t unmasked_end = p.causal ? p.N - p.Tq + 1 : p.N;  // keys [0, unmasked_end) are visible to every row
+  int mid = (int)min((int64_t)blk1, unmasked_end / 32);
+  mid = mid <= blk ? blk : blk + ((mid - blk) & ~1);
+  for (; blk < mid; blk += 2) {
+    load_wide(b1, sb, (blk + 1) * 32, l16, g4);
+    process_wide<KB, QJL, VB, SCORES, CT, false>(ws, b0, blk * 32, p, srow, l16, g4);
+    load_wide(b0, sb, (blk + 2) * 32, l16, g4);
+    process_wide<KB, QJL, VB, SCORES, CT, false>(ws, b1, (blk + 1) * 32, p, srow, l16, g4);
+  }
   for (; blk < blk1; blk += 2) {
     load_wide(b1, sb, (blk + 1) * 32, l16, g4);
-    process_wide<KB, QJL, VB, SCORES, CT>(ws, b0, blk * 32, p, srow, l16, g4);
+    process_wide<KB, QJL, VB, SCORES, CT, true>(ws, b0, blk * 32, p, srow, l16, g4);
     if (blk + 1 >= blk1) break;
     load_wide(b0, sb, (blk + 2) * 32, l16, g4);
-    process_wide<KB, QJL, VB, SCORES, CT>(ws, b1, (blk + 1) * 32, p, srow, l16, g4);
+    process_wide<KB, QJL, VB, SCORES, CT, true>(ws, b1, (blk + 1) * 32, p, srow, l16, g4);
   }
 
   // Partials of the wave's rows: accumulator rows 4 g4 + r of each tile hold
