@@ -81,9 +81,11 @@ struct WideState {
   // Scores are kept in units of 1/ca (ca: the row's factor to log2 units), the
   // factor applied in the exponent's FMA: s = kn (sc + kg r2 ss), with the
   // sign product ss started at r0 (the offset of the masked-exponent operand).
-  float m[CT], cm[CT], sl[CT], lsum[CT], ca[CT], r2[CT], r0[CT];  // cm = -ca * max, sl = kSlack / ca
+  // The value-norm factor vsc (a power of two) rides in the exponent: cm =
+  // log2(vsc) - ca * max, so the weights and lsum carry it too.
+  float m[CT], cm[CT], sl[CT], lsum[CT], ca[CT], r2[CT], r0[CT];  // sl = kSlack / ca
   int limit[CT];
-  float vsc, vlim;
+  float vsc, vlim, lv;  // lv = log2(vsc)
   const uint32_t *ktab, *vtab;
 };
 
@@ -157,13 +159,18 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
       vl = max_over_row_groups(vl);
       int e = 0;
       frexpf(vl, &e);
-      const float nsc = fminf(ws.vsc, ldexpf(1.f, kVExp - e));
+      const float nlv = fminf(ws.lv, (float)(kVExp - e));
+      const float nsc = ldexpf(1.f, (int)nlv);
       const float ratio = nsc / ws.vsc;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) ws.acc[ct][cb] *= ratio;
+        ws.lsum[ct] *= ratio;
+        ws.cm[ct] += nlv - ws.lv;
+      }
       ws.vsc = nsc;
+      ws.lv = nlv;
       ws.vlim = ldexpf(1.f, kVExp) / nsc;
     }
   }
@@ -201,7 +208,7 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
 #pragma unroll
         for (int r = 0; r < 4; ++r) ws.acc[ct][cb][r] *= ar[r];
       ws.m[ct] = mnew;
-      ws.cm[ct] = mnew == -INFINITY ? 0.f : -ws.ca[ct] * mnew;
+      ws.cm[ct] = mnew == -INFINITY ? ws.lv : fmaf(-ws.ca[ct], mnew, ws.lv);
     }
     float ls = 0.f;
 #pragma unroll
@@ -211,7 +218,7 @@ __device__ __forceinline__ void process_wide(WideState<QJL, CT>& ws, const WideB
         const int e = 4 * t + i;
         const float pr = __builtin_amdgcn_exp2f(fmaf(ws.ca[ct], s[e], ws.cm[ct]));
         ls += pr;
-        const float q = pr * vnv[e] * ws.vsc;
+        const float q = pr * vnv[e];
         const _Float16 h = (_Float16)q;
         ph[ct][e] = h;
         pl[ct][e] = (_Float16)(q - (float)h);
@@ -446,7 +453,7 @@ decode_wide_kernel(DecodeMfmaParams p) {
       const int c = row0 + 16 * ct + l16;
       ws.limit[ct] = c < RH ? (int)(p.causal ? p.N - p.Tq + (c % p.Tq) + 1 : p.N) : -1;
       ws.m[ct] = -INFINITY;
-      ws.cm[ct] = 0.f;
+      ws.cm[ct] = -kSlack;  // log2(kInvSlack), the initial vsc
       ws.lsum[ct] = 0.f;
     }
   }
@@ -455,6 +462,7 @@ decode_wide_kernel(DecodeMfmaParams p) {
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) ws.acc[ct][cb] = f4{0.f, 0.f, 0.f, 0.f};
   ws.vsc = kInvSlack;
+  ws.lv = -kSlack;
   ws.vlim = ldexpf(1.f, kVExp) / kInvSlack;
   __syncthreads();  // the code tables are filled
 
@@ -484,6 +492,7 @@ decode_wide_kernel(DecodeMfmaParams p) {
   // coordinates 8 l16 + cb; (max, sum) of row l16 come from the lanes with g4 = 0.
   const int64_t rows_total = (int64_t)(gridDim.x / p.rgroups) / p.Hkv * p.Hq * p.Tq;
   const float inv_sv = 1.f / (ws.vsc * scale_v);
+  const float inv_vsc = 1.f / ws.vsc;  // exact: a power of two
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const float L = sum_over_row_groups(ws.lsum[ct]);
@@ -502,7 +511,7 @@ decode_wide_kernel(DecodeMfmaParams p) {
     if (g4 == 0 && c < RH) {
       float* dst = p.part + ((int64_t)split * rows_total + qrow_of(c)) * (kWD + kPartPad);
       dst[kWD] = ws.m[ct] * (ws.ca[ct] * kLn2);  // natural-log units, as the combine kernel expects
-      dst[kWD + 1] = L;
+      dst[kWD + 1] = L * inv_vsc;
     }
   }
 }
