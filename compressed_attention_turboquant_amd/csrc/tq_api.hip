@@ -219,6 +219,7 @@ DequantArgs dequant_args(const tq_layer* layer, int32_t which, const tq_cache* c
   a.dither = (layer->flags & TQ_LAYER_DITHER) != 0;
   a.dither_s0 = dither_stream_start(layer->seed, which == TQ_KEYS ? kDitherTagKeys : kDitherTagValues);
   a.dither_w = blob_f(layer, BL.scales) + (which == TQ_KEYS ? 4 : 5);
+  a.cscale = blob_f(layer, BL.scales) + (which == TQ_KEYS ? 0 : 1);
   return a;
 }
 

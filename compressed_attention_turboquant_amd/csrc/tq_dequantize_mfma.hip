@@ -12,6 +12,12 @@
 // adds three products per fragment (hi*hi + hi*lo + lo*hi; the dropped lo*lo
 // term is below 2^-22 relative).  Both factors are scaled by 16 (exact) so
 // that their lo parts stay normal fp16 numbers; 1/256 is folded into the norm.
+// Rows written as fp16 take two products instead: R^T hi and lo times the
+// centroids as single fp16 copies of s c, with the codebook factor s the
+// decode tables use (chosen on the host so that every s c_i is within
+// 1e-4 relative of its fp16 copy for every codebook built here, 2.3e-5 at
+// 3 bits and 1e-6 at 1 and 2); the error before the output's rounding is
+// then below 1.1e-4 of the norm, and 1/(16 s) goes into the norm.
 // A lane's accumulator holds 4 consecutive coordinates of one token, stored as
 // one float4 (or 4 halves).
 #include <hip/hip_runtime.h>
@@ -70,9 +76,11 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   constexpr int NKB = D / 32;         // k-blocks of the MFMA
   constexpr int PITCH = D + 8;        // LDS row pitch (halves): rows 16 bytes apart in the banks
   constexpr int kPairs = 1 << (2 * BITS);
-  // code pair -> {two fp16 hi parts, two fp16 lo parts} (first code in the low halves)
-  __shared__ __align__(8) u2 tpair[kPairs];
-  __shared__ __align__(16) _Float16 bhi[kTile][PITCH], blo[kTile][PITCH];
+  // code pair -> {two fp16 hi parts, two fp16 lo parts} (first code in the low
+  // halves); fp16 rows: the two fp16 copies of s c only.
+  using Pair = std::conditional_t<OUT16 != 0, uint32_t, u2>;
+  __shared__ __align__(8) Pair tpair[kPairs];
+  __shared__ __align__(16) _Float16 bhi[kTile][PITCH], blo[OUT16 ? 1 : kTile][OUT16 ? 8 : PITCH];
   __shared__ float nsh[kTile];
   __shared__ float dsh[DITHER ? kTile : 1];  // dithered variant: the tile's offsets, times kFactor^2
 
@@ -80,12 +88,18 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int l16 = lane % 16, g4 = lane / 16;
 
+  const float cs = OUT16 ? *a.cscale : kFactor;  // factor of the centroid operand
   for (int i = tid; i < kPairs; i += T) {
-    const float c0 = a.cent[i & ((1 << BITS) - 1)] * kFactor, c1 = a.cent[i >> BITS] * kFactor;
+    const float c0 = a.cent[i & ((1 << BITS) - 1)] * cs, c1 = a.cent[i >> BITS] * cs;
     const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
-    const _Float16 e0 = (_Float16)(c0 - (float)h0), e1 = (_Float16)(c1 - (float)h1);
-    tpair[i] = u2{hbits(h0) | (hbits(h1) << 16), hbits(e0) | (hbits(e1) << 16)};
+    if constexpr (OUT16) {
+      tpair[i] = hbits(h0) | (hbits(h1) << 16);
+    } else {
+      const _Float16 e0 = (_Float16)(c0 - (float)h0), e1 = (_Float16)(c1 - (float)h1);
+      tpair[i] = u2{hbits(h0) | (hbits(h1) << 16), hbits(e0) | (hbits(e1) << 16)};
+    }
   }
+  const float nscale = 1.f / (kFactor * cs);  // the operands' factors, undone with the norm
 
   // This wave's rows of 16 R^T: row j = 32 wave + 16 jb + l16, k = 32 kb + 8 g4 + e.
   h8 ahi[2][NKB], alo[2][NKB];
@@ -192,9 +206,13 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
     {
       uint32_t ph[16], pl[16];
       sfor<0, 16>([&](auto p) {
-        const u2 e = tpair[bits_at<2 * BITS * p, 2 * BITS>(w)];
-        ph[p] = e[0];
-        pl[p] = e[1];
+        const Pair e = tpair[bits_at<2 * BITS * p, 2 * BITS>(w)];
+        if constexpr (OUT16) {
+          ph[p] = e;
+        } else {
+          ph[p] = e[0];
+          pl[p] = e[1];
+        }
       });
       if constexpr (VALUES) {
         // Token i of the tile: pairs p = 4 kk + i / 2 (kk = 0..3), its half i % 2.
@@ -204,21 +222,24 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
           const uint32_t sel = i % 2 ? 0x07060302u : 0x05040100u;
           const int p0 = i / 2;
           const u2 vh = {__builtin_amdgcn_perm(ph[p0 + 4], ph[p0], sel), __builtin_amdgcn_perm(ph[p0 + 12], ph[p0 + 8], sel)};
-          const u2 vl = {__builtin_amdgcn_perm(pl[p0 + 4], pl[p0], sel), __builtin_amdgcn_perm(pl[p0 + 12], pl[p0 + 8], sel)};
           *reinterpret_cast<u2*>(&bhi[8 * vt + i][4 * q]) = vh;
-          *reinterpret_cast<u2*>(&blo[8 * vt + i][4 * q]) = vl;
+          if constexpr (!OUT16) {
+            const u2 vl = {__builtin_amdgcn_perm(pl[p0 + 4], pl[p0], sel), __builtin_amdgcn_perm(pl[p0 + 12], pl[p0 + 8], sel)};
+            *reinterpret_cast<u2*>(&blo[8 * vt + i][4 * q]) = vl;
+          }
         }
       } else {
         const int tt = tid / NKB, q = tid % NKB;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           *reinterpret_cast<u4*>(&bhi[tt][32 * q + 8 * c]) = u4{ph[4 * c], ph[4 * c + 1], ph[4 * c + 2], ph[4 * c + 3]};
-          *reinterpret_cast<u4*>(&blo[tt][32 * q + 8 * c]) = u4{pl[4 * c], pl[4 * c + 1], pl[4 * c + 2], pl[4 * c + 3]};
+          if constexpr (!OUT16)
+            *reinterpret_cast<u4*>(&blo[tt][32 * q + 8 * c]) = u4{pl[4 * c], pl[4 * c + 1], pl[4 * c + 2], pl[4 * c + 3]};
         }
       }
-      if (tid < kTile) nsh[tid] = nrm * (1.f / (kFactor * kFactor));
+      if (tid < kTile) nsh[tid] = nrm * nscale;
       if constexpr (DITHER) {
-        if (tid < kTile) dsh[tid] = dither_offset(a.dither_s0, seq, t0 + tid, dwidth) * (kFactor * kFactor);
+        if (tid < kTile) dsh[tid] = dither_offset(a.dither_s0, seq, t0 + tid, dwidth) * (kFactor * cs);
       }
     }
     lds_barrier();
@@ -234,12 +255,12 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         bh[kb] = *reinterpret_cast<const h8*>(&bhi[16 * s + l16][32 * kb + 8 * g4]);
-        bl[kb] = *reinterpret_cast<const h8*>(&blo[16 * s + l16][32 * kb + 8 * g4]);
+        if constexpr (!OUT16) bl[kb] = *reinterpret_cast<const h8*>(&blo[16 * s + l16][32 * kb + 8 * g4]);
       }
       const int tok = 16 * s + l16;
       const float nt = nsh[tok];
       const float dl = DITHER ? dsh[tok] : 0.f;
-      // Four independent accumulation chains (per row block: hi*hi, and the two
+      // Four independent accumulation chains (per row block: hi*hi, and the
       // correction products) so that no product waits on the one before it.
       f4 acc[2], cor[2];
 #pragma unroll
@@ -249,7 +270,7 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
           acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[jb][kb], bh[kb], acc[jb], 0, 0, 0);
-          cor[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[jb][kb], bl[kb], cor[jb], 0, 0, 0);
+          if constexpr (!OUT16) cor[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[jb][kb], bl[kb], cor[jb], 0, 0, 0);
         }
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)

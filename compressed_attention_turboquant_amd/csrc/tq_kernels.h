@@ -64,6 +64,7 @@ struct DequantArgs {
   int dither;  // dithered variant: offsets from the stream at dither_s0, width *dither_w
   uint64_t dither_s0;
   const float* dither_w;
+  const float* cscale;  // factor s of the codebook's fp16 copies (decode tables), for fp16 rows
 };
 
 // Arguments of the kernel that adds the QJL term n sqrt(pi/2)/d gamma S^T sigma

@@ -493,6 +493,15 @@ def _check_dequantize(cfg, which, n_out=None):
     assert err[~flipped].max() < 2e-6
     half = B.dequantize(layer, which, cache, n_out, out_dtype=torch.float16).cpu().numpy().reshape(-1, d)
     np.testing.assert_allclose(half[~flipped], got[~flipped], rtol=2e-3, atol=1e-3)
+    # fp16 rows against the oracle: half an ulp of the output (2^-11 relative,
+    # 2^-25 absolute below the normal range) plus what the arithmetic may add
+    # before that rounding -- at most 1.1e-4 of the norm (fp16 copies of the
+    # scaled centroids within 1e-4 relative, R^T split hi + lo) -- since
+    # sum_k |R_jk c_k| <= ||R_j|| ||c|| <= 1 for a unit reconstruction.
+    half64 = half.astype(np.float64)
+    tol = 2.0 ** -11 * np.abs(ref) + 1.1e-4 * scale + 2.0 ** -25
+    over = (np.abs(half64 - ref) - tol)[~flipped]
+    assert over.max() <= 0, f"fp16 rows: error above the bound by {over.max():.2e}"
     return err[~flipped].max()
 
 
