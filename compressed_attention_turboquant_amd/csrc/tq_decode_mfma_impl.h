@@ -59,6 +59,7 @@
 #include <type_traits>
 
 #include "tq_kernels.h"
+#include "tq_lanes.h"
 
 namespace tq {
 namespace {
@@ -140,23 +141,6 @@ __device__ __forceinline__ u4 decode8(const uint32_t (&w)[NW], const uint32_t* t
     });
   }
   return r;
-}
-
-// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 with the gfx950 row
-// swaps (v_permlane16_swap / v_permlane32_swap: plain VALU moves, no LDS round
-// trip).  With both operands equal, a swap leaves lane l's partner value in one
-// of the two results and its own in the other.
-__device__ __forceinline__ float max_over_row_groups(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum_over_row_groups(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint32_t half_bits(float x) {

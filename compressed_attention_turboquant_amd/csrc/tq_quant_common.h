@@ -59,20 +59,29 @@ constexpr float kBinScale = 8.f;
 constexpr int kBinCopies = 32;
 constexpr int kCodeTableEntries = kBins * kBinCopies;
 
+// Entry of bin `bin` for the 2^BITS - 1 sorted boundaries bnd (ubin =
+// sqrt(d) * kBinScale): the boundary inside the bin in bin units, or +inf, and
+// the count of boundaries below the bin.
+template <int BITS>
+__device__ __forceinline__ void bin_entry(const float* bnd, float ubin, int bin, float& inner, uint32_t& below) {
+  constexpr int L = 1 << BITS;
+  below = 0;
+  inner = INFINITY;
+  for (int i = 0; i + 1 < L; ++i) {
+    const float ub = fmaf(bnd[i], ubin, 0.5f * kBins);
+    if (ub < (float)bin) ++below;
+    else if (ub < (float)(bin + 1)) inner = ub;
+  }
+}
+
 // Fills the table (kCodeTableEntries entries) from the 2^BITS - 1 sorted
 // boundaries bnd; ubin = sqrt(d) * kBinScale.  Threads tid of nthreads share the work.
 template <int BITS>
 __device__ __forceinline__ void fill_code_table(uint2* tab, const float* bnd, float ubin, int tid, int nthreads) {
-  constexpr int L = 1 << BITS;
   for (int e = tid; e < kCodeTableEntries; e += nthreads) {
-    const int bin = e / kBinCopies;
-    uint32_t below = 0;
-    float inner = INFINITY;
-    for (int i = 0; i + 1 < L; ++i) {
-      const float ub = fmaf(bnd[i], ubin, 0.5f * kBins);
-      if (ub < (float)bin) ++below;
-      else if (ub < (float)(bin + 1)) inner = ub;
-    }
+    float inner;
+    uint32_t below;
+    bin_entry<BITS>(bnd, ubin, e / kBinCopies, inner, below);
     tab[e] = make_uint2(__float_as_uint(inner), below);
   }
 }
@@ -83,6 +92,31 @@ __device__ __forceinline__ uint32_t table_code(const uint2* lane_tab, float u) {
   const int bin = (int)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kBins - 1));
   const uint2 ent = lane_tab[bin * kBinCopies];
   return ent.y + (u > __uint_as_float(ent.x) ? 1u : 0u);
+}
+
+// The same table with each entry also holding the centroids of its two
+// possible codes, c[below] and c[below + 1], times cscale: a code's centroid is
+// then a select on the code's own compare (no second lookup).
+template <int BITS>
+__device__ __forceinline__ void fill_code_cent_table(uint4* tab, const float* bnd, const float* cent, float ubin,
+                                                     float cscale, int tid, int nthreads) {
+  constexpr uint32_t L = 1u << BITS;
+  for (int e = tid; e < kCodeTableEntries; e += nthreads) {
+    float inner;
+    uint32_t below;
+    bin_entry<BITS>(bnd, ubin, e / kBinCopies, inner, below);
+    const uint32_t above = below + 1 < L ? below + 1 : below;
+    tab[e] = make_uint4(__float_as_uint(inner), below, __float_as_uint(cent[below] * cscale),
+                        __float_as_uint(cent[above] * cscale));
+  }
+}
+
+__device__ __forceinline__ uint32_t table_code_cent(const uint4* lane_tab, float u, float& c) {
+  const int bin = (int)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kBins - 1));
+  const uint4 ent = lane_tab[bin * kBinCopies];
+  const bool up = u > __uint_as_float(ent.x);
+  c = __uint_as_float(up ? ent.w : ent.z);
+  return ent.y + (up ? 1u : 0u);
 }
 
 // Workgroup barrier that orders LDS only: global loads and stores stay in

@@ -31,6 +31,7 @@
 #include <type_traits>
 
 #include "tq_kernels.h"
+#include "tq_lanes.h"
 #include "tq_quant_common.h"
 
 namespace tq {
@@ -38,6 +39,16 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Raw buffer records: an access that must not happen gets an offset past the
+// record (a load returns 0, a store is dropped) instead of a branch.
+constexpr uint32_t kOob = 0x80000000u;  // past every record used here
+__device__ __forceinline__ Rsrc record(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
 
 constexpr int D = 128;
 constexpr int kWaves = 4;
@@ -46,6 +57,18 @@ constexpr int kSlots = 32;  // tokens per tile: 4 value tiles of 8
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// The fp16 pair {a - hi.x, b - hi.y} for hi = {fp16(a), fp16(b)}: the lo
+// halves of the two values' hi + lo split, one mixed-precision FMA each
+// (a * 1.0 - hi.x in fp32, rounded to fp16 into the low or high half).
+__device__ __forceinline__ uint32_t split_lo(float a, float b, uint32_t hi) {
+  uint32_t lo;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(lo)
+      : "v"(a), "v"(b), "v"(hi));
+  return lo;
 }
 
 // Output coordinate held by weight row rho (0..15) of coordinate tile ct in
@@ -59,15 +82,17 @@ __device__ __forceinline__ int out_coord(int w, int ct, int rho) {
 template <int BITS, int QJL, int VALUES>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(VALUES ? 3 : 2)))
 quantize_mfma_kernel(QuantMfmaParams p) {
-  __shared__ __align__(16) _Float16 xs[kSlots][D + 8];       // token rows (padded)
-  __shared__ __align__(16) _Float16 rs[2][kSlots][D + 8];    // residual hi / lo
+  constexpr bool kTable = BITS >= 3;             // 3- and 4-bit codes from the binned table
+  constexpr bool kCentTable = kTable && QJL;     // its entries also carry the centroids
+  __shared__ __align__(16) _Float16 xs[kSlots][D + 8];                                  // token rows (padded)
+  __shared__ __align__(16) _Float16 rs[QJL ? 2 : 1][QJL ? kSlots : 1][D + 8];           // residual hi / lo
   __shared__ float nrm[kSlots];
-  __shared__ float rsq[kSlots][16];
-  constexpr bool kTable = BITS >= 3;  // 3- and 4-bit codes from the binned table
-  __shared__ __align__(16) uint2 ctabl[kTable ? kCodeTableEntries : 1];
+  __shared__ __align__(16) float rsq[kSlots][kWaves];                                   // per-wave sums of r^2
+  __shared__ __align__(16) uint2 ctabl[kTable && !kCentTable ? kCodeTableEntries : 1];
+  __shared__ __align__(16) uint4 ctabc[kCentTable ? kCodeTableEntries : 1];
 
   const int tid = threadIdx.x;
-  const int w = tid / 64, lane = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int l16 = lane % 16, g4 = lane / 16;
 
   // Stationary weights: rows out_coord(w, ct, l16), columns 32 kb + 8 g4 + e.
@@ -86,57 +111,74 @@ quantize_mfma_kernel(QuantMfmaParams p) {
       }
     }
   }
-  // Positive half of the symmetric boundaries, and the centroids as a register
-  // table (lane i holds c[i mod 16]) read with ds_bpermute.
+  // The residual is formed as kRes (y - c): kRes keeps the lo half of its fp16
+  // split away from subnormals; the residual norm is divided by it once.
+  constexpr float kRes = 64.f;
+  // Positive half of the symmetric boundaries, and the centroids (times kRes
+  // for keys with QJL) as a register table (lane i holds c[i mod 16]) read with
+  // ds_bpermute (1- and 2-bit codes).
   constexpr int KP = BITS > 1 ? (1 << (BITS - 1)) - 1 : 1;
   float beta[KP];
 #pragma unroll
   for (int i = 0; i < KP; ++i) beta[i] = BITS > 1 ? p.bnd[(1 << (BITS - 1)) + i] : 0.f;
-  const int ctab = __float_as_int(p.cent[lane % 16]);
+  const int ctab = __float_as_int(p.cent[lane % 16] * (QJL ? kRes : 1.f));
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   const float ubin = sqrtf((float)D) * kBinScale;  // unit-vector coordinate -> bin units
-  if constexpr (kTable) {
-    fill_code_table<BITS>(ctabl, p.bnd, ubin, tid, kThreads);
-    __syncthreads();
-  }
-  const uint2* ctab_lane = ctabl + (kTable ? lane % kBinCopies : 0);
+  if constexpr (kCentTable) fill_code_cent_table<BITS>(ctabc, p.bnd, p.cent, ubin, kRes, tid, kThreads);
+  else if constexpr (kTable) fill_code_table<BITS>(ctabl, p.bnd, ubin, tid, kThreads);
+  const uint2* ctab_lane = ctabl + (kTable && !kCentTable ? lane % kBinCopies : 0);
+  const uint4* ctabc_lane = ctabc + (kCentTable ? lane % kBinCopies : 0);
 
   // Work unit: 4 consecutive value tiles (32 token slots) of one sequence.
+  // Group g is (sequence g / gps, group g % gps of it); the grid strides by
+  // gridDim.x groups, i.e. by a fixed quotient and remainder, so the pair
+  // advances with one carry instead of a 64-bit division per group.
   const int tiles = (int)(p.tile_last - p.tile_first + 1);  // tiles per sequence touched
   const int gps = (tiles + 3) / 4;                             // groups per sequence
   const int groups = (int)p.seqs * gps;  // < 2^31 (checked on the host)
+  const int step_q = (int)gridDim.x / gps, step_r = (int)gridDim.x % gps;
   const int t0 = (int)p.t0, tend = (int)(p.t0 + p.n);
+  const int tfirst = (int)p.tile_first * 8;
   const int rowb = D * BITS / 8;
-
-  // Loader role: 8 threads per token slot, 16 halves each.
-  const int lslot = tid / 8, lpart = tid % 8;
-  auto load_x = [&](int grp, h8& v0, h8& v1) {
-    v0 = h8{0, 0, 0, 0, 0, 0, 0, 0};
-    v1 = v0;
-    if (grp >= groups) return;
-    const int64_t s = grp / gps;  // uniform
-    const int tile = (int)p.tile_first + 4 * (grp % gps) + lslot / 8;
-    const int t = tile * 8 + lslot % 8;
-    if (4 * (grp % gps) + lslot / 8 < tiles && t >= t0 && t < tend) {
-      const _Float16* src = p.x + s * p.n * D + (t - t0) * D + lpart * 16;
-      v0 = *reinterpret_cast<const h8*>(src);
-      v1 = *reinterpret_cast<const h8*>(src + 8);
+  auto advance = [&](int& s_, int& g_) {
+    s_ += step_q;
+    g_ += step_r;
+    if (g_ >= gps) {
+      g_ -= gps;
+      ++s_;
     }
   };
-  h8 nx0, nx1;
-  load_x((int)blockIdx.x, nx0, nx1);
 
-  for (int grp = blockIdx.x; grp < groups; grp += gridDim.x) {
-    const int64_t s = grp / gps;  // wave-uniform: scalar
-    const int gt = 4 * (grp % gps);  // first tile of the group, relative to tile_first
+  // Loader role: 8 threads per token slot, 16 halves each.  The group's rows
+  // load through a record starting at its first token slot; slots outside
+  // [t0, t0 + n) (and every slot of a group past the end) get an offset past
+  // the record, so the loads return 0 without a branch.
+  const int lslot = tid / 8, lpart = tid % 8;
+  auto load_x = [&](int gs, int gg, bool live, h8& v0, h8& v1) {
+    const int tb = tfirst + 32 * gg;  // first token slot of the group
+    const int t = tb + lslot;
+    const Rsrc rec = record(p.x + ((int64_t)gs * p.n + (tb - t0)) * D, kSlots * D * 2);
+    const uint32_t off = live && t >= t0 && t < tend ? (uint32_t)(lslot * D * 2 + lpart * 32) : kOob;
+    v0 = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rec, off, 0, 0));
+    v1 = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rec, off + 16, 0, 0));
+  };
+  int grp = (int)blockIdx.x;
+  int cs = grp / gps, cg = grp % gps;  // sequence and group within it
+  h8 nx0, nx1;
+  load_x(cs, cg, grp < groups, nx0, nx1);
+  __syncthreads();  // the code table is filled
+
+  for (; grp < groups; grp += gridDim.x) {
+    int ns = cs, ng = cg;
+    advance(ns, ng);
+    const int tb = tfirst + 32 * cg;  // first token slot of the group
     // ---- token rows into LDS, with their norms; prefetch the next group ----
     {
       const h8 v0 = nx0, v1 = nx1;
       *reinterpret_cast<h8*>(&xs[lslot][lpart * 16]) = v0;
       *reinterpret_cast<h8*>(&xs[lslot][lpart * 16 + 8]) = v1;
       // Sum of squares: fp16 products are exact in fp32; two independent
-      // chains of packed dot products.
-      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      // chains of packed dot products, then the slot's 8 lanes.
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -144,14 +186,11 @@ quantize_mfma_kernel(QuantMfmaParams p) {
         s0 = __builtin_amdgcn_fdot2(a, a, s0, false);
         s1 = __builtin_amdgcn_fdot2(b, b, s1, false);
       }
-      float ss = s0 + s1;
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      ss += __shfl_xor(ss, 4);
+      const float ss = sum_over_8_lanes(s0 + s1);
       if (lpart == 0) nrm[lslot] = __builtin_amdgcn_sqrtf(ss);
-      load_x(grp + (int)gridDim.x, nx0, nx1);
+      load_x(ns, ng, grp + (int)gridDim.x < groups, nx0, nx1);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- rotation: acc[ct][tt] ----
     f4 acc[2][2];
@@ -196,15 +235,23 @@ quantize_mfma_kernel(QuantMfmaParams p) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
     if constexpr (!VALUES) {
-      uint8_t* idx_s = p.idx + s * p.cap * rowb;
-      // Lane (g4, l16) holds coordinates 32w + 8g4 + 4ct + r of token slot 16tt + l16.
+      // Lane (g4, l16) holds coordinates 32w + 8g4 + 4ct + r of token slot
+      // 16tt + l16.  Stores go through records from the group's first token
+      // slot on; slots outside [t0, t0 + n) get an offset past the record.
+      const int64_t row0 = (int64_t)cs * p.cap + tb;
+      const Rsrc irec = record(p.idx + row0 * rowb, kSlots * rowb);
+      const Rsrc nrec = record(p.norm + row0, kSlots * 4);
+      uint32_t ioff[2];
+      bool okv[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int slot = 16 * tt + l16;
-        const int t = ((int)p.tile_first + gt + slot / 8) * 8 + slot % 8;
-        const bool ok = gt + slot / 8 < tiles && t >= t0 && t < tend;
+        const int t = tb + slot;
+        okv[tt] = t >= t0 && t < tend;
+        ioff[tt] = okv[tt] ? (uint32_t)(slot * rowb + (4 * w + g4) * BITS) : kOob;
         const float nn = nrm[slot];
         const float inv = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
+        const float inv_r = inv * kRes;
         uint32_t packed = 0;
         float r[8];
         float rr = 0.f;
@@ -212,36 +259,51 @@ quantize_mfma_kernel(QuantMfmaParams p) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float y = acc[ct][tt][q] * inv;
+            const float a = acc[ct][tt][q];
             uint32_t code;
-            if constexpr (kTable) code = table_code(ctab_lane, fmaf(acc[ct][tt][q], inv * ubin, 0.5f * kBins));
-            else code = symmetric_code<BITS>(y, beta);
-            const float c = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(code << 2), ctab));
+            float c = 0.f;
+            if constexpr (kCentTable) {
+              code = table_code_cent(ctabc_lane, fmaf(a, inv * ubin, 0.5f * kBins), c);
+            } else {
+              if constexpr (kTable) code = table_code(ctab_lane, fmaf(a, inv * ubin, 0.5f * kBins));
+              else code = symmetric_code<BITS>(a * inv, beta);
+              if constexpr (QJL) c = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(code << 2), ctab));
+            }
             packed |= code << (BITS * (4 * ct + q));
-            r[4 * ct + q] = y - c;
-            rr = fmaf(r[4 * ct + q], r[4 * ct + q], rr);
+            if constexpr (QJL) {
+              r[4 * ct + q] = fmaf(a, inv_r, -c);  // kRes (y - c)
+              rr = fmaf(r[4 * ct + q], r[4 * ct + q], rr);
+            }
           }
-        if (ok) {
-          uint8_t* dst = idx_s + t * rowb + (4 * w + g4) * BITS;
-#pragma unroll
-          for (int b = 0; b < BITS; ++b) dst[b] = (uint8_t)(packed >> (8 * b));
-          if (w == 0 && g4 == 0) p.norm[s * p.cap + t] = nn;
+        if constexpr (BITS == 4) {
+          __builtin_amdgcn_raw_buffer_store_b32(packed, irec, ioff[tt], 0, 0);
+        } else if constexpr (BITS == 3) {
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed, irec, ioff[tt], 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(packed >> 16), irec, ioff[tt] + 2, 0, 0);
+        } else if constexpr (BITS == 2) {
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed, irec, ioff[tt], 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)packed, irec, ioff[tt], 0, 0);
         }
+        if (w == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nn), nrec,
+                                                g4 == 0 && okv[tt] ? (uint32_t)(slot * 4) : kOob, 0, 0);
         if constexpr (QJL) {
-          h8 hi, lo;
+          u4 hi, lo;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = r[e] * 64.f;  // keep the lo half away from fp16 subnormals
-            hi[e] = (_Float16)v;
-            lo[e] = (_Float16)(v - (float)hi[e]);
+          for (int j = 0; j < 4; ++j) {
+            const h2 hv{(_Float16)r[2 * j], (_Float16)r[2 * j + 1]};
+            hi[j] = __builtin_bit_cast(uint32_t, hv);
+            lo[j] = split_lo(r[2 * j], r[2 * j + 1], hi[j]);
           }
-          *reinterpret_cast<h8*>(&rs[0][slot][32 * w + 8 * g4]) = hi;
-          *reinterpret_cast<h8*>(&rs[1][slot][32 * w + 8 * g4]) = lo;
-          rsq[slot][4 * w + g4] = rr;
+          *reinterpret_cast<u4*>(&rs[0][slot][32 * w + 8 * g4]) = hi;
+          *reinterpret_cast<u4*>(&rs[1][slot][32 * w + 8 * g4]) = lo;
+          rr = sum_over_row_groups(rr);  // the wave's 32 coordinates of the slot
+          if (g4 == 0) rsq[slot][w] = rr;
         }
       }
       if constexpr (QJL) {
-        __syncthreads();
+        lds_barrier();
         f4 pacc[2][2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
@@ -274,35 +336,33 @@ quantize_mfma_kernel(QuantMfmaParams p) {
           if (st < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-        uint8_t* sign_s = p.sign + s * p.cap * (D / 8);
-        float* rn_s = p.rnorm + s * p.cap;
+        const Rsrc srec = record(p.sign + row0 * (D / 8), kSlots * (D / 8));
+        const Rsrc grec = record(p.rnorm + row0, kSlots * 4);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int slot = 16 * tt + l16;
-          const int t = ((int)p.tile_first + gt + slot / 8) * 8 + slot % 8;
-          const bool ok = gt + slot / 8 < tiles && t >= t0 && t < tend;
+          // Bit 4ct + q is 1 for a projection >= +0: shift the float sign bits
+          // in from the highest bit down (one funnel shift each), then invert.
           uint32_t bits = 0;
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)  // sign bit of the float, inverted: 1 for >= +0
-              bits |= ((__float_as_uint(pacc[ct][tt][q]) >> 31) ^ 1u) << (4 * ct + q);
-          if (ok) {
-            sign_s[t * (D / 8) + 4 * w + g4] = (uint8_t)bits;
-            if (w == 0 && g4 == 0) {
-              float g = 0.f;
-#pragma unroll
-              for (int i = 0; i < 16; ++i) g += rsq[slot][i];
-              rn_s[t] = __builtin_amdgcn_sqrtf(g);
-            }
+          for (int e = 7; e >= 0; --e)
+            bits = __builtin_amdgcn_alignbit(bits, __float_as_uint(pacc[e / 4][tt][e % 4]), 31);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)~bits, srec,
+                                               okv[tt] ? (uint32_t)(slot * (D / 8) + 4 * w + g4) : kOob, 0, 0);
+          if (w == 0) {
+            const f4 g = *reinterpret_cast<const f4*>(&rsq[slot][0]);
+            const float gamma = __builtin_amdgcn_sqrtf((g[0] + g[1]) + (g[2] + g[3])) * (1.f / kRes);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gamma), grec,
+                                                  g4 == 0 && okv[tt] ? (uint32_t)(slot * 4) : kOob, 0, 0);
           }
         }
       }
     } else {
       // Lane (g4, l16) holds, for coordinate tile ct, coordinate out_coord(w, ct, l16)
       // of the 8 tokens of value tile g4 (token 4 tt + r in D row 4 g4 + r of tile tt).
-      const bool tile_ok = gt + g4 < tiles;
-      const int tile = (int)p.tile_first + gt + g4;
+      const int s = cs;
+      const bool tile_ok = 4 * cg + g4 < tiles;
+      const int tile = (int)p.tile_first + 4 * cg + g4;
       uint32_t keep = 0;  // code bits of tokens outside [t0, t0+n) are left unchanged
       float inv[8];
 #pragma unroll
@@ -316,9 +376,9 @@ quantize_mfma_kernel(QuantMfmaParams p) {
       // Norms: lane l16 < 8 of wave 0 stores token l16 of value tile g4.
       if (w == 0 && l16 < 8 && tile_ok) {
         const int t = tile * 8 + l16;
-        if (t >= t0 && t < tend) p.norm[s * p.cap + t] = nrm[8 * g4 + l16];
+        if (t >= t0 && t < tend) p.norm[(int64_t)s * p.cap + t] = nrm[8 * g4 + l16];
       }
-      uint8_t* tile_base = p.idx + s * (p.cap / 8) * (D * BITS) + tile * (D * BITS);
+      uint8_t* tile_base = p.idx + (int64_t)s * (p.cap / 8) * (D * BITS) + (int64_t)tile * (D * BITS);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         uint32_t packed = 0;
@@ -345,7 +405,9 @@ quantize_mfma_kernel(QuantMfmaParams p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
+    cs = ns;
+    cg = ng;
   }
 }
 
