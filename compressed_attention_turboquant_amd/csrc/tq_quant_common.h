@@ -97,23 +97,25 @@ __device__ __forceinline__ uint32_t table_code(const uint2* lane_tab, float u) {
 // The same table with each entry also holding the centroids of its two
 // possible codes, c[below] and c[below + 1], times cscale: a code's centroid is
 // then a select on the code's own compare (no second lookup).
-template <int BITS>
+// COPIES copies of each bin's entry (kBins * COPIES entries).
+template <int BITS, int COPIES>
 __device__ __forceinline__ void fill_code_cent_table(uint4* tab, const float* bnd, const float* cent, float ubin,
                                                      float cscale, int tid, int nthreads) {
   constexpr uint32_t L = 1u << BITS;
-  for (int e = tid; e < kCodeTableEntries; e += nthreads) {
+  for (int e = tid; e < kBins * COPIES; e += nthreads) {
     float inner;
     uint32_t below;
-    bin_entry<BITS>(bnd, ubin, e / kBinCopies, inner, below);
+    bin_entry<BITS>(bnd, ubin, e / COPIES, inner, below);
     const uint32_t above = below + 1 < L ? below + 1 : below;
     tab[e] = make_uint4(__float_as_uint(inner), below, __float_as_uint(cent[below] * cscale),
                         __float_as_uint(cent[above] * cscale));
   }
 }
 
+template <int COPIES>
 __device__ __forceinline__ uint32_t table_code_cent(const uint4* lane_tab, float u, float& c) {
   const int bin = (int)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kBins - 1));
-  const uint4 ent = lane_tab[bin * kBinCopies];
+  const uint4 ent = lane_tab[bin * COPIES];
   const bool up = u > __uint_as_float(ent.x);
   c = __uint_as_float(up ? ent.w : ent.z);
   return ent.y + (up ? 1u : 0u);

@@ -12,10 +12,13 @@
 //    on v_mfma_f32_16x16x32_f16.  fp16 inputs are exact; the weights sqrt(d) R
 //    and S R^T are split into fp16 hi + lo (2 passes, ~2^-22 relative); the fp32
 //    residual is split too (3 passes: hi*hi, hi*lo, lo*hi).
-//  * Weights are stationary: wave w of a workgroup keeps the rows of 32 output
-//    coordinates in VGPRs for the whole kernel; tokens stream through LDS in
-//    tiles of 4 x 8 tokens (one 8-token value tile each), the workgroup looping
-//    over tiles (persistent grid).
+//  * Weights are stationary: each wave keeps the rows of 32 output coordinates
+//    of its matrix in VGPRs for the whole kernel; tokens stream through LDS in
+//    groups of 4 x 8 tokens (one 8-token value tile each), the workgroup
+//    looping over groups (persistent grid).
+//  * Keys with QJL split the work by role (quantize_keys_qjl_kernel): four
+//    waves rotate and quantize, four project the residual, so that one SIMD
+//    runs one role's vector work beside the other's matrix-core work.
 //  * Operand roles are chosen per tensor so that each lane ends with exactly
 //    what it stores: keys (row-major streams) use D = W * X^T, a lane holding 8
 //    consecutive coordinates of a token; values (8-token coordinate-major
@@ -54,6 +57,11 @@ constexpr int D = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSlots = 32;  // tokens per tile: 4 value tiles of 8
+// The role-split key kernel runs 4 waves per SIMD (two workgroups of 8 waves
+// per CU: 128 VGPRs, 16 copies of the code table so that both fit in LDS).
+// Same-run timings of the C3 keys: 3.06 ms at 2 waves per SIMD, 2.76 ms at 4.
+constexpr int kKeyWaves = 4;
+constexpr int kKeyCopies = 16;
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -77,26 +85,36 @@ __device__ __forceinline__ int out_coord(int w, int ct, int rho) {
   return 32 * w + 8 * (rho / 4) + 4 * ct + (rho % 4);
 }
 
-// Two waves per SIMD for keys (the stationary weights of the rotation and the
-// projection take half the registers), three for values.
-template <int BITS, int QJL, int VALUES>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(VALUES ? 3 : 2)))
+// BITS code bits of 8 coordinates (BITS bytes) at byte offset off of r.
+template <int BITS>
+__device__ __forceinline__ void store_code_bits(uint32_t packed, Rsrc r, uint32_t off) {
+  if constexpr (BITS == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(packed, r, off, 0, 0);
+  } else if constexpr (BITS == 3) {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(packed >> 16), r, off + 2, 0, 0);
+  } else if constexpr (BITS == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed, r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)packed, r, off, 0, 0);
+  }
+}
+
+// Values, and keys without QJL: the rotation and the scalar quantizer.
+template <int BITS, int VALUES>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 quantize_mfma_kernel(QuantMfmaParams p) {
-  constexpr bool kTable = BITS >= 3;             // 3- and 4-bit codes from the binned table
-  constexpr bool kCentTable = kTable && QJL;     // its entries also carry the centroids
-  __shared__ __align__(16) _Float16 xs[kSlots][D + 8];                                  // token rows (padded)
-  __shared__ __align__(16) _Float16 rs[QJL ? 2 : 1][QJL ? kSlots : 1][D + 8];           // residual hi / lo
+  constexpr bool kTable = BITS >= 3;  // 3- and 4-bit codes from the binned table
+  __shared__ __align__(16) _Float16 xs[kSlots][D + 8];  // token rows (padded)
   __shared__ float nrm[kSlots];
-  __shared__ __align__(16) float rsq[kSlots][kWaves];                                   // per-wave sums of r^2
-  __shared__ __align__(16) uint2 ctabl[kTable && !kCentTable ? kCodeTableEntries : 1];
-  __shared__ __align__(16) uint4 ctabc[kCentTable ? kCodeTableEntries : 1];
+  __shared__ __align__(16) uint2 ctabl[kTable ? kCodeTableEntries : 1];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int l16 = lane % 16, g4 = lane / 16;
 
   // Stationary weights: rows out_coord(w, ct, l16), columns 32 kb + 8 g4 + e.
-  h8 wr[2][4][2], wp[QJL ? 2 : 1][4][2];
+  h8 wr[2][4][2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int row = out_coord(w, ct, l16);
@@ -105,29 +123,17 @@ quantize_mfma_kernel(QuantMfmaParams p) {
       const int col = 32 * kb + 8 * g4;
       wr[ct][kb][0] = *reinterpret_cast<const h8*>(p.rot_hi + row * D + col);
       wr[ct][kb][1] = *reinterpret_cast<const h8*>(p.rot_lo + row * D + col);
-      if constexpr (QJL) {
-        wp[ct][kb][0] = *reinterpret_cast<const h8*>(p.projr_hi + row * D + col);
-        wp[ct][kb][1] = *reinterpret_cast<const h8*>(p.projr_lo + row * D + col);
-      }
     }
   }
-  // The residual is formed as kRes (y - c): kRes keeps the lo half of its fp16
-  // split away from subnormals; the residual norm is divided by it once.
-  constexpr float kRes = 64.f;
-  // Positive half of the symmetric boundaries, and the centroids (times kRes
-  // for keys with QJL) as a register table (lane i holds c[i mod 16]) read with
-  // ds_bpermute (1- and 2-bit codes).
+  // Positive half of the symmetric boundaries (1- and 2-bit codes).
   constexpr int KP = BITS > 1 ? (1 << (BITS - 1)) - 1 : 1;
   float beta[KP];
 #pragma unroll
   for (int i = 0; i < KP; ++i) beta[i] = BITS > 1 ? p.bnd[(1 << (BITS - 1)) + i] : 0.f;
-  const int ctab = __float_as_int(p.cent[lane % 16] * (QJL ? kRes : 1.f));
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   const float ubin = sqrtf((float)D) * kBinScale;  // unit-vector coordinate -> bin units
-  if constexpr (kCentTable) fill_code_cent_table<BITS>(ctabc, p.bnd, p.cent, ubin, kRes, tid, kThreads);
-  else if constexpr (kTable) fill_code_table<BITS>(ctabl, p.bnd, ubin, tid, kThreads);
-  const uint2* ctab_lane = ctabl + (kTable && !kCentTable ? lane % kBinCopies : 0);
-  const uint4* ctabc_lane = ctabc + (kCentTable ? lane % kBinCopies : 0);
+  if constexpr (kTable) fill_code_table<BITS>(ctabl, p.bnd, ubin, tid, kThreads);
+  const uint2* ctab_lane = ctabl + (kTable ? lane % kBinCopies : 0);
 
   // Work unit: 4 consecutive value tiles (32 token slots) of one sequence.
   // Group g is (sequence g / gps, group g % gps of it); the grid strides by
@@ -241,121 +247,29 @@ quantize_mfma_kernel(QuantMfmaParams p) {
       const int64_t row0 = (int64_t)cs * p.cap + tb;
       const Rsrc irec = record(p.idx + row0 * rowb, kSlots * rowb);
       const Rsrc nrec = record(p.norm + row0, kSlots * 4);
-      uint32_t ioff[2];
-      bool okv[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int slot = 16 * tt + l16;
         const int t = tb + slot;
-        okv[tt] = t >= t0 && t < tend;
-        ioff[tt] = okv[tt] ? (uint32_t)(slot * rowb + (4 * w + g4) * BITS) : kOob;
+        const bool ok = t >= t0 && t < tend;
+        const uint32_t ioff = ok ? (uint32_t)(slot * rowb + (4 * w + g4) * BITS) : kOob;
         const float nn = nrm[slot];
         const float inv = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
-        const float inv_r = inv * kRes;
         uint32_t packed = 0;
-        float r[8];
-        float rr = 0.f;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float a = acc[ct][tt][q];
             uint32_t code;
-            float c = 0.f;
-            if constexpr (kCentTable) {
-              code = table_code_cent(ctabc_lane, fmaf(a, inv * ubin, 0.5f * kBins), c);
-            } else {
-              if constexpr (kTable) code = table_code(ctab_lane, fmaf(a, inv * ubin, 0.5f * kBins));
-              else code = symmetric_code<BITS>(a * inv, beta);
-              if constexpr (QJL) c = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(code << 2), ctab));
-            }
+            if constexpr (kTable) code = table_code(ctab_lane, fmaf(a, inv * ubin, 0.5f * kBins));
+            else code = symmetric_code<BITS>(a * inv, beta);
             packed |= code << (BITS * (4 * ct + q));
-            if constexpr (QJL) {
-              r[4 * ct + q] = fmaf(a, inv_r, -c);  // kRes (y - c)
-              rr = fmaf(r[4 * ct + q], r[4 * ct + q], rr);
-            }
           }
-        if constexpr (BITS == 4) {
-          __builtin_amdgcn_raw_buffer_store_b32(packed, irec, ioff[tt], 0, 0);
-        } else if constexpr (BITS == 3) {
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed, irec, ioff[tt], 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(packed >> 16), irec, ioff[tt] + 2, 0, 0);
-        } else if constexpr (BITS == 2) {
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed, irec, ioff[tt], 0, 0);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)packed, irec, ioff[tt], 0, 0);
-        }
+        store_code_bits<BITS>(packed, irec, ioff);
         if (w == 0)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nn), nrec,
-                                                g4 == 0 && okv[tt] ? (uint32_t)(slot * 4) : kOob, 0, 0);
-        if constexpr (QJL) {
-          u4 hi, lo;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const h2 hv{(_Float16)r[2 * j], (_Float16)r[2 * j + 1]};
-            hi[j] = __builtin_bit_cast(uint32_t, hv);
-            lo[j] = split_lo(r[2 * j], r[2 * j + 1], hi[j]);
-          }
-          *reinterpret_cast<u4*>(&rs[0][slot][32 * w + 8 * g4]) = hi;
-          *reinterpret_cast<u4*>(&rs[1][slot][32 * w + 8 * g4]) = lo;
-          rr = sum_over_row_groups(rr);  // the wave's 32 coordinates of the slot
-          if (g4 == 0) rsq[slot][w] = rr;
-        }
-      }
-      if constexpr (QJL) {
-        lds_barrier();
-        f4 pacc[2][2];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) pacc[ct][tt] = f4{0.f, 0.f, 0.f, 0.f};
-        // Same one-step-ahead operand reads as the rotation.
-        auto r_operand = [&](int st, int part) {
-          const int kb = st / 2, tt = st % 2;
-          return *reinterpret_cast<const h8*>(&rs[part][16 * tt + l16][32 * kb + 8 * g4]);
-        };
-        h8 rh = r_operand(0, 0), rl = r_operand(0, 1);
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const int kb = st / 2, tt = st % 2;
-          const h8 nh = st < 7 ? r_operand(st + 1, 0) : rh;
-          const h8 nl = st < 7 ? r_operand(st + 1, 1) : rl;
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            pacc[ct][tt] = mfma(wp[ct][kb][0], rh, pacc[ct][tt]);
-            pacc[ct][tt] = mfma(wp[ct][kb][0], rl, pacc[ct][tt]);
-            pacc[ct][tt] = mfma(wp[ct][kb][1], rh, pacc[ct][tt]);
-          }
-          rh = nh;
-          rl = nl;
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int st = 0; st < 7; ++st) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-          if (st < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-        const Rsrc srec = record(p.sign + row0 * (D / 8), kSlots * (D / 8));
-        const Rsrc grec = record(p.rnorm + row0, kSlots * 4);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int slot = 16 * tt + l16;
-          // Bit 4ct + q is 1 for a projection >= +0: shift the float sign bits
-          // in from the highest bit down (one funnel shift each), then invert.
-          uint32_t bits = 0;
-#pragma unroll
-          for (int e = 7; e >= 0; --e)
-            bits = __builtin_amdgcn_alignbit(bits, __float_as_uint(pacc[e / 4][tt][e % 4]), 31);
-          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)~bits, srec,
-                                               okv[tt] ? (uint32_t)(slot * (D / 8) + 4 * w + g4) : kOob, 0, 0);
-          if (w == 0) {
-            const f4 g = *reinterpret_cast<const f4*>(&rsq[slot][0]);
-            const float gamma = __builtin_amdgcn_sqrtf((g[0] + g[1]) + (g[2] + g[3])) * (1.f / kRes);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gamma), grec,
-                                                  g4 == 0 && okv[tt] ? (uint32_t)(slot * 4) : kOob, 0, 0);
-          }
-        }
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nn), nrec, g4 == 0 && ok ? (uint32_t)(slot * 4) : kOob,
+                                                0, 0);
       }
     } else {
       // Lane (g4, l16) holds, for coordinate tile ct, coordinate out_coord(w, ct, l16)
@@ -411,22 +325,308 @@ quantize_mfma_kernel(QuantMfmaParams p) {
   }
 }
 
+// Keys with QJL, split by role.  Each SIMD holds one wave of each role:
+//  * rotation waves (0-3): the rotation of group k from LDS, the scalar
+//    quantizer, codes and norms to memory, the residual (hi + lo) and its
+//    squared norm to LDS;
+//  * projection waves (4-7): the projection of group k - 1's residual, its sign
+//    bits and residual norm to memory, and the rows of group k + 1 into LDS
+//    with their norms (loaded one iteration ahead).
+// One SIMD then runs one wave's vector work beside the other's matrix-core
+// work (a single wave issues vector instructions well below the SIMD's rate,
+// and the two units only overlap across waves).  Rows, residuals and norms
+// are double-buffered by group parity, so one barrier per group orders them.
+template <int BITS>
+__global__ void __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(kKeyWaves, kKeyWaves)))
+quantize_keys_qjl_kernel(QuantMfmaParams p) {
+  constexpr bool kTable = BITS >= 3;
+  constexpr int kCopies = kKeyCopies;
+  __shared__ __align__(16) _Float16 xs[2][kSlots][D + 8];     // token rows (padded)
+  __shared__ __align__(16) _Float16 rs[2][2][kSlots][D + 8];  // [buffer][hi, lo] residual
+  __shared__ float nrm[2][kSlots];
+  __shared__ __align__(16) float rsq[2][kSlots][kWaves];      // per-wave sums of r^2
+  __shared__ __align__(16) uint4 ctabc[kTable ? kBins * kCopies : 1];
+
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int w = wv % kWaves;  // the wave's output coordinates: 32w .. 32w + 31
+  const int lane = tid % 64;
+  const int l16 = lane % 16, g4 = lane / 16;
+  constexpr float kRes = 64.f;  // the residual is formed as kRes (y - c)
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  const float ubin = sqrtf((float)D) * kBinScale;
+  if constexpr (kTable) fill_code_cent_table<BITS, kCopies>(ctabc, p.bnd, p.cent, ubin, kRes, tid, 2 * kThreads);
+
+  const int tiles = (int)(p.tile_last - p.tile_first + 1);
+  const int gps = (tiles + 3) / 4;
+  const int groups = (int)p.seqs * gps;  // < 2^31 (checked on the host)
+  const int step_q = (int)gridDim.x / gps, step_r = (int)gridDim.x % gps;
+  const int t0 = (int)p.t0, tend = (int)(p.t0 + p.n);
+  const int tfirst = (int)p.tile_first * 8;
+  const int rowb = D * BITS / 8;
+  auto advance = [&](int& s_, int& g_) {
+    s_ += step_q;
+    g_ += step_r;
+    if (g_ >= gps) {
+      g_ -= gps;
+      ++s_;
+    }
+  };
+  // Groups of this workgroup: blockIdx.x + k gridDim.x for k < nk.
+  const int nk = (int)(((int64_t)groups - blockIdx.x + gridDim.x - 1) / gridDim.x);
+  const int s0 = (int)blockIdx.x / gps, g0 = (int)blockIdx.x % gps;
+
+  if (wv < kWaves) {
+    // ---------------- rotation waves ----------------
+    h8 wr[2][4][2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int row = out_coord(w, ct, l16);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int col = 32 * kb + 8 * g4;
+        wr[ct][kb][0] = *reinterpret_cast<const h8*>(p.rot_hi + row * D + col);
+        wr[ct][kb][1] = *reinterpret_cast<const h8*>(p.rot_lo + row * D + col);
+      }
+    }
+    constexpr int KP = BITS > 1 ? (1 << (BITS - 1)) - 1 : 1;
+    float beta[KP];
+#pragma unroll
+    for (int i = 0; i < KP; ++i) beta[i] = BITS > 1 ? p.bnd[(1 << (BITS - 1)) + i] : 0.f;
+    const int ctab = __float_as_int(p.cent[lane % 16] * kRes);  // 1- and 2-bit centroids (ds_bpermute)
+    const uint4* ctabc_lane = ctabc + (kTable ? lane % kCopies : 0);
+    lds_barrier();  // code table filled, rows of group 0 staged
+
+    int cs = s0, cg = g0;
+    for (int k = 0; k <= nk; ++k) {
+      if (k < nk) {
+        const int b = k & 1;
+        const int tb = tfirst + 32 * cg;
+        f4 acc[2][2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) acc[ct][tt] = f4{0.f, 0.f, 0.f, 0.f};
+        auto x_operand = [&](int st) {
+          const int kb = st / 2, tt = st % 2;
+          return *reinterpret_cast<const h8*>(&xs[b][16 * tt + l16][32 * kb + 8 * g4]);
+        };
+        h8 xv = x_operand(0);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int kb = st / 2, tt = st % 2;
+          const h8 xn = st < 7 ? x_operand(st + 1) : xv;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            acc[ct][tt] = mfma(wr[ct][kb][0], xv, acc[ct][tt]);
+            acc[ct][tt] = mfma(wr[ct][kb][1], xv, acc[ct][tt]);
+          }
+          xv = xn;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int st = 0; st < 7; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          if (st < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+        // Lane (g4, l16) holds coordinates 32w + 8g4 + 4ct + r of token slot
+        // 16tt + l16.  Stores go through records from the group's first token
+        // slot on; slots outside [t0, t0 + n) get an offset past the record.
+        const int64_t row0 = (int64_t)cs * p.cap + tb;
+        const Rsrc irec = record(p.idx + row0 * rowb, kSlots * rowb);
+        const Rsrc nrec = record(p.norm + row0, kSlots * 4);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int slot = 16 * tt + l16;
+          const int t = tb + slot;
+          const bool ok = t >= t0 && t < tend;
+          const uint32_t ioff = ok ? (uint32_t)(slot * rowb + (4 * w + g4) * BITS) : kOob;
+          const float nn = nrm[b][slot];
+          const float inv = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
+          const float inv_r = inv * kRes;
+          uint32_t packed = 0;
+          float r[8];
+          float rr = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float a = acc[ct][tt][q];
+              uint32_t code;
+              float c;
+              if constexpr (kTable) {
+                code = table_code_cent<kCopies>(ctabc_lane, fmaf(a, inv * ubin, 0.5f * kBins), c);
+              } else {
+                code = symmetric_code<BITS>(a * inv, beta);
+                c = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(code << 2), ctab));
+              }
+              packed |= code << (BITS * (4 * ct + q));
+              r[4 * ct + q] = fmaf(a, inv_r, -c);  // kRes (y - c)
+              rr = fmaf(r[4 * ct + q], r[4 * ct + q], rr);
+            }
+          store_code_bits<BITS>(packed, irec, ioff);
+          if (w == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nn), nrec,
+                                                  g4 == 0 && ok ? (uint32_t)(slot * 4) : kOob, 0, 0);
+          u4 hi, lo;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const h2 hv{(_Float16)r[2 * j], (_Float16)r[2 * j + 1]};
+            hi[j] = __builtin_bit_cast(uint32_t, hv);
+            lo[j] = split_lo(r[2 * j], r[2 * j + 1], hi[j]);
+          }
+          *reinterpret_cast<u4*>(&rs[b][0][slot][32 * w + 8 * g4]) = hi;
+          *reinterpret_cast<u4*>(&rs[b][1][slot][32 * w + 8 * g4]) = lo;
+          rr = sum_over_row_groups(rr);  // the wave's 32 coordinates of the slot
+          if (g4 == 0) rsq[b][slot][w] = rr;
+        }
+        advance(cs, cg);
+      }
+      lds_barrier();
+    }
+  } else {
+    // ---------------- projection waves ----------------
+    h8 wp[2][4][2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int row = out_coord(w, ct, l16);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int col = 32 * kb + 8 * g4;
+        wp[ct][kb][0] = *reinterpret_cast<const h8*>(p.projr_hi + row * D + col);
+        wp[ct][kb][1] = *reinterpret_cast<const h8*>(p.projr_lo + row * D + col);
+      }
+    }
+    // Loader role: 8 threads per token slot, 16 halves each, through a record
+    // from the group's first token slot (slots outside [t0, t0 + n), and
+    // groups past the end, read 0 without touching memory).
+    const int pt = tid - kThreads;
+    const int lslot = pt / 8, lpart = pt % 8;
+    auto load_x = [&](int gs, int gg, bool live, h8& v0, h8& v1) {
+      const int tb = tfirst + 32 * gg;
+      const int t = tb + lslot;
+      const Rsrc rec = record(p.x + ((int64_t)gs * p.n + (tb - t0)) * D, kSlots * D * 2);
+      const uint32_t off = live && t >= t0 && t < tend ? (uint32_t)(lslot * D * 2 + lpart * 32) : kOob;
+      v0 = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rec, off, 0, 0));
+      v1 = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rec, off + 16, 0, 0));
+    };
+    auto stage = [&](int b, const h8& v0, const h8& v1) {
+      *reinterpret_cast<h8*>(&xs[b][lslot][lpart * 16]) = v0;
+      *reinterpret_cast<h8*>(&xs[b][lslot][lpart * 16 + 8]) = v1;
+      // Sum of squares: fp16 products are exact in fp32; then the slot's 8 lanes.
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const h2 a{v0[e], v0[e + 1]}, c{v1[e], v1[e + 1]};
+        s0 = __builtin_amdgcn_fdot2(a, a, s0, false);
+        s1 = __builtin_amdgcn_fdot2(c, c, s1, false);
+      }
+      const float ss = sum_over_8_lanes(s0 + s1);
+      if (lpart == 0) nrm[b][lslot] = __builtin_amdgcn_sqrtf(ss);
+    };
+    int ls = s0, lg = g0;  // next group to load
+    h8 nx0, nx1;
+    load_x(ls, lg, nk > 0, nx0, nx1);
+    advance(ls, lg);
+    stage(0, nx0, nx1);
+    load_x(ls, lg, nk > 1, nx0, nx1);
+    advance(ls, lg);
+    lds_barrier();
+
+    int ps = s0, pg = g0;  // group k - 1
+    for (int k = 0; k <= nk; ++k) {
+      if (k + 1 < nk) stage((k + 1) & 1, nx0, nx1);
+      load_x(ls, lg, k + 2 < nk, nx0, nx1);
+      advance(ls, lg);
+      if (k >= 1) {
+        const int b = (k - 1) & 1;
+        const int tb = tfirst + 32 * pg;
+        f4 pacc[2][2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) pacc[ct][tt] = f4{0.f, 0.f, 0.f, 0.f};
+        auto r_operand = [&](int st, int part) {
+          const int kb = st / 2, tt = st % 2;
+          return *reinterpret_cast<const h8*>(&rs[b][part][16 * tt + l16][32 * kb + 8 * g4]);
+        };
+        h8 rh = r_operand(0, 0), rl = r_operand(0, 1);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int kb = st / 2, tt = st % 2;
+          const h8 nh = st < 7 ? r_operand(st + 1, 0) : rh;
+          const h8 nl = st < 7 ? r_operand(st + 1, 1) : rl;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            pacc[ct][tt] = mfma(wp[ct][kb][0], rh, pacc[ct][tt]);
+            pacc[ct][tt] = mfma(wp[ct][kb][0], rl, pacc[ct][tt]);
+            pacc[ct][tt] = mfma(wp[ct][kb][1], rh, pacc[ct][tt]);
+          }
+          rh = nh;
+          rl = nl;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int st = 0; st < 7; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+          if (st < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        const int64_t row0 = (int64_t)ps * p.cap + tb;
+        const Rsrc srec = record(p.sign + row0 * (D / 8), kSlots * (D / 8));
+        const Rsrc grec = record(p.rnorm + row0, kSlots * 4);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int slot = 16 * tt + l16;
+          const int t = tb + slot;
+          const bool ok = t >= t0 && t < tend;
+          // Bit 4ct + q is 1 for a projection >= +0: shift the float sign bits
+          // in from the highest bit down (one funnel shift each), then invert.
+          uint32_t bits = 0;
+#pragma unroll
+          for (int e = 7; e >= 0; --e)
+            bits = __builtin_amdgcn_alignbit(bits, __float_as_uint(pacc[e / 4][tt][e % 4]), 31);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)~bits, srec,
+                                               ok ? (uint32_t)(slot * (D / 8) + 4 * w + g4) : kOob, 0, 0);
+          if (w == 0) {
+            const f4 g = *reinterpret_cast<const f4*>(&rsq[b][slot][0]);
+            const float gamma = __builtin_amdgcn_sqrtf((g[0] + g[1]) + (g[2] + g[3])) * (1.f / kRes);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gamma), grec,
+                                                  g4 == 0 && ok ? (uint32_t)(slot * 4) : kOob, 0, 0);
+          }
+        }
+        advance(ps, pg);
+      }
+      lds_barrier();
+    }
+  }
+}
+
 // Persistent grid: as many workgroups as the CUs hold at once (a second,
 // partial round of workgroups would run the last share at low occupancy).
-template <int BITS, int QJL, int VALUES>
-hipError_t launch(const QuantMfmaParams& p, int64_t groups, hipStream_t st) {
+template <typename Kernel>
+hipError_t launch_persistent(Kernel kernel, int threads, const QuantMfmaParams& p, int64_t groups, hipStream_t st) {
   int dev = 0, cus = 256, per_cu = 0;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quantize_mfma_kernel<BITS, QJL, VALUES>, kThreads, 0) !=
-          hipSuccess || per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   const int64_t slots = (int64_t)cus * per_cu;
   const int64_t grid = groups < slots ? groups : slots;
-  hipLaunchKernelGGL((quantize_mfma_kernel<BITS, QJL, VALUES>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, st, p);
   return hipGetLastError();
+}
+
+template <int BITS, int QJL, int VALUES>
+hipError_t launch(const QuantMfmaParams& p, int64_t groups, hipStream_t st) {
+  if constexpr (QJL)
+    return launch_persistent(quantize_keys_qjl_kernel<BITS>, 2 * kThreads, p, groups, st);
+  else
+    return launch_persistent(quantize_mfma_kernel<BITS, VALUES>, kThreads, p, groups, st);
 }
 
 template <int QJL, int VALUES>
