@@ -60,15 +60,16 @@ constexpr int kBinCopies = 32;
 constexpr int kCodeTableEntries = kBins * kBinCopies;
 
 // Entry of bin `bin` for the 2^BITS - 1 sorted boundaries bnd (ubin =
-// sqrt(d) * kBinScale): the boundary inside the bin in bin units, or +inf, and
-// the count of boundaries below the bin.
+// sqrt(d) * kBinScale, the table's bins starting at u = -offset): the boundary
+// inside the bin in bin units, or +inf, and the count of boundaries below the bin.
 template <int BITS>
-__device__ __forceinline__ void bin_entry(const float* bnd, float ubin, int bin, float& inner, uint32_t& below) {
+__device__ __forceinline__ void bin_entry(const float* bnd, float ubin, float offset, int bin, float& inner,
+                                          uint32_t& below) {
   constexpr int L = 1 << BITS;
   below = 0;
   inner = INFINITY;
   for (int i = 0; i + 1 < L; ++i) {
-    const float ub = fmaf(bnd[i], ubin, 0.5f * kBins);
+    const float ub = fmaf(bnd[i], ubin, offset);
     if (ub < (float)bin) ++below;
     else if (ub < (float)(bin + 1)) inner = ub;
   }
@@ -81,7 +82,7 @@ __device__ __forceinline__ void fill_code_table(uint2* tab, const float* bnd, fl
   for (int e = tid; e < kCodeTableEntries; e += nthreads) {
     float inner;
     uint32_t below;
-    bin_entry<BITS>(bnd, ubin, e / kBinCopies, inner, below);
+    bin_entry<BITS>(bnd, ubin, 0.5f * kBins, e / kBinCopies, inner, below);
     tab[e] = make_uint2(__float_as_uint(inner), below);
   }
 }
@@ -94,28 +95,57 @@ __device__ __forceinline__ uint32_t table_code(const uint2* lane_tab, float u) {
   return ent.y + (u > __uint_as_float(ent.x) ? 1u : 0u);
 }
 
-// The same table with each entry also holding the centroids of its two
-// possible codes, c[below] and c[below + 1], times cscale: a code's centroid is
-// then a select on the code's own compare (no second lookup).
-// COPIES copies of each bin's entry (kBins * COPIES entries).
+// Full-range tables for head dimension 128: a coordinate y of a unit vector
+// has |z| = |y| sqrt(128) <= 11.32, i.e. |z| kBinScale <= 90.6, so kFullBins
+// bins from u = -kFullOffset hold every value the rotation can produce (with
+// two bins of margin for rounding).  The bin index then needs no clamp, only
+// a float-to-unsigned conversion, which gives bin 0 for a negative value or
+// NaN (the code of a row with a non-finite norm, whose scale is 0).
+constexpr int kFullBins = 186;
+constexpr float kFullOffset = 93.f;
+__device__ __forceinline__ uint32_t full_bin(float u) {
+  uint32_t b;
+  asm("v_cvt_u32_f32 %0, %1" : "=v"(b) : "v"(u));
+  return b;
+}
+
+// COPIES copies of each full-range bin's entry (one per lane of the group of
+// lanes one LDS cycle serves: 16 for 8-byte entries, 8 for 16-byte ones).
 template <int BITS, int COPIES>
-__device__ __forceinline__ void fill_code_cent_table(uint4* tab, const float* bnd, const float* cent, float ubin,
-                                                     float cscale, int tid, int nthreads) {
-  constexpr uint32_t L = 1u << BITS;
-  for (int e = tid; e < kBins * COPIES; e += nthreads) {
+__device__ __forceinline__ void fill_full_code_table(uint2* tab, const float* bnd, float ubin, int tid,
+                                                     int nthreads) {
+  for (int e = tid; e < kFullBins * COPIES; e += nthreads) {
     float inner;
     uint32_t below;
-    bin_entry<BITS>(bnd, ubin, e / COPIES, inner, below);
+    bin_entry<BITS>(bnd, ubin, kFullOffset, e / COPIES, inner, below);
+    tab[e] = make_uint2(__float_as_uint(inner), below);
+  }
+}
+template <int COPIES>
+__device__ __forceinline__ uint32_t full_table_code(const uint2* lane_tab, float u) {
+  const uint2 ent = lane_tab[full_bin(u) * COPIES];
+  return ent.y + (u > __uint_as_float(ent.x) ? 1u : 0u);
+}
+
+// The full-range table with each entry also holding the centroids of its two
+// possible codes, c[below] and c[below + 1], times cscale: a code's centroid is
+// then a select on the code's own compare (no second lookup).
+template <int BITS, int COPIES>
+__device__ __forceinline__ void fill_full_code_cent_table(uint4* tab, const float* bnd, const float* cent, float ubin,
+                                                          float cscale, int tid, int nthreads) {
+  constexpr uint32_t L = 1u << BITS;
+  for (int e = tid; e < kFullBins * COPIES; e += nthreads) {
+    float inner;
+    uint32_t below;
+    bin_entry<BITS>(bnd, ubin, kFullOffset, e / COPIES, inner, below);
     const uint32_t above = below + 1 < L ? below + 1 : below;
     tab[e] = make_uint4(__float_as_uint(inner), below, __float_as_uint(cent[below] * cscale),
                         __float_as_uint(cent[above] * cscale));
   }
 }
-
 template <int COPIES>
-__device__ __forceinline__ uint32_t table_code_cent(const uint4* lane_tab, float u, float& c) {
-  const int bin = (int)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kBins - 1));
-  const uint4 ent = lane_tab[bin * COPIES];
+__device__ __forceinline__ uint32_t full_table_code_cent(const uint4* lane_tab, float u, float& c) {
+  const uint4 ent = lane_tab[full_bin(u) * COPIES];
   const bool up = u > __uint_as_float(ent.x);
   c = __uint_as_float(up ? ent.w : ent.z);
   return ent.y + (up ? 1u : 0u);

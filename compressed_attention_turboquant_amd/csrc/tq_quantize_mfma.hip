@@ -58,10 +58,13 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSlots = 32;  // tokens per tile: 4 value tiles of 8
 // The role-split key kernel runs 4 waves per SIMD (two workgroups of 8 waves
-// per CU: 128 VGPRs, 16 copies of the code table so that both fit in LDS).
+// per CU: 128 VGPRs, and a code table small enough that both fit in LDS).
 // Same-run timings of the C3 keys: 3.06 ms at 2 waves per SIMD, 2.76 ms at 4.
+// Table copies: one per lane of the group one LDS cycle serves (8 lanes for
+// the keys' 16-byte entries, 16 for the values' 8-byte entries).
 constexpr int kKeyWaves = 4;
-constexpr int kKeyCopies = 16;
+constexpr int kKeyCopies = 8;
+constexpr int kValCopies = 16;
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -107,7 +110,8 @@ quantize_mfma_kernel(QuantMfmaParams p) {
   constexpr bool kTable = BITS >= 3;  // 3- and 4-bit codes from the binned table
   __shared__ __align__(16) _Float16 xs[kSlots][D + 8];  // token rows (padded)
   __shared__ float nrm[kSlots];
-  __shared__ __align__(16) uint2 ctabl[kTable ? kCodeTableEntries : 1];
+  __shared__ __align__(16) float nsc[kSlots];  // each slot's scale into the code step (0 for a zero row)
+  __shared__ __align__(16) uint2 ctabl[kTable ? kFullBins * kValCopies : 1];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -132,8 +136,8 @@ quantize_mfma_kernel(QuantMfmaParams p) {
   for (int i = 0; i < KP; ++i) beta[i] = BITS > 1 ? p.bnd[(1 << (BITS - 1)) + i] : 0.f;
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   const float ubin = sqrtf((float)D) * kBinScale;  // unit-vector coordinate -> bin units
-  if constexpr (kTable) fill_code_table<BITS>(ctabl, p.bnd, ubin, tid, kThreads);
-  const uint2* ctab_lane = ctabl + (kTable ? lane % kBinCopies : 0);
+  if constexpr (kTable) fill_full_code_table<BITS, kValCopies>(ctabl, p.bnd, ubin, tid, kThreads);
+  const uint2* ctab_lane = ctabl + (kTable ? lane % kValCopies : 0);
 
   // Work unit: 4 consecutive value tiles (32 token slots) of one sequence.
   // Group g is (sequence g / gps, group g % gps of it); the grid strides by
@@ -193,7 +197,12 @@ quantize_mfma_kernel(QuantMfmaParams p) {
         s1 = __builtin_amdgcn_fdot2(b, b, s1, false);
       }
       const float ss = sum_over_8_lanes(s0 + s1);
-      if (lpart == 0) nrm[lslot] = __builtin_amdgcn_sqrtf(ss);
+      if (lpart == 0) {
+        const float nn = __builtin_amdgcn_sqrtf(ss);
+        const float inv = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
+        nrm[lslot] = nn;
+        nsc[lslot] = kTable ? inv * ubin : inv;  // bin units, or unit-vector units for the search
+      }
       load_x(ns, ng, grp + (int)gridDim.x < groups, nx0, nx1);
     }
     lds_barrier();
@@ -253,8 +262,7 @@ quantize_mfma_kernel(QuantMfmaParams p) {
         const int t = tb + slot;
         const bool ok = t >= t0 && t < tend;
         const uint32_t ioff = ok ? (uint32_t)(slot * rowb + (4 * w + g4) * BITS) : kOob;
-        const float nn = nrm[slot];
-        const float inv = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
+        const float nn = nrm[slot], sc = nsc[slot];
         uint32_t packed = 0;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
@@ -262,8 +270,8 @@ quantize_mfma_kernel(QuantMfmaParams p) {
           for (int q = 0; q < 4; ++q) {
             const float a = acc[ct][tt][q];
             uint32_t code;
-            if constexpr (kTable) code = table_code(ctab_lane, fmaf(a, inv * ubin, 0.5f * kBins));
-            else code = symmetric_code<BITS>(a * inv, beta);
+            if constexpr (kTable) code = full_table_code<kValCopies>(ctab_lane, fmaf(a, sc, kFullOffset));
+            else code = symmetric_code<BITS>(a * sc, beta);
             packed |= code << (BITS * (4 * ct + q));
           }
         store_code_bits<BITS>(packed, irec, ioff);
@@ -275,18 +283,19 @@ quantize_mfma_kernel(QuantMfmaParams p) {
       // Lane (g4, l16) holds, for coordinate tile ct, coordinate out_coord(w, ct, l16)
       // of the 8 tokens of value tile g4 (token 4 tt + r in D row 4 g4 + r of tile tt).
       const int s = cs;
-      const bool tile_ok = 4 * cg + g4 < tiles;
       const int tile = (int)p.tile_first + 4 * cg + g4;
+      // Tokens k of the tile inside [t0, t0 + n): lo <= k < hi (none for a
+      // tile past the last one).
+      const int lo = max(t0 - tile * 8, 0), hi = min(tend - tile * 8, 8);
+      const bool tile_ok = hi > lo;
       uint32_t keep = 0;  // code bits of tokens outside [t0, t0+n) are left unchanged
-      float inv[8];
+      if (lo > 0 || hi < 8) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int t = tile * 8 + k;
-        const bool ok = t >= t0 && t < tend;
-        if (!ok) keep |= ((1u << BITS) - 1u) << (BITS * k);
-        const float nn = nrm[8 * g4 + k];
-        inv[k] = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
+        for (int k = 0; k < 8; ++k)
+          if (k < lo || k >= hi) keep |= ((1u << BITS) - 1u) << (BITS * k);
       }
+      const f4 sc0 = *reinterpret_cast<const f4*>(&nsc[8 * g4]), sc1 = *reinterpret_cast<const f4*>(&nsc[8 * g4 + 4]);
+      const float inv[8] = {sc0[0], sc0[1], sc0[2], sc0[3], sc1[0], sc1[1], sc1[2], sc1[3]};
       // Norms: lane l16 < 8 of wave 0 stores token l16 of value tile g4.
       if (w == 0 && l16 < 8 && tile_ok) {
         const int t = tile * 8 + l16;
@@ -302,7 +311,7 @@ quantize_mfma_kernel(QuantMfmaParams p) {
           for (int q = 0; q < 4; ++q) {
             const int k = 4 * tt + q;
             if constexpr (kTable)
-              packed |= table_code(ctab_lane, fmaf(acc[ct][tt][q], inv[k] * ubin, 0.5f * kBins)) << (BITS * k);
+              packed |= full_table_code<kValCopies>(ctab_lane, fmaf(acc[ct][tt][q], inv[k], kFullOffset)) << (BITS * k);
             else
               packed |= symmetric_code<BITS>(acc[ct][tt][q] * inv[k], beta) << (BITS * k);
           }
@@ -344,8 +353,9 @@ quantize_keys_qjl_kernel(QuantMfmaParams p) {
   __shared__ __align__(16) _Float16 xs[2][kSlots][D + 8];     // token rows (padded)
   __shared__ __align__(16) _Float16 rs[2][2][kSlots][D + 8];  // [buffer][hi, lo] residual
   __shared__ float nrm[2][kSlots];
+  __shared__ __align__(16) float2 nsc[2][kSlots];             // {scale into the code step, into kRes (y - c)}
   __shared__ __align__(16) float rsq[2][kSlots][kWaves];      // per-wave sums of r^2
-  __shared__ __align__(16) uint4 ctabc[kTable ? kBins * kCopies : 1];
+  __shared__ __align__(16) uint4 ctabc[kTable ? kFullBins * kCopies : 1];
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -355,7 +365,7 @@ quantize_keys_qjl_kernel(QuantMfmaParams p) {
   constexpr float kRes = 64.f;  // the residual is formed as kRes (y - c)
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   const float ubin = sqrtf((float)D) * kBinScale;
-  if constexpr (kTable) fill_code_cent_table<BITS, kCopies>(ctabc, p.bnd, p.cent, ubin, kRes, tid, 2 * kThreads);
+  if constexpr (kTable) fill_full_code_cent_table<BITS, kCopies>(ctabc, p.bnd, p.cent, ubin, kRes, tid, 2 * kThreads);
 
   const int tiles = (int)(p.tile_last - p.tile_first + 1);
   const int gps = (tiles + 3) / 4;
@@ -444,8 +454,7 @@ quantize_keys_qjl_kernel(QuantMfmaParams p) {
           const bool ok = t >= t0 && t < tend;
           const uint32_t ioff = ok ? (uint32_t)(slot * rowb + (4 * w + g4) * BITS) : kOob;
           const float nn = nrm[b][slot];
-          const float inv = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
-          const float inv_r = inv * kRes;
+          const float2 sc = nsc[b][slot];
           uint32_t packed = 0;
           float r[8];
           float rr = 0.f;
@@ -457,13 +466,13 @@ quantize_keys_qjl_kernel(QuantMfmaParams p) {
               uint32_t code;
               float c;
               if constexpr (kTable) {
-                code = table_code_cent<kCopies>(ctabc_lane, fmaf(a, inv * ubin, 0.5f * kBins), c);
+                code = full_table_code_cent<kCopies>(ctabc_lane, fmaf(a, sc.x, kFullOffset), c);
               } else {
-                code = symmetric_code<BITS>(a * inv, beta);
+                code = symmetric_code<BITS>(a * sc.x, beta);
                 c = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(code << 2), ctab));
               }
               packed |= code << (BITS * (4 * ct + q));
-              r[4 * ct + q] = fmaf(a, inv_r, -c);  // kRes (y - c)
+              r[4 * ct + q] = fmaf(a, sc.y, -c);  // kRes (y - c)
               rr = fmaf(r[4 * ct + q], r[4 * ct + q], rr);
             }
           store_code_bits<BITS>(packed, irec, ioff);
@@ -524,7 +533,12 @@ quantize_keys_qjl_kernel(QuantMfmaParams p) {
         s1 = __builtin_amdgcn_fdot2(c, c, s1, false);
       }
       const float ss = sum_over_8_lanes(s0 + s1);
-      if (lpart == 0) nrm[b][lslot] = __builtin_amdgcn_sqrtf(ss);
+      if (lpart == 0) {
+        const float nn = __builtin_amdgcn_sqrtf(ss);
+        const float inv = nn > 0.f ? inv_sqrt_d * __builtin_amdgcn_rcpf(nn) : 0.f;
+        nrm[b][lslot] = nn;
+        nsc[b][lslot] = make_float2(kTable ? inv * ubin : inv, inv * kRes);
+      }
     };
     int ls = s0, lg = g0;  // next group to load
     h8 nx0, nx1;
