@@ -17,6 +17,7 @@ Printed (one JSON line on stdout):
   roofline           decode kernels vs the 8 TB/s HBM peak
   roofline_quantize, roofline_dequantize   the other two calls vs the same peak
   stream_read_gbs    the best rate of a streaming-read kernel on this GPU
+                     (grid-stride and one contiguous chunk per workgroup)
   stream_rw_probe    the best rates of plain kernels that read 4 bytes per
                      byte written and 1 per 4 written (the mixes of quantize and
                      dequantize), with *_frac_of_stream_rw against them
@@ -188,6 +189,10 @@ class Probe:
         self.lib.tq_probe_stream_rw.restype = ctypes.c_int
         self.lib.tq_probe_stream_rw.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                                 ctypes.c_void_p]
+        self.lib.tq_probe_chunk_read.restype = ctypes.c_int
+        self.lib.tq_probe_chunk_read.argtypes = self.lib.tq_probe_stream_read.argtypes
+        self.lib.tq_probe_chunk_rw.restype = ctypes.c_int
+        self.lib.tq_probe_chunk_rw.argtypes = self.lib.tq_probe_stream_rw.argtypes
         self.sink = torch.empty(self.lib.tq_probe_stream_threads() * 16, dtype=torch.uint8, device=dev)
         self.flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
 
@@ -205,21 +210,27 @@ class Probe:
 
     def peak(self, dev, stream, nbytes=4 << 30, reps=6):
         """Best read rate over a 4 GiB buffer (16x the last-level cache), GB/s,
-        for non-temporal and for plain loads."""
+        for non-temporal and for plain loads, in a grid-stride pattern and one
+        contiguous chunk per workgroup at a time (the faster one here)."""
         import torch
         buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
         out = {}
-        for nt in (True, False):
-            best = 0.0
-            for i in range(reps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                self.read(buf, nt, stream)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                if i > 0:
-                    best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-            out["nontemporal" if nt else "plain"] = round(best, 1)
+        for chunked in (False, True):
+            fn = self.lib.tq_probe_chunk_read if chunked else self.lib.tq_probe_stream_read
+            for nt in (True, False):
+                best = 0.0
+                for i in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    rc = fn(buf.data_ptr(), nbytes, self.sink.data_ptr(), int(nt), stream.cuda_stream)
+                    e1.record(stream)
+                    if rc != 0:
+                        raise RuntimeError(f"stream probe launch failed: {rc}")
+                    torch.cuda.synchronize()
+                    if i > 0:
+                        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+                tag = ("chunked_" if chunked else "grid_stride_") + ("nontemporal" if nt else "plain")
+                out[tag] = round(best, 1)
         del buf
         return out
 
@@ -235,16 +246,17 @@ class Probe:
         for read4, tag in ((1, "read4_write1"), (0, "read1_write4")):
             src, dst = (large, small) if read4 else (small, large)
             best = 0.0
-            for i in range(reps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                rc = self.lib.tq_probe_stream_rw(src.data_ptr(), dst.data_ptr(), words, read4, stream.cuda_stream)
-                e1.record(stream)
-                if rc != 0:
-                    raise RuntimeError(f"stream probe launch failed: {rc}")
-                torch.cuda.synchronize()
-                if i > 0:
-                    best = max(best, 5 * small_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+            for fn in (self.lib.tq_probe_stream_rw, self.lib.tq_probe_chunk_rw):  # both patterns, the best counts
+                for i in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    rc = fn(src.data_ptr(), dst.data_ptr(), words, read4, stream.cuda_stream)
+                    e1.record(stream)
+                    if rc != 0:
+                        raise RuntimeError(f"stream probe launch failed: {rc}")
+                    torch.cuda.synchronize()
+                    if i > 0:
+                        best = max(best, 5 * small_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
             out[tag] = round(best, 1)
         del small, large
         return out

@@ -3,9 +3,10 @@
 // 4:1 and 1:4 read/write mixes for quantize and dequantize).  Not part of the
 // TurboQuant path; built into its own library (libtqprobe.so) for bench.py.
 //
-// Every thread reads 16-byte words in a grid-stride loop, four loads in flight,
-// folds them with XOR and stores one word at the end, so that no load can be
-// dropped.  The grid fills every CU with 8 workgroups of 256 threads.  With
+// Every thread reads 16-byte words, four loads in flight, folds them with XOR
+// and stores one word at the end, so that no load can be dropped; in a
+// grid-stride loop, or (the faster pattern here) a contiguous chunk per
+// workgroup at a time.  The grid fills every CU with 8 workgroups of 256 threads.  With
 // plain loads the same kernel also serves bench.py as a cache flush: reading
 // 2 GiB of unrelated data leaves none of a workload's cache and no dirty lines
 // in the 256 MB last-level cache.
@@ -65,6 +66,53 @@ __global__ void __launch_bounds__(256) stream_rw_kernel(const u4* __restrict__ s
   }
 }
 
+// The same streams with each workgroup taking one contiguous chunk of kChunk
+// words at a time (chunks dealt to workgroups in turn), four loads in flight
+// per thread, two workgroups per CU.  On this part this pattern reads about
+// 15% faster than the grid-stride one above (7.1-7.2 vs 6.0-6.2 TB/s):
+// requests spread over the whole buffer instead of one narrow window moving
+// through it.
+constexpr int64_t kChunk = 16384;  // 256 KiB per chunk
+
+template <bool NT>
+__global__ void __launch_bounds__(256) chunk_read_kernel(const u4* __restrict__ src, int64_t words,
+                                                         u4* __restrict__ sink) {
+  u4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t c0 = (int64_t)blockIdx.x * kChunk; c0 < words; c0 += (int64_t)gridDim.x * kChunk) {
+    const int64_t c1 = c0 + kChunk < words ? c0 + kChunk : words;
+    for (int64_t i = c0 + threadIdx.x; i < c1; i += 4 * 256) {
+      u4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t j = i + 256 * k;
+        v[k] = j < c1 ? ld<NT>(src + j) : u4{0u, 0u, 0u, 0u};
+      }
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+  }
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// Chunked read/write mixes: READ4 writes dst[i] = XOR of src[4i .. 4i + 3]
+// (4 bytes read per byte written), else dst[4i + k] = src[i] + k.  `words`
+// counts the smaller side; chunks are kChunk words of it.
+template <bool READ4>
+__global__ void __launch_bounds__(256) chunk_rw_kernel(const u4* __restrict__ src, u4* __restrict__ dst,
+                                                       int64_t words) {
+  for (int64_t c0 = (int64_t)blockIdx.x * kChunk; c0 < words; c0 += (int64_t)gridDim.x * kChunk) {
+    const int64_t c1 = c0 + kChunk < words ? c0 + kChunk : words;
+    for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
+      if constexpr (READ4) {
+        dst[i] = src[4 * i] ^ src[4 * i + 1] ^ src[4 * i + 2] ^ src[4 * i + 3];
+      } else {
+        const u4 v = src[i];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[4 * i + k] = v + (uint32_t)k;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +156,35 @@ int tq_probe_stream_rw(const void* src, void* dst, int64_t words, int read4, voi
                        static_cast<u4*>(dst), words);
   else
     hipLaunchKernelGGL(stream_rw_kernel<false>, grid, dim3(256), 0, st, static_cast<const u4*>(src),
+                       static_cast<u4*>(dst), words);
+  return (int)hipGetLastError();
+}
+
+// Workgroups of the chunked probes: two per CU.
+static int64_t chunk_grid() { return tq_probe_stream_threads() / 256 / 4; }
+
+// The chunked read: same arguments as tq_probe_stream_read.
+int tq_probe_chunk_read(const void* src, int64_t bytes, void* sink, int nontemporal, void* stream) {
+  const dim3 grid((unsigned)chunk_grid());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const u4* s = static_cast<const u4*>(src);
+  u4* k = static_cast<u4*>(sink);
+  if (nontemporal)
+    hipLaunchKernelGGL(chunk_read_kernel<true>, grid, dim3(256), 0, st, s, bytes / 16, k);
+  else
+    hipLaunchKernelGGL(chunk_read_kernel<false>, grid, dim3(256), 0, st, s, bytes / 16, k);
+  return (int)hipGetLastError();
+}
+
+// The chunked read/write mixes: same arguments as tq_probe_stream_rw (any word count).
+int tq_probe_chunk_rw(const void* src, void* dst, int64_t words, int read4, void* stream) {
+  const dim3 grid((unsigned)chunk_grid());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (read4)
+    hipLaunchKernelGGL(chunk_rw_kernel<true>, grid, dim3(256), 0, st, static_cast<const u4*>(src),
+                       static_cast<u4*>(dst), words);
+  else
+    hipLaunchKernelGGL(chunk_rw_kernel<false>, grid, dim3(256), 0, st, static_cast<const u4*>(src),
                        static_cast<u4*>(dst), words);
   return (int)hipGetLastError();
 }
