@@ -83,6 +83,10 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   __shared__ __align__(16) _Float16 bhi[kTile][PITCH], blo[OUT16 ? 1 : kTile][OUT16 ? 8 : PITCH];
   __shared__ float nsh[kTile];
   __shared__ float dsh[DITHER ? kTile : 1];  // dithered variant: the tile's offsets, times kFactor^2
+  // fp16 rows: the finished tile is staged here and written back as whole
+  // rows, 16 bytes per lane (the accumulator layout would write 8-byte pieces
+  // of 16 rows per instruction, which measured at about half the HBM rate).
+  __shared__ __align__(16) _Float16 ot[OUT16 ? kTile : 1][OUT16 ? PITCH : 8];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -189,7 +193,7 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
                                                                tid < kTile ? 4u * tid : kOob, 0, 0));
   };
   load_codes(item, seq, tile);
-  {
+  if constexpr (!OUT16) {
     // The loop's own path to its top has the tile's stores after these loads;
     // as many dropped stores to an empty record give the path from here the
     // same count, so the wait at the top leaves the stores in flight.
@@ -197,11 +201,27 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
 #pragma unroll
     for (int i = 0; i < 2 * (kTile / 16); ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 64 * i, 0, 0);
   }
+  // fp16 rows: the staged tile (sequence pseq, first token pt0, prows rows;
+  // none before the first) is written back at the top of the next iteration,
+  // beside that tile's decode.  Every thread stores 4 x 16 bytes; rows past
+  // the tile's end (or no tile) get an offset past the record.
+  int64_t pseq = 0, pt0 = 0, prows = 0;
+  auto write_tile = [&]() {
+    constexpr int kCpr = D / 8;  // 16-byte chunks per row
+    const Rsrc prec = record(static_cast<uint8_t*>(a.out) + (pseq * n + pt0) * D * 2, prows * D * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + T * i, row = c / kCpr, part = c % kCpr;
+      const u4 v = *reinterpret_cast<const u4*>(&ot[row][8 * part]);
+      __builtin_amdgcn_raw_buffer_store_b128(v, prec, row < prows ? (uint32_t)(row * D * 2 + part * 16) : kOob, 0, 0);
+    }
+  };
   int64_t nitem = item, nseq = seq, ntile = tile;
   advance(nitem, nseq, ntile);
   for (; item < items; item = nitem, seq = nseq, tile = ntile, advance(nitem, nseq, ntile)) {
     const int64_t t0 = tile * kTile;
-    lds_barrier();  // the previous tile's operands have been read
+    lds_barrier();  // the previous tile's operands have been read (and its output staged)
+    if constexpr (OUT16) write_tile();
     // Decode: thread -> 32 consecutive codes of the packed stream.
     {
       uint32_t ph[16], pl[16];
@@ -286,12 +306,22 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
         if constexpr (OUT16) {
           const u2 hv = {hbits((_Float16)v[0]) | (hbits((_Float16)v[1]) << 16),
                          hbits((_Float16)v[2]) | (hbits((_Float16)v[3]) << 16)};
-          __builtin_amdgcn_raw_buffer_store_b64(hv, orec, off, 0, 0);
+          *reinterpret_cast<u2*>(&ot[tok][col]) = hv;
+          (void)off;
         } else {
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), orec, off, 0, 0);
         }
       }
     }
+    if constexpr (OUT16) {
+      pseq = seq;
+      pt0 = t0;
+      prows = rows;
+    }
+  }
+  if constexpr (OUT16) {
+    lds_barrier();  // the last tile is staged
+    write_tile();
   }
 }
 
