@@ -87,14 +87,6 @@ __device__ __forceinline__ void fill_code_table(uint2* tab, const float* bnd, fl
   }
 }
 
-// Code of a value at u = z kBinScale + kBins / 2 (bin units) from the lane's
-// copy of the table (tab + lane % kBinCopies).
-__device__ __forceinline__ uint32_t table_code(const uint2* lane_tab, float u) {
-  const int bin = (int)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kBins - 1));
-  const uint2 ent = lane_tab[bin * kBinCopies];
-  return ent.y + (u > __uint_as_float(ent.x) ? 1u : 0u);
-}
-
 // Full-range tables for head dimension 128: a coordinate y of a unit vector
 // has |z| = |y| sqrt(128) <= 11.32, i.e. |z| kBinScale <= 90.6, so kFullBins
 // bins from u = -kFullOffset hold every value the rotation can produce (with
