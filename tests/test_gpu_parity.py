@@ -522,6 +522,12 @@ DEQUANT_SHAPES = {
     "haar d128 K2 V3, 128 tokens": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=128), None),
     "hadamard d256 K3 V2, first 67 of 200": (workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=200, k_bits=3,
                                                                             v_bits=2), 67),
+    # fp16 rows of the Haar kernel at the other head dimensions (its output
+    # tile is staged in LDS and written as whole rows): several 64-token
+    # steps and a ragged last one.
+    "haar d64 fp16 K2 V3, 150 tokens": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=150, d=64), None),
+    "haar d256 fp16 K3 V4, 131 tokens": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=131, d=256, k_bits=3,
+                                                                        v_bits=4), None),
 }
 
 
