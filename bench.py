@@ -1,12 +1,15 @@
 """Benchmark of the TurboQuant KV-cache path on one MI355X.
 
-One step = quantize the layer's keys, quantize its values, dequantize both
-caches (into the input's dtype), flush the last-level cache, then run decode
-attention over the compressed cache, on synthetic inputs already resident in
-HBM.  The flush (plain reads of 2 GiB of unrelated data by the probe kernel,
-outside the decode's timing events) leaves the 256 MB last-level cache with
-none of the packed cache and no dirty lines: the decode reads its whole cache
-from HBM and pays for no earlier kernel's write-back.  The default workload is the Llama-3-8B-shaped layer (batch
+One step = quantize the layer's keys, quantize its values, flush the
+last-level cache, run decode attention over the compressed cache, then
+dequantize both caches (into the input's dtype), on synthetic inputs already
+resident in HBM.  The flush (plain reads of 2 GiB of unrelated data by the
+probe kernel, outside the decode's timing events) leaves the 256 MB
+last-level cache with none of the packed cache and no dirty lines: the decode
+reads its whole cache from HBM and pays for no earlier kernel's write-back.
+(Decode runs 5-15% slower for about a millisecond after heavy kernels, most
+after the dequantize's 8.6 GB of writes; the workloads section times it
+alone, back to back and after writes as well.)  The default workload is the Llama-3-8B-shaped layer (batch
 16, 32 query / 8 KV heads, d=128, 131072 keys, fp16 inputs with per-channel
 LogNormal(0, 0.5) scales, keys 3-bit MSE + 1-bit QJL, values 3-bit, Haar
 rotation).
@@ -445,11 +448,11 @@ def main():
         if ev: ev[1].record(stream)
         L.quantize_v()
         if ev: ev[2].record(stream)
-        L.dequantize()
-        if ev: ev[3].record(stream)
         probe.flush(stream)
-        if ev: ev[4].record(stream)
+        if ev: ev[3].record(stream)
         L.decode()
+        if ev: ev[4].record(stream)
+        L.dequantize()
         if ev: ev[5].record(stream)
 
     log(f"warmup {args.warmup} steps")
@@ -466,8 +469,8 @@ def main():
     wall = time.perf_counter() - t0
     qk_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     qv_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    dq_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
-    dec_ms = sum(e[4].elapsed_time(e[5]) for e in events) / args.steps
+    dec_ms = sum(e[3].elapsed_time(e[4]) for e in events) / args.steps
+    dq_ms = sum(e[4].elapsed_time(e[5]) for e in events) / args.steps
     kb, vb = packed_bytes_per_token(cfg)
     rows = cfg.rows
     packed = (kb + vb) * rows
