@@ -278,7 +278,12 @@ class Layer:
         self.Vx = Vx if Vx is not None else workloads.kv_torch(cfg, 0, "V", dev)
         self.q = q if q is not None else workloads.q_torch(cfg, 0, dev)
         rot = B.TQ_ROT_HAAR if cfg.rot == "haar" else B.TQ_ROT_HADAMARD
-        self.layer = B.make_rotation(d, rot, cfg.layer_seed, cfg.k_bits, cfg.k_qjl, cfg.v_bits)
+        flags = ((B.TQ_LAYER_BETA_CODEBOOK if cfg.codebook == "beta" else 0) | (B.TQ_LAYER_DITHER if cfg.dither else 0)
+                 | (B.TQ_LAYER_VALUE_QJL if cfg.v_qjl else 0))
+        t = time.perf_counter()
+        self.layer = B.make_rotation(d, rot, cfg.layer_seed, cfg.k_bits, cfg.k_qjl, cfg.v_bits, flags=flags)
+        torch.cuda.synchronize()
+        self.layer_ms = (time.perf_counter() - t) * 1e3  # host tables and codebooks, and their upload
         self.Kc = B.Cache(self.layer, B.TQ_KEYS, S, cap)
         self.Vc = B.Cache(self.layer, B.TQ_VALUES, S, cap)
         view = lambda x: x.view(S, cap, d)[:, : cfg.N] if cap == cfg.N else x.view(S, cap, d)[:, : cfg.N].contiguous()
@@ -298,6 +303,10 @@ class Layer:
     def dequantize(self):
         self.B.dequantize(self.layer, self.B.TQ_KEYS, self.Kc, self.cfg.N, out=self.xhat)
         self.B.dequantize(self.layer, self.B.TQ_VALUES, self.Vc, self.cfg.N, out=self.xhat)
+
+    def dequantize_prod(self, which):
+        cache = self.Kc if which == self.B.TQ_KEYS else self.Vc
+        self.B.dequantize(self.layer, which, cache, self.cfg.N, out=self.xhat, prod=True)
 
     def decode(self):
         self.B.attn_decode(self.layer, self.q, self.Kc, self.Vc, self.cfg.N, self.cfg.Hkv, self.cfg.causal,
@@ -378,6 +387,104 @@ def measure_workload(L, stream, probe, iters, stream_gbs, rw=None):
     if cfg.name == "C2":
         rec["decode_ms_graph"] = round(graph_decode_ms(L, 20), 4)
     return rec
+
+
+def measure_next_rows(stage, W, stream, probe, iters, dev):
+    """The rows past the hot path, each on the workload it extends: NEXT-2
+    (reconstruction with the QJL term) and NEXT-3 (exact-law codebooks) at C3,
+    NEXT-4 (dithered Hadamard) at C5, NEXT-1 (append one token per step, then
+    decode) and NEXT-2 on values at C2's shape."""
+    import torch
+    import workloads
+    B = W.B if W is not None else None
+    out = {}
+    if stage == "C3":
+        cfg = W.cfg
+        in_b = 2 if cfg.dtype == "f16" else 4
+        kb, _ = packed_bytes_per_token(cfg)
+        plain = timed(stream, lambda: B.dequantize(W.layer, B.TQ_KEYS, W.Kc, cfg.N, out=W.xhat), iters)
+        prod = timed(stream, lambda: W.dequantize_prod(B.TQ_KEYS), iters)
+        out["NEXT-2 keys"] = {
+            "what": "tq_dequantize_prod of C3's keys (3-bit codes + QJL signs) into fp16 rows",
+            "ms": round(prod, 4), "mse_only_ms": round(plain, 4),
+            "gbs": round(cfg.rows * (kb + 2 * cfg.d * in_b) / (prod * 1e-3) / 1e9, 1)}
+        Lb = Layer(cfg.with_(codebook="beta"), dev, Kx=W.Kx, Vx=W.Vx, q=W.q)
+        Lb.quantize_k()
+        Lb.quantize_v()
+        qk = timed(stream, Lb.quantize_k, iters)
+        qv = timed(stream, Lb.quantize_v, iters)
+        dec = timed(stream, Lb.decode, iters, before=lambda: probe.flush(stream))
+        kb, vb = packed_bytes_per_token(cfg)
+        out["NEXT-3 exact-law codebook"] = {
+            "what": "C3 with codebooks for the exact coordinate law (host Lloyd-Max solver at layer creation)",
+            "layer_build_ms": round(Lb.layer_ms, 1), "quantize_k_ms": round(qk, 4), "quantize_v_ms": round(qv, 4),
+            "decode_ms": round(dec, 4), "decode_gbs": round((kb + vb) * cfg.rows / (dec * 1e-3) / 1e9, 1)}
+        del Lb
+    elif stage == "C5":
+        cfg = W.cfg.with_(dither=1)
+        Ld = Layer(cfg, dev, Kx=W.Kx, Vx=W.Vx, q=W.q)
+        Ld.quantize_k()
+        Ld.quantize_v()
+        qk = timed(stream, Ld.quantize_k, iters)
+        qv = timed(stream, Ld.quantize_v, iters)
+        dec = timed(stream, Ld.decode, iters, before=lambda: probe.flush(stream))
+        deq = timed(stream, Ld.dequantize, iters)
+        kb, vb = packed_bytes_per_token(cfg)
+        out["NEXT-4 dithered Hadamard"] = {
+            "what": "C5 with the dithered randomized Hadamard (per-token offset before quantizing)",
+            "quantize_k_ms": round(qk, 4), "quantize_v_ms": round(qv, 4), "decode_ms": round(dec, 4),
+            "decode_gbs": round((kb + vb) * cfg.rows / (dec * 1e-3) / 1e9, 1), "dequantize_ms": round(deq, 4)}
+        del Ld
+    else:  # after the workloads: C2's shape
+        from compressed_attention_turboquant_amd import binding as B
+        base = workloads.CONFIGS["C2"]
+        # values with QJL (TurboQuant_prod on V; quantize and decode on the reference kernels)
+        Lv = Layer(base.with_(v_qjl=1), dev)
+        Lv.quantize_k()
+        Lv.quantize_v()
+        qv = timed(stream, Lv.quantize_v, iters)
+        dec = timed(stream, Lv.decode, iters, before=lambda: probe.flush(stream))
+        prod = timed(stream, lambda: Lv.dequantize_prod(B.TQ_VALUES), iters)
+        out["NEXT-2 values"] = {
+            "what": "C2's shape with QJL on values: quantize V, decode, tq_dequantize_prod of V",
+            "quantize_v_ms": round(qv, 4), "decode_ms": round(dec, 4), "dequantize_prod_ms": round(prod, 4)}
+        del Lv
+        # append one token per step into caches with room for 64 more, then decode
+        steps = 16
+        cfg = base.with_(N=base.N + 64)
+        S, d, N0 = cfg.B * cfg.Hkv, cfg.d, base.N
+        Kx = workloads.kv_torch(cfg, 0, "K", dev).view(S, cfg.cap, d)
+        Vx = workloads.kv_torch(cfg, 0, "V", dev).view(S, cfg.cap, d)
+        q = workloads.q_torch(base, 0, dev)
+        rot = B.TQ_ROT_HAAR if cfg.rot == "haar" else B.TQ_ROT_HADAMARD
+        layer = B.make_rotation(d, rot, cfg.layer_seed, cfg.k_bits, cfg.k_qjl, cfg.v_bits)
+        Kc, Vc = B.Cache(layer, B.TQ_KEYS, S, cfg.cap), B.Cache(layer, B.TQ_VALUES, S, cfg.cap)
+        B.quantize_kv(layer, B.TQ_KEYS, Kx[:, :N0].contiguous(), Kc)
+        B.quantize_kv(layer, B.TQ_VALUES, Vx[:, :N0].contiguous(), Vc)
+        toks_k = [Kx[:, N0 + i:N0 + i + 1].contiguous() for i in range(steps)]
+        toks_v = [Vx[:, N0 + i:N0 + i + 1].contiguous() for i in range(steps)]
+        o = torch.empty((cfg.B, cfg.Hq, cfg.Tq, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(B.decode_workspace_bytes(layer, cfg.B, cfg.Hq, cfg.Hkv, cfg.Tq, N0 + i + 1)
+                             for i in range(steps)), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            B.quantize_kv(layer, B.TQ_KEYS, toks_k[i], Kc, t0=N0 + i)
+            ev[i][1].record(stream)
+            B.quantize_kv(layer, B.TQ_VALUES, toks_v[i], Vc, t0=N0 + i)
+            ev[i][2].record(stream)
+            B.attn_decode(layer, q, Kc, Vc, N0 + i + 1, cfg.Hkv, 0, out=o, workspace=ws)
+            ev[i][3].record(stream)
+        torch.cuda.synchronize()
+        mean = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in ev[1:]) / (steps - 1) * 1e3
+        out["NEXT-1 append and decode"] = {
+            "what": f"C2's shape, {steps} steps: append one token per (batch, KV head) to K and V at t0 = N, "
+                    "N + 1, ..., then decode over the cache so far",
+            "append_k_us": round(mean(0, 1), 1), "append_v_us": round(mean(1, 2), 1),
+            "decode_us": round(mean(2, 3), 1), "step_us": round(mean(0, 3), 1)}
+        del Kx, Vx, Kc, Vc, ws
+    return out
 
 
 def graph_decode_ms(L, calls):
@@ -544,7 +651,7 @@ def main():
         res["quantize_frac_of_stream_rw"] = round(q_gbs / rw["read4_write1"], 4)
         res["dequantize_frac_of_stream_rw"] = round(dq_gbs / rw["read1_write4"], 4)
         log(f"read/write streaming probe: {rw} GB/s")
-        wl = {}
+        wl, nxt = {}, {}
         for name in ("C1", "C2", "C3", "C4", "C5"):
             c = workloads.CONFIGS[name]
             if name == cfg.name:
@@ -553,6 +660,8 @@ def main():
                 log(f"workload {name}: generating and quantizing")
                 W = Layer(c, dev)
             wl[name] = measure_workload(W, stream, probe, args.workload_iters, sgbs, rw)
+            if name in ("C3", "C5"):
+                nxt.update(measure_next_rows(name, W, stream, probe, 3, dev))
             r = wl[name]
             log(f"  {name}: decode {r['decode_ms']:.4f} ms after a cache flush ({r['decode_gbs']:.0f} GB/s), "
                 f"{r['decode_ms_back_to_back']:.4f} ms back to back; quantize {r['quantize_k_ms']:.3f} + "
@@ -562,6 +671,9 @@ def main():
                 del W
                 torch.cuda.empty_cache()
         res["workloads"] = wl
+        nxt.update(measure_next_rows("C2", None, stream, probe, 3, dev))
+        res["next_rows"] = nxt
+        log(f"next rows: {json.dumps(nxt)}")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a sample)")
         res["cpu_baseline"] = cpu_baseline(cfg, L.Kx, L.Vx, L.q)
