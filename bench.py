@@ -315,8 +315,12 @@ class Layer:
 
 def timed(stream, fn, iters, before=None):
     """Mean duration (ms) of fn() over iters calls, each bracketed by HIP events
-    on `stream`; before() (untimed) runs ahead of each call."""
+    on `stream`; before() (untimed) runs ahead of each call.  One untimed call
+    first: the first launch of a kernel in a process also loads its code."""
     import torch
+    if before:
+        before()
+    fn()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for e0, e1 in ev:
         if before:
