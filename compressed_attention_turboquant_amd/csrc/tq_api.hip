@@ -567,9 +567,18 @@ tq_status tq_dequantize_prod(const tq_layer* layer, int32_t which, const tq_cach
   tq_status s = check_dequantize(layer, which, cache, n, out, out_dtype, true);
   if (s != TQ_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  s = hip_status(launch_dequant(dequant_args(layer, which, cache, n, out, out_dtype), st), "dequantize launch");
-  if (s != TQ_OK) return s;
   const BlobLayout BL = blob_layout(layer->d);
+  DequantArgs a = dequant_args(layer, which, cache, n, out, out_dtype);
+  if (which == TQ_KEYS && layer->rot != TQ_ROT_HADAMARD && layer->d == 128 && !a.dither) {
+    // One pass: the matrix-core dequantize adds the QJL term before it stores.
+    a.qjl = 1;
+    a.sign = cache->sign;
+    a.rnorm = cache->rnorm;
+    a.St = blob_f(layer, BL.proj_t);
+    return hip_status(launch_dequant(a, st), "dequantize launch");
+  }
+  s = hip_status(launch_dequant(a, st), "dequantize launch");
+  if (s != TQ_OK) return s;
   DequantQjlArgs q{};
   q.sign = cache->sign;
   q.norm = cache->norm;

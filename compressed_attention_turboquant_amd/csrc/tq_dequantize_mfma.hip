@@ -67,9 +67,77 @@ __device__ __forceinline__ void sfor(F&& f) {
   }
 }
 
+// QJL term of the two-stage reconstruction ([Mobilint] "Two-Stage Approach",
+// stage 2 and the final reconstruction):
+//   x_hat += n * sqrt(pi/2)/d * gamma * S^T sigma.
+//
+// Y^T[j][t] = sum_k S^T[j][k] sigma_t[k] runs on v_mfma_f32_16x16x32_f16 with
+// output coordinates as rows and tokens as columns.  The B operand comes
+// straight from the packed sign bits: a half whose only set bit is exponent
+// bit p is 2^(2^(p-10) - 15), so rotating a token's 32 sign bits and masking
+// bits 10+w and 26+w (w = 0..3) gives four dwords of such powers (or 0), one
+// AND each.  The A operand carries S^T times the inverse powers (and 1/8, so
+// that it stays inside the fp16 range), split hi + lo; the product is
+// M = sum over sigma = +1 of S^T / 8, and S^T sigma = 16 M - sum_k S^T[j][k].
+// Lane (row block, k-group g4) of k-block kb covers coordinate
+// 32 kb + ((10 + w + 16 h + 4 g4) mod 32) with its element e = 2 w + h; the
+// four k-groups together cover the block's 32 coordinates.
+constexpr float kSignScale = 0.125f;
+
+__device__ __forceinline__ float sign_power_inverse(int w) {  // 2^(15 - 2^w)
+  return w == 0 ? 16384.f : w == 1 ? 8192.f : w == 2 ? 2048.f : 128.f;
+}
+
+// Stationary A operand of the QJL product for rows j = 32 wave + 16 jb + l16
+// of S^T, in the coordinate order of the sign operand, and the row sums of S^T
+// for the lane's accumulator rows (32 wave + 16 jb + 4 g4 + r).
+template <int D>
+__device__ __forceinline__ void sign_operand(const float* St, int wave, int l16, int g4, h8 (&shi)[2][D / 32],
+                                             h8 (&slo)[2][D / 32], float (&rs)[2][4]) {
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb) {
+    const int row = 32 * wave + 16 * jb + l16;
+    float part = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) {
+      h8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e / 2, h = e % 2;
+        const int coord = 32 * kb + ((10 + w + 16 * h + 4 * g4) & 31);
+        const float v = St[(size_t)row * D + coord];
+        part += v;
+        const float x = v * kSignScale * sign_power_inverse(w);
+        hi[e] = (_Float16)x;
+        lo[e] = (_Float16)(x - (float)hi[e]);
+      }
+      shi[jb][kb] = hi;
+      slo[jb][kb] = lo;
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rs[jb][r] = __shfl(part, 4 * g4 + r);
+  }
+}
+
+// B operand of the QJL product from one sign dword of a token (k-group g4).
+__device__ __forceinline__ h8 sign_b(uint32_t sw, int g4) {
+  const uint32_t rot = __builtin_amdgcn_alignbit(sw, sw, 4 * g4);
+  u4 b;
+  sfor<0, 4>([&](auto w) {
+    constexpr int W = decltype(w)::value;
+    b[W] = rot & ((1u << (10 + W)) | (1u << (26 + W)));
+  });
+  return __builtin_bit_cast(h8, b);
+}
+
 // DITHER: the dithered variant, x_hat = n * R^T (c[idx] + delta): the offset
 // term n * delta * (R^T 1)_j is added with the row sums of R^T.
-template <int D, int BITS, int VALUES, int OUT16, int DITHER>
+// QJL: keys with QJL, the two-stage reconstruction in one pass: each tile's
+// sign dwords go to LDS beside its codes, and the QJL product runs on the
+// same accumulator rows with its own chain, so the rows are stored once.
+template <int D, int BITS, int VALUES, int OUT16, int DITHER, int QJL>
 __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   constexpr int W = D / 32;           // waves: each owns 32 output coordinates
   constexpr int T = 64 * W;           // threads: 2 D, one per 32 codes of a tile
@@ -83,6 +151,9 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   __shared__ __align__(16) _Float16 bhi[kTile][PITCH], blo[OUT16 ? 1 : kTile][OUT16 ? 8 : PITCH];
   __shared__ float nsh[kTile];
   __shared__ float dsh[DITHER ? kTile : 1];  // dithered variant: the tile's offsets, times kFactor^2
+  // QJL: the tile's sign dwords (token, k-block) and n sqrt(pi/2)/d gamma.
+  __shared__ __align__(16) uint32_t sgs[QJL ? kTile : 1][NKB];
+  __shared__ float fsh[QJL ? kTile : 1];
   // fp16 rows: the finished tile is staged here and written back as whole
   // rows, 16 bytes per lane (the accumulator layout would write 8-byte pieces
   // of 16 rows per instruction, which measured at about half the HBM rate).
@@ -141,6 +212,10 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
     }
   }
   const float dwidth = DITHER ? *a.dither_w : 0.f;
+  h8 shi[2][NKB], slo[2][NKB];
+  float qrs[2][4];
+  if constexpr (QJL) sign_operand<D>(a.St, wave, l16, g4, shi, slo, qrs);
+  const float kappa = sqrtf(0.5f * (float)M_PI) / (float)D;
 
   const int64_t n = a.n, cap = a.cap;
   const int64_t tiles = (n + kTile - 1) / kTile;
@@ -166,6 +241,8 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   // memory instructions and the compiler's waits can count them.
   uint32_t w[BITS];
   float nrm = 0.f;
+  uint32_t sgw = 0;  // QJL: the thread's sign dword (token tid / NKB, k-block tid % NKB)
+  float rn = 0.f;    // QJL: a token's gamma (threads < 64)
   auto load_codes = [&](int64_t it, int64_t sq, int64_t tl) {
     const bool live = it < items;  // uniform
     const int64_t t0 = tl * kTile;
@@ -191,6 +268,13 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
     for (int i = 0; i < BITS; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, off + 4 * i, 0, 0);
     nrm = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(record(a.norm + sq * cap + t0, 4 * rows),
                                                                tid < kTile ? 4u * tid : kOob, 0, 0));
+    if constexpr (QJL) {
+      const int tt = tid / NKB, q = tid % NKB;
+      sgw = __builtin_amdgcn_raw_buffer_load_b32(record(a.sign + (sq * cap + t0) * (D / 8), rows * (D / 8)),
+                                                 tt < rows ? (uint32_t)(tt * (D / 8) + 4 * q) : kOob, 0, 0);
+      rn = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(record(a.rnorm + sq * cap + t0, 4 * rows),
+                                                                tid < kTile ? 4u * tid : kOob, 0, 0));
+    }
   };
   load_codes(item, seq, tile);
   if constexpr (!OUT16) {
@@ -261,6 +345,10 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
       if constexpr (DITHER) {
         if (tid < kTile) dsh[tid] = dither_offset(a.dither_s0, seq, t0 + tid, dwidth) * (kFactor * cs);
       }
+      if constexpr (QJL) {
+        sgs[tid / NKB][tid % NKB] = sgw;
+        if (tid < kTile) fsh[tid] = nrm * kappa * rn;
+      }
     }
     lds_barrier();
     load_codes(nitem, nseq, ntile);
@@ -282,9 +370,11 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
       const float dl = DITHER ? dsh[tok] : 0.f;
       // Four independent accumulation chains (per row block: hi*hi, and the
       // correction products) so that no product waits on the one before it.
-      f4 acc[2], cor[2];
+      f4 acc[2], cor[2], qacc[2];
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) acc[jb] = cor[jb] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int jb = 0; jb < 2; ++jb) acc[jb] = cor[jb] = qacc[jb] = f4{0.f, 0.f, 0.f, 0.f};
+      u4 sg4 = {0u, 0u, 0u, 0u};
+      if constexpr (QJL) sg4 = *reinterpret_cast<const u4*>(&sgs[tok][0]);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -295,7 +385,17 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
           cor[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[jb][kb], bh[kb], cor[jb], 0, 0, 0);
+        if constexpr (QJL) {
+          const uint32_t sw = sg4[kb];
+          const h8 sb = sign_b(sw, g4);
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb) {
+            qacc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi[jb][kb], sb, qacc[jb], 0, 0, 0);
+            qacc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(slo[jb][kb], sb, qacc[jb], 0, 0, 0);
+          }
+        }
       }
+      const float fq = QJL ? fsh[tok] : 0.f;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
         const int col = 32 * wave + 16 * jb + 4 * g4;
@@ -303,6 +403,10 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
         f4 v = acc[jb] + cor[jb];
         if constexpr (DITHER) v += dl * rsum[jb];
         v *= nt;
+        if constexpr (QJL) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = fmaf(fq, fmaf(qacc[jb][r], 2.f / kSignScale, -qrs[jb][r]), v[r]);
+        }
         if constexpr (OUT16) {
           const u2 hv = {hbits((_Float16)v[0]) | (hbits((_Float16)v[1]) << 16),
                          hbits((_Float16)v[2]) | (hbits((_Float16)v[3]) << 16)};
@@ -327,9 +431,9 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
 
 // Persistent grid: as many workgroups as the CUs hold at once, or one per
 // tile if there are fewer.
-template <int D, int BITS, int VALUES, int OUT16, int DITHER>
+template <int D, int BITS, int VALUES, int OUT16, int DITHER, int QJL = 0>
 hipError_t launch(const DequantArgs& a, hipStream_t st) {
-  auto kern = dequant_mfma_kernel<D, BITS, VALUES, OUT16, DITHER>;
+  auto kern = dequant_mfma_kernel<D, BITS, VALUES, OUT16, DITHER, QJL>;
   int dev = 0, cus = 256, per_cu = 0;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
@@ -352,6 +456,15 @@ hipError_t dispatch_out(const DequantArgs& a, hipStream_t st) {
 
 template <int D, int BITS>
 hipError_t dispatch_layout(const DequantArgs& a, hipStream_t st) {
+  if (a.qjl) {
+    // The fused pass: keys of undithered layers at d = 128 only (the sign
+    // operand's registers beside R^T's fit there).
+    if constexpr (D == 128) {
+      if (a.value_layout || a.dither) return hipErrorInvalidValue;
+      return a.out_dtype == TQ_F16 ? launch<D, BITS, 0, 1, 0, 1>(a, st) : launch<D, BITS, 0, 0, 0, 1>(a, st);
+    }
+    return hipErrorInvalidValue;
+  }
   return a.dither ? dispatch_out<D, BITS, 1>(a, st) : dispatch_out<D, BITS, 0>(a, st);
 }
 
@@ -365,29 +478,8 @@ hipError_t dispatch_bits(const DequantArgs& a, hipStream_t st) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// QJL term of the two-stage reconstruction ([Mobilint] "Two-Stage Approach",
-// stage 2 and the final reconstruction):
-//   x_hat += n * sqrt(pi/2)/d * gamma * S^T sigma,
-// added to rows that dequant_mfma_kernel has written (the MSE part).
-//
-// Y^T[j][t] = sum_k S^T[j][k] sigma_t[k] runs on v_mfma_f32_16x16x32_f16 with
-// output coordinates as rows and tokens as columns.  The B operand comes
-// straight from the packed sign bits: a half whose only set bit is exponent
-// bit p is 2^(2^(p-10) - 15), so rotating a token's 32 sign bits and masking
-// bits 10+w and 26+w (w = 0..3) gives four dwords of such powers (or 0), one
-// AND each.  The A operand carries S^T times the inverse powers (and 1/8, so
-// that it stays inside the fp16 range), split hi + lo; the product is
-// M = sum over sigma = +1 of S^T / 8, and S^T sigma = 16 M - sum_k S^T[j][k].
-// Lane (row block, k-group g4) of k-block kb covers coordinate
-// 32 kb + ((10 + w + 16 h + 4 g4) mod 32) with its element e = 2 w + h; the
-// four k-groups together cover the block's 32 coordinates.
-constexpr float kSignScale = 0.125f;
-
-__device__ __forceinline__ float sign_power_inverse(int w) {  // 2^(15 - 2^w)
-  return w == 0 ? 16384.f : w == 1 ? 8192.f : w == 2 ? 2048.f : 128.f;
-}
-
+// The QJL term alone, added to rows that dequant_mfma_kernel or
+// dequant_fwht_kernel has written (the cases without the fused pass).
 template <int D, int OUT16>
 __global__ void __launch_bounds__(2 * D) dequant_qjl_kernel(DequantQjlArgs a) {
   constexpr int NKB = D / 32;      // k-blocks, = sign dwords per token
@@ -395,35 +487,9 @@ __global__ void __launch_bounds__(2 * D) dequant_qjl_kernel(DequantQjlArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int l16 = lane % 16, g4 = lane / 16;
 
-  // Stationary A operand: rows j = 32 wave + 16 jb + l16 of S^T, and the row
-  // sums the lane's accumulator rows (32 wave + 16 jb + 4 g4 + r) need.
   h8 shi[2][NKB], slo[2][NKB];
   float rs[2][4];
-#pragma unroll
-  for (int jb = 0; jb < 2; ++jb) {
-    const int row = 32 * wave + 16 * jb + l16;
-    float part = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      h8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e / 2, h = e % 2;
-        const int coord = 32 * kb + ((10 + w + 16 * h + 4 * g4) & 31);
-        const float v = a.St[(size_t)row * D + coord];
-        part += v;
-        const float x = v * kSignScale * sign_power_inverse(w);
-        hi[e] = (_Float16)x;
-        lo[e] = (_Float16)(x - (float)hi[e]);
-      }
-      shi[jb][kb] = hi;
-      slo[jb][kb] = lo;
-    }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rs[jb][r] = __shfl(part, 4 * g4 + r);
-  }
+  sign_operand<D>(a.St, wave, l16, g4, shi, slo, rs);
 
   const float kappa = sqrtf(0.5f * (float)M_PI) / (float)D;
   const int64_t n = a.n, cap = a.cap;
@@ -446,13 +512,7 @@ __global__ void __launch_bounds__(2 * D) dequant_qjl_kernel(DequantQjlArgs a) {
       acc[0] = acc[1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const uint32_t rot = __builtin_amdgcn_alignbit(sw[kb], sw[kb], 4 * g4);
-        u4 b;
-        sfor<0, 4>([&](auto w) {
-          constexpr int W = decltype(w)::value;
-          b[W] = rot & ((1u << (10 + W)) | (1u << (26 + W)));
-        });
-        const h8 bh = __builtin_bit_cast(h8, b);
+        const h8 bh = sign_b(sw[kb], g4);
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
           acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi[jb][kb], bh, acc[jb], 0, 0, 0);

@@ -547,6 +547,8 @@ def test_dequantize_shapes(name, which):
 PROD_CASES = {
     "haar d128 fp16 K2+QJL": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=203, k_bits=2), None, B.TQ_KEYS),
     "haar d128 fp16 K3+QJL, first 100 of 130": (workloads.CONFIGS["C3"].with_(B=1, N=130), 100, B.TQ_KEYS),
+    "haar d128 fp32 K1+QJL": (workloads.CONFIGS["C1"].with_(N=150, k_bits=1), None, B.TQ_KEYS),
+    "haar d128 fp32 K4+QJL, first 129 of 200": (workloads.CONFIGS["C1"].with_(N=200, k_bits=4), 129, B.TQ_KEYS),
     "hadamard d256 fp16 K3+QJL": (workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=77, k_qjl=1, k_bits=3), None,
                                   B.TQ_KEYS),
     "haar d64 fp32 K1+QJL": (workloads.CONFIGS["C1"].with_(d=64, Hq=2, Hkv=2, N=70, k_bits=1), None, B.TQ_KEYS),
