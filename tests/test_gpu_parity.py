@@ -587,7 +587,13 @@ def test_dequantize_prod(name):
     assert (np.abs(mse - got) / kf["norm"][keep][:, None]).max() > 1e-2
     half = B.dequantize(layer, which, cache, n_out, out_dtype=torch.float16, prod=True).cpu().numpy()
     np.testing.assert_allclose(half.reshape(-1, d), got, rtol=2e-3, atol=2e-3)
-    H.log(f"  max error / norm {err.max():.2e} (band rows: codes {st['code_rows']}, signs {st['sign_rows']})")
+    # fp16 rows: the output's rounding (2^-11 of each coordinate) plus 2e-4 of
+    # the norm for the single fp16 copies of the centroids and of S^T
+    herr = np.abs(half.reshape(-1, d).astype(np.float64) - ref) - 2.0 ** -11 * np.abs(ref)
+    hmax = (herr / np.maximum(kf["norm"][keep][:, None], 1e-30)).max()
+    assert hmax < 2e-4, f"{name}: fp16 rows off by {hmax:.2e} of the norm beyond their rounding"
+    H.log(f"  max error / norm {err.max():.2e}, fp16 rows {hmax:.2e} beyond rounding "
+          f"(band rows: codes {st['code_rows']}, signs {st['sign_rows']})")
 
 
 APPEND_CASES = {
