@@ -14,7 +14,12 @@ inputs itself and decodes from its own codes:
     2e-3, and the scores of those rows, from a second decode call with the
     scores output on -- both against the oracle's decode of the cache the GPU
     wrote (validated codes and signs, the oracle's norms and gammas), every
-    key included.
+    key included;
+  * the dequantized rows of those sequences, keys and values, into the
+    input's dtype (as the bench step writes them), and for keys with QJL the
+    two-stage reconstruction: against the oracle's reconstruction of the same
+    fields, to 2e-6 of the norm for fp32 rows and to the fp16 rounding plus
+    1.1e-4 (MSE) or 2e-4 (two-stage) of the norm for fp16 rows.
 """
 import numpy as np
 import pytest
@@ -52,6 +57,19 @@ def _seq_value_codes(cache, s, cap, N, d, bits):
     return codec.unpack_value_codes(raw, bits, 1, cap, d)[0, :N]
 
 
+def _check_rows(got, ref, norm, half, extra, what):
+    """Largest error of dequantized rows against the oracle's, as a fraction
+    of the norm beyond what the output dtype allows."""
+    scale = np.maximum(norm[:, None], 1e-30)
+    if half:
+        over = (np.abs(got - ref) - 2.0 ** -11 * np.abs(ref) - 2.0 ** -25) / scale
+        assert over.max() <= extra, f"{what}: fp16 rows off by {over.max():.2e} of the norm beyond rounding"
+        return over.max()
+    err = np.abs(got - ref) / scale
+    assert err.max() < 2e-6, f"{what}: error {err.max():.2e} of the norm"
+    return err.max()
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
 def test_full_size_sampled(name):
@@ -73,6 +91,7 @@ def test_full_size_sampled(name):
     torch.cuda.synchronize()
     Sk = ol.S if cfg.k_qjl else None
     worst_rel, worst_out = 0.0, 0.0
+    fields = {}
     for s in _sampled_sequences(cfg):
         b, h = divmod(s, cfg.Hkv)
         H.log(f"  sequence {s} (batch {b}, KV head {h})")
@@ -101,4 +120,24 @@ def test_full_size_sampled(name):
         worst_rel = max(worst_rel, H.compare_scores(gs, ref_scores, scale, f"{name} scores s={s}"))
         H.log(f"    keys with a band code difference {st['code_rows']}, with a band sign difference "
               f"{st['sign_rows']}; values with a band code difference {vflips}")
+        fields[s] = (kf, vf)
     H.log(f"  worst score rel {worst_rel:.2e}, worst out abs {worst_out:.2e}")
+
+    half = cfg.dtype == "f16"
+    xhat = torch.empty((S, N, d), dtype=torch.float16 if half else torch.float32, device=dev)
+    runs = [("K", B.TQ_KEYS, Kc, False), ("V", B.TQ_VALUES, Vc, False)]
+    if cfg.k_qjl:
+        runs.append(("K two-stage", B.TQ_KEYS, Kc, True))
+    for what, which, cache, prod in runs:
+        B.dequantize(layer, which, cache, N, out=xhat, prod=prod)
+        torch.cuda.synchronize()
+        worst = 0.0
+        for s, (kf, vf) in fields.items():
+            f = kf if which == B.TQ_KEYS else vf
+            c = ol.ck if which == B.TQ_KEYS else ol.cv
+            ref = (codec.reconstruct_prod(f["idx"], f["norm"], f["sign"], f["rnorm"], ol.R, c, ol.S) if prod
+                   else codec.reconstruct_mse(f["idx"], f["norm"], ol.R, c, dither=f.get("dither")))
+            got = xhat[s].double().cpu().numpy()
+            worst = max(worst, _check_rows(got, ref, f["norm"], half, 2e-4 if prod else 1.1e-4,
+                                           f"{name} dequantize {what} s={s}"))
+        H.log(f"  dequantize {what}: worst {worst:.2e} of the norm" + (" beyond fp16 rounding" if half else ""))
