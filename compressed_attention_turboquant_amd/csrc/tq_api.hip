@@ -569,7 +569,7 @@ tq_status tq_dequantize_prod(const tq_layer* layer, int32_t which, const tq_cach
   hipStream_t st = static_cast<hipStream_t>(stream);
   const BlobLayout BL = blob_layout(layer->d);
   DequantArgs a = dequant_args(layer, which, cache, n, out, out_dtype);
-  if (which == TQ_KEYS && layer->rot != TQ_ROT_HADAMARD && layer->d == 128 && !a.dither) {
+  if (which == TQ_KEYS && layer->rot != TQ_ROT_HADAMARD && layer->d <= 128 && !a.dither) {
     // One pass: the matrix-core dequantize adds the QJL term before it stores.
     a.qjl = 1;
     a.sign = cache->sign;

@@ -140,7 +140,8 @@ __device__ __forceinline__ h8 sign_b(uint32_t sw, int g4) {
 // fp16 rows take S^T's hi part only: each element is then off by at most
 // 2^-11 of itself, which over the d signs puts about 2^-11 sqrt(d) of
 // sqrt(pi/2)/d gamma on a coordinate (near 1e-5 of the norm at 3 bits, d = 128),
-// below the rounding of the fp16 output itself.
+// below the rounding of the fp16 output itself.  Instantiated for d = 64 and
+// 128: at 256, S^T's registers beside R^T's would not fit.
 template <int D, int BITS, int VALUES, int OUT16, int DITHER, int QJL>
 __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
   constexpr int W = D / 32;           // waves: each owns 32 output coordinates
@@ -377,8 +378,9 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
       f4 acc[2], cor[2], qacc[2];
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) acc[jb] = cor[jb] = qacc[jb] = f4{0.f, 0.f, 0.f, 0.f};
-      u4 sg4 = {0u, 0u, 0u, 0u};
-      if constexpr (QJL) sg4 = *reinterpret_cast<const u4*>(&sgs[tok][0]);
+      uint32_t sgv[NKB];  // the token's sign dwords
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sgv[kb] = QJL ? sgs[tok][kb] : 0u;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -390,8 +392,7 @@ __global__ void __launch_bounds__(2 * D) dequant_mfma_kernel(DequantArgs a) {
         for (int jb = 0; jb < 2; ++jb)
           cor[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[jb][kb], bh[kb], cor[jb], 0, 0, 0);
         if constexpr (QJL) {
-          const uint32_t sw = sg4[kb];
-          const h8 sb = sign_b(sw, g4);
+          const h8 sb = sign_b(sgv[kb], g4);
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb) {
             qacc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi[jb][kb], sb, qacc[jb], 0, 0, 0);
@@ -461,9 +462,9 @@ hipError_t dispatch_out(const DequantArgs& a, hipStream_t st) {
 template <int D, int BITS>
 hipError_t dispatch_layout(const DequantArgs& a, hipStream_t st) {
   if (a.qjl) {
-    // The fused pass: keys of undithered layers at d = 128 only (the sign
-    // operand's registers beside R^T's fit there).
-    if constexpr (D == 128) {
+    // The fused pass: keys of undithered layers at d = 64 and 128 (at d = 256
+    // the sign operand's registers beside R^T's do not fit).
+    if constexpr (D <= 128) {
       if (a.value_layout || a.dither) return hipErrorInvalidValue;
       return a.out_dtype == TQ_F16 ? launch<D, BITS, 0, 1, 0, 1>(a, st) : launch<D, BITS, 0, 0, 0, 1>(a, st);
     }

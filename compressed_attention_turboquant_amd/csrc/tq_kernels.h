@@ -65,7 +65,7 @@ struct DequantArgs {
   uint64_t dither_s0;
   const float* dither_w;
   const float* cscale;  // factor s of the codebook's fp16 copies (decode tables), for fp16 rows
-  // Keys with QJL (Haar, d = 128): the two-stage reconstruction in the same
+  // Keys with QJL (Haar, d = 64 or 128): the two-stage reconstruction in the same
   // pass, adding n sqrt(pi/2)/d gamma S^T sigma to each row before it is stored.
   int qjl;
   const uint8_t* sign;  // the rows' sign bits

@@ -252,7 +252,7 @@ tq_status tq_dequantize(const tq_layer* layer, int32_t which, const tq_cache* ca
  * residual's sign bits.  Same arguments as tq_dequantize; `which` must be
  * TQ_KEYS of a layer with k_qjl = 1, or TQ_VALUES of a layer with
  * TQ_LAYER_VALUE_QJL, and the cache must hold sign and rnorm (else
- * TQ_ERR_INVALID_ARG).  Keys of a Haar layer at d = 128: one launch on
+ * TQ_ERR_INVALID_ARG).  Keys of a Haar layer at d = 64 or 128: one launch on
  * `stream` that stores each row once.  Otherwise two: the MSE rows, then the
  * QJL term added to them in place. */
 tq_status tq_dequantize_prod(const tq_layer* layer, int32_t which, const tq_cache* cache, int64_t n,

@@ -552,6 +552,8 @@ PROD_CASES = {
     "hadamard d256 fp16 K3+QJL": (workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=77, k_qjl=1, k_bits=3), None,
                                   B.TQ_KEYS),
     "haar d64 fp32 K1+QJL": (workloads.CONFIGS["C1"].with_(d=64, Hq=2, Hkv=2, N=70, k_bits=1), None, B.TQ_KEYS),
+    "haar d64 fp16 K3+QJL, first 140 of 150": (workloads.CONFIGS["C2"].with_(d=64, Hq=4, Hkv=2, N=150, k_bits=3,
+                                                                              k_qjl=1), 140, B.TQ_KEYS),
     "haar d128 fp16 V3+QJL, first 90 of 203": (workloads.CONFIGS["C2"].with_(Hq=4, Hkv=2, N=203, v_qjl=1), 90,
                                                B.TQ_VALUES),
     "hadamard d256 fp16 V4+QJL": (workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=77, v_qjl=1), None,
