@@ -598,6 +598,42 @@ def test_dequantize_prod(name):
           f"(band rows: codes {st['code_rows']}, signs {st['sign_rows']})")
 
 
+PROD_EDGE_CASES = {
+    "haar d128 fp16 K3+QJL (one pass)": workloads.CONFIGS["C3"].with_(B=1, Hkv=2, Hq=4, N=70),
+    "haar d64 fp32 K2+QJL (one pass)": workloads.CONFIGS["C1"].with_(d=64, N=70),
+    "hadamard d256 fp16 K3+QJL (two passes)": workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=70, k_qjl=1,
+                                                                            k_bits=3),
+}
+
+
+@pytest.mark.parametrize("name", list(PROD_EDGE_CASES))
+def test_dequantize_prod_edges(name):
+    """n = 0 writes nothing and succeeds; token 0 of every sequence is a zero
+    input row (norm 0), which comes back as exact zeros in both output dtypes;
+    a two-token prefix matches the oracle on token 1."""
+    cfg = PROD_EDGE_CASES[name]
+    H.log(f"[dequantize prod edges] {name}")
+    x = _kv(cfg, "K", seed=23)
+    x[:, 0] = 0
+    S, n, d = x.shape
+    layer, ol, cache, enc, cap = H.run_quantize_both(cfg, x, B.TQ_KEYS)
+    rows = _rows(S, cap, n)
+    kf, _ = H.check_keys(H.gpu_codes_key(cache, S, cap, d, cfg.k_bits, rows), cache["norm"].cpu().numpy()[rows],
+                         enc, ol, name, H.gpu_signs(cache, S, cap, d, rows), cache["rnorm"].cpu().numpy()[rows])
+    keep = np.array([s * n + 1 for s in range(S)], dtype=np.int64)
+    ref = codec.reconstruct_prod(kf["idx"][keep], kf["norm"][keep], kf["sign"][keep], kf["rnorm"][keep],
+                                 ol.R, ol.ck, ol.S)
+    for dt in (torch.float32, torch.float16):
+        empty = B.dequantize(layer, B.TQ_KEYS, cache, 0, out_dtype=dt, prod=True)
+        assert tuple(empty.shape) == (S, 0, d)
+        two = B.dequantize(layer, B.TQ_KEYS, cache, 2, out_dtype=dt, prod=True).cpu().double().numpy()
+        assert np.all(two[:, 0] == 0), f"{name}: zero rows came back nonzero"
+        err = np.abs(two[:, 1] - ref) / kf["norm"][keep][:, None]
+        bar = 2e-6 if dt == torch.float32 else 2.0 ** -11 * np.abs(ref).max() / kf["norm"][keep].min() + 2e-4
+        assert err.max() < bar, f"{name} {dt}: token 1 off by {err.max():.2e} of the norm"
+    H.log(f"  zero rows exact, token 1 within the bars")
+
+
 APPEND_CASES = {
     "haar-d128-f16": workloads.CONFIGS["C2"].with_(N=40),
     "dithered-hadamard-d128-f16": workloads.CONFIGS["C5"].with_(B=1, Hq=4, Hkv=2, N=40, d=128, k_bits=2,
